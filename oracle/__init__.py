@@ -1,0 +1,199 @@
+"""CPU oracle of the BitNet b1.58 BitLinear forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package; the product library never does.  It is a
+thin numpy front-end over ``bitlinear_oracle.c`` (plain C, built by
+``oracle/build.py``) and shares no code with the HIP library.
+
+Every function follows a passage of the source pages (cited by title and
+section in the C file):
+  gamma / ternarize   -- "BitNet b1.58 in Production", The Mathematical
+                         Mechanism, item 1 (absmean scale, RoundClip);
+  pack / unpack       -- "BitNet 1-bit LLM Inference Framework", How the LUT
+                         Kernel Works (codes 00 = 0, 01 = +1, 10 = -1);
+  quant_act           -- "BitNet b1.58 in Production", item 2 (per-token
+                         absmax, Q_b = 127);
+  contract            -- item 3 (add / skip / subtract) and the LUT section's
+                         scalar loop;
+  dequant             -- item 4 (gamma * max|x| / Q_b).
+All of them are pinned by tests in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import ctypes as _ct
+import os as _os
+
+import numpy as np
+
+_HERE = _os.path.dirname(_os.path.abspath(__file__))
+# BITLINEAR_ORACLE_LIB lets the mutation test load a deliberately broken copy.
+_LIB_PATH = _os.environ.get("BITLINEAR_ORACLE_LIB") or _os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_i64 = _ct.c_int64
+_p = _ct.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _os.path.exists(_LIB_PATH):
+        from . import build as _build  # compile on first use (CPU-only, gcc)
+        _build.build()
+    lib = _ct.CDLL(_LIB_PATH)
+    lib.oracle_abs_sum.argtypes = [_p, _i64, _i64, _p]
+    lib.oracle_abs_sum.restype = _ct.c_double
+    lib.oracle_gamma_from_sum.argtypes = [_ct.c_double, _i64, _i64]
+    lib.oracle_gamma_from_sum.restype = _ct.c_float
+    lib.oracle_ternarize.argtypes = [_p, _i64, _i64, _ct.c_float, _p]
+    lib.oracle_ternarize.restype = None
+    lib.oracle_pack_canonical.argtypes = [_p, _i64, _i64, _p]
+    lib.oracle_pack_canonical.restype = None
+    lib.oracle_unpack_canonical.argtypes = [_p, _i64, _i64, _p]
+    lib.oracle_unpack_canonical.restype = _ct.c_int
+    lib.oracle_quant_act.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.oracle_quant_act.restype = None
+    lib.oracle_contract.argtypes = [_p, _p, _i64, _i64, _i64, _p]
+    lib.oracle_contract.restype = _ct.c_int
+    lib.oracle_contract_pairs.argtypes = [_p, _p, _i64, _p, _p, _i64, _p]
+    lib.oracle_contract_pairs.restype = _ct.c_int
+    lib.oracle_dequant.argtypes = [_p, _i64, _i64, _ct.c_float, _p, _p]
+    lib.oracle_dequant.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = _ct.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def abs_sum(w: np.ndarray) -> float:
+    """binary64 sum of |W| (rows left to right, then rows in order)."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    rows = np.empty(n, dtype=np.float64)
+    return float(_load().oracle_abs_sum(_ptr(w), n, k, _ptr(rows)))
+
+
+def gamma(w: np.ndarray) -> np.float32:
+    """Absmean scale: mean |W| in binary64, rounded once to binary32."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    return np.float32(_load().oracle_gamma_from_sum(abs_sum(w), n, k))
+
+
+def gamma_from_sum(s: float, n: int, k: int) -> np.float32:
+    return np.float32(_load().oracle_gamma_from_sum(float(s), n, k))
+
+
+def ternarize(w: np.ndarray, g) -> np.ndarray:
+    """int8 [n][k] = Clip(Round(W / (gamma + 1e-5)), -1, 1)."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    q = np.empty((n, k), dtype=np.int8)
+    _load().oracle_ternarize(_ptr(w), n, k, float(np.float32(g)), _ptr(q))
+    return q
+
+
+def pack_canonical(q: np.ndarray) -> np.ndarray:
+    """uint8 [n][ceil(k/4)]: 4 codes per byte, least significant field first."""
+    q = _c(q, np.int8)
+    n, k = q.shape
+    out = np.empty((n, (k + 3) // 4), dtype=np.uint8)
+    _load().oracle_pack_canonical(_ptr(q), n, k, _ptr(out))
+    return out
+
+
+def unpack_canonical(b: np.ndarray, n: int, k: int) -> np.ndarray:
+    b = _c(b, np.uint8)
+    if b.size != n * ((k + 3) // 4):
+        raise OracleError("packed buffer has the wrong size")
+    q = np.empty((n, k), dtype=np.int8)
+    rc = _load().oracle_unpack_canonical(_ptr(b), n, k, _ptr(q))
+    if rc == -1:
+        raise OracleError("invalid 2-bit code 11 in packed weights")
+    if rc == -2:
+        raise OracleError("non-zero padding field in packed weights")
+    return q
+
+
+def quant_act(x_bits: np.ndarray):
+    """(xq int8 [m][k], a' fp32 [m]) from bf16 bit patterns [m][k]."""
+    x = _c(x_bits, np.uint16)
+    m, k = x.shape
+    xq = np.empty((m, k), dtype=np.int8)
+    amax = np.empty(m, dtype=np.float32)
+    _load().oracle_quant_act(_ptr(x), m, k, _ptr(xq), _ptr(amax))
+    return xq, amax
+
+
+def contract(xq: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """int32 [m][n] = sum_k xq[m][k] * q[n][k] by add / skip / subtract."""
+    xq = _c(xq, np.int8)
+    q = _c(q, np.int8)
+    m, k = xq.shape
+    n, k2 = q.shape
+    if k != k2:
+        raise OracleError("inner sizes differ")
+    acc = np.empty((m, n), dtype=np.int32)
+    rc = _load().oracle_contract(_ptr(xq), _ptr(q), m, n, k, _ptr(acc))
+    if rc == -1:
+        raise OracleError("accumulator bound |acc| <= 127*K violated")
+    if rc == -2:
+        raise OracleError("weight code outside {-1, 0, 1}")
+    return acc
+
+
+def contract_pairs(xq: np.ndarray, q_rows: np.ndarray, rows: np.ndarray,
+                   qrows: np.ndarray) -> np.ndarray:
+    """acc for the listed pairs: sum_k xq[rows[p]][k] * q_rows[qrows[p]][k]."""
+    xq = _c(xq, np.int8)
+    q_rows = _c(q_rows, np.int8)
+    rows = _c(rows, np.int64)
+    qrows = _c(qrows, np.int64)
+    k = xq.shape[1]
+    if q_rows.shape[1] != k or rows.shape != qrows.shape:
+        raise OracleError("shape mismatch")
+    acc = np.empty(rows.shape[0], dtype=np.int32)
+    rc = _load().oracle_contract_pairs(_ptr(xq), _ptr(q_rows), k, _ptr(rows), _ptr(qrows),
+                                       rows.shape[0], _ptr(acc))
+    if rc != 0:
+        raise OracleError("contraction check failed (%d)" % rc)
+    return acc
+
+
+def dequant(acc: np.ndarray, g, amax: np.ndarray) -> np.ndarray:
+    """fp32 [m][n] = acc * gamma * a' / 127 (binary64, rounded once)."""
+    acc = _c(acc, np.int32)
+    amax = _c(amax, np.float32)
+    m, n = acc.shape
+    y = np.empty((m, n), dtype=np.float32)
+    _load().oracle_dequant(_ptr(acc), m, n, float(np.float32(g)), _ptr(amax), _ptr(y))
+    return y
+
+
+def forward(x_bits: np.ndarray, w: np.ndarray, g=None) -> dict:
+    """Whole path on the CPU: gamma, ternary codes, activation codes, int32
+    accumulators and fp32 outputs.  ``g`` overrides gamma (e.g. to ternarize
+    with another computation's gamma when the two differ in the last bit)."""
+    gm = gamma(w) if g is None else np.float32(g)
+    q = ternarize(w, gm)
+    xq, amax = quant_act(x_bits)
+    acc = contract(xq, q)
+    y = dequant(acc, gm, amax)
+    return {"gamma": gm, "q": q, "xq": xq, "amax": amax, "acc": acc, "y": y}
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())

@@ -1,0 +1,59 @@
+"""The oracle pins must be sharp: each plausible mistake planted in a copy of
+the C oracle (a dropped term, a wrong sign, index, constant or rounding rule)
+must make tests/test_oracle_pins.py fail.  Runs on the CPU only; the planted
+copies are built in a temporary directory and never used elsewhere."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "bitlinear_oracle.c")
+
+MUTATIONS = {
+    "weight epsilon dropped": ("const float denom = gamma + 1e-5f;", "const float denom = gamma;"),
+    "round half away from zero": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;",
+                                  "return td > 0 ? fl + 1.0 : fl;"),
+    "Q_b = 128": ("const float s = 127.0f / a;", "const float s = 128.0f / a;"),
+    "ternary clip missing": ("q[r * k + c] = (int8_t)clip(round_half_even(t), -1.0, 1.0);",
+                             "q[r * k + c] = (int8_t)round_half_even(t);"),
+    "gamma of W, not |W|": ("s += fabs((double)row[c]);", "s += ((double)row[c]);"),
+    "gamma divides by n only": ("double mean = abs_sum / ((double)n * (double)k);",
+                                "double mean = abs_sum / ((double)n);"),
+    "act max of x, not |x|": ("float v = fabsf(bf16_to_f32(x[r * k + c]));",
+                              "float v = (bf16_to_f32(x[r * k + c]));"),
+    "act floor dropped": ("if (a < 1e-8f)\n            a = 1e-8f;", ""),
+    "pack field order reversed": ("byte |= code << (2 * i);", "byte |= code << (6 - 2 * i);"),
+    "codes +1/-1 swapped": ("code = (v == 1) ? 1u : (v == -1) ? 2u : 0u;",
+                            "code = (v == 1) ? 2u : (v == -1) ? 1u : 0u;"),
+    "subtract becomes add": ("            else if (w[c] == -1)\n                s -= a[c];\n            else if (w[c] != 0)\n                bad |= 2;\n        }\n        if (s > bound || s < -bound || s > INT32_MAX",
+                             "            else if (w[c] == -1)\n                s += a[c];\n            else if (w[c] != 0)\n                bad |= 2;\n        }\n        if (s > bound || s < -bound || s > INT32_MAX"),
+    "weight row indexed by token": ("const int8_t *w = q + col * k;", "const int8_t *w = q + (row % n) * k;"),
+    "dequant without 1/127": ("(double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0",
+                              "(double)acc[i * n + j] * (double)gamma * (double)amax[i]"),
+    "dequant uses token 0 scale": ("(double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0",
+                                   "(double)acc[i * n + j] * (double)gamma * (double)amax[0] / 127.0"),
+    "dequant drops gamma": ("(double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0",
+                            "(double)acc[i * n + j] * (double)amax[i] / 127.0"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation anchor not found exactly once: " + name
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
+                    "-fPIC", "-shared", str(mutated), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, BITLINEAR_ORACLE_LIB=str(lib), OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "pins did not catch: " + name + "\n" + r.stdout[-2000:]

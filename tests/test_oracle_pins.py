@@ -1,0 +1,459 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+None of these compares the oracle with itself: each check uses a closed form,
+an exact rational computation, a brute-force enumeration in plain Python
+integers, an invariant of the definition, a hand-worked fixture in
+tests/golden/, or an independent library routine (numpy, torch on the CPU).
+
+Definitions pinned ("BitNet b1.58 in Production: 1-Bit LLMs and Energy
+Benchmarks", section "The Mathematical Mechanism"):
+  item 1  gamma = mean |W|, W_q = Clip(Round(W / (gamma + eps)), -1, 1)
+  item 2  x_q = Clip(Round(x * Q_b / (max|x| + eps)), -Q_b, Q_b), Q_b = 127
+  item 3  acc = sum of +x (w = +1), nothing (w = 0), -x (w = -1)
+  item 4  y = acc * gamma * max|x| / Q_b
+and ("BitNet 1-bit LLM Inference Framework: Running Large Language Models on
+CPU", section "How the LUT Kernel Works") the 2-bit codes 00 = 0, 01 = +1,
+10 = -1 and the scalar conditional-add loop; section "The Difference in How
+Computation Works" gives the mask form (W == 1) @ x - (W == -1) @ x.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+EPS_W = np.float32(1e-5)
+
+
+# ---------------------------------------------------------------------------
+# helpers independent of the oracle
+# ---------------------------------------------------------------------------
+
+def f32_nearest(fr: Fraction) -> np.float32:
+    """Correctly rounded binary32 of an exact rational (ties to even mantissa)."""
+    c = np.float32(float(fr))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - fr)
+        if best is None or d < best[0]:
+            best = (d, cand)
+        elif d == best[0]:
+            # tie: even mantissa
+            if int(np.float32(cand).view(np.uint32)) % 2 == 0:
+                best = (d, cand)
+    return np.float32(best[1])
+
+
+def bits(v: np.ndarray) -> np.ndarray:
+    return synth.fp32_to_bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    a = np.asarray(a, dtype=np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, dtype=np.float32).view(np.int32).astype(np.int64)
+    a = np.where(a < 0, -(a & 0x7FFFFFFF), a)
+    b = np.where(b < 0, -(b & 0x7FFFFFFF), b)
+    return np.abs(a - b)
+
+
+# ---------------------------------------------------------------------------
+# O1 gamma
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(3, 7), (64, 1000), (1, 1)])
+@pytest.mark.parametrize("c", [0.015625, 0.0173, 3.0])
+def test_gamma_constant_magnitude(oracle_mod, shape, c):
+    """|W| == c everywhere => gamma == c exactly (the binary64 sum of at most
+    2^22 copies of a binary32 value is exact, and so is the division)."""
+    c = np.float32(c)
+    rng = np.random.default_rng(5)
+    signs = np.where(rng.random(shape) < 0.5, -1.0, 1.0).astype(np.float32)
+    w = signs * c
+    assert oracle_mod.gamma(w) == c
+
+
+@pytest.mark.parametrize("shape", [(4, 8), (16, 64), (2, 2)])
+def test_gamma_exact_rational(oracle_mod, shape):
+    """Weights on a 2^-12 grid with n*k a power of two: the mean is exact, so
+    gamma must be the correctly rounded binary32 of the exact rational mean."""
+    rng = np.random.default_rng(11)
+    ints = rng.integers(-4096, 4097, size=shape)
+    w = (ints.astype(np.float64) / 4096.0).astype(np.float32)
+    exact = sum(Fraction(abs(int(v)), 4096) for v in ints.ravel()) / (shape[0] * shape[1])
+    assert oracle_mod.gamma(w) == f32_nearest(exact)
+
+
+def test_gamma_vs_numpy_pairwise_sum(oracle_mod):
+    """numpy's pairwise binary64 summation and the oracle's sequential one
+    round to the same binary32 (or 1 ulp apart in a rare boundary case)."""
+    w = synth.latent_weights(123, 700, 900)
+    ref = np.float32(np.abs(w.astype(np.float64)).sum() / w.size)
+    assert ulp_diff(oracle_mod.gamma(w), ref) <= 1
+
+
+def test_gamma_normal_expectation(oracle_mod):
+    """E|W| = sigma * sqrt(2/pi) for W ~ N(0, sigma^2); 4M samples give a
+    relative standard error of ~3.8e-4, checked at 5 sigma."""
+    w = synth.latent_weights(7, 2000, 2000)
+    expect = 0.02 * math.sqrt(2.0 / math.pi)
+    assert abs(float(oracle_mod.gamma(w)) / expect - 1.0) < 2e-3
+
+
+# ---------------------------------------------------------------------------
+# O2-O3 ternary RoundClip
+# ---------------------------------------------------------------------------
+
+def _gamma_for_denominator(d: float) -> np.float32:
+    """A binary32 gamma with fl32(gamma + 1e-5) == d exactly."""
+    g = np.float32(np.float32(d) - EPS_W)
+    assert np.float32(g + EPS_W) == np.float32(d)
+    return g
+
+
+def test_ternary_ties_unit_denominator(oracle_mod):
+    """d = gamma + 1e-5 == 1 exactly, so W/d == W and the rounding rule is
+    visible directly.  Expected codes from Round-half-even then Clip."""
+    g = _gamma_for_denominator(1.0)
+    half_up = np.nextafter(np.float32(0.5), np.float32(1))
+    half_dn = np.nextafter(np.float32(0.5), np.float32(0))
+    w = np.array([[0.5, -0.5, half_up, -half_up, half_dn, 1.5, 2.5, -1.5, -2.5,
+                   1.0, -1.0, 0.0, 100.0, -100.0, 0.75, -0.25]], dtype=np.float32)
+    expect = [0, 0, 1, -1, 0, 1, 1, -1, -1, 1, -1, 0, 1, -1, 1, 0]
+    assert oracle_mod.ternarize(w, g).ravel().tolist() == expect
+
+
+def test_ternary_ties_half_denominator(oracle_mod):
+    """d == 0.5 exactly: W = 0.25 is the tie 0.5 -> 0; W = 0.75 is 1.5 -> 2
+    -> clip 1; the neighbour above 0.25 rounds to 1.  A dropped epsilon would
+    make d = 0.49999 and turn the first tie into +1."""
+    g = _gamma_for_denominator(0.5)
+    w = np.array([[0.25, 0.75, np.nextafter(np.float32(0.25), np.float32(1)), -0.25,
+                   0.125, -0.75]], dtype=np.float32)
+    assert oracle_mod.ternarize(w, g).ravel().tolist() == [0, 1, 1, 0, 0, -1]
+
+
+def test_ternary_closed_forms(oracle_mod):
+    """W == 0: gamma == 0 and the epsilon alone keeps W/d finite -> all 0.
+    W == +c: every W/d = c/(c+1e-5) is in (0.5, 1] -> +1; W == -c -> -1."""
+    z = np.zeros((5, 9), dtype=np.float32)
+    g0 = oracle_mod.gamma(z)
+    assert g0 == 0.0
+    assert (oracle_mod.ternarize(z, g0) == 0).all()
+    for c in (1e-4, 0.02, 7.0):
+        w = np.full((4, 6), c, dtype=np.float32)
+        g = oracle_mod.gamma(w)
+        assert (oracle_mod.ternarize(w, g) == 1).all()
+        assert (oracle_mod.ternarize(-w, g) == -1).all()
+
+
+def test_ternary_sign_symmetry(oracle_mod):
+    w = synth.latent_weights(3, 300, 300)
+    g = oracle_mod.gamma(w)
+    assert np.array_equal(oracle_mod.ternarize(-w, g), -oracle_mod.ternarize(w, g))
+
+
+def test_ternary_zero_and_clip_fraction(oracle_mod):
+    """Fraction of zero codes is P(|W| <= d/2) and of codes whose quotient
+    reaches the clip is P(|W| >= 3d/2) for W ~ N(0, 0.02^2): erf closed forms
+    (binomial standard error ~2.3e-4, checked at ~5 sigma)."""
+    w = synth.latent_weights(0, 2048, 2048)
+    g = oracle_mod.gamma(w)
+    q = oracle_mod.ternarize(w, g)
+    d = float(np.float32(g + EPS_W))
+    sig = 0.02 * math.sqrt(2.0)
+    p_zero = math.erf(0.5 * d / sig)
+    p_clip = 1.0 - math.erf(1.5 * d / sig)
+    assert abs((q == 0).mean() - p_zero) < 1.2e-3
+    t = np.abs(w.astype(np.float64)) / d
+    assert abs((t >= 1.5).mean() - p_clip) < 1.2e-3
+    # the values the survey of the recipe expects (~31% zeros, ~23% clipped)
+    assert abs(p_zero - 0.3102) < 2e-3 and abs(p_clip - 0.2311) < 2e-3
+
+
+def test_ternary_vs_torch_listing_expression(oracle_mod):
+    """The page's weight_quant expression evaluated by torch on the CPU in
+    binary32 (torch.round is half-to-even), with the additive 1e-5 reading."""
+    torch = pytest.importorskip("torch")
+    w = synth.latent_weights(21, 512, 777)
+    g = oracle_mod.gamma(w)
+    tw = torch.from_numpy(w)
+    denom = torch.tensor(g, dtype=torch.float32) + torch.tensor(1e-5, dtype=torch.float32)
+    ref = torch.clamp(torch.round(tw / denom), -1, 1).to(torch.int8).numpy()
+    assert np.array_equal(oracle_mod.ternarize(w, g), ref)
+
+
+# ---------------------------------------------------------------------------
+# O4 canonical 2-bit packing
+# ---------------------------------------------------------------------------
+
+CODE = {0: 0b00, 1: 0b01, -1: 0b10}
+
+
+def test_pack_all_81_valid_bytes(oracle_mod):
+    seen = set()
+    for combo in itertools.product((-1, 0, 1), repeat=4):
+        q = np.array([combo], dtype=np.int8)
+        b = oracle_mod.pack_canonical(q)
+        expect = sum(CODE[v] << (2 * i) for i, v in enumerate(combo))
+        assert b.tolist() == [[expect]]
+        assert oracle_mod.unpack_canonical(b, 1, 4).tolist() == [list(combo)]
+        seen.add(expect)
+    assert len(seen) == 81
+
+
+def test_unpack_rejects_all_175_invalid_bytes(oracle_mod):
+    rejected = 0
+    for v in range(256):
+        fields = [(v >> (2 * i)) & 3 for i in range(4)]
+        b = np.array([[v]], dtype=np.uint8)
+        if 3 in fields:
+            with pytest.raises(oracle_mod.OracleError):
+                oracle_mod.unpack_canonical(b, 1, 4)
+            rejected += 1
+        else:
+            oracle_mod.unpack_canonical(b, 1, 4)
+    assert rejected == 175
+
+
+def test_pack_golden_bytes(oracle_mod):
+    with open(os.path.join(GOLDEN, "pack_canonical.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        q = np.array([c["codes"]], dtype=np.int8)
+        assert oracle_mod.pack_canonical(q).ravel().tolist() == c["bytes"], c["note"]
+        assert oracle_mod.unpack_canonical(np.array(c["bytes"], np.uint8), 1, c["k"]).ravel().tolist() == c["codes"]
+
+
+def test_unpack_rejects_nonzero_padding(oracle_mod):
+    # k = 5: the second byte may only use its lowest field
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.unpack_canonical(np.array([0, 0b0100], np.uint8), 1, 5)
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (3, 5), (17, 255), (8, 2048), (5, 1027)])
+def test_pack_roundtrip_random(oracle_mod, n, k):
+    rng = np.random.default_rng(n * 1000 + k)
+    q = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+    b = oracle_mod.pack_canonical(q)
+    assert b.shape == (n, (k + 3) // 4)
+    assert np.array_equal(oracle_mod.unpack_canonical(b, n, k), q)
+
+
+# ---------------------------------------------------------------------------
+# O5 per-token activation quantization
+# ---------------------------------------------------------------------------
+
+def test_quant_ties_round_half_even(oracle_mod):
+    """a' = 127/64 is exact in bf16, so s = fl32(127 / a') = 64 exactly and
+    x = j/128 lands on j/2: the .5 cases expose the rounding rule (round half
+    away from zero would give 3, 4, 2, 1, -3, -2 instead)."""
+    vals = [127 / 64, 5 / 128, 7 / 128, 3 / 128, 1 / 128, -5 / 128, -3 / 128, 0.0, 9 / 128, 64 / 128]
+    assert np.float32(127.0) / np.float32(127 / 64) == np.float32(64.0)
+    xq, amax = oracle_mod.quant_act(bits([vals]))
+    assert amax.tolist() == [np.float32(127 / 64)]
+    assert xq.ravel().tolist() == [127, 2, 4, 2, 0, -2, -2, 0, 4, 32]
+
+
+def test_quant_golden_scale(oracle_mod):
+    """a' = 2: s = 63.5 exactly; 63.5 -> 64 (tie to even), -31.75 -> -32."""
+    xq, amax = oracle_mod.quant_act(bits([[1.0, -0.5, 2.0, 0.25]]))
+    assert xq.tolist() == [[64, -32, 127, 16]] and amax.tolist() == [2.0]
+
+
+def test_quant_invariants(oracle_mod):
+    x = synth.activations_bf16(9, 64, 1536, 0.01)
+    xq, amax = oracle_mod.quant_act(x)
+    xf = synth.bf16_bits_to_fp32(x)
+    # a' is the exact per-token max |x| (all tokens far above the 1e-8 floor)
+    assert np.array_equal(amax, np.abs(xf).max(axis=1))
+    # the max element always maps to +-127; -128 never appears
+    assert (np.abs(xq.astype(np.int32)).max(axis=1) == 127).all()
+    assert xq.min() >= -127
+    # odd symmetry
+    xq_neg, amax_neg = oracle_mod.quant_act(x ^ np.uint16(0x8000))
+    assert np.array_equal(xq_neg, -xq) and np.array_equal(amax_neg, amax)
+    # exact power-of-two scaling of the token leaves the codes unchanged
+    for j in (-3, 5):
+        xs = synth.fp32_to_bf16_bits(xf * np.float32(2.0 ** j))
+        assert np.array_equal(synth.bf16_bits_to_fp32(xs), xf * np.float32(2.0 ** j))
+        xq_s, amax_s = oracle_mod.quant_act(xs)
+        assert np.array_equal(xq_s, xq)
+        assert np.array_equal(amax_s, amax * np.float32(2.0 ** j))
+
+
+def test_quant_zero_and_tiny_tokens(oracle_mod):
+    x = np.zeros((3, 40), dtype=np.uint16)
+    x[1, 5] = bits([[1e-12]])[0, 0]          # below the 1e-8 floor
+    x[2, 7] = bits([[-3.0]])[0, 0]
+    xq, amax = oracle_mod.quant_act(x)
+    assert (xq[0] == 0).all() and amax[0] == np.float32(1e-8)
+    # a 1e-12 element against a' = 1e-8: 1e-12 * 127e8 = 0.0127 -> 0
+    assert (xq[1] == 0).all() and amax[1] == np.float32(1e-8)
+    assert xq[2, 7] == -127 and (np.delete(xq[2], 7) == 0).all() and amax[2] == 3.0
+
+
+@pytest.mark.parametrize("amax_val", [127 / 64, 3.0, 0.0078125, 1.7e4, 3.3e38])
+def test_quant_exhaustive_bf16_vs_torch(oracle_mod, amax_val):
+    """Every finite bf16 pattern with |x| <= a' as a token element, against the
+    page's activation_quant expression evaluated by torch (binary32)."""
+    torch = pytest.importorskip("torch")
+    all_bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = synth.bf16_bits_to_fp32(all_bits)
+    a_bits = bits([[amax_val]])[0, 0]
+    a = synth.bf16_bits_to_fp32(np.array([a_bits]))[0]
+    keep = np.isfinite(vals) & (np.abs(vals) <= a)
+    cand = all_bits[keep]
+    width = 4096
+    pad = (-len(cand)) % (width - 1)
+    cand = np.concatenate([cand, np.zeros(pad, np.uint16)])
+    rows = cand.reshape(-1, width - 1)
+    x = np.concatenate([np.full((rows.shape[0], 1), a_bits, np.uint16), rows], axis=1)
+    xq, amax = oracle_mod.quant_act(x)
+    tx = torch.from_numpy(synth.bf16_bits_to_fp32(x))
+    qmax = 127
+    scale = torch.max(torch.abs(tx), dim=-1, keepdim=True)[0].clamp(min=1e-8)
+    ref = torch.clamp(torch.round(tx * (qmax / scale)), -qmax, qmax).to(torch.int8).numpy()
+    assert np.array_equal(xq, ref)
+    assert np.array_equal(amax, scale.squeeze(1).numpy())
+
+
+# ---------------------------------------------------------------------------
+# O6 contraction
+# ---------------------------------------------------------------------------
+
+def _rand_xq(rng, m, k):
+    return rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+
+
+def test_contract_closed_forms(oracle_mod):
+    rng = np.random.default_rng(2)
+    m, n, k = 5, 7, 333
+    xq = _rand_xq(rng, m, k)
+    rowsum = xq.astype(np.int64).sum(axis=1)
+    ones = np.ones((n, k), np.int8)
+    assert np.array_equal(oracle_mod.contract(xq, ones), np.repeat(rowsum[:, None], n, 1))
+    assert np.array_equal(oracle_mod.contract(xq, -ones), -np.repeat(rowsum[:, None], n, 1))
+    assert (oracle_mod.contract(xq, np.zeros((n, k), np.int8)) == 0).all()
+    # one-hot rows pick single activations (with sign)
+    pos = rng.integers(0, k, size=n)
+    sgn = np.where(np.arange(n) % 2 == 0, 1, -1)
+    oh = np.zeros((n, k), np.int8)
+    oh[np.arange(n), pos] = sgn
+    expect = xq[:, pos].astype(np.int64) * sgn[None, :]
+    assert np.array_equal(oracle_mod.contract(xq, oh), expect)
+
+
+def test_contract_brute_force_4x8(oracle_mod):
+    """All 3^8 = 6561 ternary rows of K = 8 against 4 tokens (including the
+    +-127 extremes), checked against a plain-Python integer double loop and
+    against the mask form (W == 1) @ x - (W == -1) @ x."""
+    q = np.array(list(itertools.product((-1, 0, 1), repeat=8)), dtype=np.int8)
+    rng = np.random.default_rng(4)
+    xq = np.stack([np.full(8, 127), np.full(8, -127),
+                   np.array([127, -127, 0, 1, -1, 64, -64, 3]),
+                   rng.integers(-127, 128, 8)]).astype(np.int8)
+    acc = oracle_mod.contract(xq, q)
+    assert acc.shape == (4, 6561)
+    xl = xq.astype(int).tolist()
+    ql = q.astype(int).tolist()
+    brute = [[sum(a * w for a, w in zip(xl[i], ql[j])) for j in range(6561)] for i in range(4)]
+    assert acc.tolist() == brute
+    mask = ((q == 1).astype(np.int64) @ xq.T.astype(np.int64)
+            - (q == -1).astype(np.int64) @ xq.T.astype(np.int64)).T
+    assert np.array_equal(acc, mask)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1000), (5, 129, 2049), (16, 64, 4096)])
+def test_contract_vs_numpy_int64(oracle_mod, m, n, k):
+    rng = np.random.default_rng(m + n + k)
+    xq = _rand_xq(rng, m, k)
+    q = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+    ref = xq.astype(np.int64) @ q.T.astype(np.int64)
+    assert np.array_equal(oracle_mod.contract(xq, q), ref)
+
+
+def test_contract_k_permutation_invariance(oracle_mod):
+    rng = np.random.default_rng(8)
+    xq = _rand_xq(rng, 3, 517)
+    q = rng.integers(-1, 2, size=(11, 517)).astype(np.int8)
+    perm = rng.permutation(517)
+    assert np.array_equal(oracle_mod.contract(xq, q), oracle_mod.contract(xq[:, perm], q[:, perm]))
+
+
+def test_contract_overflow_bound_at_largest_k(oracle_mod):
+    """|acc| <= 127 K; at K = 28672 the extreme is 3,641,344 < 2^31, reached
+    exactly by all-127 activations against all-(+1) weights."""
+    k = 28672
+    xq = np.full((2, k), 127, np.int8)
+    xq[1] = -127
+    q = np.ones((3, k), np.int8)
+    q[1] = -1
+    q[2, ::2] = -1
+    acc = oracle_mod.contract(xq, q)
+    assert acc.tolist() == [[127 * k, -127 * k, 0], [-127 * k, 127 * k, 0]]
+    assert 127 * k == 3641344 < 2 ** 31
+
+
+def test_contract_rejects_non_ternary(oracle_mod):
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.contract(np.ones((1, 4), np.int8), np.array([[0, 2, 0, 0]], np.int8))
+
+
+def test_contract_pairs_match_full(oracle_mod):
+    rng = np.random.default_rng(10)
+    xq = _rand_xq(rng, 6, 300)
+    q = rng.integers(-1, 2, size=(20, 300)).astype(np.int8)
+    full = xq.astype(np.int64) @ q.T.astype(np.int64)
+    rows = rng.integers(0, 6, 50)
+    cols = rng.integers(0, 20, 50)
+    assert np.array_equal(oracle_mod.contract_pairs(xq, q, rows, cols), full[rows, cols])
+
+
+# ---------------------------------------------------------------------------
+# O7 dequantization
+# ---------------------------------------------------------------------------
+
+def test_dequant_exact_rational(oracle_mod):
+    """y is the correctly rounded binary32 of acc * gamma * a' / 127 (the
+    binary64 evaluation may differ by one ulp only at a rounding boundary)."""
+    rng = np.random.default_rng(12)
+    m, n = 6, 40
+    acc = rng.integers(-3641344, 3641345, size=(m, n)).astype(np.int32)
+    acc[0, :5] = 0
+    g = np.float32(0.0159)
+    amax = (rng.random(m) * 20 + 0.25).astype(np.float32)
+    y = oracle_mod.dequant(acc, g, amax)
+    exact = [[f32_nearest(Fraction(int(acc[i, j])) * Fraction(float(g)) * Fraction(float(amax[i])) / 127)
+              for j in range(n)] for i in range(m)]
+    d = ulp_diff(y, np.array(exact, np.float32))
+    assert d.max() <= 1 and (d == 0).mean() > 0.99
+    assert ((y == 0) == (acc == 0)).all()
+
+
+# ---------------------------------------------------------------------------
+# end to end: hand-worked examples
+# ---------------------------------------------------------------------------
+
+def test_golden_end_to_end(oracle_mod):
+    with open(os.path.join(GOLDEN, "bitlinear_small.json")) as f:
+        exs = json.load(f)["examples"]
+    for ex in exs:
+        w = np.array(ex["w"], np.float32)
+        x = bits(ex["x"])
+        r = oracle_mod.forward(x, w)
+        assert r["gamma"] == f32_nearest(Fraction(ex["gamma"])), ex["name"]
+        assert r["q"].tolist() == ex["q"], ex["name"]
+        amax = [np.float32(1e-8) if a == "1e-8f" else f32_nearest(Fraction(a)) for a in ex["amax"]]
+        assert r["amax"].tolist() == amax, ex["name"]
+        assert r["xq"].tolist() == ex["xq"], ex["name"]
+        assert r["acc"].tolist() == ex["acc"], ex["name"]
+        y = np.array([[f32_nearest(Fraction(v)) for v in row] for row in ex["y"]], np.float32)
+        assert ulp_diff(r["y"], y).max() <= 1, ex["name"]
