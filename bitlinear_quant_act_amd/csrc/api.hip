@@ -1,0 +1,107 @@
+// C ABI of libbitlinear.so (declared in include/bitlinear.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so an argument error leaves outputs untouched and needs no
+// device; then it enqueues its kernels on the caller's stream and returns
+// without synchronising.  No device memory is allocated here.
+#include "bitlinear.h"
+#include "bitlinear_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxK = int64_t(1) << 24;         // |acc| <= 127 k < 2^31
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxBatchedM = int64_t(1) << 21;  // token tiles fit a grid dimension
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? BITLINEAR_OK : BITLINEAR_E_HIP; }
+
+int check_nk(int64_t n, int64_t k) {
+  if (n < 1 || n > kMaxRows || k < 1 || k > kMaxK) return BITLINEAR_E_SHAPE;
+  return BITLINEAR_OK;
+}
+
+int check_forward(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+                  const float* amax, int64_t m, float* y, int32_t* acc) {
+  if (!packed || !gamma || !xq || !amax || !y) return BITLINEAR_E_NULL;
+  if (int rc = check_nk(n, k)) return rc;
+  if (m < 1 || m > kMaxRows) return BITLINEAR_E_SHAPE;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(amax, 4) || !aligned(y, 4) ||
+      (acc && !aligned(acc, 4)))
+    return BITLINEAR_E_ALIGN;
+  return BITLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+const char* bitlinear_status_string(int status) {
+  switch (status) {
+    case BITLINEAR_OK: return "ok";
+    case BITLINEAR_E_NULL: return "a required pointer is NULL";
+    case BITLINEAR_E_SHAPE: return "a size is outside its allowed range";
+    case BITLINEAR_E_ALIGN: return "a pointer does not meet its alignment requirement";
+    case BITLINEAR_E_UNSUPPORTED: return "valid arguments not handled by this entry point";
+    case BITLINEAR_E_SIZE: return "a caller-provided buffer is too small";
+    case BITLINEAR_E_HIP: return "the HIP runtime reported a launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t bitlinear_packed_bytes(int64_t n, int64_t k) {
+  if (check_nk(n, k)) return 0;
+  return static_cast<size_t>(bitlinear::row_blocks(n) * bitlinear::k_tiles(k) * bitlinear::kTileBytes);
+}
+
+size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k) {
+  if (check_nk(n, k)) return 0;
+  return static_cast<size_t>(bitlinear::pack_partial_count(n, k)) * sizeof(double);
+}
+
+int bitlinear_pack_weights(const float* w, int64_t n, int64_t k, void* packed, size_t packed_bytes,
+                           float* gamma, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w || !packed || !gamma || !workspace) return BITLINEAR_E_NULL;
+  if (int rc = check_nk(n, k)) return rc;
+  if (!aligned(w, 4) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 8))
+    return BITLINEAR_E_ALIGN;
+  if (packed_bytes < bitlinear_packed_bytes(n, k) || workspace_bytes < bitlinear_pack_workspace_bytes(n, k))
+    return BITLINEAR_E_SIZE;
+  return status_of(bitlinear::launch_pack(w, n, k, packed, gamma, static_cast<double*>(workspace),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_unpack_weights(const void* packed, int64_t n, int64_t k, int8_t* codes, void* stream) {
+  if (!packed || !codes) return BITLINEAR_E_NULL;
+  if (int rc = check_nk(n, k)) return rc;
+  if (!aligned(packed, 16)) return BITLINEAR_E_ALIGN;
+  return status_of(bitlinear::launch_unpack(packed, n, k, codes, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* x_absmax, void* stream) {
+  if (!x || !xq || !x_absmax) return BITLINEAR_E_NULL;
+  if (m < 1 || m > kMaxRows || k < 1 || k > kMaxK) return BITLINEAR_E_SHAPE;
+  if (!aligned(x, 2) || !aligned(x_absmax, 4)) return BITLINEAR_E_ALIGN;
+  return status_of(bitlinear::launch_quant_act(x, m, k, xq, x_absmax, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+                      const float* x_absmax, int64_t m, float* y, int32_t* acc_or_null, void* stream) {
+  if (int rc = check_forward(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null)) return rc;
+  if (m > BITLINEAR_FORWARD_MAX_M) return BITLINEAR_E_UNSUPPORTED;
+  return status_of(bitlinear::launch_gemv(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_batched(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+                              const float* x_absmax, int64_t m, float* y, int32_t* acc_or_null, void* stream) {
+  if (int rc = check_forward(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null)) return rc;
+  if (m > kMaxBatchedM) return BITLINEAR_E_UNSUPPORTED;
+  return status_of(bitlinear::launch_gemm(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

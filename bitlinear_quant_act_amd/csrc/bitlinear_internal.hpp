@@ -1,0 +1,45 @@
+// Internal declarations of libbitlinear.so: device layout constants and the
+// kernel launchers the C ABI (api.hip) dispatches to.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bitlinear {
+
+// ---- packed ternary layout, version 1 -------------------------------------
+// A tile is 16 weight rows x 256 columns = 1024 bytes: 64 slots of 16 bytes,
+// one per lane of a wave64, so a wave reads a tile with one fully coalesced
+// 16-byte-per-lane load.  Slot l: row (l % 16), columns 64*(l/16) + [0, 64).
+// Word s of a slot: 16 columns, column t at bits 8*(t%4) + 2*(t/4), so
+// (word >> 2j) & 0x03030303 yields columns 4j..4j+3 as four bytes in order.
+// Field value = w + 1.
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 256;
+constexpr int kTileBytes = 1024;
+constexpr uint32_t kZeroCode = 1u;         // w = 0
+constexpr uint32_t kZeroWord = 0x55555555u; // sixteen zero-weight fields
+
+__host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kTileRows - 1) / kTileRows; }
+__host__ __device__ inline int64_t k_tiles(int64_t k) { return (k + kTileCols - 1) / kTileCols; }
+
+constexpr int kPackPartials = 1024;  // fp64 partial sums of |W| (max)
+
+// ---- launchers (return the hipGetLastError of their launches) --------------
+hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* amax,
+                            hipStream_t s);
+
+int pack_partial_count(int64_t n, int64_t k);
+hipError_t launch_pack(const float* w, int64_t n, int64_t k, void* packed, float* gamma,
+                       double* partials, hipStream_t s);
+hipError_t launch_unpack(const void* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t s);
+
+hipError_t launch_gemv(const void* packed, const float* gamma, int64_t n, int64_t k,
+                       const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc,
+                       hipStream_t s);
+hipError_t launch_gemm(const void* packed, const float* gamma, int64_t n, int64_t k,
+                       const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc,
+                       hipStream_t s);
+
+}  // namespace bitlinear

@@ -1,0 +1,136 @@
+// Per-token absmax int8 activation quantisation.
+//
+// "BitNet b1.58 in Production: 1-Bit LLMs and Energy Benchmarks", section
+// "The Mathematical Mechanism", item 2: x_q = Clip(Round(x * Q_b / a'),
+// -Q_b, Q_b) with Q_b = 127 and one scale per token; a' = max(max|x|, 1e-8).
+//
+// One workgroup per token.  The token's bf16 row is read once with 16-byte
+// loads and kept in registers; |x| is reduced as integer bit patterns (for
+// finite non-negative floats the bit order is the numeric order), first
+// across the wave with cross-lane shuffles, then across the four waves in
+// LDS.  The scale is one IEEE fp32 divide (127 / a'); every code is one fp32
+// multiply followed by v_rndne_f32 (round half to even) and a clamp, so the
+// result is bit-identical to any other evaluation of the same two roundings.
+#include "bitlinear_internal.hpp"
+
+namespace bitlinear {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t quant_code(uint32_t bits16, float s) {
+  float r = rintf(bf16_to_f32(bits16) * s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
+}
+
+__device__ __forceinline__ uint32_t abs_max2(uint32_t word) {
+  // two bf16 values in one 32-bit word; clear the sign bits and compare
+  return max(word & 0x7fffu, (word >> 16) & 0x7fffu);
+}
+
+// max over the workgroup; every thread receives the result
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = max(r, red[i]);
+  return r;
+}
+
+// Vector path: k % 8 == 0, x 16-byte aligned, xq 8-byte aligned; the row
+// (k / 8 chunks of 8 values) fits in CPT chunks per thread.
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void quant_act_vec(const uint16_t* __restrict__ x, int k,
+                                                          int8_t* __restrict__ xq,
+                                                          float* __restrict__ amax) {
+  __shared__ uint32_t red[kWaves];
+  const int64_t row = blockIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * k);
+  const int chunks = k >> 3;
+  uint4 c[CPT];
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < chunks) {
+      c[i] = xr[idx];
+      mx = max(mx, max(max(abs_max2(c[i].x), abs_max2(c[i].y)), max(abs_max2(c[i].z), abs_max2(c[i].w))));
+    }
+  }
+  mx = block_max(mx, red);
+  const float a = fmaxf(bf16_to_f32(mx), 1e-8f);
+  const float s = 127.0f / a;
+  uint2* out = reinterpret_cast<uint2*>(xq + row * k);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < chunks) {
+      const uint32_t w[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        lo |= quant_code(w[j] & 0xffffu, s) << (16 * j);
+        lo |= quant_code(w[j] >> 16, s) << (16 * j + 8);
+        hi |= quant_code(w[j + 2] & 0xffffu, s) << (16 * j);
+        hi |= quant_code(w[j + 2] >> 16, s) << (16 * j + 8);
+      }
+      out[idx] = make_uint2(lo, hi);
+    }
+  }
+  if (threadIdx.x == 0) amax[row] = a;
+}
+
+// General path: any k and alignment; two passes over the row with 2-byte loads.
+__global__ __launch_bounds__(kThreads) void quant_act_any(const uint16_t* __restrict__ x, int64_t k,
+                                                          int8_t* __restrict__ xq,
+                                                          float* __restrict__ amax) {
+  __shared__ uint32_t red[kWaves];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * k;
+  uint32_t mx = 0;
+  for (int64_t i = threadIdx.x; i < k; i += kThreads) mx = max(mx, static_cast<uint32_t>(xr[i]) & 0x7fffu);
+  mx = block_max(mx, red);
+  const float a = fmaxf(bf16_to_f32(mx), 1e-8f);
+  const float s = 127.0f / a;
+  int8_t* out = xq + row * k;
+  for (int64_t i = threadIdx.x; i < k; i += kThreads)
+    out[i] = static_cast<int8_t>(quant_code(xr[i], s));
+  if (threadIdx.x == 0) amax[row] = a;
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* amax,
+                            hipStream_t s) {
+  const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(xq) % 8 == 0);
+  const int64_t chunks = k / 8;
+  const int64_t per_thread = (chunks + kThreads - 1) / kThreads;
+  const dim3 grid(static_cast<unsigned>(m));
+  const int ki = static_cast<int>(k);
+  if (vec && per_thread <= 1)
+    quant_act_vec<1><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else if (vec && per_thread <= 2)
+    quant_act_vec<2><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else if (vec && per_thread <= 4)
+    quant_act_vec<4><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else if (vec && per_thread <= 8)
+    quant_act_vec<8><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else if (vec && per_thread <= 16)
+    quant_act_vec<16><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else
+    quant_act_any<<<grid, kThreads, 0, s>>>(x, k, xq, amax);
+  return hipGetLastError();
+}
+
+}  // namespace bitlinear

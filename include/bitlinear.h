@@ -1,0 +1,154 @@
+/*
+ * bitlinear.h -- C ABI of libbitlinear.so, the BitNet b1.58 BitLinear forward
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (from "BitNet b1.58 in Production: 1-Bit LLMs and Energy
+ * Benchmarks", section "The Mathematical Mechanism"):
+ *   item 1  gamma = mean |W| over the whole [N][K] weight matrix;
+ *           W_q = Clip(Round(W / (gamma + eps)), -1, 1), eps = 1e-5;
+ *   item 2  per token (one row of K activations):
+ *           x_q = Clip(Round(x * Q_b / a'), -Q_b, Q_b), Q_b = 127,
+ *           a' = max(max_k |x|, 1e-8);
+ *   item 3  acc[m][n] = sum_k x_q[m][k] * W_q[n][k] in int32 -- an add where
+ *           the weight is +1, nothing where it is 0, a subtract where it is -1;
+ *   item 4  y[m][n] = acc[m][n] * gamma * a'[m] / Q_b in fp32.
+ * "Round" is round-half-to-even throughout.  The 2-bit storage of ternary
+ * weights follows "BitNet 1-bit LLM Inference Framework: Running Large
+ * Language Models on CPU", section "How the LUT Kernel Works" (four ternary
+ * values per byte); the tiled order of those 2-bit fields on the device is
+ * this library's own (see bitlinear_packed_bytes).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer on the current HIP device.  The
+ *    caller allocates and frees every buffer; the library allocates nothing
+ *    and keeps no mutable state, so calls on different streams may overlap
+ *    as long as their output buffers do not.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it and the call returns without synchronising.
+ *  - Row-major layouts: weights W fp32 [n][k]; activations bf16 [m][k] as raw
+ *    uint16 bit patterns; activation codes int8 [m][k]; outputs fp32 [m][n].
+ *  - Errors: arguments are validated on the host before any launch; on an
+ *    argument error the call returns a negative status and leaves every
+ *    output untouched.  A failed launch returns BITLINEAR_E_HIP.  Nothing is
+ *    thrown and errno is not used.
+ *  - Inputs containing NaN or Inf are outside the contract.
+ *  - Sizes: 1 <= n, m <= 2^31 - 1 and 1 <= k <= 2^24 (so |acc| <= 127 k
+ *    stays inside int32).
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_ABI_VERSION 1
+
+/* Largest token count accepted by bitlinear_forward (the decode path). */
+#define BITLINEAR_FORWARD_MAX_M 16
+
+typedef enum {
+    BITLINEAR_OK = 0,
+    BITLINEAR_E_NULL = -1,        /* a required pointer is NULL               */
+    BITLINEAR_E_SHAPE = -2,       /* a size is outside its range              */
+    BITLINEAR_E_ALIGN = -3,       /* a pointer breaks its alignment rule      */
+    BITLINEAR_E_UNSUPPORTED = -4, /* valid, but not handled by this entry     */
+    BITLINEAR_E_SIZE = -5,        /* a caller buffer is smaller than required */
+    BITLINEAR_E_HIP = -6          /* the HIP runtime reported a launch error  */
+} bitlinear_status;
+
+/* Version of this ABI and of the device weight layout (BITLINEAR_ABI_VERSION). */
+int bitlinear_abi_version(void);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char *bitlinear_status_string(int status);
+
+/*
+ * Bytes of the packed ternary weights of an [n][k] matrix on the device.
+ * Layout (version 1): the matrix is cut into tiles of 16 rows x 256 columns;
+ * tile (rb, kt) is 1024 contiguous bytes at offset (rb * ceil(k/256) + kt) *
+ * 1024, so one 16-row block is a contiguous stream along k.  Inside a tile,
+ * 16-byte lane slot l (0..63) holds row 16*rb + (l % 16) and columns
+ * 256*kt + 64*(l / 16) + [0, 64); its 32-bit word s covers 16 of those
+ * columns, column t of the word in bits 8*(t % 4) + 2*(t / 4).  Each 2-bit
+ * field stores w + 1 (0 = -1, 1 = 0, 2 = +1; 3 unused); rows >= n and
+ * columns >= k are padded with the code of 0.  Pure host function; returns 0
+ * if n or k is out of range.
+ */
+size_t bitlinear_packed_bytes(int64_t n, int64_t k);
+
+/* Bytes of device workspace bitlinear_pack_weights needs (at most 8 KiB). */
+size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k);
+
+/*
+ * One-time weight preparation ("The Mathematical Mechanism", item 1):
+ * gamma = mean |W| accumulated in fp64 and rounded once to fp32; every
+ * weight is ternarised as Clip(Round(W / (gamma + 1e-5)), -1, 1) with one
+ * IEEE fp32 divide and round-half-to-even, and written in the tiled 2-bit
+ * layout above.
+ *   w          in   fp32 [n][k], any 4-byte alignment
+ *   packed     out  >= bitlinear_packed_bytes(n, k) bytes, 16-byte aligned
+ *   gamma      out  1 fp32
+ *   workspace  tmp  >= bitlinear_pack_workspace_bytes(n, k) bytes, 8-byte aligned
+ * Two kernels; the gamma of one call never depends on another call.
+ */
+int bitlinear_pack_weights(const float *w, int64_t n, int64_t k,
+                           void *packed, size_t packed_bytes,
+                           float *gamma,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * Decode the packed layout back to ternary codes (for tests and inspection).
+ *   packed  in   bitlinear_packed_bytes(n, k) bytes, 16-byte aligned
+ *   codes   out  int8 [n][k] in {-1, 0, 1}
+ */
+int bitlinear_unpack_weights(const void *packed, int64_t n, int64_t k,
+                             int8_t *codes, void *stream);
+
+/*
+ * Per-token absmax int8 activation quantisation ("The Mathematical
+ * Mechanism", item 2): for each of the m tokens, a' = max(max_k |x|, 1e-8),
+ * s = 127 / a' (one IEEE fp32 divide), x_q = Clip(Round(x * s), -127, 127)
+ * (one fp32 multiply, round-half-to-even).
+ *   x         in   bf16 bit patterns [m][k], 2-byte aligned
+ *   xq        out  int8 [m][k]
+ *   x_absmax  out  fp32 [m], receives a'
+ */
+int bitlinear_quant_act(const uint16_t *x, int64_t m, int64_t k,
+                        int8_t *xq, float *x_absmax, void *stream);
+
+/*
+ * Decode-path forward for 1 <= m <= BITLINEAR_FORWARD_MAX_M tokens
+ * ("The Mathematical Mechanism", items 3 and 4): streams the packed weights
+ * once, accumulates acc = sum_k x_q * W_q exactly in int32 and writes
+ * y = acc * gamma * a' / 127 in fp32.
+ *   packed       in   from bitlinear_pack_weights(n, k), 16-byte aligned
+ *   gamma        in   1 fp32 (device)
+ *   xq, x_absmax in   from bitlinear_quant_act(m, k)
+ *   y            out  fp32 [m][n], 4-byte aligned
+ *   acc_or_null  out  optional int32 [m][n] copy of the exact accumulators
+ * m > BITLINEAR_FORWARD_MAX_M returns BITLINEAR_E_UNSUPPORTED.
+ */
+int bitlinear_forward(const void *packed, const float *gamma, int64_t n, int64_t k,
+                      const int8_t *xq, const float *x_absmax, int64_t m,
+                      float *y, int32_t *acc_or_null, void *stream);
+
+/*
+ * Batched (prefill) forward for any m >= 1: the same result as
+ * bitlinear_forward, computed as a tiled int8 matrix-core contraction with
+ * the ternary tiles expanded on chip.
+ */
+int bitlinear_forward_batched(const void *packed, const float *gamma, int64_t n, int64_t k,
+                              const int8_t *xq, const float *x_absmax, int64_t m,
+                              float *y, int32_t *acc_or_null, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/bitlinear.h declares, and rejects bad arguments on the host before
+any HIP call (so these run on a machine without a device).  Only argument
+combinations that fail validation are passed here; no call reaches a launch.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+@pytest.fixture(scope="module")
+def blq():
+    import bitlinear_quant_act_amd as m
+    m.load_library()
+    return m
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward",
+              "bitlinear_forward_batched"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(blq):
+    lib = blq.load_library()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the Python binding exposes the same names
+    assert all(hasattr(blq, n) for n in declared_functions())
+
+
+def test_single_hip_runtime_mapped(blq):
+    assert len(blq._mapped_hip_runtimes()) <= 1
+
+
+def test_version_and_status_strings(blq):
+    assert blq.bitlinear_abi_version() == 1
+    for s in range(-6, 1):
+        assert blq.bitlinear_status_string(s) not in ("", "unknown status")
+    assert blq.bitlinear_status_string(12345) == "unknown status"
+
+
+def test_packed_bytes(blq):
+    # 16 x 256 tiles of 1024 bytes
+    assert blq.bitlinear_packed_bytes(2048, 2048) == 2048 * 2048 // 4
+    assert blq.bitlinear_packed_bytes(1, 1) == 1024
+    assert blq.bitlinear_packed_bytes(17, 257) == 2 * 2 * 1024
+    assert blq.bitlinear_packed_bytes(57344, 8192) == 57344 * 8192 // 4
+    assert blq.bitlinear_packed_bytes(0, 5) == 0
+    assert blq.bitlinear_packed_bytes(5, 0) == 0
+    assert blq.bitlinear_packed_bytes(5, (1 << 24) + 1) == 0
+    assert 8 <= blq.bitlinear_pack_workspace_bytes(2048, 2048) <= 8192
+    assert blq.bitlinear_pack_workspace_bytes(57344, 8192) == 8192
+
+
+# fake device addresses: never dereferenced, every call below fails validation
+A16 = 0x10000
+A8 = 0x10008
+A2 = 0x10002
+
+
+def test_pack_validation(blq):
+    lib = blq.load_library()
+    nb = blq.bitlinear_packed_bytes(64, 512)
+    ws = blq.bitlinear_pack_workspace_bytes(64, 512)
+    E = blq
+    assert lib.bitlinear_pack_weights(None, 64, 512, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_pack_weights(A16, 64, 512, None, nb, A16, A16, ws, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_pack_weights(A16, 64, 512, A16, nb, None, A16, ws, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_pack_weights(A16, 64, 512, A16, nb, A16, None, ws, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_pack_weights(A16, 0, 512, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
+    assert lib.bitlinear_pack_weights(A16, 64, -3, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
+    assert lib.bitlinear_pack_weights(A16, 64, 1 << 25, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
+    assert lib.bitlinear_pack_weights(A16, 64, 512, A8, nb, A16, A16, ws, None) == E.BITLINEAR_E_ALIGN
+    assert lib.bitlinear_pack_weights(A2, 64, 512, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_ALIGN
+    assert lib.bitlinear_pack_weights(A16, 64, 512, A16, nb, A16, A2, ws, None) == E.BITLINEAR_E_ALIGN
+    assert lib.bitlinear_pack_weights(A16, 64, 512, A16, nb - 1, A16, A16, ws, None) == E.BITLINEAR_E_SIZE
+    assert lib.bitlinear_pack_weights(A16, 64, 512, A16, nb, A16, A16, ws - 1, None) == E.BITLINEAR_E_SIZE
+
+
+def test_unpack_and_quant_validation(blq):
+    lib = blq.load_library()
+    E = blq
+    assert lib.bitlinear_unpack_weights(None, 4, 4, A16, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_unpack_weights(A16, 4, 4, None, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_unpack_weights(A16, 0, 4, A16, None) == E.BITLINEAR_E_SHAPE
+    assert lib.bitlinear_unpack_weights(A8, 4, 4, A16, None) == E.BITLINEAR_E_ALIGN
+    assert lib.bitlinear_quant_act(None, 1, 8, A16, A16, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_quant_act(A16, 1, 8, None, A16, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_quant_act(A16, 1, 8, A16, None, None) == E.BITLINEAR_E_NULL
+    assert lib.bitlinear_quant_act(A16, 0, 8, A16, A16, None) == E.BITLINEAR_E_SHAPE
+    assert lib.bitlinear_quant_act(A16, 1, 0, A16, A16, None) == E.BITLINEAR_E_SHAPE
+    assert lib.bitlinear_quant_act(A16 + 1, 1, 8, A16, A16, None) == E.BITLINEAR_E_ALIGN
+    assert lib.bitlinear_quant_act(A16, 1, 8, A16, A2, None) == E.BITLINEAR_E_ALIGN
+
+
+@pytest.mark.parametrize("fname", ["bitlinear_forward", "bitlinear_forward_batched"])
+def test_forward_validation(blq, fname):
+    fn = getattr(blq.load_library(), fname)
+    E = blq
+    ok = dict(packed=A16, gamma=A16, n=64, k=512, xq=A16, amax=A16, m=1, y=A16, acc=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return fn(a["packed"], a["gamma"], a["n"], a["k"], a["xq"], a["amax"], a["m"], a["y"], a["acc"], None)
+
+    for key in ("packed", "gamma", "xq", "amax", "y"):
+        assert call(**{key: None, "n": 64}) == E.BITLINEAR_E_NULL, key
+    assert call(n=0) == E.BITLINEAR_E_SHAPE
+    assert call(k=0) == E.BITLINEAR_E_SHAPE
+    assert call(k=(1 << 24) + 1) == E.BITLINEAR_E_SHAPE
+    assert call(m=0) == E.BITLINEAR_E_SHAPE
+    assert call(packed=A8) == E.BITLINEAR_E_ALIGN
+    assert call(y=A2) == E.BITLINEAR_E_ALIGN
+    assert call(gamma=A2) == E.BITLINEAR_E_ALIGN
+    assert call(acc=A2) == E.BITLINEAR_E_ALIGN
+    if fname == "bitlinear_forward":
+        assert call(m=17) == E.BITLINEAR_E_UNSUPPORTED
+    else:
+        assert call(m=(1 << 21) + 1) == E.BITLINEAR_E_UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors(blq):
+    torch = pytest.importorskip("torch")
+    w = torch.zeros(16, 256)
+    with pytest.raises(ValueError):
+        blq.bitlinear_pack_weights(w)

@@ -1,0 +1,260 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same
+seeded inputs.
+
+Bar (stated once, applied everywhere):
+  * int8 activation codes, ternary codes and int32 accumulators: bit-exact;
+  * a' (per-token absmax): bit-exact (it is a max of exact values);
+  * gamma: within 1e-6 relative (fp64 sums in different orders, one rounding
+    to fp32 each; in practice the bits agree);
+  * fp32 outputs y: within 1e-5 relative, and exactly 0 where the oracle's is 0.
+Shapes span several 16 x 256 weight tiles with ragged tails in n and k, token
+counts on both sides of the decode/batched split, and the degenerate cases of
+the method (all-zero weights, all-zero tokens, k = 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import (check_gamma, compare_codes, compare_y, host, log, to_dev, to_dev_bits,
+                            torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def blq():
+    torch_mod()
+    import bitlinear_quant_act_amd as m
+    m.load_library()
+    return m
+
+
+def gpu_pack(blq, w: np.ndarray):
+    packed, gamma = blq.bitlinear_pack_weights(to_dev(w))
+    return packed, gamma
+
+
+def run_case(blq, n, k, m, seed, batched, outliers=0.01, w=None, x=None, check_acc=True):
+    tag = "n=%d k=%d m=%d seed=%d %s" % (n, k, m, seed, "batched" if batched else "decode")
+    log("case", tag)
+    if w is None:
+        w = synth.latent_weights(seed, n, k)
+    if x is None:
+        x = synth.activations_bf16(seed + 1000, m, k, outliers)
+    packed, gamma = gpu_pack(blq, w)
+    xq_d, amax_d = blq.bitlinear_quant_act(to_dev_bits(x))
+    torch = torch_mod()
+    acc_d = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    fwd = blq.bitlinear_forward_batched if batched else blq.bitlinear_forward
+    y_d = fwd(packed, gamma, n, k, xq_d, amax_d, acc=acc_d)
+    ref = oracle.forward(x, w)
+    g_same = check_gamma(host(gamma)[0], ref["gamma"], tag)
+    codes = host(blq.bitlinear_unpack_weights(packed, n, k))
+    bad_rows = compare_codes(codes, ref["q"], w, ref["gamma"], g_same, tag)
+    assert np.array_equal(host(xq_d), ref["xq"]), tag
+    assert np.array_equal(host(amax_d), ref["amax"]), tag
+    keep = np.setdiff1d(np.arange(n), bad_rows)
+    acc = host(acc_d)
+    if check_acc:
+        assert np.array_equal(acc[:, keep], ref["acc"][:, keep]), tag
+    compare_y(host(y_d)[:, keep], ref["y"][:, keep], tag)
+    return acc, host(y_d)
+
+
+def test_native_library_is_loaded(blq):
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert blq.LIB_PATH in maps
+
+
+# ---------------------------------------------------------------------------
+# activation quantisation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,k", [(1, 1), (1, 7), (3, 255), (2, 256), (5, 257), (1, 2048), (4, 2560),
+                                 (9, 4096), (16, 6912), (1, 28672), (64, 8192), (512, 4096),
+                                 (3, 40000)])
+def test_quant_act_parity(blq, m, k):
+    log("quant m=%d k=%d" % (m, k))
+    x = synth.activations_bf16(m * 7 + k, m, k, 0.01)
+    xq, amax = blq.bitlinear_quant_act(to_dev_bits(x))
+    rq, ra = oracle.quant_act(x)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(amax), ra)
+
+
+def test_quant_act_special_tokens(blq):
+    k = 512
+    x = np.zeros((6, k), dtype=np.float32)
+    x[1, 3] = 1e-12                                   # below the 1e-8 floor
+    x[2, :10] = [127 / 64, 5 / 128, 7 / 128, 3 / 128, 1 / 128, -5 / 128, -3 / 128, 9 / 128, 0.5, -127 / 64]
+    x[3] = np.linspace(-3, 3, k)
+    x[4] = 3.3e38 * np.sign(np.linspace(-1, 1, k))    # near the top of the bf16 range
+    x[5, ::2] = 2.0 ** -126                           # smallest normal values
+    xb = synth.fp32_to_bf16_bits(x)
+    xq, amax = blq.bitlinear_quant_act(to_dev_bits(xb))
+    rq, ra = oracle.quant_act(xb)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(amax), ra)
+    assert (host(xq)[0] == 0).all()
+
+
+def test_quant_act_misaligned_rows(blq):
+    """Rows that start off a 16-byte boundary take the general path."""
+    torch = torch_mod()
+    m, k = 3, 1000
+    x = synth.activations_bf16(77, m, k, 0.01)
+    base = torch.zeros(m * k + 8, dtype=torch.int16, device="cuda")
+    base[1:1 + m * k] = to_dev_bits(x).view(-1)
+    xv = base[1:1 + m * k].view(m, k)
+    out = torch.zeros(m * k + 8, dtype=torch.int8, device="cuda")
+    xq = out[3:3 + m * k].view(m, k)
+    _, amax = blq.bitlinear_quant_act(xv, xq=xq)
+    rq, ra = oracle.quant_act(x)
+    assert np.array_equal(host(xq), rq) and np.array_equal(host(amax), ra)
+    o = host(out)
+    assert (o[:3] == 0).all() and (o[3 + m * k:] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# pack / unpack
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(1, 1), (3, 5), (16, 256), (17, 257), (33, 1000), (128, 2048),
+                                 (100, 4099), (2048, 2048)])
+def test_pack_parity(blq, n, k):
+    tag = "pack n=%d k=%d" % (n, k)
+    log(tag)
+    w = synth.latent_weights(n * 31 + k, n, k)
+    packed, gamma = gpu_pack(blq, w)
+    g_or = oracle.gamma(w)
+    same = check_gamma(host(gamma)[0], g_or, tag)
+    codes = host(blq.bitlinear_unpack_weights(packed, n, k))
+    compare_codes(codes, oracle.ternarize(w, g_or), w, g_or, same, tag)
+    assert packed.numel() == blq.bitlinear_packed_bytes(n, k)
+
+
+def test_pack_degenerate_weights(blq):
+    for name, w in [("zeros", np.zeros((20, 300), np.float32)),
+                    ("constant", np.full((20, 300), 0.37, np.float32)),
+                    ("negative constant", np.full((20, 300), -1e-3, np.float32)),
+                    ("single", np.array([[-0.25]], np.float32))]:
+        log("pack", name)
+        packed, gamma = gpu_pack(blq, w)
+        g_or = oracle.gamma(w)
+        assert host(gamma)[0] == g_or, name
+        assert np.array_equal(host(blq.bitlinear_unpack_weights(packed, *w.shape)), oracle.ternarize(w, g_or)), name
+
+
+def test_pack_misaligned_weights(blq):
+    torch = torch_mod()
+    n, k = 40, 600
+    w = synth.latent_weights(5, n, k)
+    base = torch.zeros(n * k + 4, dtype=torch.float32, device="cuda")
+    base[1:1 + n * k] = to_dev(w).view(-1)
+    packed, gamma = blq.bitlinear_pack_weights(base[1:1 + n * k].view(n, k))
+    g_or = oracle.gamma(w)
+    same = check_gamma(host(gamma)[0], g_or, "misaligned")
+    compare_codes(host(blq.bitlinear_unpack_weights(packed, n, k)), oracle.ternarize(w, g_or), w, g_or, same,
+                  "misaligned")
+
+
+def test_pack_is_deterministic(blq):
+    w = synth.latent_weights(99, 300, 3000)
+    p1, g1 = gpu_pack(blq, w)
+    p2, g2 = gpu_pack(blq, w)
+    assert np.array_equal(host(p1), host(p2)) and host(g1)[0] == host(g2)[0]
+
+
+# ---------------------------------------------------------------------------
+# forward: decode and batched paths
+# ---------------------------------------------------------------------------
+
+SHAPES = [(16, 256), (17, 257), (48, 1000), (200, 2048), (257, 4112), (64, 6912), (5, 1), (40, 16)]
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 9, 16])
+def test_forward_decode_parity(blq, n, k, m):
+    run_case(blq, n, k, m, seed=n + 7 * k + m, batched=False)
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("m", [1, 9, 17, 64, 100, 129, 300])
+def test_forward_batched_parity(blq, n, k, m):
+    run_case(blq, n, k, m, seed=n + 11 * k + m, batched=True)
+
+
+def test_forward_degenerate(blq):
+    # all-zero weights: gamma 0, every output exactly 0
+    run_case(blq, 30, 500, 3, seed=1, batched=False, w=np.zeros((30, 500), np.float32))
+    run_case(blq, 30, 500, 70, seed=1, batched=True, w=np.zeros((30, 500), np.float32))
+    # an all-zero token beside ordinary ones
+    x = synth.activations_bf16(5, 4, 512, 0.01)
+    x[2] = 0
+    run_case(blq, 40, 512, 4, seed=2, batched=False, x=x)
+    run_case(blq, 40, 512, 4, seed=2, batched=True, x=x)
+    # extreme accumulators: every code +-127 against all-(+1) weights
+    k = 28672
+    w = np.full((16, k), 0.5, np.float32)
+    w[1] = -0.5
+    xb = synth.fp32_to_bf16_bits(np.stack([np.ones(k, np.float32), -np.ones(k, np.float32)]))
+    acc, _ = run_case(blq, 16, k, 2, seed=3, batched=False, w=w, x=xb)
+    assert acc[0, 0] == 127 * k and acc[1, 0] == -127 * k and acc[0, 1] == -127 * k
+    acc, _ = run_case(blq, 16, k, 2, seed=3, batched=True, w=w, x=xb)
+    assert acc[0, 0] == 127 * k
+
+
+def test_decode_and_batched_agree_bitwise(blq):
+    torch = torch_mod()
+    n, k = 300, 4096
+    w = synth.latent_weights(3, n, k)
+    packed, gamma = gpu_pack(blq, w)
+    for m in (1, 5, 16):
+        xq, amax = blq.bitlinear_quant_act(to_dev_bits(synth.activations_bf16(m, m, k, 0.005)))
+        a1 = torch.empty((m, n), dtype=torch.int32, device="cuda")
+        a2 = torch.empty((m, n), dtype=torch.int32, device="cuda")
+        blq.bitlinear_forward(packed, gamma, n, k, xq, amax, acc=a1)
+        blq.bitlinear_forward_batched(packed, gamma, n, k, xq, amax, acc=a2)
+        assert torch.equal(a1, a2)
+
+
+def test_forward_is_deterministic_and_stays_in_bounds(blq):
+    """Two runs are bitwise equal; guard bands around every output stay intact."""
+    torch = torch_mod()
+    n, k, m = 100, 3000, 7
+    w = synth.latent_weights(4, n, k)
+    packed, gamma = gpu_pack(blq, w)
+    xq, amax = blq.bitlinear_quant_act(to_dev_bits(synth.activations_bf16(4, m, k, 0.01)))
+    for fwd in (blq.bitlinear_forward, blq.bitlinear_forward_batched):
+        guard = 64
+        yb = torch.full((m * n + 2 * guard,), float("nan"), device="cuda")
+        ab = torch.full((m * n + 2 * guard,), -7, dtype=torch.int32, device="cuda")
+        y1 = yb[guard:guard + m * n].view(m, n)
+        a1 = ab[guard:guard + m * n].view(m, n)
+        fwd(packed, gamma, n, k, xq, amax, y=y1, acc=a1)
+        y2 = fwd(packed, gamma, n, k, xq, amax)
+        assert torch.equal(y1, y2)
+        yh, ah = host(yb), host(ab)
+        assert np.isnan(yh[:guard]).all() and np.isnan(yh[-guard:]).all()
+        assert (ah[:guard] == -7).all() and (ah[-guard:] == -7).all()
+
+
+def test_forward_on_a_side_stream(blq):
+    torch = torch_mod()
+    n, k, m = 64, 2048, 3
+    w = synth.latent_weights(8, n, k)
+    x = synth.activations_bf16(8, m, k, 0.01)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        wd = to_dev(w)
+        xd = to_dev_bits(x)
+        packed, gamma = blq.bitlinear_pack_weights(wd, stream=s)
+        xq, amax = blq.bitlinear_quant_act(xd, stream=s)
+        y = blq.bitlinear_forward(packed, gamma, n, k, xq, amax, stream=s)
+    s.synchronize()
+    ref = oracle.forward(x, w)
+    compare_y(y.cpu().numpy(), ref["y"], "side stream")
