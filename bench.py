@@ -1,0 +1,451 @@
+#!/usr/bin/env python3
+"""Benchmark of the BitLinear forward on one MI355X.
+
+One step = one pass of the per-token path over every BitLinear of the
+workload, in layer order: bitlinear_quant_act (bf16 -> int8 codes + a') then
+bitlinear_forward (m <= 16) or bitlinear_forward_batched (m > 16) per matrix.
+The weights are packed once before timing (the one-time preparation step);
+packing is timed separately and reported under "pack".  The step is captured
+once into a HIP graph and replayed; inputs are resident in HBM and the
+weights of consecutive steps are not cache-resident (the stack is larger than
+the 256 MB last-level cache, or is replicated until it is).
+
+Prints ONE JSON line:
+  value        algorithmic bytes per step / step time (GB/s) for decode
+               workloads, or 2*M*N*K per step / step time (TOPS) for the
+               batched workload;
+  roofline     the dominant kernel (forward) against HBM or int8 MFMA peak,
+               from HIP events around each of its launches;
+  cpu_baseline the CPU oracle timed on the host cores on a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload KEY] [--m M]
+Workloads: single2048, b2b_decode (default), l8b_decode, l8b_prefill, l70b_layer.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, published
+MALL_BYTES = 256 << 20         # last-level (Infinity) cache
+COLD_BYTES = 1 << 30           # walk at least this many weight bytes between reuses
+KERNEL_SOURCES = ("gemv.hip", "gemm.hip", "quant_act.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bitlinear_quant_act_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def forward_bytes(m: int, n: int, k: int) -> int:
+    """Algorithmic bytes of one forward call: packed weights, int8 codes, a',
+    gamma, fp32 outputs."""
+    return (n * k + 3) // 4 + m * k + 4 * m + 4 + 4 * m * n
+
+
+def quant_bytes(m: int, k: int) -> int:
+    return 2 * m * k + m * k + 4 * m
+
+
+class Mat:
+    __slots__ = ("layer", "j", "n", "k", "packed", "gamma", "x", "xq", "amax", "y", "q_or", "g_or", "x_np")
+
+
+def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod):
+    """Generate, upload and pack every matrix; returns replicas x [Mat]."""
+    dev = torch.device("cuda")
+    mats = []
+    jobs = list(synth.iter_layer_matrices(wl))
+    batch = 8
+    t_pack = 0.0
+    pack_bytes = 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for b0 in range(0, len(jobs), batch):
+        chunk = jobs[b0:b0 + batch]
+        ws = synth.generate_many([(synth.seed_for(wl, l, j, synth.ROLE_WEIGHT), mt.n, mt.k) for l, j, mt in chunk])
+        for (layer, j, mt), w in zip(chunk, ws):
+            wd = torch.from_numpy(w).to(dev)
+            packed = torch.empty(blq.bitlinear_packed_bytes(mt.n, mt.k), dtype=torch.uint8, device=dev)
+            gamma = torch.empty(1, dtype=torch.float32, device=dev)
+            work = torch.empty(blq.bitlinear_pack_workspace_bytes(mt.n, mt.k), dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+            e0.record()
+            blq.bitlinear_pack_weights(wd, packed, gamma, work)
+            e1.record()
+            torch.cuda.synchronize()
+            t_pack += e0.elapsed_time(e1) * 1e-3
+            pack_bytes += 4 * mt.n * mt.k + (mt.n * mt.k + 3) // 4
+            mat = Mat()
+            mat.layer, mat.j, mat.n, mat.k = layer, j, mt.n, mt.k
+            mat.packed, mat.gamma = packed, gamma
+            x = synth.activations_bf16(synth.seed_for(wl, layer, j, synth.ROLE_ACT, extra=m), m, mt.k,
+                                       wl.outlier_frac)
+            keep_oracle_codes = len(mats) < oracle_quota
+            mat.x_np = x if keep_oracle_codes else None
+            mat.x = torch.from_numpy(x.view(np.int16)).to(dev)
+            mat.xq = torch.empty((m, mt.k), dtype=torch.int8, device=dev)
+            mat.amax = torch.empty(m, dtype=torch.float32, device=dev)
+            mat.y = torch.empty((m, mt.n), dtype=torch.float32, device=dev)
+            if keep_oracle_codes:
+                mat.g_or = oracle_mod.gamma(w)
+                mat.q_or = oracle_mod.ternarize(w, mat.g_or)
+            else:
+                mat.g_or = mat.q_or = None
+            mats.append(mat)
+            del wd
+        del ws
+        log("  packed %d/%d matrices" % (min(b0 + batch, len(jobs)), len(jobs)))
+    reps = [mats]
+    for r in range(1, replicas):
+        cp = []
+        for mat in mats:
+            c = Mat()
+            for s in Mat.__slots__:
+                setattr(c, s, getattr(mat, s))
+            c.packed = mat.packed.clone()
+            c.x, c.xq, c.amax, c.y = mat.x.clone(), torch.empty_like(mat.xq), torch.empty_like(mat.amax), torch.empty_like(mat.y)
+            c.q_or = None
+            cp.append(c)
+        reps.append(cp)
+    return reps, {"seconds": t_pack, "bytes": pack_bytes}
+
+
+def launch_step(blq, mats, m, stream, fused):
+    """One pass of the per-token path over every matrix, in layer order."""
+    if fused:
+        for mat in mats:
+            blq.bitlinear_quant_forward(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
+        return
+    fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
+    for mat in mats:
+        blq.bitlinear_quant_act(mat.x, mat.xq, mat.amax, stream=stream)
+        fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+
+
+def launch_kernel_only(blq, mats, m, stream, which):
+    """Launches of one kernel over every matrix ('quant', 'forward', 'fused')."""
+    fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
+    for mat in mats:
+        if which == "quant":
+            blq.bitlinear_quant_act(mat.x, mat.xq, mat.amax, stream=stream)
+        elif which == "forward":
+            fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+        else:
+            blq.bitlinear_quant_forward(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
+
+
+def fused_bytes(m: int, n: int, k: int) -> int:
+    """Algorithmic bytes of one fused quant + forward call: packed weights,
+    bf16 activations, gamma, fp32 outputs."""
+    return (n * k + 3) // 4 + 2 * m * k + 4 + 4 * m * n
+
+
+def time_graph(torch, stream, fn, replays):
+    """Capture fn(stream) once, replay it `replays` times between two HIP
+    events on that stream; returns ms per replay."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / replays
+
+
+def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s):
+    """The oracle (quant + contraction + dequant) over the workload's matrices
+    in layer order, on the host cores, until the sample is done or the time
+    budget is spent.  Also checks the GPU outputs of the same matrices."""
+    mats = [mt for mt in reps_mats if mt.q_or is not None]
+    done_bytes = 0
+    done_ops = 0
+    t_total = 0.0
+    worst = 0.0
+    nmat = 0
+    for mat in mats:
+        t0 = time.perf_counter()
+        xq, amax = oracle_mod.quant_act(mat.x_np)
+        if m * mat.n * mat.k <= 2e10:
+            acc = oracle_mod.contract(xq, mat.q_or)
+            y = oracle_mod.dequant(acc, mat.g_or, amax)
+            t_total += time.perf_counter() - t0
+            rows_used = m
+        else:  # a bounded slice of tokens for the very large batched case
+            sl = max(1, int(2e10 // (mat.n * mat.k)))
+            acc = oracle_mod.contract(xq[:sl], mat.q_or)
+            y = oracle_mod.dequant(acc, mat.g_or, amax[:sl])
+            t_total += time.perf_counter() - t0
+            rows_used = sl
+        done_bytes += forward_bytes(rows_used, mat.n, mat.k)
+        done_ops += 2 * rows_used * mat.n * mat.k
+        yg = mat.y[:rows_used].cpu().numpy().astype(np.float64)
+        yo = y.astype(np.float64)
+        nz = yo != 0
+        if (yg[~nz] != 0).any():
+            worst = float("inf")
+        if nz.any():
+            worst = max(worst, float((np.abs(yg[nz] - yo[nz]) / np.abs(yo[nz])).max()))
+        nmat += 1
+        if t_total > budget_s:
+            break
+    return {"seconds": t_total, "bytes": done_bytes, "ops": done_ops, "matrices": nmat, "rows": rows_used,
+            "max_rel_err": worst}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b2b_decode", choices=sorted(synth.BY_KEY))
+    ap.add_argument("--m", type=int, default=None, help="tokens per matrix (default: workload's first)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bound)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the path is single-device; "
+              "--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bitlinear_quant_act_amd as blq
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    blq.load_library()
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": nbytes, "launches": 3}))
+        return
+
+    wl = synth.BY_KEY[args.workload]
+    m = args.m if args.m is not None else wl.ms[0]
+    batched = m > blq.BITLINEAR_FORWARD_MAX_M
+    # the fused entry point re-quantises the tokens in every workgroup, which
+    # pays off for a single token; several tokens go through quant + forward
+    fused = (m == 1 and not args.unfused and
+             all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
+    want_cpu = not args.no_cpu_baseline
+    oracle_mod = None
+    if want_cpu:
+        import oracle as oracle_mod  # CPU baseline leg only
+        oracle_mod._load()
+
+    total_packed = synth.packed_weight_bytes_2bit(wl)
+    replicas = max(1, -(-COLD_BYTES // total_packed)) if total_packed < 2 * MALL_BYTES else 1
+    log("workload %s m=%d: %d matrices, %.1f MB packed, %d replica(s)" % (
+        wl.key, m, wl.layers * len(wl.matrices), total_packed / 1e6, replicas))
+    t0 = time.time()
+    # the oracle re-derives ternary codes only for the matrices its bounded
+    # sample can cover (about cpu_budget seconds of contraction work)
+    oracle_quota = 0
+    if want_cpu:
+        macs = 0.0
+        for _, _, mt in synth.iter_layer_matrices(wl):
+            rows = m if m * mt.n * mt.k <= 2e10 else max(1, int(2e10 // (mt.n * mt.k)))
+            macs += rows * mt.n * mt.k
+            oracle_quota += 1
+            if macs > args.cpu_budget * 3e9:
+                break
+    reps, pack = setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod)
+    log("setup %.1f s" % (time.time() - t0))
+
+    mats0 = reps[0]
+    step_bytes = sum(forward_bytes(m, mt.n, mt.k) for mt in mats0)
+    step_quant_bytes = sum(quant_bytes(m, mt.k) for mt in mats0)
+    step_ops = sum(2 * m * mt.n * mt.k for mt in mats0)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graphs = []
+    if not args.eager:
+        for mats in reps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                launch_step(blq, mats, m, torch.cuda.current_stream(), fused)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if args.eager:
+            with torch.cuda.stream(stream):
+                launch_step(blq, reps[i % len(reps)], m, stream, fused)
+        else:
+            graphs[i % len(graphs)].replay()
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    log("warmup done")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        run(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
+
+    # Dominant kernel (the forward, or the fused quant + forward): HIP events
+    # on its stream around graph replays that hold only that kernel's
+    # launches over every matrix of the workload (no event per launch: an
+    # event pair costs more than a small kernel).  Average launch duration =
+    # elapsed / launches.  The quantisation kernel is timed the same way.
+    if not fused:  # make sure the codes are current for forward-only replays
+        with torch.cuda.stream(stream):
+            launch_kernel_only(blq, mats0, m, stream, "quant")
+        torch.cuda.synchronize()
+    replays = max(2, min(10, args.steps))
+    dom = "fused" if fused else "forward"
+    dom_ms = 0.0
+    for r, mats in enumerate(reps):
+        dom_ms += time_graph(torch, stream, lambda st, mats=mats: launch_kernel_only(blq, mats, m, st, dom), replays)
+    dom_ms /= len(reps)
+    nlaunch = len(mats0) * replays * len(reps)
+    fw_avg_us = dom_ms / len(mats0) * 1e3
+    q_ms = time_graph(torch, stream, lambda st: launch_kernel_only(blq, mats0, m, st, "quant"), replays)
+    q_avg_us = q_ms / len(mats0) * 1e3
+    per_call = fused_bytes if fused else forward_bytes
+    fw_bytes = sum(per_call(m, mt.n, mt.k) for mt in mats0)
+    fw_ops = step_ops
+    fw_ms = dom_ms
+    if batched:
+        value = step_ops / (ms_per_step * 1e-3) / 1e12
+        unit = "TOPS"
+        achieved = fw_ops / (fw_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_I8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_I8_PEAK_TOPS, 4)}
+    else:
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = fw_bytes / (fw_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = ("bitlinear_forward_batched (gemm_kernel)" if batched else
+                      "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)" if fused else
+                      "bitlinear_forward (gemv kernel)")
+    roof["avg_launch_us"] = round(fw_avg_us, 3)
+    roof["launches_timed"] = nlaunch
+    roof["per_launch"] = "mean over the workload's matrices of %s" % (
+        "2*M*N*K" if batched else "ceil(N*K/4)+2*M*K+4+4*M*N bytes" if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
+    roof["timing"] = "HIP events around %d graph replays of the kernel's %d launches" % (replays, len(mats0))
+    roof["traffic"] = None
+    prof = os.path.join(ROOT, "profiles", "counters_%s_m%d.json" % (wl.key, m))
+    if os.path.exists(prof):
+        with open(prof) as f:
+            c = json.load(f)
+        if c.get("kernel_source_hash") == kernel_source_hash():
+            roof["traffic"] = c.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": "BitLinear GEMV effective HBM GB/s (% of peak); batched int8 TOPS (% MFMA peak)",
+        "value": round(value, 2 if batched else 1),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded N(0,0.02) latent weights, N(0,1) bf16 activations)",
+        "config": {
+            "workload": wl.title,
+            "key": wl.key,
+            "m": m,
+            "layers": wl.layers,
+            "matrices_per_step": len(mats0),
+            "shapes_kxn": ["%dx%d" % (mt.k, mt.n) for mt in wl.matrices],
+            "entry_points": ("bitlinear_quant_forward" if fused else
+                             "bitlinear_quant_act + " + ("bitlinear_forward_batched" if batched else "bitlinear_forward")),
+            "launch": ("hip graph, %d kernels per step" % ((1 if fused else 2) * len(mats0))
+                       if not args.eager else "eager"),
+            "cold_cache": "weights %.0f MB per step x %d replica(s)" % (total_packed / 1e6, len(reps)),
+            "step_bytes": step_bytes,
+            "step_ops": step_ops,
+        },
+        "pct_of_peak": round(100 * value / (MFMA_I8_PEAK_TOPS if batched else HBM_PEAK_GBS), 2),
+        "roofline": roof,
+        "quant_kernel": {"avg_launch_us": round(q_avg_us, 3),
+                         "gbs": round(step_quant_bytes / (q_ms * 1e-3) / 1e9, 1)},
+        "pack": {"seconds": round(pack["seconds"], 4),
+                 "gbs": round(pack["bytes"] / pack["seconds"] / 1e9, 1) if pack["seconds"] > 0 else None},
+    }
+
+    if want_cpu:
+        log("cpu baseline (oracle) ...")
+        cb = cpu_baseline(oracle_mod, mats0, m, wl, args.cpu_budget)
+        cores = oracle_mod.num_threads()
+        if batched:
+            v = cb["ops"] / cb["seconds"] / 1e12
+            u = "TOPS"
+        else:
+            v = cb["bytes"] / cb["seconds"] / 1e9
+            u = "GB/s"
+        out["cpu_baseline"] = {
+            "value": round(v, 4), "unit": u, "cores": cores, "kind": "oracle",
+            "sample": "%d of %d matrices in layer order, %d token(s) each: quant + contraction + dequant "
+                      "(%.2f s)" % (cb["matrices"], len(mats0), cb["rows"], cb["seconds"]),
+            "cpu": _cpu_model(),
+        }
+        out["parity_vs_oracle"] = {"matrices": cb["matrices"], "max_rel_err_y": cb["max_rel_err"],
+                                   "ok": bool(cb["max_rel_err"] <= 1e-5)}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

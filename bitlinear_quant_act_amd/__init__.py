@@ -78,6 +78,10 @@ def load_library(path: str = LIB_PATH):
     lib.bitlinear_unpack_weights.restype = _ct.c_int
     lib.bitlinear_quant_act.argtypes = [_p, _i64, _i64, _p, _p, _p]
     lib.bitlinear_quant_act.restype = _ct.c_int
+    lib.bitlinear_quant_forward.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
+    lib.bitlinear_quant_forward.restype = _ct.c_int
+    lib.bitlinear_quant_forward_supported.argtypes = [_i64, _i64]
+    lib.bitlinear_quant_forward_supported.restype = _ct.c_int
     for name in ("bitlinear_forward", "bitlinear_forward_batched"):
         fn = getattr(lib, name)
         fn.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
@@ -221,8 +225,41 @@ def bitlinear_forward_batched(packed, gamma, n: int, k: int, xq, x_absmax, y=Non
     return _forward("bitlinear_forward_batched", packed, gamma, n, k, xq, x_absmax, y, acc, stream)
 
 
+def bitlinear_quant_forward_supported(m: int, k: int) -> bool:
+    return bool(load_library().bitlinear_quant_forward_supported(m, k))
+
+
+def bitlinear_quant_forward(packed, gamma, n: int, k: int, x, y=None, acc=None, xq=None, x_absmax=None,
+                            stream=None):
+    """Fused activation quantisation + decode forward (1 <= m <= 16, m*k codes
+    within the on-chip budget).  x: bf16 [m][k] (or int16 bit patterns).
+    Optional outputs: exact int32 acc [m][n]; the codes xq [m][k] and a' [m]
+    (pass both or neither).  Returns y fp32 [m][n]."""
+    lib = load_library()
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m][k]")
+    m = x.shape[0]
+    if packed.numel() * packed.element_size() < bitlinear_packed_bytes(n, k):
+        raise BitlinearError(BITLINEAR_E_SIZE, "bitlinear_quant_forward")
+    if y is None:
+        y = _torch.empty((m, n), dtype=_torch.float32, device=x.device)
+    rc = lib.bitlinear_quant_forward(
+        _dev(packed, "packed", (_torch.uint8,)), _dev(gamma, "gamma", (_torch.float32,), 1), n, k,
+        _dev(x, "x", (_torch.bfloat16, _torch.int16, _torch.uint16)), m,
+        _dev(y, "y", (_torch.float32,), m * n),
+        None if acc is None else _dev(acc, "acc", (_torch.int32,), m * n),
+        None if xq is None else _dev(xq, "xq", (_torch.int8,), m * k),
+        None if x_absmax is None else _dev(x_absmax, "x_absmax", (_torch.float32,), m),
+        _stream_handle(stream))
+    _check(rc, "bitlinear_quant_forward")
+    return y
+
+
 def bitlinear(x, packed, gamma, n: int, k: int, stream=None):
-    """Convenience: quantise x (bf16 [m][k]) and run the forward path that fits m."""
+    """Convenience: run the fastest entry point that fits x (bf16 [m][k])."""
+    m = x.shape[0]
+    if m == 1 and bitlinear_quant_forward_supported(m, k):
+        return bitlinear_quant_forward(packed, gamma, n, k, x, stream=stream)
     xq, amax = bitlinear_quant_act(x, stream=stream)
     if x.shape[0] <= BITLINEAR_FORWARD_MAX_M:
         return bitlinear_forward(packed, gamma, n, k, xq, amax, stream=stream)

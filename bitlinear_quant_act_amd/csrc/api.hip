@@ -96,6 +96,26 @@ int bitlinear_forward(const void* packed, const float* gamma, int64_t n, int64_t
                                           static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_quant_forward(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
+                            int64_t m, float* y, int32_t* acc_or_null, int8_t* xq_or_null, float* x_absmax_or_null,
+                            void* stream) {
+  if (!packed || !gamma || !x || !y) return BITLINEAR_E_NULL;
+  if (int rc = check_nk(n, k)) return rc;
+  if (m < 1 || m > kMaxRows) return BITLINEAR_E_SHAPE;
+  if ((xq_or_null == nullptr) != (x_absmax_or_null == nullptr)) return BITLINEAR_E_NULL;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(x, 2) || !aligned(y, 4) ||
+      (acc_or_null && !aligned(acc_or_null, 4)) || (x_absmax_or_null && !aligned(x_absmax_or_null, 4)))
+    return BITLINEAR_E_ALIGN;
+  if (m > BITLINEAR_FORWARD_MAX_M || !bitlinear::gemv_fits_lds(m, k)) return BITLINEAR_E_UNSUPPORTED;
+  return status_of(bitlinear::launch_quant_gemv(packed, gamma, n, k, x, m, y, acc_or_null, xq_or_null,
+                                                x_absmax_or_null, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quant_forward_supported(int64_t m, int64_t k) {
+  if (m < 1 || m > BITLINEAR_FORWARD_MAX_M || k < 1 || k > kMaxK) return 0;
+  return bitlinear::gemv_fits_lds(m, k) ? 1 : 0;
+}
+
 int bitlinear_forward_batched(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                               const float* x_absmax, int64_t m, float* y, int32_t* acc_or_null, void* stream) {
   if (int rc = check_forward(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null)) return rc;

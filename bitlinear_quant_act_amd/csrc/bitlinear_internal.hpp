@@ -38,6 +38,9 @@ hipError_t launch_unpack(const void* packed, int64_t n, int64_t k, int8_t* codes
 hipError_t launch_gemv(const void* packed, const float* gamma, int64_t n, int64_t k,
                        const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc,
                        hipStream_t s);
+bool gemv_fits_lds(int64_t m, int64_t k);
+hipError_t launch_quant_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
+                             int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s);
 hipError_t launch_gemm(const void* packed, const float* gamma, int64_t n, int64_t k,
                        const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc,
                        hipStream_t s);

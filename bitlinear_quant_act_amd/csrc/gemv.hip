@@ -1,39 +1,522 @@
 // Decode-path BitLinear forward for 1..16 tokens.
 //
 // "BitNet b1.58 in Production: 1-Bit LLMs and Energy Benchmarks", section
-// "The Mathematical Mechanism", items 3-4: acc = sum_k x_q * W_q with
-// W_q in {-1, 0, +1} (adds and subtracts only), then y = acc * gamma * a' / 127.
-// "BitNet 1-bit LLM Inference Framework", section "Scalability with Thread
-// Count": generation is bound by memory bandwidth, so the kernel is built to
-// stream the 2-bit weights from HBM exactly once at full width.
+// "The Mathematical Mechanism", items 2-4: per-token int8 codes, acc =
+// sum_k x_q * W_q with W_q in {-1, 0, +1} (adds and subtracts only), then
+// y = acc * gamma * a' / 127.  "BitNet 1-bit LLM Inference Framework",
+// section "Scalability with Thread Count": generation is bound by memory
+// bandwidth, so the kernel is built to stream the 2-bit weights from HBM
+// exactly once, with as many bytes in flight as the chip can hold.
 //
 // Work split: one workgroup per 16-row block of W; its waves take the block's
 // 256-column tiles round-robin (wave w: tiles w, w + WAVES, ...), so at any
 // moment the workgroup reads consecutive KiB of one contiguous stream.  Each
-// wave issues U tile loads (16 B per lane, fully coalesced 1 KiB per wave)
-// before it consumes any, to keep enough bytes in flight.
+// wave keeps two batches of U tiles in flight (16 B per lane per tile, one
+// fully coalesced 1 KiB load per wave): the next batch is requested before
+// the current one is consumed.
 //
-// Contraction on the matrix cores, not a dot-product loop: one
-// v_mfma_i32_16x16x64_i8 takes 16 tokens x 64 columns of int8 activations
-// (A; rows >= m are zero) and 64 columns x 16 weight rows (B).  The B operand
-// of a lane is exactly one 32-bit word of its packed slot expanded with one
-// shift and one mask per 4 weights: (word >> 2j) & 0x03030303 gives the
-// stored values w + 1 in {0, 1, 2} as int8.  The offset is removed exactly
-// with a second MFMA against an all-ones B (sum_k x), which runs on the
-// otherwise idle matrix pipe:  acc = sum (w + 1) x - sum x.  Both sums are
-// exact int32.  The activation operand of a lane is the 16 bytes of its own
-// token at the same 16 columns, so the k order inside the instruction is the
-// same for A and B and needs no shuffling.
+// Activation codes live in LDS for the whole kernel (m rows of k bytes,
+// padded pitch so the 16 token rows of one operand read hit distinct banks).
+// They are staged once per workgroup by one of two prologues:
+//   * kFromCodes: copied from the int8 codes of bitlinear_quant_act;
+//   * kFromBf16:  computed from the bf16 activations (the activation
+//     quantisation fused into the GEMV prologue) -- per-token max|x| as
+//     integer bit patterns, a' = max(., 1e-8), s = 127 / a' (IEEE divide),
+//     code = clamp(rint(x * s)), bit-identical to bitlinear_quant_act.
+// The weight loads of the first batch are issued before the prologue, so the
+// two latencies overlap.
+//
+// Contraction on the matrix cores: one v_mfma_i32_16x16x64_i8 takes 16
+// tokens x 64 columns of int8 codes (A; rows >= m are zero) and 64 columns x
+// 16 weight rows (B).  The B operand of a lane is one 32-bit word of its
+// packed slot expanded with one shift and one mask per 4 weights: (word >>
+// 2j) & 0x03030303 gives the stored values w + 1 in {0, 1, 2} as int8.  The
+// offset is removed exactly with a second MFMA against an all-ones B (sum_k
+// x), which runs on the otherwise idle matrix pipe:  acc = sum (w + 1) x -
+// sum x, both exact in int32.  A lane's A operand is the 16 codes of its own
+// token at the same 16 columns, so A and B share the k order.
 //
 // Epilogue: the waves' int32 partials are summed through LDS and scaled by
 // gamma * a'[m] / 127 in fp32; lanes 0..15 of a result row write 16
 // consecutive floats.
+//
+// When the codes do not fit the LDS budget (m * k beyond ~64 KiB) the
+// global-operand variant reads each lane's 16-byte A operand straight from
+// the int8 codes in memory instead.
 #include "bitlinear_internal.hpp"
 
 namespace bitlinear {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+
+#ifndef BITLINEAR_GEMV_MAX_GROUPS
+#define BITLINEAR_GEMV_MAX_GROUPS 1024
+#endif
+#ifndef BITLINEAR_GEMV_WAVES
+#define BITLINEAR_GEMV_WAVES 8
+#endif
+constexpr int64_t kMaxResidentGroups = BITLINEAR_GEMV_MAX_GROUPS;  // persistent grid cap
+constexpr int kWaves = BITLINEAR_GEMV_WAVES;                        // waves per workgroup
+// dynamic LDS budget: 64 KiB less the static reduction buffer and scalars
+constexpr int kMaxLdsBytes = 65536 - kWaves * 4 * 64 * 4 - 512;
+constexpr int kCachedChunks = 4;  // bf16 chunks per thread kept in registers between prologue passes
+
+enum Source { kFromCodes = 0, kFromBf16 = 1 };
+
+__device__ __forceinline__ v4i expand(uint32_t word) {
+  return v4i{static_cast<int>(word & 0x03030303u), static_cast<int>((word >> 2) & 0x03030303u),
+             static_cast<int>((word >> 4) & 0x03030303u), static_cast<int>((word >> 6) & 0x03030303u)};
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ uint32_t quant_code(uint32_t bits16, float s) {
+  float r = rintf(bf16_to_f32(bits16) * s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
+}
+
+// LDS row pitch of the staged codes: the padded k extent plus 16 bytes, so
+// consecutive token rows start 4 banks apart.
+__host__ __device__ inline int64_t lds_pitch(int64_t kt_count) { return kt_count * kTileCols + 16; }
+
+// dynamic LDS of the LDS-operand kernel: the staged codes
+inline size_t lds_bytes(int64_t m, int64_t kt_count) { return static_cast<size_t>(m * lds_pitch(kt_count)); }
+
+// ---------------------------------------------------------------------------
+// prologues: fill xs[t][0 .. kt_count*256) for t < m (zero past k)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int byte_sum(uint32_t w, int acc) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(w), 0x01010101, acc, false);
+}
+
+// Per-token partial sums of codes, flushed to xsum_s when the token changes.
+struct TokenSum {
+  int t = -1;
+  int v = 0;
+  __device__ void add(int* xsum_s, int token, int x) {
+    if (token != t) {
+      flush(xsum_s);
+      t = token;
+    }
+    v += x;
+  }
+  __device__ void flush(int* xsum_s) {
+    if (t >= 0 && v != 0) atomicAdd(&xsum_s[t], v);
+    v = 0;
+  }
+};
+
+// Vector path, first step: request the thread's first kCachedChunks 16-byte
+// chunks of codes (chunk c = thread + j * blockDim.x) before anything else.
+__device__ __forceinline__ void prefetch_codes(uint4 (&cache)[kCachedChunks], const int8_t* __restrict__ xq, int m,
+                                               int64_t k, int kpad) {
+  const int cpr = kpad / 16;
+#pragma unroll
+  for (int j = 0; j < kCachedChunks; ++j) {
+    const int c = threadIdx.x + j * static_cast<int>(blockDim.x);
+    cache[j] = make_uint4(0, 0, 0, 0);
+    if (c < m * cpr) {
+      const int t = c / cpr, cc = c - t * cpr;
+      const int64_t col = static_cast<int64_t>(cc) * 16;
+      if (col < k) cache[j] = *reinterpret_cast<const uint4*>(xq + t * k + col);
+    }
+  }
+}
+
+__device__ void stage_codes(int8_t* xs, int pitch, int* xsum_s, const uint4 (&cache)[kCachedChunks],
+                            const int8_t* __restrict__ xq, int m, int64_t k, int kpad, bool vec) {
+  const int nthreads = blockDim.x;
+  TokenSum ts;
+  if (vec) {  // k % 16 == 0 and xq 16-byte aligned
+    const int cpr = kpad / 16;
+    int j = 0;
+    for (int c = threadIdx.x; c < m * cpr; c += nthreads, ++j) {
+      const int t = c / cpr, cc = c - t * cpr;
+      const int64_t col = static_cast<int64_t>(cc) * 16;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j < kCachedChunks) {
+#pragma unroll
+        for (int q = 0; q < kCachedChunks; ++q)
+          if (q == j) v = cache[q];
+      } else if (col < k) {
+        v = *reinterpret_cast<const uint4*>(xq + t * k + col);
+      }
+      *reinterpret_cast<uint4*>(xs + t * pitch + cc * 16) = v;
+      ts.add(xsum_s, t, byte_sum(v.w, byte_sum(v.z, byte_sum(v.y, byte_sum(v.x, 0)))));
+    }
+  } else {
+    for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
+      const int t = c / kpad, col = c - t * kpad;
+      const int8_t q = col < k ? xq[t * k + col] : static_cast<int8_t>(0);
+      xs[t * pitch + col] = q;
+      ts.add(xsum_s, t, q);
+    }
+  }
+  ts.flush(xsum_s);
+}
+
+// Quantise m bf16 rows into xs; a' to amax_s[t].  Optionally also writes the
+// codes and a' to global memory (done by workgroup 0 only).
+// Vector path, first step: request the thread's first kCachedChunks chunks of
+// 8 bf16 values (chunk c = thread + j * blockDim.x) before anything else.
+__device__ __forceinline__ void prefetch_bf16(uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int m,
+                                              int64_t k) {
+  const int total = m * static_cast<int>(k / 8);
+#pragma unroll
+  for (int j = 0; j < kCachedChunks; ++j) {
+    const int c = threadIdx.x + j * static_cast<int>(blockDim.x);
+    cache[j] = c < total ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s, int* xsum_s,
+                           const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x,
+                           int m, int64_t k, int kpad, bool vec, int8_t* __restrict__ xq_out,
+                           float* __restrict__ amax_out) {
+  const int nthreads = blockDim.x;
+  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
+  if (threadIdx.x < m) max_s[threadIdx.x] = 0u;
+  __syncthreads();
+  if (vec) {  // k % 8 == 0 and x 16-byte aligned: chunks of 8 values
+    const int cpr = static_cast<int>(k / 8);
+    const int total = m * cpr;
+    // pass 1: per-token max of |x| bit patterns; the first chunks of each
+    // thread are already in registers (prefetch_bf16)
+    int cur_t = -1;
+    unsigned cur = 0;
+    int j = 0;
+    for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+      const int t = c / cpr;
+      if (t != cur_t) {
+        if (cur_t >= 0) atomicMax(&max_s[cur_t], cur);
+        cur_t = t;
+        cur = 0;
+      }
+      uint4 v;
+      if (j < kCachedChunks) {
+#pragma unroll
+        for (int q = 0; q < kCachedChunks; ++q)
+          if (q == j) v = cache[q];
+      } else {
+        v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8);
+      }
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cur = max(cur, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+    }
+    if (cur_t >= 0) atomicMax(&max_s[cur_t], cur);
+    __syncthreads();
+    if (threadIdx.x < m) amax_s[threadIdx.x] = fmaxf(bf16_to_f32(max_s[threadIdx.x]), 1e-8f);
+    __syncthreads();
+    // pass 2: codes (chunks past the register cache are re-read from L1/L2)
+    TokenSum ts;
+    j = 0;
+    for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+      const int t = c / cpr, cc = c - t * cpr;
+      const float s = 127.0f / amax_s[t];
+      uint4 v;
+      if (j < kCachedChunks) {
+#pragma unroll
+        for (int q = 0; q < kCachedChunks; ++q)
+          if (q == j) v = cache[q];
+      } else {
+        v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8);
+      }
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        lo |= quant_code(w[j] & 0xffffu, s) << (16 * j);
+        lo |= quant_code(w[j] >> 16, s) << (16 * j + 8);
+        hi |= quant_code(w[j + 2] & 0xffffu, s) << (16 * j);
+        hi |= quant_code(w[j + 2] >> 16, s) << (16 * j + 8);
+      }
+      *reinterpret_cast<uint2*>(xs + t * pitch + cc * 8) = make_uint2(lo, hi);
+      if (write_out) *reinterpret_cast<uint2*>(xq_out + t * k + cc * 8) = make_uint2(lo, hi);
+      ts.add(xsum_s, t, byte_sum(hi, byte_sum(lo, 0)));
+    }
+    ts.flush(xsum_s);
+    // zero the padding past k
+    const int padc = (kpad - static_cast<int>(k)) / 8;
+    for (int c = threadIdx.x; c < m * padc; c += nthreads) {
+      const int t = c / padc, cc = c - t * padc;
+      *reinterpret_cast<uint2*>(xs + t * pitch + static_cast<int>(k) + cc * 8) = make_uint2(0, 0);
+    }
+  } else {
+    for (int t = 0; t < m; ++t) {
+      unsigned cur = 0;
+      for (int64_t i = threadIdx.x; i < k; i += nthreads) cur = max(cur, static_cast<unsigned>(x[t * k + i]) & 0x7fffu);
+      atomicMax(&max_s[t], cur);
+    }
+    __syncthreads();
+    if (threadIdx.x < m) amax_s[threadIdx.x] = fmaxf(bf16_to_f32(max_s[threadIdx.x]), 1e-8f);
+    __syncthreads();
+    TokenSum ts;
+    for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
+      const int t = c / kpad, col = c - t * kpad;
+      int8_t q = 0;
+      if (col < k) {
+        q = static_cast<int8_t>(quant_code(x[t * k + col], 127.0f / amax_s[t]));
+        if (write_out) xq_out[t * k + col] = q;
+      }
+      xs[t * pitch + col] = q;
+      ts.add(xsum_s, t, q);
+    }
+    ts.flush(xsum_s);
+  }
+  if (write_out && threadIdx.x < m) amax_out[threadIdx.x] = amax_s[threadIdx.x];
+}
+
+// ---------------------------------------------------------------------------
+// single-token prologues (m == 1, vector path): reductions across the wave
+// with lane shuffles and across waves through one LDS slot per wave -- no
+// same-address atomics and one barrier fewer than the general prologues.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ unsigned wave_max(unsigned v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int WAVES>
+__device__ void stage_codes_single(int8_t* xs, int* wsum_s, const uint4 (&cache)[kCachedChunks],
+                                   const int8_t* __restrict__ xq, int64_t k, int kpad) {
+  const int nthreads = blockDim.x;
+  const int cpr = kpad / 16;
+  int sum = 0;
+  int j = 0;
+  for (int c = threadIdx.x; c < cpr; c += nthreads, ++j) {
+    const int64_t col = static_cast<int64_t>(c) * 16;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (j < kCachedChunks) {
+#pragma unroll
+      for (int q = 0; q < kCachedChunks; ++q)
+        if (q == j) v = cache[q];
+    } else if (col < k) {
+      v = *reinterpret_cast<const uint4*>(xq + col);
+    }
+    *reinterpret_cast<uint4*>(xs + c * 16) = v;
+    sum = byte_sum(v.w, byte_sum(v.z, byte_sum(v.y, byte_sum(v.x, sum))));
+  }
+  sum = wave_sum(sum);
+  if ((threadIdx.x & 63) == 0) wsum_s[threadIdx.x >> 6] = sum;
+}
+
+template <int WAVES>
+__device__ void stage_bf16_single(int8_t* xs, float* amax_s, unsigned* wmax_s, int* wsum_s,
+                                  const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int64_t k,
+                                  int kpad, int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
+  const int nthreads = blockDim.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
+  const int total = static_cast<int>(k / 8);
+  unsigned mx = 0;
+  int j = 0;
+  for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+    uint4 v;
+    if (j < kCachedChunks) {
+#pragma unroll
+      for (int q = 0; q < kCachedChunks; ++q)
+        if (q == j) v = cache[q];
+    } else {
+      v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8);
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx = max(mx, max(w[q] & 0x7fffu, (w[q] >> 16) & 0x7fffu));
+  }
+  mx = wave_max(mx);
+  if (lane == 0) wmax_s[wave] = mx;
+  __syncthreads();
+  unsigned mall = wmax_s[0];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) mall = max(mall, wmax_s[w]);
+  const float a = fmaxf(bf16_to_f32(mall), 1e-8f);
+  const float s = 127.0f / a;
+  if (threadIdx.x == 0) {
+    amax_s[0] = a;
+    if (write_out) amax_out[0] = a;
+  }
+  int sum = 0;
+  j = 0;
+  for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+    uint4 v;
+    if (j < kCachedChunks) {
+#pragma unroll
+      for (int q = 0; q < kCachedChunks; ++q)
+        if (q == j) v = cache[q];
+    } else {
+      v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8);
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      lo |= quant_code(w[q] & 0xffffu, s) << (16 * q);
+      lo |= quant_code(w[q] >> 16, s) << (16 * q + 8);
+      hi |= quant_code(w[q + 2] & 0xffffu, s) << (16 * q);
+      hi |= quant_code(w[q + 2] >> 16, s) << (16 * q + 8);
+    }
+    *reinterpret_cast<uint2*>(xs + c * 8) = make_uint2(lo, hi);
+    if (write_out) *reinterpret_cast<uint2*>(xq_out + c * 8) = make_uint2(lo, hi);
+    sum = byte_sum(hi, byte_sum(lo, sum));
+  }
+  for (int c = total + threadIdx.x; c < kpad / 8; c += nthreads) *reinterpret_cast<uint2*>(xs + c * 8) = make_uint2(0, 0);
+  sum = wave_sum(sum);
+  if (lane == 0) wsum_s[wave] = sum;
+}
+
+// ---------------------------------------------------------------------------
+// main kernel: activation codes in LDS, persistent over row blocks
+// ---------------------------------------------------------------------------
+
+// Work items of a workgroup: its row blocks rb = blockIdx.x + i * gridDim.x,
+// each cut into chunks of U * WAVES tiles (one chunk unless k is long).  A
+// wave's share of item (rb, c) is tiles c*U*WAVES + wave + u*WAVES, u < U.
+template <int WAVES, int U>
+__device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict__ packed, int64_t rb, int c,
+                                          int kt_count, int wave, int lane, bool valid) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int kt = c * U * WAVES + wave + u * WAVES;
+    w[u] = (valid && kt < kt_count) ? packed[(rb * kt_count + kt) * 64 + lane]
+                                    : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
+  }
+}
+
+template <int WAVES, int U, int SRC, bool VEC>
+__global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __restrict__ packed,
+                                                              const float* __restrict__ gamma_p, int64_t n,
+                                                              int64_t k, int kt_count, int64_t rb_count,
+                                                              const void* __restrict__ xsrc,
+                                                              const float* __restrict__ amax_in, int m,
+                                                              float* __restrict__ y, int32_t* __restrict__ acc_out,
+                                                              int8_t* __restrict__ xq_out,
+                                                              float* __restrict__ amax_out) {
+  extern __shared__ __attribute__((aligned(16))) int8_t xs[];
+  __shared__ int red[WAVES * 4 * 64];
+  __shared__ float amax_s[16];
+  __shared__ int xsum_s[16];
+  __shared__ unsigned max_s[16];
+  __shared__ unsigned wmax_s[WAVES];
+  __shared__ int wsum_s[WAVES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;    // 64-column group of the lane inside a tile
+  const int tok = lane & 15;  // token row of the lane's A operand
+  const bool has_tok = tok < m;
+  const bool single = VEC && m == 1;
+  const int pitch = static_cast<int>(lds_pitch(kt_count));
+  const int nchunks = (kt_count + U * WAVES - 1) / (U * WAVES);
+
+  int64_t rb = blockIdx.x;
+  int c = 0;
+  // Request order matters: vector-memory results are waited for in issue
+  // order, so the activations go first and the prologue can run while the
+  // first item's weight tiles are still in flight.
+  uint4 cache[kCachedChunks];
+  if (VEC) {
+    if (SRC == kFromCodes)
+      prefetch_codes(cache, static_cast<const int8_t*>(xsrc), m, k, kt_count * kTileCols);
+    else
+      prefetch_bf16(cache, static_cast<const uint16_t*>(xsrc), m, k);
+  }
+  uint4 wcur[U];
+  load_item<WAVES, U>(wcur, packed, rb, c, kt_count, wave, lane, rb < rb_count);
+
+  if (single) {
+    if (SRC == kFromCodes) {
+      stage_codes_single<WAVES>(xs, wsum_s, cache, static_cast<const int8_t*>(xsrc), k, kt_count * kTileCols);
+      if (threadIdx.x == 0) amax_s[0] = amax_in[0];
+    } else {
+      stage_bf16_single<WAVES>(xs, amax_s, wmax_s, wsum_s, cache, static_cast<const uint16_t*>(xsrc), k,
+                               kt_count * kTileCols, xq_out, amax_out);
+    }
+  } else {
+    if (threadIdx.x < 16) xsum_s[threadIdx.x] = 0;
+    if (SRC == kFromCodes) {
+      __syncthreads();
+      stage_codes(xs, pitch, xsum_s, cache, static_cast<const int8_t*>(xsrc), m, k, kt_count * kTileCols, VEC);
+      if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x];
+    } else {
+      stage_bf16(xs, pitch, amax_s, max_s, xsum_s, cache, static_cast<const uint16_t*>(xsrc), m, k,
+                 kt_count * kTileCols, VEC, xq_out, amax_out);
+    }
+  }
+  __syncthreads();
+  int sum0 = 0;  // token 0's code sum on the single-token path
+  if (single) {
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum0 += wsum_s[w];
+  }
+
+  const float gamma = *gamma_p;
+  const v4i zero4 = {0, 0, 0, 0};
+  const int8_t* xrow = xs + (has_tok ? tok : 0) * pitch + g * 64;
+  v4i acc = zero4;
+  while (rb < rb_count) {
+    int64_t rbn = rb;
+    int cn = c + 1;
+    if (cn == nchunks) {
+      cn = 0;
+      rbn = rb + gridDim.x;
+    }
+    uint4 wnext[U];
+    load_item<WAVES, U>(wnext, packed, rbn, cn, kt_count, wave, lane, rbn < rb_count);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kt = c * U * WAVES + wave + u * WAVES;
+      if (kt < kt_count) {
+        const uint32_t words[4] = {wcur[u].x, wcur[u].y, wcur[u].z, wcur[u].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const v4i a = has_tok ? *reinterpret_cast<const v4i*>(xrow + kt * kTileCols + 16 * s) : zero4;
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand(words[s]), acc, 0, 0, 0);
+        }
+      }
+    }
+    if (c == nchunks - 1) {
+      // lane holds sum (w + 1) x for tokens 4g + r (r = 0..3) of weight row 16 rb + tok
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
+      __syncthreads();
+      const int64_t row = rb * kTileRows + tok;
+      for (int r = wave; r < 4; r += WAVES) {
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) v += red[(w * 4 + r) * 64 + lane];
+        const int t = 4 * g + r;
+        if (t < m && row < n) {
+          v -= single ? sum0 : xsum_s[t];
+          const float scale = gamma * amax_s[t] / 127.0f;
+          y[t * n + row] = static_cast<float>(v) * scale;
+          if (acc_out) acc_out[t * n + row] = v;
+        }
+      }
+      __syncthreads();
+      acc = zero4;
+    }
+    rb = rbn;
+    c = cn;
+#pragma unroll
+    for (int u = 0; u < U; ++u) wcur[u] = wnext[u];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fallback: A operand read from the int8 codes in global memory
+// ---------------------------------------------------------------------------
 
 __device__ __forceinline__ v4i load_x16(const int8_t* __restrict__ row, int64_t col, int64_t k, bool valid,
                                         bool vec) {
@@ -51,23 +534,19 @@ __device__ __forceinline__ v4i load_x16(const int8_t* __restrict__ row, int64_t 
   return r;
 }
 
-__device__ __forceinline__ v4i expand(uint32_t word) {
-  return v4i{static_cast<int>(word & 0x03030303u), static_cast<int>((word >> 2) & 0x03030303u),
-             static_cast<int>((word >> 4) & 0x03030303u), static_cast<int>((word >> 6) & 0x03030303u)};
-}
-
 template <int WAVES, int U, bool VEC>
-__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint4* __restrict__ packed,
-                                                          const float* __restrict__ gamma_p, int64_t n,
-                                                          int64_t k, int kt_count,
-                                                          const int8_t* __restrict__ xq,
-                                                          const float* __restrict__ amax, int m,
-                                                          float* __restrict__ y, int32_t* __restrict__ acc_out) {
+__global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __restrict__ packed,
+                                                                 const float* __restrict__ gamma_p, int64_t n,
+                                                                 int64_t k, int kt_count,
+                                                                 const int8_t* __restrict__ xq,
+                                                                 const float* __restrict__ amax, int m,
+                                                                 float* __restrict__ y, int32_t* __restrict__ acc_out) {
+  __shared__ int red[WAVES][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t rb = blockIdx.x;
-  const int g = lane >> 4;    // 64-column group of the lane inside a tile
-  const int tok = lane & 15;  // token row of the lane's A operand
+  const int g = lane >> 4;
+  const int tok = lane & 15;
   const bool has_tok = tok < m;
   const uint4* tiles = packed + rb * kt_count * 64 + lane;
   const int8_t* xrow = xq + static_cast<int64_t>(has_tok ? tok : 0) * k;
@@ -97,24 +576,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint4* __restric
       }
     }
   }
-  // lane holds tokens 4g + r (r = 0..3) for weight row 16 rb + (lane % 16)
-  v4i res = acc - sum;
-
+  const v4i res = acc - sum;
   const int64_t row = rb * kTileRows + tok;
   const float gamma = *gamma_p;
-  if (WAVES == 1) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * g + r;
-      if (t < m && row < n) {
-        const float scale = gamma * amax[t] / 127.0f;
-        y[t * n + row] = static_cast<float>(res[r]) * scale;
-        if (acc_out) acc_out[t * n + row] = res[r];
-      }
-    }
-    return;
-  }
-  __shared__ int red[WAVES][4][64];
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][r][lane] = res[r];
   __syncthreads();
@@ -131,28 +595,63 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint4* __restric
   }
 }
 
-template <int WAVES, int U>
-hipError_t launch(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
-                  const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s, bool vec) {
+template <int SRC, int WAVES, int U>
+hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
+                      const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
+                      hipStream_t s, bool vec) {
   const int kt = static_cast<int>(k_tiles(k));
-  const dim3 grid(static_cast<unsigned>(row_blocks(n)));
+  const int64_t rbs = row_blocks(n);
+  // balanced persistent grid: every workgroup takes the same number of row blocks (+-1)
+  const int64_t per = (rbs + kMaxResidentGroups - 1) / kMaxResidentGroups;
+  const dim3 grid(static_cast<unsigned>((rbs + per - 1) / per));
+  const size_t lds = lds_bytes(m, kt);
   const uint4* p = static_cast<const uint4*>(packed);
   if (vec)
-    gemv_kernel<WAVES, U, true><<<grid, WAVES * 64, 0, s>>>(p, gamma, n, k, kt, xq, amax, static_cast<int>(m), y, acc);
+    gemv_lds_kernel<WAVES, U, SRC, true><<<grid, WAVES * 64, lds, s>>>(p, gamma, n, k, kt, rbs, xsrc, amax_in,
+                                                                       static_cast<int>(m), y, acc, xq_out, amax_out);
   else
-    gemv_kernel<WAVES, U, false><<<grid, WAVES * 64, 0, s>>>(p, gamma, n, k, kt, xq, amax, static_cast<int>(m), y, acc);
+    gemv_lds_kernel<WAVES, U, SRC, false><<<grid, WAVES * 64, lds, s>>>(p, gamma, n, k, kt, rbs, xsrc, amax_in,
+                                                                        static_cast<int>(m), y, acc, xq_out, amax_out);
   return hipGetLastError();
+}
+
+// U = tiles per wave per item: enough for one item to cover a row block of up
+// to 32 tiles (k <= 8192); longer rows are walked in chunks of 32 tiles.
+template <int SRC>
+hipError_t dispatch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
+                        const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
+                        hipStream_t s, bool vec) {
+  const int64_t kt = k_tiles(k);
+  if (kt <= kWaves) return launch_lds<SRC, kWaves, 1>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+  if (kt <= 2 * kWaves) return launch_lds<SRC, kWaves, 2>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+  if (kt <= 4 * kWaves) return launch_lds<SRC, kWaves, 4>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+  return launch_lds<SRC, kWaves, 8>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
 }
 
 }  // namespace
 
+bool gemv_fits_lds(int64_t m, int64_t k) { return lds_bytes(m, k_tiles(k)) <= kMaxLdsBytes; }
+
 hipError_t launch_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
-  const int64_t kt = k_tiles(k);
-  if (kt <= 1) return launch<1, 1>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
-  if (kt <= 4) return launch<4, 1>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
-  return launch<4, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
+  if (gemv_fits_lds(m, k))
+    return dispatch_lds<kFromCodes>(packed, gamma, n, k, xq, amax, m, y, acc, nullptr, nullptr, s, vec);
+  const int kt = static_cast<int>(k_tiles(k));
+  const dim3 grid(static_cast<unsigned>(row_blocks(n)));
+  const uint4* p = static_cast<const uint4*>(packed);
+  if (vec)
+    gemv_global_kernel<4, 4, true><<<grid, 256, 0, s>>>(p, gamma, n, k, kt, xq, amax, static_cast<int>(m), y, acc);
+  else
+    gemv_global_kernel<4, 4, false><<<grid, 256, 0, s>>>(p, gamma, n, k, kt, xq, amax, static_cast<int>(m), y, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
+                             int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s) {
+  const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 8 == 0);
+  return dispatch_lds<kFromBf16>(packed, gamma, n, k, x, nullptr, m, y, acc, xq_out, amax_out, s, vec);
 }
 
 }  // namespace bitlinear

@@ -139,9 +139,33 @@ int bitlinear_forward(const void *packed, const float *gamma, int64_t n, int64_t
                       float *y, int32_t *acc_or_null, void *stream);
 
 /*
- * Batched (prefill) forward for any m >= 1: the same result as
+ * Activation quantisation fused into the decode forward: one launch that
+ * computes exactly bitlinear_quant_act followed by bitlinear_forward
+ * ("The Mathematical Mechanism", items 2-4).  Every workgroup quantises the
+ * m tokens into on-chip memory in its prologue while its first weight tiles
+ * are in flight, so the int8 codes never round-trip through HBM.
+ *   x                 in   bf16 bit patterns [m][k], 2-byte aligned
+ *   y                 out  fp32 [m][n]
+ *   acc_or_null       out  optional int32 [m][n] exact accumulators
+ *   xq_or_null,       out  optional (both or neither): the int8 codes [m][k]
+ *   x_absmax_or_null       and a' [m], identical to bitlinear_quant_act's
+ * Supported when 1 <= m <= BITLINEAR_FORWARD_MAX_M and the m x k codes fit
+ * the workgroup's on-chip budget (bitlinear_quant_forward_supported);
+ * otherwise returns BITLINEAR_E_UNSUPPORTED.
+ */
+int bitlinear_quant_forward(const void *packed, const float *gamma, int64_t n, int64_t k,
+                            const uint16_t *x, int64_t m,
+                            float *y, int32_t *acc_or_null,
+                            int8_t *xq_or_null, float *x_absmax_or_null, void *stream);
+
+/* 1 if bitlinear_quant_forward accepts (m, k), else 0.  Pure host function. */
+int bitlinear_quant_forward_supported(int64_t m, int64_t k);
+
+/*
+ * Batched (prefill) forward for 1 <= m <= 2^21: the same result as
  * bitlinear_forward, computed as a tiled int8 matrix-core contraction with
- * the ternary tiles expanded on chip.
+ * the ternary tiles expanded on chip.  Larger m returns
+ * BITLINEAR_E_UNSUPPORTED (split the tokens into several calls).
  */
 int bitlinear_forward_batched(const void *packed, const float *gamma, int64_t n, int64_t k,
                               const int8_t *xq, const float *x_absmax, int64_t m,

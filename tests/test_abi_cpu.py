@@ -140,3 +140,36 @@ def test_binding_rejects_host_tensors(blq):
     w = torch.zeros(16, 256)
     with pytest.raises(ValueError):
         blq.bitlinear_pack_weights(w)
+
+
+def test_quant_forward_validation(blq):
+    lib = blq.load_library()
+    fn = lib.bitlinear_quant_forward
+    E = blq
+    ok = dict(packed=A16, gamma=A16, n=64, k=512, x=A16, m=1, y=A16, acc=None, xq=None, amax=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return fn(a["packed"], a["gamma"], a["n"], a["k"], a["x"], a["m"], a["y"], a["acc"], a["xq"], a["amax"], None)
+
+    for key in ("packed", "gamma", "x", "y"):
+        assert call(**{key: None}) == E.BITLINEAR_E_NULL, key
+    assert call(xq=A16) == E.BITLINEAR_E_NULL          # codes without a'
+    assert call(amax=A16) == E.BITLINEAR_E_NULL        # a' without codes
+    assert call(n=0) == E.BITLINEAR_E_SHAPE
+    assert call(m=0) == E.BITLINEAR_E_SHAPE
+    assert call(packed=A8) == E.BITLINEAR_E_ALIGN
+    assert call(x=A16 + 1) == E.BITLINEAR_E_ALIGN
+    assert call(m=17) == E.BITLINEAR_E_UNSUPPORTED
+    assert call(m=16, k=14336) == E.BITLINEAR_E_UNSUPPORTED
+    assert lib.bitlinear_quant_forward_supported(1, 2560) == 1
+    assert lib.bitlinear_quant_forward_supported(1, 28672) == 1
+    assert lib.bitlinear_quant_forward_supported(2, 14336) == 1
+    assert lib.bitlinear_quant_forward_supported(8, 14336) == 0
+    assert lib.bitlinear_quant_forward_supported(17, 256) == 0
+    assert lib.bitlinear_quant_forward_supported(0, 256) == 0
+    # supported sizes keep the staged codes (padded rows) inside 64 KiB of LDS
+    for m in range(1, 17):
+        for k in (1, 255, 256, 4096, 6912, 14336, 28672, 40000):
+            if lib.bitlinear_quant_forward_supported(m, k):
+                assert m * (((k + 255) // 256) * 256 + 16) <= 65536

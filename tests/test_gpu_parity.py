@@ -258,3 +258,74 @@ def test_forward_on_a_side_stream(blq):
     s.synchronize()
     ref = oracle.forward(x, w)
     compare_y(y.cpu().numpy(), ref["y"], "side stream")
+
+
+# ---------------------------------------------------------------------------
+# fused activation quantisation + decode forward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", SHAPES + [(2560, 6912), (64, 14336)])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
+def test_quant_forward_parity(blq, n, k, m):
+    if not blq.bitlinear_quant_forward_supported(m, k):
+        pytest.skip("m*k beyond the fused path's on-chip budget")
+    torch = torch_mod()
+    tag = "fused n=%d k=%d m=%d" % (n, k, m)
+    log("case", tag)
+    w = synth.latent_weights(n + 13 * k + m, n, k)
+    x = synth.activations_bf16(n + 17 * k + m, m, k, 0.01)
+    packed, gamma = gpu_pack(blq, w)
+    xd = to_dev_bits(x)
+    acc = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    amax = torch.empty(m, dtype=torch.float32, device="cuda")
+    y = blq.bitlinear_quant_forward(packed, gamma, n, k, xd, acc=acc, xq=xq, x_absmax=amax)
+    ref = oracle.forward(x, w)
+    g_same = check_gamma(host(gamma)[0], ref["gamma"], tag)
+    bad = compare_codes(host(blq.bitlinear_unpack_weights(packed, n, k)), ref["q"], w, ref["gamma"], g_same, tag)
+    keep = np.setdiff1d(np.arange(n), bad)
+    assert np.array_equal(host(xq), ref["xq"]), tag
+    assert np.array_equal(host(amax), ref["amax"]), tag
+    assert np.array_equal(host(acc)[:, keep], ref["acc"][:, keep]), tag
+    compare_y(host(y)[:, keep], ref["y"][:, keep], tag)
+    # the two-launch path gives the same bits
+    xq2, amax2 = blq.bitlinear_quant_act(xd)
+    y2 = blq.bitlinear_forward(packed, gamma, n, k, xq2, amax2)
+    assert torch.equal(y, y2), tag
+
+
+def test_quant_forward_without_optional_outputs(blq):
+    torch = torch_mod()
+    n, k, m = 300, 2560, 1
+    w = synth.latent_weights(21, n, k)
+    x = synth.activations_bf16(22, m, k, 0.0)
+    packed, gamma = gpu_pack(blq, w)
+    y = blq.bitlinear_quant_forward(packed, gamma, n, k, to_dev_bits(x))
+    compare_y(host(y), oracle.forward(x, w)["y"], "fused, no optional outputs")
+
+
+def test_quant_forward_misaligned_input(blq):
+    torch = torch_mod()
+    n, k, m = 48, 1000, 3
+    w = synth.latent_weights(31, n, k)
+    x = synth.activations_bf16(32, m, k, 0.01)
+    packed, gamma = gpu_pack(blq, w)
+    base = torch.zeros(m * k + 8, dtype=torch.int16, device="cuda")
+    base[1:1 + m * k] = to_dev_bits(x).view(-1)
+    acc = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    y = blq.bitlinear_quant_forward(packed, gamma, n, k, base[1:1 + m * k].view(m, k), acc=acc)
+    ref = oracle.forward(x, w)
+    assert np.array_equal(host(acc), ref["acc"])
+    compare_y(host(y), ref["y"], "fused misaligned")
+
+
+def test_quant_forward_unsupported_sizes(blq):
+    torch = torch_mod()
+    n, k = 32, 14336
+    w = torch.zeros((n, k), dtype=torch.float32, device="cuda")
+    packed, gamma = blq.bitlinear_pack_weights(w)
+    x = torch.zeros((16, k), dtype=torch.int16, device="cuda")
+    assert not blq.bitlinear_quant_forward_supported(16, k)
+    with pytest.raises(blq.BitlinearError) as e:
+        blq.bitlinear_quant_forward(packed, gamma, n, k, x)
+    assert e.value.status == blq.BITLINEAR_E_UNSUPPORTED
