@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int64_t kMaxK = int64_t(1) << 24;         // |acc| <= 127 k < 2^31
+constexpr int64_t kMaxK = int64_t(1) << 18;         // |64 acc| <= 64 * 127 k < 2^31
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxBatchedM = int64_t(1) << 21;  // token tiles fit a grid dimension
 

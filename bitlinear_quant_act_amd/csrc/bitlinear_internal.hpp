@@ -8,21 +8,32 @@
 
 namespace bitlinear {
 
-// ---- packed ternary layout, version 1 -------------------------------------
+// ---- packed ternary layout, version 2 -------------------------------------
 // A tile is 16 weight rows x 256 columns = 1024 bytes: 64 slots of 16 bytes,
 // one per lane of a wave64, so a wave reads a tile with one fully coalesced
 // 16-byte-per-lane load.  Slot l: row (l % 16), columns 64*(l/16) + [0, 64).
-// Word s of a slot: 16 columns, column t at bits 8*(t%4) + 2*(t/4), so
-// (word >> 2j) & 0x03030303 yields columns 4j..4j+3 as four bytes in order.
-// Field value = w + 1.
+// Word s of a slot: 16 columns, column t at bits 8*(t%4) + 2*(t/4).  Each
+// 2-bit field holds w in two's complement (00 = 0, 01 = +1, 11 = -1; 10 is
+// never written), so (word << (6 - 2j)) & 0xC0C0C0C0 yields columns
+// 4j..4j+3 in order as four int8 bytes equal to 64 * w.
 constexpr int kTileRows = 16;
 constexpr int kTileCols = 256;
 constexpr int kTileBytes = 1024;
-constexpr uint32_t kZeroCode = 1u;         // w = 0
-constexpr uint32_t kZeroWord = 0x55555555u; // sixteen zero-weight fields
+constexpr uint32_t kZeroCode = 0u;  // w = 0
+constexpr uint32_t kZeroWord = 0u;  // sixteen zero weights
+constexpr int kWeightShift = 6;     // expanded weight bytes are 64 * w
 
 __host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kTileRows - 1) / kTileRows; }
 __host__ __device__ inline int64_t k_tiles(int64_t k) { return (k + kTileCols - 1) / kTileCols; }
+
+// One packed word (16 weights) -> the 16-byte int8 operand 64 * w of one
+// 16x16x64 MFMA, columns in order: three shifts and four masks.
+typedef int expand_v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ expand_v4i expand_ternary(uint32_t word) {
+  const uint32_t m = 0xC0C0C0C0u;
+  return expand_v4i{static_cast<int>((word << 6) & m), static_cast<int>((word << 4) & m),
+                    static_cast<int>((word << 2) & m), static_cast<int>(word & m)};
+}
 
 constexpr int kPackPartials = 1024;  // fp64 partial sums of |W| (max)
 

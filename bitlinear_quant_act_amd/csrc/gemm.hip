@@ -7,32 +7,36 @@
 // Framework", section "Scalability with Thread Count": prompt processing is
 // compute-intensive), so it runs on the int8 matrix cores.
 //
-// Tiling: a workgroup of 4 waves (2 x 2) owns a BM x BN output tile (tokens x
-// weight rows) and walks k in 256-column steps.  Per step it copies the BM x
-// 256 int8 activation tile and the BN/16 packed weight tiles (1 KiB each,
-// copied verbatim -- still 2 bits per weight) into LDS; the next step's
-// global loads are issued into registers before the current step's math, so
-// HBM/L2 latency overlaps the matrix-core work.  Each wave expands its packed
-// weight slots to int8 in registers -- one shift and one mask per 4 weights,
-// done once per slot and reused by every token block of the wave -- and runs
-// v_mfma_i32_16x16x64_i8 on (16 tokens x 64 cols) x (64 cols x 16 rows).
-// The stored weight is w + 1; the per-token sum of x_q that this offset adds
-// is accumulated exactly with v_dot4 while the activation tile passes
-// through registers on its way to LDS, and subtracted in the epilogue.
+// Tiling: a workgroup of 4 waves (WM x WN) owns a BM x BN output tile
+// (tokens x weight rows) and walks k in 256-column steps, the width of one
+// packed weight tile.  Each step's BM x 256 int8 activation tile and BN/16
+// packed weight tiles (1 KiB each, copied verbatim: still 2 bits per weight)
+// go to one of two LDS stages while the other stage feeds the matrix cores:
+// the next step's global loads are issued before the current step's math and
+// land in the idle stage after it, so there is one barrier per step.
+//
+// Each wave expands its packed weight slots to int8 in registers -- one
+// shift and one mask per 4 weights, 64 * w in two's complement (see
+// expand_ternary) -- once per slot and step, and reuses them for all its
+// 16-token blocks, then runs v_mfma_i32_16x16x64_i8 on (16 tokens x 64
+// cols) x (64 cols x 16 rows).  The accumulators hold 64 * acc exactly; the
+// epilogue shifts, scales by gamma * a'[t] / 127 and stores fp32.
+//
+// Workgroup order is XCD-aware: hardware deals workgroups to the 8 XCDs
+// round-robin, so the linear id is remapped to give each XCD a contiguous
+// range of tiles in (weight tile, token tile) order -- the token tiles that
+// share a weight tile run on one XCD, at the same time, and share its L2.
 #include "bitlinear_internal.hpp"
 
 namespace bitlinear {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int kAStride = kTileCols + 16;  // LDS row pitch of the activation tile (bytes)
-
-__device__ __forceinline__ v4i expand(uint32_t word) {
-  return v4i{static_cast<int>(word & 0x03030303u), static_cast<int>((word >> 2) & 0x03030303u),
-             static_cast<int>((word >> 4) & 0x03030303u), static_cast<int>((word >> 6) & 0x03030303u)};
-}
+constexpr int kAPitch = kTileCols + 16;  // LDS row pitch of the activation tile (bytes)
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ uint4 load_a16(const int8_t* __restrict__ xq, int64_t row, int64_t col, int64_t m,
                                           int64_t k, bool vec) {
@@ -51,127 +55,141 @@ __device__ __forceinline__ uint4 load_a16(const int8_t* __restrict__ xq, int64_t
   return r;
 }
 
-template <int BM, int BN, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint4* __restrict__ packed,
-                                                           const float* __restrict__ gamma_p, int64_t n,
-                                                           int64_t k, int kt_count,
-                                                           const int8_t* __restrict__ xq,
-                                                           const float* __restrict__ amax, int64_t m,
-                                                           float* __restrict__ y, int32_t* __restrict__ acc_out) {
-  constexpr int MB = BM / 32;                 // 16-token blocks per wave
-  constexpr int NB = BN / 32;                 // 16-row blocks per wave
-  constexpr int A_PER_THREAD = BM * 16 / kThreads;
-  constexpr int B_CHUNKS = (BN / 16) * 64;
-  constexpr int B_PER_THREAD = B_CHUNKS / kThreads;
-  static_assert(A_PER_THREAD >= 1 && B_PER_THREAD >= 1, "tile too small for the workgroup");
+template <int BM, int BN>
+struct TileShape {
+  static constexpr int kABytes = BM * kAPitch;
+  static constexpr int kBBytes = (BN / kTileRows) * kTileBytes;
+  static constexpr int kStage = kABytes + kBBytes;
+  static constexpr int kLds = 2 * kStage;
+};
 
-  __shared__ __attribute__((aligned(16))) int8_t As[BM * kAStride];
-  __shared__ uint4 Bs[B_CHUNKS];
-  __shared__ int rowsum_s[BM];
+template <int BM, int BN, int WM, int WN, bool VEC>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restrict__ packed,
+                                                           const float* __restrict__ gamma_p, int64_t n, int64_t k,
+                                                           int kt_count, const int8_t* __restrict__ xq,
+                                                           const float* __restrict__ amax, int64_t m, int mt_count,
+                                                           int nt_count, float* __restrict__ y,
+                                                           int32_t* __restrict__ acc_out) {
+  static_assert(WM * WN == kThreads / 64, "4 waves");
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int MB = TM / 32, NB = TN / 32;  // 32 x 32 output blocks per wave
+  constexpr int A_PER = BM * 16 / kThreads;  // 16-byte activation chunks per thread per step
+  constexpr int B_CHUNKS = (BN / kTileRows) * 64;
+  constexpr int B_PER = (B_CHUNKS + kThreads - 1) / kThreads;
+  using TS = TileShape<BM, BN>;
+  static_assert(A_PER >= 1 && MB >= 1 && NB >= 1 && TM % 32 == 0 && TN % 32 == 0, "tile too small");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31;  // operand row (token for A, weight row for B)
+  const int h = lane >> 5;    // which 16 of the step's 32 columns
+
+  // XCD-aware tile order
+  const int total = mt_count * nt_count;
+  int id = blockIdx.x;
+  if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
+  const int nt = id / mt_count, mt = id - nt * mt_count;
+  const int64_t m0 = static_cast<int64_t>(mt) * BM;
+  const int64_t n0 = static_cast<int64_t>(nt) * BN;
   const int64_t rb0 = n0 / kTileRows;
   const int64_t rb_count = row_blocks(n);
 
-  uint4 areg[A_PER_THREAD];
-  uint4 breg[B_PER_THREAD];
-  int rsum[A_PER_THREAD];
+  uint4 areg[A_PER];
+  uint4 breg[B_PER];
+  auto load_global = [&](int kt) {
 #pragma unroll
-  for (int i = 0; i < A_PER_THREAD; ++i) rsum[i] = 0;
-
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_PER_THREAD; ++i) {
+    for (int i = 0; i < A_PER; ++i) {
       const int c = tid + kThreads * i;
       areg[i] = load_a16(xq, m0 + (c >> 4), static_cast<int64_t>(kt) * kTileCols + (c & 15) * 16, m, k, VEC);
     }
 #pragma unroll
-    for (int i = 0; i < B_PER_THREAD; ++i) {
+    for (int i = 0; i < B_PER; ++i) {
       const int c = tid + kThreads * i;
       const int64_t rbg = rb0 + (c >> 6);
-      breg[i] = rbg < rb_count ? packed[(rbg * kt_count + kt) * 64 + (c & 63)]
-                               : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
+      breg[i] = (c < B_CHUNKS && rbg < rb_count) ? packed[(rbg * kt_count + kt) * 64 + (c & 63)]
+                                                 : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
+    }
+  };
+  auto store_lds = [&](int stage) {
+    uint8_t* As = smem + stage * TS::kStage;
+    uint4* Bs = reinterpret_cast<uint4*>(As + TS::kABytes);
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<uint4*>(As + (c >> 4) * kAPitch + (c & 15) * 16) = areg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+      const int c = tid + kThreads * i;
+      if (c < B_CHUNKS) Bs[c] = breg[i];
     }
   };
 
-  v4i acc[MB][NB];
+  v16i acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < NB; ++j) acc[i][j] = v16i{};
 
-  load_tile(0);
+  // per-lane LDS offsets: A row (token), B slot of the lane's weight row
+  const int a_off = (wm * TM + l32) * kAPitch + 16 * h;
+  const int b_row = wn * TN + l32;                              // + nb * 32
+  const int b_off = (b_row >> 4) * kTileBytes + (b_row & 15) * 16;  // + nb * 2 KiB + g * 256
+
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
   for (int kt = 0; kt < kt_count; ++kt) {
+    const bool more = kt + 1 < kt_count;
+    if (more) load_global(kt + 1);
+    const uint8_t* As = smem + (kt & 1) * TS::kStage;
+    const uint8_t* Bs = As + TS::kABytes;
 #pragma unroll
-    for (int i = 0; i < A_PER_THREAD; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(As + (c >> 4) * kAStride + (c & 15) * 16) = areg[i];
-      int s = rsum[i];
-      s = __builtin_amdgcn_sdot4(static_cast<int>(areg[i].x), 0x01010101, s, false);
-      s = __builtin_amdgcn_sdot4(static_cast<int>(areg[i].y), 0x01010101, s, false);
-      s = __builtin_amdgcn_sdot4(static_cast<int>(areg[i].z), 0x01010101, s, false);
-      s = __builtin_amdgcn_sdot4(static_cast<int>(areg[i].w), 0x01010101, s, false);
-      rsum[i] = s;
-    }
+    for (int g = 0; g < 4; ++g) {
+      // the lane's packed slot for column group g: words h (columns 64g + 16h
+      // + [0,16)) and 2 + h (columns 64g + 32 + 16h + [0,16))
+      uint4 slot[NB];
 #pragma unroll
-    for (int i = 0; i < B_PER_THREAD; ++i) Bs[tid + kThreads * i] = breg[i];
-    __syncthreads();
-    if (kt + 1 < kt_count) load_tile(kt + 1);
-
-    v4i b[NB][4];
+      for (int nb = 0; nb < NB; ++nb) slot[nb] = *reinterpret_cast<const uint4*>(Bs + b_off + nb * 2 * kTileBytes + g * 256);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint4 w = Bs[(wn * NB + nb) * 64 + lane];
-      b[nb][0] = expand(w.x);
-      b[nb][1] = expand(w.y);
-      b[nb][2] = expand(w.z);
-      b[nb][3] = expand(w.w);
-    }
+      for (int half = 0; half < 2; ++half) {
+        v4i b[NB];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t word = half == 0 ? (h == 0 ? slot[nb].x : slot[nb].y) : (h == 0 ? slot[nb].z : slot[nb].w);
+          b[nb] = expand_ternary(word);
+        }
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const v4i a = *reinterpret_cast<const v4i*>(As + (wm * (BM / 2) + mb * 16 + l16) * kAStride + g * 64 + s * 16);
+        for (int mb = 0; mb < MB; ++mb) {
+          const v4i a = *reinterpret_cast<const v4i*>(As + a_off + mb * 32 * kAPitch + g * 64 + half * 32);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[nb][s], acc[mb][nb], 0, 0, 0);
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[nb], acc[mb][nb], 0, 0, 0);
+        }
       }
     }
+    if (more) store_lds((kt + 1) & 1);
     __syncthreads();
   }
 
-  // per-token sums of x_q: the 16 threads of one token row are 16 consecutive lanes
-#pragma unroll
-  for (int i = 0; i < A_PER_THREAD; ++i) {
-    int v = rsum[i];
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
-    if ((tid & 15) == 0) rowsum_s[(tid >> 4) + 16 * i] = v;
-  }
-  __syncthreads();
-
+  // 32 x 32 block layout: element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
   const float gamma = *gamma_p;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tl = wm * (BM / 2) + mb * 16 + 4 * g + r;
-      const int64_t t = m0 + tl;
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = m0 + wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       if (t >= m) continue;
       const float scale = gamma * amax[t] / 127.0f;
-      const int rs = rowsum_s[tl];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int64_t j = n0 + wn * (BN / 2) + nb * 16 + l16;
+        const int64_t j = n0 + wn * TN + nb * 32 + l32;
         if (j < n) {
-          const int v = acc[mb][nb][r] - rs;
+          const int v = acc[mb][nb][r] >> kWeightShift;  // exact: multiples of 64
           y[t * n + j] = static_cast<float>(v) * scale;
           if (acc_out) acc_out[t * n + j] = v;
         }
@@ -180,17 +198,307 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint4* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// S-stage pipeline with direct-to-LDS loads (k % 16 == 0, codes 16-byte aligned)
+// ---------------------------------------------------------------------------
+//
+// global_load_lds_dwordx4 moves 16 bytes per lane straight into LDS (64
+// lanes -> 1 KiB contiguous), so no registers stage the tiles and S - 1 tiles
+// can be in flight while one is consumed.  Each stage is its own LDS array so
+// the compiler tracks the outstanding copies per stage; a wave waits for its
+// own copies of the tile it is about to read (s_waitcnt vmcnt), then a plain
+// s_barrier (no memory fence, which would drain every copy) publishes them.
+//
+// The activation tile has no padding; instead the 16 chunks of 16 bytes in
+// a 256-byte row are stored XOR-swizzled by (row % 16), which keeps the 32
+// token rows of one MFMA operand read on distinct banks.  Rows past m and
+// columns past k read valid memory (row m-1, column 0): they only meet
+// discarded output rows or zero weights.
+
+#define BITLINEAR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 template <int BM, int BN>
+struct DmaShape {
+  static constexpr int kABytes = BM * kTileCols;
+  static constexpr int kBBytes = (BN / kTileRows) * kTileBytes;
+  static constexpr int kStage = kABytes + kBBytes;
+  static constexpr int kADma = BM / 16;   // 1 KiB copies per wave for the activation tile
+  static constexpr int kBDma = BN / 64;   // 1 KiB copies per wave for the weight tiles
+  static constexpr int kDma = kADma + kBDma;
+};
+
+constexpr int DmaStageBytes(int bm, int bn) { return bm * kTileCols + (bn / kTileRows) * kTileBytes; }
+
+template <int BM, int BN>
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* __restrict__ packed_b,
+                                           const int8_t* __restrict__ xq, int64_t m0, int64_t m, int64_t k,
+                                           int64_t rb0, int64_t rb_count, int kt_count, int kt, int wave, int lane) {
+  using DS = DmaShape<BM, BN>;
+  const int ktc = kt < kt_count ? kt : 0;  // tiles past the end re-read tile 0 into an unused stage
+#pragma unroll
+  for (int i = 0; i < DS::kADma; ++i) {
+    const int blk = wave * DS::kADma + i;  // 1 KiB = 4 rows
+    const int row = 4 * blk + (lane >> 4);
+    const int chunk = (lane & 15) ^ (row & 15);
+    int64_t grow = m0 + row;
+    grow = grow < m ? grow : m - 1;
+    int64_t col = static_cast<int64_t>(ktc) * kTileCols + chunk * 16;
+    col = col < k ? col : 0;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + grow * k + col), BITLINEAR_LDS(stage + blk * 1024),
+                                     16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < DS::kBDma; ++i) {
+    const int rbl = wave * DS::kBDma + i;
+    int64_t rbg = rb0 + rbl;
+    rbg = rbg < rb_count ? rbg : rb_count - 1;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(packed_b + (rbg * kt_count + ktc) * kTileBytes + lane * 16),
+                                     BITLINEAR_LDS(stage + DS::kABytes + rbl * 1024), 16, 0, 0);
+  }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt low bits [3:0], high bits [15:14]; expcnt [6:4] and lgkmcnt [11:8] at max)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const uint8_t* __restrict__ packed_b,
+                                                               const float* __restrict__ gamma_p, int64_t n,
+                                                               int64_t k, int kt_count, const int8_t* __restrict__ xq,
+                                                               const float* __restrict__ amax, int64_t m,
+                                                               int mt_count, int nt_count, float* __restrict__ y,
+                                                               int32_t* __restrict__ acc_out) {
+  static_assert(WM * WN == kThreads / 64, "4 waves");
+  static_assert(S >= 2 && S <= 4, "2..4 stages");
+  using DS = DmaShape<BM, BN>;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int MB = TM / 32, NB = TN / 32;
+  static_assert(MB >= 1 && NB >= 1 && TM % 32 == 0 && TN % 32 == 0 && BN % 64 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[DS::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[DS::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? DS::kStage : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? DS::kStage : 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  const int total = mt_count * nt_count;
+  int id = blockIdx.x;
+  if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
+  const int nt = id / mt_count, mt = id - nt * mt_count;
+  const int64_t m0 = static_cast<int64_t>(mt) * BM;
+  const int64_t n0 = static_cast<int64_t>(nt) * BN;
+  const int64_t rb0 = n0 / kTileRows;
+  const int64_t rb_count = row_blocks(n);
+
+  v16i acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v16i{};
+
+  // per-lane LDS offsets
+  const int a_row0 = wm * TM + l32;                                   // + mb * 32; row % 16 == l32 % 16
+  const int a_x = (l32 & 15) ^ h;                                     // swizzle key with the lane's half folded in
+  const int b_row = wn * TN + l32;                                    // + nb * 32
+  const int b_off = DS::kABytes + (b_row >> 4) * kTileBytes + (b_row & 15) * 16;  // + nb * 2 KiB + g * 256
+
+  auto compute = [&](const uint8_t* st) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint4 slot[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) slot[nb] = *reinterpret_cast<const uint4*>(st + b_off + nb * 2 * kTileBytes + g * 256);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        v4i b[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t word = half == 0 ? (h == 0 ? slot[nb].x : slot[nb].y) : (h == 0 ? slot[nb].z : slot[nb].w);
+          b[nb] = expand_ternary(word);
+        }
+        const int chunk = (4 * g + 2 * half) ^ a_x;  // logical chunk 4g + 2 half + h, swizzled by row % 16
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const v4i a = *reinterpret_cast<const v4i*>(st + (a_row0 + mb * 32) * kTileCols + chunk * 16);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[nb], acc[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // prologue: tiles 0 .. S-2 in flight
+  issue_tile<BM, BN>(st0, packed_b, xq, m0, m, k, rb0, rb_count, kt_count, 0, wave, lane);
+  if (S > 2) issue_tile<BM, BN>(st1, packed_b, xq, m0, m, k, rb0, rb_count, kt_count, 1, wave, lane);
+  if (S > 3) issue_tile<BM, BN>(st2, packed_b, xq, m0, m, k, rb0, rb_count, kt_count, 2, wave, lane);
+
+  // one pipeline step: tile kt sits in stage `cur`; tile kt + S - 1 goes to `nxt`
+  auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
+    wait_vmcnt<(S - 2) * DS::kDma>();
+    __builtin_amdgcn_s_barrier();
+    issue_tile<BM, BN>(nxt, packed_b, xq, m0, m, k, rb0, rb_count, kt_count, kt + S - 1, wave, lane);
+    compute(cur);
+  };
+  for (int kt = 0; kt < kt_count; kt += S) {
+    step(kt, st0, S == 2 ? st1 : S == 3 ? st2 : st3);
+    if (kt + 1 < kt_count) step(kt + 1, st1, S == 2 ? st0 : S == 3 ? st0 : st0);
+    if (S > 2 && kt + 2 < kt_count) step(kt + 2, st2, S == 3 ? st1 : st1);
+    if (S > 3 && kt + 3 < kt_count) step(kt + 3, st3, st2);
+  }
+  wait_vmcnt<0>();
+
+  const float gamma = *gamma_p;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = m0 + wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (t >= m) continue;
+      const float scale = gamma * amax[t] / 127.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int64_t j = n0 + wn * TN + nb * 32 + l32;
+        if (j < n) {
+          const int v = acc[mb][nb][r] >> kWeightShift;
+          y[t * n + j] = static_cast<float>(v) * scale;
+          if (acc_out) acc_out[t * n + j] = v;
+        }
+      }
+    }
+  }
+}
+
+int max_lds_per_block() {
+  static int cached = -1;
+  if (cached < 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+      cached = v;
+    else
+      cached = 65536;
+  }
+  return cached;
+}
+
+template <int BM, int BN, int WM, int WN>
 hipError_t launch(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                   const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s, bool vec) {
   const int kt = static_cast<int>(k_tiles(k));
-  const dim3 grid(static_cast<unsigned>((n + BN - 1) / BN), static_cast<unsigned>((m + BM - 1) / BM));
+  const int64_t mt = (m + BM - 1) / BM;
+  const int64_t ntl = (n + BN - 1) / BN;
+  if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;  // beyond one grid dimension
+  const dim3 grid(static_cast<unsigned>(mt * ntl));
+  constexpr int lds = TileShape<BM, BN>::kLds;
   const uint4* p = static_cast<const uint4*>(packed);
-  if (vec)
-    gemm_kernel<BM, BN, true><<<grid, kThreads, 0, s>>>(p, gamma, n, k, kt, xq, amax, m, y, acc);
-  else
-    gemm_kernel<BM, BN, false><<<grid, kThreads, 0, s>>>(p, gamma, n, k, kt, xq, amax, m, y, acc);
+  if (vec) {
+    static const bool attr = lds <= 65536 || hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, true>),
+                                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
+    (void)attr;
+    gemm_kernel<BM, BN, WM, WN, true><<<grid, kThreads, lds, s>>>(p, gamma, n, k, kt, xq, amax, m, static_cast<int>(mt),
+                                                                  static_cast<int>(ntl), y, acc);
+  } else {
+    static const bool attr = lds <= 65536 || hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, false>),
+                                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
+    (void)attr;
+    gemm_kernel<BM, BN, WM, WN, false><<<grid, kThreads, lds, s>>>(p, gamma, n, k, kt, xq, amax, m, static_cast<int>(mt),
+                                                                   static_cast<int>(ntl), y, acc);
+  }
   return hipGetLastError();
+}
+
+// LDS bytes of a tile configuration (two stages), matching TileShape::kLds
+constexpr int TileShapeBytes(int bm, int bn) { return 2 * (bm * kAPitch + (bn / kTileRows) * kTileBytes); }
+
+// Candidate tiles (BM, BN, WM, WN).  The choice maximises the fraction of
+// the 256 CUs kept busy over the rounds of workgroups (one resident
+// workgroup per CU) times the useful fraction of each tile, preferring the
+// earlier (larger) tile on ties: more reuse per loaded byte.
+struct Cand {
+  int bm, bn, wm, wn;
+};
+constexpr Cand kConfigs[] = {{256, 128, 2, 2}, {128, 256, 2, 2}, {128, 128, 2, 2}, {64, 192, 2, 2}, {128, 64, 2, 2},
+                             {128, 32, 4, 1},  {64, 256, 2, 2},  {64, 128, 2, 2},  {64, 64, 2, 2}};
+
+Cand choose(int64_t m, int64_t n) {
+  const int64_t cus = 256;
+  Cand best = kConfigs[0];
+  double best_score = -1.0;
+  for (const Cand& c : kConfigs) {
+    if (m > 64 && c.bm < 128) continue;     // large token counts: 128+ token tiles
+    if (m <= 64 && c.bm != 64) continue;
+    if (TileShapeBytes(c.bm, c.bn) > max_lds_per_block()) continue;
+    const int64_t wgs = ((m + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    const double fill = static_cast<double>(wgs) / static_cast<double>(rounds * cus);
+    const double used = static_cast<double>(m * n) / static_cast<double>(wgs * c.bm * c.bn);
+    const double score = fill * used;
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = c;
+    }
+  }
+  return best;
+}
+
+// ---- direct-to-LDS pipeline configurations ---------------------------------
+
+template <int BM, int BN, int WM, int WN, int S>
+hipError_t launch_dma(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+                      const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
+  const int kt = static_cast<int>(k_tiles(k));
+  const int64_t mt = (m + BM - 1) / BM;
+  const int64_t ntl = (n + BN - 1) / BN;
+  if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
+  gemm_dma_kernel<BM, BN, WM, WN, S><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+      static_cast<const uint8_t*>(packed), gamma, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl),
+      y, acc);
+  return hipGetLastError();
+}
+
+struct DmaCand {
+  int bm, bn, wm, wn, stages;
+};
+constexpr DmaCand kDmaConfigs[] = {{128, 256, 2, 2, 3}, {128, 128, 2, 2, 4}, {128, 64, 2, 2, 4},
+                                   {64, 256, 2, 2, 4},  {64, 192, 2, 2, 4},  {64, 128, 2, 2, 4},
+                                   {64, 64, 2, 2, 4}};
+
+#ifndef BITLINEAR_GEMM_FORCE
+#define BITLINEAR_GEMM_FORCE -1
+#endif
+
+int choose_dma(int64_t m, int64_t n) {
+  if (BITLINEAR_GEMM_FORCE >= 0) return BITLINEAR_GEMM_FORCE;
+  const int64_t cus = 256;
+  int best = -1;
+  double best_score = -1.0;
+  for (int i = 0; i < static_cast<int>(sizeof(kDmaConfigs) / sizeof(kDmaConfigs[0])); ++i) {
+    const DmaCand& c = kDmaConfigs[i];
+    if (m > 64 && c.bm < 128) continue;
+    if (m <= 64 && c.bm != 64) continue;
+    if (c.stages * DmaStageBytes(c.bm, c.bn) > max_lds_per_block()) continue;
+    const int64_t wgs = ((m + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    const double fill = static_cast<double>(wgs) / static_cast<double>(rounds * cus);
+    const double used = static_cast<double>(m * n) / static_cast<double>(wgs * c.bm * c.bn);
+    const double score = fill * used;
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = i;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -198,14 +506,34 @@ hipError_t launch(const void* packed, const float* gamma, int64_t n, int64_t k, 
 hipError_t launch_gemm(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
-  if (m <= 64) {
-    const int64_t tiles128 = (n + 127) / 128;
-    if (tiles128 >= 512) return launch<64, 128>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
-    return launch<64, 64>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
+  if (vec) {
+    const int i = choose_dma(m, n);
+    switch (i) {
+      case 0: return launch_dma<128, 256, 2, 2, 3>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case 1: return launch_dma<128, 128, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case 2: return launch_dma<128, 64, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case 3: return launch_dma<64, 256, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case 4: return launch_dma<64, 192, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case 5: return launch_dma<64, 128, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case 6: return launch_dma<64, 64, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      default: break;
+    }
   }
-  const int64_t mt = (m + 127) / 128;
-  if (((n + 127) / 128) * mt >= 512) return launch<128, 128>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
-  return launch<128, 64>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
+  const Cand c = choose(m, n);
+#define BITLINEAR_GEMM_CASE(BM_, BN_, WM_, WN_)                 \
+  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_) \
+    return launch<BM_, BN_, WM_, WN_>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
+  BITLINEAR_GEMM_CASE(256, 128, 2, 2)
+  BITLINEAR_GEMM_CASE(128, 256, 2, 2)
+  BITLINEAR_GEMM_CASE(128, 128, 2, 2)
+  BITLINEAR_GEMM_CASE(64, 192, 2, 2)
+  BITLINEAR_GEMM_CASE(128, 64, 2, 2)
+  BITLINEAR_GEMM_CASE(128, 32, 4, 1)
+  BITLINEAR_GEMM_CASE(64, 256, 2, 2)
+  BITLINEAR_GEMM_CASE(64, 128, 2, 2)
+  BITLINEAR_GEMM_CASE(64, 64, 2, 2)
+#undef BITLINEAR_GEMM_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace bitlinear

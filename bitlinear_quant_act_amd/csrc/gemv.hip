@@ -5,44 +5,45 @@
 // sum_k x_q * W_q with W_q in {-1, 0, +1} (adds and subtracts only), then
 // y = acc * gamma * a' / 127.  "BitNet 1-bit LLM Inference Framework",
 // section "Scalability with Thread Count": generation is bound by memory
-// bandwidth, so the kernel is built to stream the 2-bit weights from HBM
-// exactly once, with as many bytes in flight as the chip can hold.
+// bandwidth, so the kernel streams the 2-bit weights from HBM exactly once,
+// with as many bytes in flight as the chip can hold.
 //
-// Work split: one workgroup per 16-row block of W; its waves take the block's
-// 256-column tiles round-robin (wave w: tiles w, w + WAVES, ...), so at any
-// moment the workgroup reads consecutive KiB of one contiguous stream.  Each
-// wave keeps two batches of U tiles in flight (16 B per lane per tile, one
-// fully coalesced 1 KiB load per wave): the next batch is requested before
-// the current one is consumed.
+// Work split: a persistent grid (at most kMaxResidentGroups workgroups, each
+// taking the same number of 16-row blocks of W).  The WAVES waves of a
+// workgroup take a row block's 256-column tiles round-robin (wave w: tiles w,
+// w + WAVES, ...), so the workgroup reads consecutive KiB of one contiguous
+// stream; every tile is one fully coalesced 16-byte-per-lane load.  A wave
+// requests all its tiles of the next row block before it consumes the
+// current one (rows longer than U * WAVES tiles are walked in chunks).
 //
-// Activation codes live in LDS for the whole kernel (m rows of k bytes,
-// padded pitch so the 16 token rows of one operand read hit distinct banks).
-// They are staged once per workgroup by one of two prologues:
+// Activation codes live in LDS for the whole kernel (m rows, padded pitch so
+// the 16 token rows of one operand read start in distinct banks).  They are
+// staged once per workgroup by one of two prologues:
 //   * kFromCodes: copied from the int8 codes of bitlinear_quant_act;
-//   * kFromBf16:  computed from the bf16 activations (the activation
-//     quantisation fused into the GEMV prologue) -- per-token max|x| as
-//     integer bit patterns, a' = max(., 1e-8), s = 127 / a' (IEEE divide),
-//     code = clamp(rint(x * s)), bit-identical to bitlinear_quant_act.
-// The weight loads of the first batch are issued before the prologue, so the
-// two latencies overlap.
+//   * kFromBf16:  computed from the bf16 activations -- the activation
+//     quantisation fused into the GEMV: per-token max|x| as integer bit
+//     patterns, a' = max(., 1e-8), s = 127 / a' (IEEE divide), code =
+//     clamp(rint(x * s)), bit-identical to bitlinear_quant_act.
+// The activations are requested before the first weight tiles: vector-memory
+// results are waited for in issue order, so the prologue then runs while the
+// weights are still in flight.
 //
-// Contraction on the matrix cores: one v_mfma_i32_16x16x64_i8 takes 16
-// tokens x 64 columns of int8 codes (A; rows >= m are zero) and 64 columns x
-// 16 weight rows (B).  The B operand of a lane is one 32-bit word of its
-// packed slot expanded with one shift and one mask per 4 weights: (word >>
-// 2j) & 0x03030303 gives the stored values w + 1 in {0, 1, 2} as int8.  The
-// offset is removed exactly with a second MFMA against an all-ones B (sum_k
-// x), which runs on the otherwise idle matrix pipe:  acc = sum (w + 1) x -
-// sum x, both exact in int32.  A lane's A operand is the 16 codes of its own
-// token at the same 16 columns, so A and B share the k order.
+// Contraction on the matrix cores: one v_mfma_i32_16x16x64_i8 multiplies 16
+// tokens x 64 columns of codes (A; token rows >= m are zero) by 64 columns x
+// 16 weight rows (B).  A lane's B operand is one 32-bit word of its packed
+// slot, expanded with one shift and one mask per 4 weights (expand_ternary:
+// each 2-bit two's-complement field lands in the top bits of its byte, the
+// int8 value 64 * w).  The MFMA therefore accumulates 64 * acc exactly; the
+// epilogue shifts it back.  A lane's A operand is the 16 codes of its own
+// token at the same 16 columns, so A and B share the k order without any
+// shuffling.
 //
 // Epilogue: the waves' int32 partials are summed through LDS and scaled by
 // gamma * a'[m] / 127 in fp32; lanes 0..15 of a result row write 16
 // consecutive floats.
 //
-// When the codes do not fit the LDS budget (m * k beyond ~64 KiB) the
-// global-operand variant reads each lane's 16-byte A operand straight from
-// the int8 codes in memory instead.
+// When m x k codes exceed the LDS budget, the global-operand variant reads
+// each lane's 16-byte A operand straight from the codes in memory instead.
 #include "bitlinear_internal.hpp"
 
 namespace bitlinear {
@@ -60,14 +61,9 @@ constexpr int64_t kMaxResidentGroups = BITLINEAR_GEMV_MAX_GROUPS;  // persistent
 constexpr int kWaves = BITLINEAR_GEMV_WAVES;                        // waves per workgroup
 // dynamic LDS budget: 64 KiB less the static reduction buffer and scalars
 constexpr int kMaxLdsBytes = 65536 - kWaves * 4 * 64 * 4 - 512;
-constexpr int kCachedChunks = 4;  // bf16 chunks per thread kept in registers between prologue passes
+constexpr int kCachedChunks = 4;  // activation chunks per thread held in registers by the prologue
 
 enum Source { kFromCodes = 0, kFromBf16 = 1 };
-
-__device__ __forceinline__ v4i expand(uint32_t word) {
-  return v4i{static_cast<int>(word & 0x03030303u), static_cast<int>((word >> 2) & 0x03030303u),
-             static_cast<int>((word >> 4) & 0x03030303u), static_cast<int>((word >> 6) & 0x03030303u)};
-}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -77,40 +73,55 @@ __device__ __forceinline__ uint32_t quant_code(uint32_t bits16, float s) {
   return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
 }
 
+// 8 bf16 values (one 16-byte chunk) -> 8 codes (two words)
+__device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    lo |= quant_code(w[q] & 0xffffu, s) << (16 * q);
+    lo |= quant_code(w[q] >> 16, s) << (16 * q + 8);
+    hi |= quant_code(w[q + 2] & 0xffffu, s) << (16 * q);
+    hi |= quant_code(w[q + 2] >> 16, s) << (16 * q + 8);
+  }
+  return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ unsigned chunk_absmax(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  unsigned mx = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mx = max(mx, max(w[q] & 0x7fffu, (w[q] >> 16) & 0x7fffu));
+  return mx;
+}
+
+__device__ __forceinline__ unsigned wave_max(unsigned v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+
 // LDS row pitch of the staged codes: the padded k extent plus 16 bytes, so
 // consecutive token rows start 4 banks apart.
 __host__ __device__ inline int64_t lds_pitch(int64_t kt_count) { return kt_count * kTileCols + 16; }
 
-// dynamic LDS of the LDS-operand kernel: the staged codes
 inline size_t lds_bytes(int64_t m, int64_t kt_count) { return static_cast<size_t>(m * lds_pitch(kt_count)); }
 
-// ---------------------------------------------------------------------------
-// prologues: fill xs[t][0 .. kt_count*256) for t < m (zero past k)
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ int byte_sum(uint32_t w, int acc) {
-  return __builtin_amdgcn_sdot4(static_cast<int>(w), 0x01010101, acc, false);
+// chunk j of this thread held in registers (j is uniform per loop trip)
+__device__ __forceinline__ uint4 cached(const uint4 (&cache)[kCachedChunks], int j) {
+  uint4 v = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int q = 0; q < kCachedChunks; ++q)
+    if (q == j) v = cache[q];
+  return v;
 }
 
-// Per-token partial sums of codes, flushed to xsum_s when the token changes.
-struct TokenSum {
-  int t = -1;
-  int v = 0;
-  __device__ void add(int* xsum_s, int token, int x) {
-    if (token != t) {
-      flush(xsum_s);
-      t = token;
-    }
-    v += x;
-  }
-  __device__ void flush(int* xsum_s) {
-    if (t >= 0 && v != 0) atomicAdd(&xsum_s[t], v);
-    v = 0;
-  }
-};
+// ---------------------------------------------------------------------------
+// prologues: fill xs[t][0 .. kpad) for t < m (zero past k); a' to amax_s
+// ---------------------------------------------------------------------------
 
-// Vector path, first step: request the thread's first kCachedChunks 16-byte
-// chunks of codes (chunk c = thread + j * blockDim.x) before anything else.
+// Vector paths, first step: request this thread's first kCachedChunks 16-byte
+// chunks (chunk c = thread + j * blockDim.x) before anything else.
 __device__ __forceinline__ void prefetch_codes(uint4 (&cache)[kCachedChunks], const int8_t* __restrict__ xq, int m,
                                                int64_t k, int kpad) {
   const int cpr = kpad / 16;
@@ -119,49 +130,13 @@ __device__ __forceinline__ void prefetch_codes(uint4 (&cache)[kCachedChunks], co
     const int c = threadIdx.x + j * static_cast<int>(blockDim.x);
     cache[j] = make_uint4(0, 0, 0, 0);
     if (c < m * cpr) {
-      const int t = c / cpr, cc = c - t * cpr;
-      const int64_t col = static_cast<int64_t>(cc) * 16;
+      const int t = c / cpr;
+      const int64_t col = static_cast<int64_t>(c - t * cpr) * 16;
       if (col < k) cache[j] = *reinterpret_cast<const uint4*>(xq + t * k + col);
     }
   }
 }
 
-__device__ void stage_codes(int8_t* xs, int pitch, int* xsum_s, const uint4 (&cache)[kCachedChunks],
-                            const int8_t* __restrict__ xq, int m, int64_t k, int kpad, bool vec) {
-  const int nthreads = blockDim.x;
-  TokenSum ts;
-  if (vec) {  // k % 16 == 0 and xq 16-byte aligned
-    const int cpr = kpad / 16;
-    int j = 0;
-    for (int c = threadIdx.x; c < m * cpr; c += nthreads, ++j) {
-      const int t = c / cpr, cc = c - t * cpr;
-      const int64_t col = static_cast<int64_t>(cc) * 16;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < kCachedChunks) {
-#pragma unroll
-        for (int q = 0; q < kCachedChunks; ++q)
-          if (q == j) v = cache[q];
-      } else if (col < k) {
-        v = *reinterpret_cast<const uint4*>(xq + t * k + col);
-      }
-      *reinterpret_cast<uint4*>(xs + t * pitch + cc * 16) = v;
-      ts.add(xsum_s, t, byte_sum(v.w, byte_sum(v.z, byte_sum(v.y, byte_sum(v.x, 0)))));
-    }
-  } else {
-    for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
-      const int t = c / kpad, col = c - t * kpad;
-      const int8_t q = col < k ? xq[t * k + col] : static_cast<int8_t>(0);
-      xs[t * pitch + col] = q;
-      ts.add(xsum_s, t, q);
-    }
-  }
-  ts.flush(xsum_s);
-}
-
-// Quantise m bf16 rows into xs; a' to amax_s[t].  Optionally also writes the
-// codes and a' to global memory (done by workgroup 0 only).
-// Vector path, first step: request the thread's first kCachedChunks chunks of
-// 8 bf16 values (chunk c = thread + j * blockDim.x) before anything else.
 __device__ __forceinline__ void prefetch_bf16(uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int m,
                                               int64_t k) {
   const int total = m * static_cast<int>(k / 8);
@@ -172,10 +147,70 @@ __device__ __forceinline__ void prefetch_bf16(uint4 (&cache)[kCachedChunks], con
   }
 }
 
-__device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s, int* xsum_s,
-                           const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x,
-                           int m, int64_t k, int kpad, bool vec, int8_t* __restrict__ xq_out,
-                           float* __restrict__ amax_out) {
+__device__ void stage_codes(int8_t* xs, int pitch, const uint4 (&cache)[kCachedChunks],
+                            const int8_t* __restrict__ xq, int m, int64_t k, int kpad, bool vec) {
+  const int nthreads = blockDim.x;
+  if (vec) {  // k % 16 == 0 and xq 16-byte aligned
+    const int cpr = kpad / 16;
+    int j = 0;
+    for (int c = threadIdx.x; c < m * cpr; c += nthreads, ++j) {
+      const int t = c / cpr, cc = c - t * cpr;
+      const int64_t col = static_cast<int64_t>(cc) * 16;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j < kCachedChunks)
+        v = cached(cache, j);
+      else if (col < k)
+        v = *reinterpret_cast<const uint4*>(xq + t * k + col);
+      *reinterpret_cast<uint4*>(xs + t * pitch + cc * 16) = v;
+    }
+  } else {
+    for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
+      const int t = c / kpad, col = c - t * kpad;
+      xs[t * pitch + col] = col < k ? xq[t * k + col] : static_cast<int8_t>(0);
+    }
+  }
+}
+
+// Single token, vector path: wave shuffles + one LDS slot per wave, no atomics.
+template <int WAVES>
+__device__ void stage_bf16_single(int8_t* xs, float* amax_s, unsigned* wmax_s, const uint4 (&cache)[kCachedChunks],
+                                  const uint16_t* __restrict__ x, int64_t k, int kpad, int8_t* __restrict__ xq_out,
+                                  float* __restrict__ amax_out) {
+  const int nthreads = blockDim.x;
+  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
+  const int total = static_cast<int>(k / 8);
+  unsigned mx = 0;
+  int j = 0;
+  for (int c = threadIdx.x; c < total; c += nthreads, ++j)
+    mx = max(mx, chunk_absmax(j < kCachedChunks ? cached(cache, j)
+                                                : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8)));
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) wmax_s[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  unsigned mall = wmax_s[0];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) mall = max(mall, wmax_s[w]);
+  const float a = fmaxf(bf16_to_f32(mall), 1e-8f);
+  const float s = 127.0f / a;
+  if (threadIdx.x == 0) {
+    amax_s[0] = a;
+    if (write_out) amax_out[0] = a;
+  }
+  j = 0;
+  for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+    const uint2 q = quant_chunk(j < kCachedChunks ? cached(cache, j)
+                                                  : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
+                                s);
+    *reinterpret_cast<uint2*>(xs + c * 8) = q;
+    if (write_out) *reinterpret_cast<uint2*>(xq_out + c * 8) = q;
+  }
+  for (int c = total + threadIdx.x; c < kpad / 8; c += nthreads) *reinterpret_cast<uint2*>(xs + c * 8) = make_uint2(0, 0);
+}
+
+// Any token count: per-token max through LDS atomics (one per token change).
+__device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s, const uint4 (&cache)[kCachedChunks],
+                           const uint16_t* __restrict__ x, int m, int64_t k, int kpad, bool vec,
+                           int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
   const int nthreads = blockDim.x;
   const bool write_out = xq_out != nullptr && blockIdx.x == 0;
   if (threadIdx.x < m) max_s[threadIdx.x] = 0u;
@@ -183,8 +218,6 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
   if (vec) {  // k % 8 == 0 and x 16-byte aligned: chunks of 8 values
     const int cpr = static_cast<int>(k / 8);
     const int total = m * cpr;
-    // pass 1: per-token max of |x| bit patterns; the first chunks of each
-    // thread are already in registers (prefetch_bf16)
     int cur_t = -1;
     unsigned cur = 0;
     int j = 0;
@@ -195,51 +228,22 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
         cur_t = t;
         cur = 0;
       }
-      uint4 v;
-      if (j < kCachedChunks) {
-#pragma unroll
-        for (int q = 0; q < kCachedChunks; ++q)
-          if (q == j) v = cache[q];
-      } else {
-        v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8);
-      }
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cur = max(cur, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+      cur = max(cur, chunk_absmax(j < kCachedChunks ? cached(cache, j)
+                                                    : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8)));
     }
     if (cur_t >= 0) atomicMax(&max_s[cur_t], cur);
     __syncthreads();
     if (threadIdx.x < m) amax_s[threadIdx.x] = fmaxf(bf16_to_f32(max_s[threadIdx.x]), 1e-8f);
     __syncthreads();
-    // pass 2: codes (chunks past the register cache are re-read from L1/L2)
-    TokenSum ts;
     j = 0;
     for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
       const int t = c / cpr, cc = c - t * cpr;
-      const float s = 127.0f / amax_s[t];
-      uint4 v;
-      if (j < kCachedChunks) {
-#pragma unroll
-        for (int q = 0; q < kCachedChunks; ++q)
-          if (q == j) v = cache[q];
-      } else {
-        v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8);
-      }
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        lo |= quant_code(w[j] & 0xffffu, s) << (16 * j);
-        lo |= quant_code(w[j] >> 16, s) << (16 * j + 8);
-        hi |= quant_code(w[j + 2] & 0xffffu, s) << (16 * j);
-        hi |= quant_code(w[j + 2] >> 16, s) << (16 * j + 8);
-      }
-      *reinterpret_cast<uint2*>(xs + t * pitch + cc * 8) = make_uint2(lo, hi);
-      if (write_out) *reinterpret_cast<uint2*>(xq_out + t * k + cc * 8) = make_uint2(lo, hi);
-      ts.add(xsum_s, t, byte_sum(hi, byte_sum(lo, 0)));
+      const uint2 q = quant_chunk(j < kCachedChunks ? cached(cache, j)
+                                                    : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
+                                  127.0f / amax_s[t]);
+      *reinterpret_cast<uint2*>(xs + t * pitch + cc * 8) = q;
+      if (write_out) *reinterpret_cast<uint2*>(xq_out + t * k + cc * 8) = q;
     }
-    ts.flush(xsum_s);
-    // zero the padding past k
     const int padc = (kpad - static_cast<int>(k)) / 8;
     for (int c = threadIdx.x; c < m * padc; c += nthreads) {
       const int t = c / padc, cc = c - t * padc;
@@ -254,7 +258,6 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
     __syncthreads();
     if (threadIdx.x < m) amax_s[threadIdx.x] = fmaxf(bf16_to_f32(max_s[threadIdx.x]), 1e-8f);
     __syncthreads();
-    TokenSum ts;
     for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
       const int t = c / kpad, col = c - t * kpad;
       int8_t q = 0;
@@ -263,117 +266,9 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
         if (write_out) xq_out[t * k + col] = q;
       }
       xs[t * pitch + col] = q;
-      ts.add(xsum_s, t, q);
     }
-    ts.flush(xsum_s);
   }
   if (write_out && threadIdx.x < m) amax_out[threadIdx.x] = amax_s[threadIdx.x];
-}
-
-// ---------------------------------------------------------------------------
-// single-token prologues (m == 1, vector path): reductions across the wave
-// with lane shuffles and across waves through one LDS slot per wave -- no
-// same-address atomics and one barrier fewer than the general prologues.
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ unsigned wave_max(unsigned v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));
-  return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-template <int WAVES>
-__device__ void stage_codes_single(int8_t* xs, int* wsum_s, const uint4 (&cache)[kCachedChunks],
-                                   const int8_t* __restrict__ xq, int64_t k, int kpad) {
-  const int nthreads = blockDim.x;
-  const int cpr = kpad / 16;
-  int sum = 0;
-  int j = 0;
-  for (int c = threadIdx.x; c < cpr; c += nthreads, ++j) {
-    const int64_t col = static_cast<int64_t>(c) * 16;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (j < kCachedChunks) {
-#pragma unroll
-      for (int q = 0; q < kCachedChunks; ++q)
-        if (q == j) v = cache[q];
-    } else if (col < k) {
-      v = *reinterpret_cast<const uint4*>(xq + col);
-    }
-    *reinterpret_cast<uint4*>(xs + c * 16) = v;
-    sum = byte_sum(v.w, byte_sum(v.z, byte_sum(v.y, byte_sum(v.x, sum))));
-  }
-  sum = wave_sum(sum);
-  if ((threadIdx.x & 63) == 0) wsum_s[threadIdx.x >> 6] = sum;
-}
-
-template <int WAVES>
-__device__ void stage_bf16_single(int8_t* xs, float* amax_s, unsigned* wmax_s, int* wsum_s,
-                                  const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int64_t k,
-                                  int kpad, int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
-  const int nthreads = blockDim.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
-  const int total = static_cast<int>(k / 8);
-  unsigned mx = 0;
-  int j = 0;
-  for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
-    uint4 v;
-    if (j < kCachedChunks) {
-#pragma unroll
-      for (int q = 0; q < kCachedChunks; ++q)
-        if (q == j) v = cache[q];
-    } else {
-      v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8);
-    }
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mx = max(mx, max(w[q] & 0x7fffu, (w[q] >> 16) & 0x7fffu));
-  }
-  mx = wave_max(mx);
-  if (lane == 0) wmax_s[wave] = mx;
-  __syncthreads();
-  unsigned mall = wmax_s[0];
-#pragma unroll
-  for (int w = 1; w < WAVES; ++w) mall = max(mall, wmax_s[w]);
-  const float a = fmaxf(bf16_to_f32(mall), 1e-8f);
-  const float s = 127.0f / a;
-  if (threadIdx.x == 0) {
-    amax_s[0] = a;
-    if (write_out) amax_out[0] = a;
-  }
-  int sum = 0;
-  j = 0;
-  for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
-    uint4 v;
-    if (j < kCachedChunks) {
-#pragma unroll
-      for (int q = 0; q < kCachedChunks; ++q)
-        if (q == j) v = cache[q];
-    } else {
-      v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8);
-    }
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      lo |= quant_code(w[q] & 0xffffu, s) << (16 * q);
-      lo |= quant_code(w[q] >> 16, s) << (16 * q + 8);
-      hi |= quant_code(w[q + 2] & 0xffffu, s) << (16 * q);
-      hi |= quant_code(w[q + 2] >> 16, s) << (16 * q + 8);
-    }
-    *reinterpret_cast<uint2*>(xs + c * 8) = make_uint2(lo, hi);
-    if (write_out) *reinterpret_cast<uint2*>(xq_out + c * 8) = make_uint2(lo, hi);
-    sum = byte_sum(hi, byte_sum(lo, sum));
-  }
-  for (int c = total + threadIdx.x; c < kpad / 8; c += nthreads) *reinterpret_cast<uint2*>(xs + c * 8) = make_uint2(0, 0);
-  sum = wave_sum(sum);
-  if (lane == 0) wsum_s[wave] = sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -406,60 +301,41 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ int red[WAVES * 4 * 64];
   __shared__ float amax_s[16];
-  __shared__ int xsum_s[16];
   __shared__ unsigned max_s[16];
   __shared__ unsigned wmax_s[WAVES];
-  __shared__ int wsum_s[WAVES];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;    // 64-column group of the lane inside a tile
   const int tok = lane & 15;  // token row of the lane's A operand
   const bool has_tok = tok < m;
-  const bool single = VEC && m == 1;
   const int pitch = static_cast<int>(lds_pitch(kt_count));
+  const int kpad = kt_count * kTileCols;
   const int nchunks = (kt_count + U * WAVES - 1) / (U * WAVES);
 
   int64_t rb = blockIdx.x;
   int c = 0;
-  // Request order matters: vector-memory results are waited for in issue
-  // order, so the activations go first and the prologue can run while the
-  // first item's weight tiles are still in flight.
   uint4 cache[kCachedChunks];
   if (VEC) {
     if (SRC == kFromCodes)
-      prefetch_codes(cache, static_cast<const int8_t*>(xsrc), m, k, kt_count * kTileCols);
+      prefetch_codes(cache, static_cast<const int8_t*>(xsrc), m, k, kpad);
     else
       prefetch_bf16(cache, static_cast<const uint16_t*>(xsrc), m, k);
   }
   uint4 wcur[U];
   load_item<WAVES, U>(wcur, packed, rb, c, kt_count, wave, lane, rb < rb_count);
 
-  if (single) {
-    if (SRC == kFromCodes) {
-      stage_codes_single<WAVES>(xs, wsum_s, cache, static_cast<const int8_t*>(xsrc), k, kt_count * kTileCols);
-      if (threadIdx.x == 0) amax_s[0] = amax_in[0];
-    } else {
-      stage_bf16_single<WAVES>(xs, amax_s, wmax_s, wsum_s, cache, static_cast<const uint16_t*>(xsrc), k,
-                               kt_count * kTileCols, xq_out, amax_out);
-    }
+  if (SRC == kFromCodes) {
+    stage_codes(xs, pitch, cache, static_cast<const int8_t*>(xsrc), m, k, kpad, VEC);
+    if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x];
+  } else if (VEC && m == 1) {
+    stage_bf16_single<WAVES>(xs, amax_s, wmax_s, cache, static_cast<const uint16_t*>(xsrc), k, kpad, xq_out,
+                             amax_out);
   } else {
-    if (threadIdx.x < 16) xsum_s[threadIdx.x] = 0;
-    if (SRC == kFromCodes) {
-      __syncthreads();
-      stage_codes(xs, pitch, xsum_s, cache, static_cast<const int8_t*>(xsrc), m, k, kt_count * kTileCols, VEC);
-      if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x];
-    } else {
-      stage_bf16(xs, pitch, amax_s, max_s, xsum_s, cache, static_cast<const uint16_t*>(xsrc), m, k,
-                 kt_count * kTileCols, VEC, xq_out, amax_out);
-    }
+    stage_bf16(xs, pitch, amax_s, max_s, cache, static_cast<const uint16_t*>(xsrc), m, k, kpad, VEC, xq_out,
+               amax_out);
   }
   __syncthreads();
-  int sum0 = 0;  // token 0's code sum on the single-token path
-  if (single) {
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum0 += wsum_s[w];
-  }
 
   const float gamma = *gamma_p;
   const v4i zero4 = {0, 0, 0, 0};
@@ -482,12 +358,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const v4i a = has_tok ? *reinterpret_cast<const v4i*>(xrow + kt * kTileCols + 16 * s) : zero4;
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand(words[s]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_ternary(words[s]), acc, 0, 0, 0);
         }
       }
     }
     if (c == nchunks - 1) {
-      // lane holds sum (w + 1) x for tokens 4g + r (r = 0..3) of weight row 16 rb + tok
+      // lane holds 64 * acc for tokens 4g + r (r = 0..3) of weight row 16 rb + tok
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
       __syncthreads();
@@ -498,7 +374,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
         for (int w = 0; w < WAVES; ++w) v += red[(w * 4 + r) * 64 + lane];
         const int t = 4 * g + r;
         if (t < m && row < n) {
-          v -= single ? sum0 : xsum_s[t];
+          v >>= kWeightShift;  // exact: the sum is a multiple of 64
           const float scale = gamma * amax_s[t] / 127.0f;
           y[t * n + row] = static_cast<float>(v) * scale;
           if (acc_out) acc_out[t * n + row] = v;
@@ -550,10 +426,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
   const bool has_tok = tok < m;
   const uint4* tiles = packed + rb * kt_count * 64 + lane;
   const int8_t* xrow = xq + static_cast<int64_t>(has_tok ? tok : 0) * k;
-  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
   v4i acc = {0, 0, 0, 0};
-  v4i sum = {0, 0, 0, 0};
   for (int kt0 = wave; kt0 < kt_count; kt0 += WAVES * U) {
     uint4 wv[U];
     v4i xv[U][4];
@@ -570,17 +444,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
     for (int u = 0; u < U; ++u) {
       const uint32_t words[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv[u][s], expand(words[s]), acc, 0, 0, 0);
-        sum = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv[u][s], ones, sum, 0, 0, 0);
-      }
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv[u][s], expand_ternary(words[s]), acc, 0, 0, 0);
     }
   }
-  const v4i res = acc - sum;
   const int64_t row = rb * kTileRows + tok;
   const float gamma = *gamma_p;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][r][lane] = res[r];
+  for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
   __syncthreads();
   for (int r = wave; r < 4; r += WAVES) {
     int v = 0;
@@ -588,6 +459,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
     for (int w = 0; w < WAVES; ++w) v += red[w][r][lane];
     const int t = 4 * g + r;
     if (t < m && row < n) {
+      v >>= kWeightShift;
       const float scale = gamma * amax[t] / 127.0f;
       y[t * n + row] = static_cast<float>(v) * scale;
       if (acc_out) acc_out[t * n + row] = v;
@@ -615,16 +487,19 @@ hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t
   return hipGetLastError();
 }
 
-// U = tiles per wave per item: enough for one item to cover a row block of up
-// to 32 tiles (k <= 8192); longer rows are walked in chunks of 32 tiles.
+// U = tiles per wave per item: one item covers a row block of up to
+// 8 * WAVES tiles; longer rows are walked in chunks of that many tiles.
 template <int SRC>
 hipError_t dispatch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
                         const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
                         hipStream_t s, bool vec) {
   const int64_t kt = k_tiles(k);
-  if (kt <= kWaves) return launch_lds<SRC, kWaves, 1>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
-  if (kt <= 2 * kWaves) return launch_lds<SRC, kWaves, 2>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
-  if (kt <= 4 * kWaves) return launch_lds<SRC, kWaves, 4>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+  if (kt <= kWaves)
+    return launch_lds<SRC, kWaves, 1>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+  if (kt <= 2 * kWaves)
+    return launch_lds<SRC, kWaves, 2>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+  if (kt <= 4 * kWaves)
+    return launch_lds<SRC, kWaves, 4>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
   return launch_lds<SRC, kWaves, 8>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
 }
 

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void absmean_partial(const float* __restr
 __device__ __forceinline__ uint32_t ternary_field(float wv, float d) {
   float r = rintf(wv / d);  // one IEEE fp32 divide, round half to even
   r = fminf(fmaxf(r, -1.0f), 1.0f);
-  return static_cast<uint32_t>(static_cast<int32_t>(r) + 1);  // stored as w + 1
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 3u;  // two's complement in 2 bits
 }
 
 // position of column t (0..15) of a 16-column word
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint32_t* __rest
     for (int t = 0; t < 16; ++t) {
       if (k0 + t < k) {
         const int f = static_cast<int>((word >> field_shift(t)) & 3u);
-        codes[row * k + k0 + t] = static_cast<int8_t>(f - 1);  // 3 (unused) would decode to +2
+        codes[row * k + k0 + t] = static_cast<int8_t>((f ^ 2) - 2);  // sign-extend (10, never written, -> -2)
       }
     }
   }

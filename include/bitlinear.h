@@ -33,8 +33,8 @@
  *    output untouched.  A failed launch returns BITLINEAR_E_HIP.  Nothing is
  *    thrown and errno is not used.
  *  - Inputs containing NaN or Inf are outside the contract.
- *  - Sizes: 1 <= n, m <= 2^31 - 1 and 1 <= k <= 2^24 (so |acc| <= 127 k
- *    stays inside int32).
+ *  - Sizes: 1 <= n, m <= 2^31 - 1 and 1 <= k <= 2^18 (the matrix cores
+ *    accumulate 64 * acc, and |64 * acc| <= 64 * 127 * k stays inside int32).
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H
@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_ABI_VERSION 2
 
 /* Largest token count accepted by bitlinear_forward (the decode path). */
 #define BITLINEAR_FORWARD_MAX_M 16
@@ -69,15 +69,15 @@ const char *bitlinear_status_string(int status);
 
 /*
  * Bytes of the packed ternary weights of an [n][k] matrix on the device.
- * Layout (version 1): the matrix is cut into tiles of 16 rows x 256 columns;
+ * Layout (version 2): the matrix is cut into tiles of 16 rows x 256 columns;
  * tile (rb, kt) is 1024 contiguous bytes at offset (rb * ceil(k/256) + kt) *
  * 1024, so one 16-row block is a contiguous stream along k.  Inside a tile,
  * 16-byte lane slot l (0..63) holds row 16*rb + (l % 16) and columns
  * 256*kt + 64*(l / 16) + [0, 64); its 32-bit word s covers 16 of those
  * columns, column t of the word in bits 8*(t % 4) + 2*(t / 4).  Each 2-bit
- * field stores w + 1 (0 = -1, 1 = 0, 2 = +1; 3 unused); rows >= n and
- * columns >= k are padded with the code of 0.  Pure host function; returns 0
- * if n or k is out of range.
+ * field holds w in two's complement (00 = 0, 01 = +1, 11 = -1; 10 unused);
+ * rows >= n and columns >= k are padded with 00.  Pure host function;
+ * returns 0 if n or k is out of range.
  */
 size_t bitlinear_packed_bytes(int64_t n, int64_t k);
 

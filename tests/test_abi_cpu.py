@@ -49,7 +49,7 @@ def test_single_hip_runtime_mapped(blq):
 
 
 def test_version_and_status_strings(blq):
-    assert blq.bitlinear_abi_version() == 1
+    assert blq.bitlinear_abi_version() == 2
     for s in range(-6, 1):
         assert blq.bitlinear_status_string(s) not in ("", "unknown status")
     assert blq.bitlinear_status_string(12345) == "unknown status"
@@ -63,7 +63,8 @@ def test_packed_bytes(blq):
     assert blq.bitlinear_packed_bytes(57344, 8192) == 57344 * 8192 // 4
     assert blq.bitlinear_packed_bytes(0, 5) == 0
     assert blq.bitlinear_packed_bytes(5, 0) == 0
-    assert blq.bitlinear_packed_bytes(5, (1 << 24) + 1) == 0
+    assert blq.bitlinear_packed_bytes(5, (1 << 18) + 1) == 0
+    assert blq.bitlinear_packed_bytes(5, 1 << 18) > 0
     assert 8 <= blq.bitlinear_pack_workspace_bytes(2048, 2048) <= 8192
     assert blq.bitlinear_pack_workspace_bytes(57344, 8192) == 8192
 
@@ -85,7 +86,7 @@ def test_pack_validation(blq):
     assert lib.bitlinear_pack_weights(A16, 64, 512, A16, nb, A16, None, ws, None) == E.BITLINEAR_E_NULL
     assert lib.bitlinear_pack_weights(A16, 0, 512, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
     assert lib.bitlinear_pack_weights(A16, 64, -3, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
-    assert lib.bitlinear_pack_weights(A16, 64, 1 << 25, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
+    assert lib.bitlinear_pack_weights(A16, 64, (1 << 18) + 1, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
     assert lib.bitlinear_pack_weights(A16, 64, 512, A8, nb, A16, A16, ws, None) == E.BITLINEAR_E_ALIGN
     assert lib.bitlinear_pack_weights(A2, 64, 512, A16, nb, A16, A16, ws, None) == E.BITLINEAR_E_ALIGN
     assert lib.bitlinear_pack_weights(A16, 64, 512, A16, nb, A16, A2, ws, None) == E.BITLINEAR_E_ALIGN
@@ -123,7 +124,7 @@ def test_forward_validation(blq, fname):
         assert call(**{key: None, "n": 64}) == E.BITLINEAR_E_NULL, key
     assert call(n=0) == E.BITLINEAR_E_SHAPE
     assert call(k=0) == E.BITLINEAR_E_SHAPE
-    assert call(k=(1 << 24) + 1) == E.BITLINEAR_E_SHAPE
+    assert call(k=(1 << 18) + 1) == E.BITLINEAR_E_SHAPE
     assert call(m=0) == E.BITLINEAR_E_SHAPE
     assert call(packed=A8) == E.BITLINEAR_E_ALIGN
     assert call(y=A2) == E.BITLINEAR_E_ALIGN
