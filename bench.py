@@ -41,16 +41,18 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, published
 MALL_BYTES = 256 << 20         # last-level (Infinity) cache
 COLD_BYTES = 1 << 30           # walk at least this many weight bytes between reuses
-KERNEL_SOURCES = ("gemv.hip", "gemm.hip", "quant_act.hip")
+# sources of the dominant kernel: the counters in profiles/ are used only while these are unchanged
+DECODE_SOURCES = ("gemv.hip", "bitlinear_internal.hpp")
+BATCHED_SOURCES = ("gemm.hip", "bitlinear_internal.hpp")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "bitlinear_quant_act_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -232,7 +234,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bound)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="CPU only: write profiles/ summaries from rocprofv3 CSVs (see summarize())")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the path is single-device; "
@@ -270,7 +277,10 @@ def main():
         oracle_mod._load()
 
     total_packed = synth.packed_weight_bytes_2bit(wl)
-    replicas = max(1, -(-COLD_BYTES // total_packed)) if total_packed < 2 * MALL_BYTES else 1
+    # a step that walks more than 1.5x the last-level cache evicts its own
+    # weights before they come round again; smaller workloads are replicated
+    # and walked in turn (the reported steps then round up to whole walks)
+    replicas = max(1, -(-COLD_BYTES // total_packed)) if total_packed < 1.5 * MALL_BYTES else 1
     log("workload %s m=%d: %d matrices, %.1f MB packed, %d replica(s)" % (
         wl.key, m, wl.layers * len(wl.matrices), total_packed / 1e6, replicas))
     t0 = time.time()
@@ -296,35 +306,41 @@ def main():
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    graphs = []
+    # One graph holds one step over every replica in turn (one replay = len(reps)
+    # steps), so a small workload is not timed as graph-launch overhead.
+    graph = None
     if not args.eager:
-        for mats in reps:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for mats in reps:
                 launch_step(blq, mats, m, torch.cuda.current_stream(), fused)
-            graphs.append(g)
         torch.cuda.synchronize()
+    per_run = len(reps)
 
-    def run(i):
+    def run():
         if args.eager:
             with torch.cuda.stream(stream):
-                launch_step(blq, reps[i % len(reps)], m, stream, fused)
+                for mats in reps:
+                    launch_step(blq, mats, m, stream, fused)
         else:
-            graphs[i % len(graphs)].replay()
+            graph.replay()
 
-    for i in range(args.warmup):
-        run(i)
+    runs_w = max(1, -(-args.warmup // per_run))
+    runs_t = max(1, -(-args.steps // per_run))
+    for _ in range(runs_w):
+        run()
     torch.cuda.synchronize()
     log("warmup done")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for i in range(args.steps):
-        run(args.warmup + i)
+    for _ in range(runs_t):
+        run()
     ev1.record()
     torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
+    steps_timed = runs_t * per_run
+    ms_per_step = ev0.elapsed_time(ev1) / steps_timed
+    log("timed %d steps: %.4f ms/step" % (steps_timed, ms_per_step))
 
     # Dominant kernel (the forward, or the fused quant + forward): HIP events
     # on its stream around graph replays that hold only that kernel's
@@ -337,13 +353,14 @@ def main():
         torch.cuda.synchronize()
     replays = max(2, min(10, args.steps))
     dom = "fused" if fused else "forward"
-    dom_ms = 0.0
-    for r, mats in enumerate(reps):
-        dom_ms += time_graph(torch, stream, lambda st, mats=mats: launch_kernel_only(blq, mats, m, st, dom), replays)
-    dom_ms /= len(reps)
+
+    def all_reps(which):
+        return lambda st: [launch_kernel_only(blq, mats, m, st, which) for mats in reps]
+
+    dom_ms = time_graph(torch, stream, all_reps(dom), replays) / len(reps)
     nlaunch = len(mats0) * replays * len(reps)
     fw_avg_us = dom_ms / len(mats0) * 1e3
-    q_ms = time_graph(torch, stream, lambda st: launch_kernel_only(blq, mats0, m, st, "quant"), replays)
+    q_ms = time_graph(torch, stream, all_reps("quant"), replays) / len(reps)
     q_avg_us = q_ms / len(mats0) * 1e3
     per_call = fused_bytes if fused else forward_bytes
     fw_bytes = sum(per_call(m, mt.n, mt.k) for mt in mats0)
@@ -368,13 +385,13 @@ def main():
     roof["launches_timed"] = nlaunch
     roof["per_launch"] = "mean over the workload's matrices of %s" % (
         "2*M*N*K" if batched else "ceil(N*K/4)+2*M*K+4+4*M*N bytes" if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
-    roof["timing"] = "HIP events around %d graph replays of the kernel's %d launches" % (replays, len(mats0))
+    roof["timing"] = "HIP events around %d graph replays of the kernel's %d launches" % (replays, len(mats0) * len(reps))
     roof["traffic"] = None
     prof = os.path.join(ROOT, "profiles", "counters_%s_m%d.json" % (wl.key, m))
     if os.path.exists(prof):
         with open(prof) as f:
             c = json.load(f)
-        if c.get("kernel_source_hash") == kernel_source_hash():
+        if c.get("kernel_source_hash") == kernel_source_hash(BATCHED_SOURCES if batched else DECODE_SOURCES):
             roof["traffic"] = c.get("hbm_bytes_per_launch")
 
     out = {
@@ -382,8 +399,8 @@ def main():
         "value": round(value, 2 if batched else 1),
         "unit": unit,
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps_timed,
+        "warmup": runs_w * per_run,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -434,6 +451,75 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_avg_kib(path, kernel_pat):
+    """Mean per-dispatch value of the one counter in a rocprofv3 counter CSV,
+    over dispatches whose kernel name contains kernel_pat."""
+    vals = {}
+    for r in _read_csv(path):
+        if kernel_pat in r["Kernel_Name"]:
+            vals.setdefault(r.get("Dispatch_Id", len(vals)), 0.0)
+            vals[r.get("Dispatch_Id", len(vals))] += float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit("no dispatch of %r in %s" % (kernel_pat, path))
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def summarize(args):
+    """Write profiles/ summaries from rocprofv3 output (CPU only).
+
+    --summarize KEY M STATS_CSV FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB KERNEL_PAT CMD..."""
+    key, m, stats, fetch, write, cfetch, cwrite, copy_mib, pat = args[:9]
+    cmds = " ".join(args[9:])
+    m = int(m)
+    copy_kib = float(copy_mib) * 1024.0
+    cf, _ = _counter_avg_kib(cfetch, "copy")
+    cw, _ = _counter_avg_kib(cwrite, "copy")
+    f_fetch = copy_kib / cf
+    f_write = copy_kib / cw
+    kf, nf = _counter_avg_kib(fetch, pat)
+    kw, nw = _counter_avg_kib(write, pat)
+    traffic = (kf * f_fetch + kw * f_write) * 1024.0
+    rows = [r for r in _read_csv(stats)]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    wl = synth.BY_KEY[key]
+    alg = sum((fused_bytes if m == 1 else forward_bytes)(m, mt.n, mt.k) for mt in wl.matrices) / len(wl.matrices)
+    out = {
+        "workload": key, "m": m, "kernel_pattern": pat,
+        "kernel_source_hash": kernel_source_hash(DECODE_SOURCES if m <= 16 else BATCHED_SOURCES),
+        "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": [nf, nw],
+        "copy_calibration": {"copy_mib": float(copy_mib), "fetch_kib": cf, "write_kib": cw,
+                             "fetch_factor": f_fetch, "write_factor": f_write},
+        "hbm_bytes_per_launch": round(traffic), "algorithmic_bytes_per_launch": round(alg),
+        "commands": cmds,
+    }
+    with open(os.path.join(ROOT, "profiles", "counters_%s_m%d.json" % (key, m)), "w") as f:
+        json.dump(out, f, indent=1)
+    lines = ["# rocprofv3 kernel statistics: %s, m=%d" % (wl.title, m), "",
+             "Commands (run from the repository root on one MI355X):", "", "```", cmds, "```", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = name.split("(")[0].replace("void bitlinear::(anonymous namespace)::", "")
+        if "<" in name:
+            short = name[:name.index("(", name.index(">"))].replace("void bitlinear::(anonymous namespace)::", "")
+        lines.append("| %s | %s | %.3f | %.3f | %.3f | %s%% |" % (short, r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                                                                 r["Percentage"][:5]))
+    lines += ["", "HBM traffic of `%s` from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by a plain "
+              "device copy of %s MiB measured the same way (factors %.4f / %.4f): %.0f bytes per launch vs "
+              "%.0f algorithmic bytes per launch (mean over the workload's matrices)." % (
+                  pat, copy_mib, f_fetch, f_write, traffic, alg)]
+    with open(os.path.join(ROOT, "profiles", "%s_m%d_kernels.md" % (key, m)), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(out))
 
 
 def _cpu_model() -> str:

@@ -9,18 +9,24 @@
 //
 // Tiling: a workgroup of 4 waves (WM x WN) owns a BM x BN output tile
 // (tokens x weight rows) and walks k in 256-column steps, the width of one
-// packed weight tile.  Each step's BM x 256 int8 activation tile and BN/16
-// packed weight tiles (1 KiB each, copied verbatim: still 2 bits per weight)
-// go to one of two LDS stages while the other stage feeds the matrix cores:
-// the next step's global loads are issued before the current step's math and
-// land in the idle stage after it, so there is one barrier per step.
+// packed weight tile.  A step's operands are the BM x 256 int8 activation
+// tile and the BN/16 packed weight tiles (1 KiB each, copied verbatim: still
+// 2 bits per weight).
 //
-// Each wave expands its packed weight slots to int8 in registers -- one
-// shift and one mask per 4 weights, 64 * w in two's complement (see
-// expand_ternary) -- once per slot and step, and reuses them for all its
-// 16-token blocks, then runs v_mfma_i32_16x16x64_i8 on (16 tokens x 64
-// cols) x (64 cols x 16 rows).  The accumulators hold 64 * acc exactly; the
-// epilogue shifts, scales by gamma * a'[t] / 127 and stores fp32.
+// Matrix-core instruction: v_mfma_i32_32x32x32_i8 (measured ~4.5 POPS on
+// MI355X, against ~2.5-3.2 for the 16x16x64 form).  With the packed layout
+// unchanged, step q (0..7) of a 256-column tile takes columns 32q .. 32q+31:
+// lane (row r, half h) supplies word 2(q%2)+h of slot (r%16)+16(q/2), i.e.
+// 16 columns, expanded to int8 64*w with one shift and one mask per 4
+// weights (expand_ternary) and reused for every 32-token block of the wave;
+// its A operand is the same 16 columns of its token.  The accumulators hold
+// 64 * acc exactly; the epilogue shifts, scales by gamma * a'[t] / 127 and
+// stores fp32.
+//
+// Main path (k % 16 == 0, 16-byte aligned codes): an S-stage ring of LDS
+// buffers filled by direct-to-LDS copies (global_load_lds_dwordx4), S - 1
+// steps in flight, one barrier per step; see gemm_dma_kernel.  Otherwise a
+// register-staged two-stage variant (gemm_kernel) handles any k.
 //
 // Workgroup order is XCD-aware: hardware deals workgroups to the 8 XCDs
 // round-robin, so the linear id is remapped to give each XCD a contiguous
@@ -265,8 +271,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int BM, int BN, int WM, int WN, int S>
-__global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const uint8_t* __restrict__ packed_b,
+template <int BM, int BN, int WM, int WN, int S, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* __restrict__ packed_b,
                                                                const float* __restrict__ gamma_p, int64_t n,
                                                                int64_t k, int kt_count, const int8_t* __restrict__ xq,
                                                                const float* __restrict__ amax, int64_t m,
@@ -379,19 +385,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(const uint8_t* __
   }
 }
 
-int max_lds_per_block() {
-  static int cached = -1;
-  if (cached < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
-      cached = v;
-    else
-      cached = 65536;
-  }
-  return cached;
-}
-
 template <int BM, int BN, int WM, int WN>
 hipError_t launch(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                   const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s, bool vec) {
@@ -418,87 +411,54 @@ hipError_t launch(const void* packed, const float* gamma, int64_t n, int64_t k, 
   return hipGetLastError();
 }
 
-// LDS bytes of a tile configuration (two stages), matching TileShape::kLds
-constexpr int TileShapeBytes(int bm, int bn) { return 2 * (bm * kAPitch + (bn / kTileRows) * kTileBytes); }
 
 // Candidate tiles (BM, BN, WM, WN).  The choice maximises the fraction of
 // the 256 CUs kept busy over the rounds of workgroups (one resident
 // workgroup per CU) times the useful fraction of each tile, preferring the
 // earlier (larger) tile on ties: more reuse per loaded byte.
+// Register-staged fallback (k % 16 != 0 or unaligned codes): two tile sizes.
 struct Cand {
   int bm, bn, wm, wn;
 };
-constexpr Cand kConfigs[] = {{256, 128, 2, 2}, {128, 256, 2, 2}, {128, 128, 2, 2}, {64, 192, 2, 2}, {128, 64, 2, 2},
-                             {128, 32, 4, 1},  {64, 256, 2, 2},  {64, 128, 2, 2},  {64, 64, 2, 2}};
 
-Cand choose(int64_t m, int64_t n) {
-  const int64_t cus = 256;
-  Cand best = kConfigs[0];
-  double best_score = -1.0;
-  for (const Cand& c : kConfigs) {
-    if (m > 64 && c.bm < 128) continue;     // large token counts: 128+ token tiles
-    if (m <= 64 && c.bm != 64) continue;
-    if (TileShapeBytes(c.bm, c.bn) > max_lds_per_block()) continue;
-    const int64_t wgs = ((m + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
-    const int64_t rounds = (wgs + cus - 1) / cus;
-    const double fill = static_cast<double>(wgs) / static_cast<double>(rounds * cus);
-    const double used = static_cast<double>(m * n) / static_cast<double>(wgs * c.bm * c.bn);
-    const double score = fill * used;
-    if (score > best_score + 1e-9) {
-      best_score = score;
-      best = c;
-    }
-  }
-  return best;
+Cand choose(int64_t m, int64_t /*n*/) {
+  if (m <= 64) return Cand{64, 64, 2, 2};
+  return Cand{128, 128, 2, 2};
 }
 
 // ---- direct-to-LDS pipeline configurations ---------------------------------
 
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int WM, int WN, int S, int OCC>
 hipError_t launch_dma(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                       const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
+  static_assert(S * DmaStageBytes(BM, BN) <= 163840, "LDS per workgroup");  // OCC: register-budget hint
   const int kt = static_cast<int>(k_tiles(k));
   const int64_t mt = (m + BM - 1) / BM;
   const int64_t ntl = (n + BN - 1) / BN;
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
-  gemm_dma_kernel<BM, BN, WM, WN, S><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+  gemm_dma_kernel<BM, BN, WM, WN, S, OCC><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
       static_cast<const uint8_t*>(packed), gamma, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl),
       y, acc);
   return hipGetLastError();
 }
 
-struct DmaCand {
-  int bm, bn, wm, wn, stages;
-};
-constexpr DmaCand kDmaConfigs[] = {{128, 256, 2, 2, 3}, {128, 128, 2, 2, 4}, {128, 64, 2, 2, 4},
-                                   {64, 256, 2, 2, 4},  {64, 192, 2, 2, 4},  {64, 128, 2, 2, 4},
-                                   {64, 64, 2, 2, 4}};
+// Tile choice, from measurements on MI355X of every (tile, stages,
+// workgroups per CU) candidate on the 8B- and 70B-shaped layers: wide weight
+// tiles with two resident workgroups per CU for wide matrices; 64 x 192 for
+// mid widths; small 64 x 64 tiles with three workgroups per CU otherwise
+// (enough workgroups to fill 256 CUs, and one workgroup's barrier and copy
+// latency hidden behind the others' matrix-core work).
+enum DmaConfig { kWide = 0, kMid = 1, kSmall = 2 };
 
 #ifndef BITLINEAR_GEMM_FORCE
 #define BITLINEAR_GEMM_FORCE -1
 #endif
 
-int choose_dma(int64_t m, int64_t n) {
-  if (BITLINEAR_GEMM_FORCE >= 0) return BITLINEAR_GEMM_FORCE;
-  const int64_t cus = 256;
-  int best = -1;
-  double best_score = -1.0;
-  for (int i = 0; i < static_cast<int>(sizeof(kDmaConfigs) / sizeof(kDmaConfigs[0])); ++i) {
-    const DmaCand& c = kDmaConfigs[i];
-    if (m > 64 && c.bm < 128) continue;
-    if (m <= 64 && c.bm != 64) continue;
-    if (c.stages * DmaStageBytes(c.bm, c.bn) > max_lds_per_block()) continue;
-    const int64_t wgs = ((m + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
-    const int64_t rounds = (wgs + cus - 1) / cus;
-    const double fill = static_cast<double>(wgs) / static_cast<double>(rounds * cus);
-    const double used = static_cast<double>(m * n) / static_cast<double>(wgs * c.bm * c.bn);
-    const double score = fill * used;
-    if (score > best_score + 1e-9) {
-      best_score = score;
-      best = i;
-    }
-  }
-  return best;
+DmaConfig choose_dma(int64_t m, int64_t n) {
+  if (BITLINEAR_GEMM_FORCE >= 0) return static_cast<DmaConfig>(BITLINEAR_GEMM_FORCE);
+  if (n >= 16384) return kWide;
+  if (m > 64 && n >= 6144) return kMid;
+  return kSmall;
 }
 
 }  // namespace
@@ -507,30 +467,17 @@ hipError_t launch_gemm(const void* packed, const float* gamma, int64_t n, int64_
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
   if (vec) {
-    const int i = choose_dma(m, n);
-    switch (i) {
-      case 0: return launch_dma<128, 256, 2, 2, 3>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      case 1: return launch_dma<128, 128, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      case 2: return launch_dma<128, 64, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      case 3: return launch_dma<64, 256, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      case 4: return launch_dma<64, 192, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      case 5: return launch_dma<64, 128, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      case 6: return launch_dma<64, 64, 2, 2, 4>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      default: break;
+    switch (choose_dma(m, n)) {
+      case kWide: return launch_dma<64, 256, 2, 2, 2, 2>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case kMid: return launch_dma<64, 192, 2, 2, 2, 2>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case kSmall: return launch_dma<64, 64, 2, 2, 3, 3>(packed, gamma, n, k, xq, amax, m, y, acc, s);
     }
   }
   const Cand c = choose(m, n);
 #define BITLINEAR_GEMM_CASE(BM_, BN_, WM_, WN_)                 \
   if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_) \
     return launch<BM_, BN_, WM_, WN_>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
-  BITLINEAR_GEMM_CASE(256, 128, 2, 2)
-  BITLINEAR_GEMM_CASE(128, 256, 2, 2)
   BITLINEAR_GEMM_CASE(128, 128, 2, 2)
-  BITLINEAR_GEMM_CASE(64, 192, 2, 2)
-  BITLINEAR_GEMM_CASE(128, 64, 2, 2)
-  BITLINEAR_GEMM_CASE(128, 32, 4, 1)
-  BITLINEAR_GEMM_CASE(64, 256, 2, 2)
-  BITLINEAR_GEMM_CASE(64, 128, 2, 2)
   BITLINEAR_GEMM_CASE(64, 64, 2, 2)
 #undef BITLINEAR_GEMM_CASE
   return hipErrorInvalidValue;
