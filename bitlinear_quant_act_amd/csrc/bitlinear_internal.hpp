@@ -26,6 +26,24 @@ constexpr int kWeightShift = 6;     // expanded weight bytes are 64 * w
 __host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kTileRows - 1) / kTileRows; }
 __host__ __device__ inline int64_t k_tiles(int64_t k) { return (k + kTileCols - 1) / kTileCols; }
 
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// accesses (lgkmcnt), not for its outstanding global loads.  __syncthreads()
+// carries a release fence that also drains every vector-memory load, which
+// would stall a kernel that keeps weight tiles in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 16-byte streaming load of packed weights: read once, so marked
+// non-temporal to keep them from displacing reused data in the caches.
+__device__ __forceinline__ uint4 load_weights_nt(const uint4* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // One packed word (16 weights) -> the 16-byte int8 operand 64 * w of one
 // 16x16x64 MFMA, columns in order: three shifts and four masks.
 typedef int expand_v4i __attribute__((ext_vector_type(4)));

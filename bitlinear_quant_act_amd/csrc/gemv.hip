@@ -38,6 +38,9 @@
 // token at the same 16 columns, so A and B share the k order without any
 // shuffling.
 //
+// Barriers are LDS-only (lds_barrier): a __syncthreads fence would wait for
+// the weight tiles still in flight.
+//
 // Epilogue: the waves' int32 partials are summed through LDS and scaled by
 // gamma * a'[m] / 127 in fp32; lanes 0..15 of a result row write 16
 // consecutive floats.
@@ -186,7 +189,7 @@ __device__ void stage_bf16_single(int8_t* xs, float* amax_s, unsigned* wmax_s, c
                                                 : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8)));
   mx = wave_max(mx);
   if ((threadIdx.x & 63) == 0) wmax_s[threadIdx.x >> 6] = mx;
-  __syncthreads();
+  lds_barrier();
   unsigned mall = wmax_s[0];
 #pragma unroll
   for (int w = 1; w < WAVES; ++w) mall = max(mall, wmax_s[w]);
@@ -214,7 +217,7 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
   const int nthreads = blockDim.x;
   const bool write_out = xq_out != nullptr && blockIdx.x == 0;
   if (threadIdx.x < m) max_s[threadIdx.x] = 0u;
-  __syncthreads();
+  lds_barrier();
   if (vec) {  // k % 8 == 0 and x 16-byte aligned: chunks of 8 values
     const int cpr = static_cast<int>(k / 8);
     const int total = m * cpr;
@@ -232,9 +235,9 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
                                                     : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8)));
     }
     if (cur_t >= 0) atomicMax(&max_s[cur_t], cur);
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < m) amax_s[threadIdx.x] = fmaxf(bf16_to_f32(max_s[threadIdx.x]), 1e-8f);
-    __syncthreads();
+    lds_barrier();
     j = 0;
     for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
       const int t = c / cpr, cc = c - t * cpr;
@@ -255,9 +258,9 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
       for (int64_t i = threadIdx.x; i < k; i += nthreads) cur = max(cur, static_cast<unsigned>(x[t * k + i]) & 0x7fffu);
       atomicMax(&max_s[t], cur);
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < m) amax_s[threadIdx.x] = fmaxf(bf16_to_f32(max_s[threadIdx.x]), 1e-8f);
-    __syncthreads();
+    lds_barrier();
     for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
       const int t = c / kpad, col = c - t * kpad;
       int8_t q = 0;
@@ -284,7 +287,7 @@ __device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int kt = c * U * WAVES + wave + u * WAVES;
-    w[u] = (valid && kt < kt_count) ? packed[(rb * kt_count + kt) * 64 + lane]
+    w[u] = (valid && kt < kt_count) ? load_weights_nt(packed + (rb * kt_count + kt) * 64 + lane)
                                     : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
   }
 }
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
     stage_bf16(xs, pitch, amax_s, max_s, cache, static_cast<const uint16_t*>(xsrc), m, k, kpad, VEC, xq_out,
                amax_out);
   }
-  __syncthreads();
+  lds_barrier();
 
   const float gamma = *gamma_p;
   const v4i zero4 = {0, 0, 0, 0};
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
       // lane holds 64 * acc for tokens 4g + r (r = 0..3) of weight row 16 rb + tok
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
-      __syncthreads();
+      lds_barrier();
       const int64_t row = rb * kTileRows + tok;
       for (int r = wave; r < 4; r += WAVES) {
         int v = 0;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
           if (acc_out) acc_out[t * n + row] = v;
         }
       }
-      __syncthreads();
+      lds_barrier();
       acc = zero4;
     }
     rb = rbn;
@@ -435,7 +438,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
     for (int u = 0; u < U; ++u) {
       const int kt = kt0 + u * WAVES;
       const bool in = kt < kt_count;
-      wv[u] = in ? tiles[static_cast<int64_t>(kt) * 64] : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
+      wv[u] = in ? load_weights_nt(tiles + static_cast<int64_t>(kt) * 64)
+                 : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
       const int64_t c0 = static_cast<int64_t>(kt) * kTileCols + g * 64;
 #pragma unroll
       for (int s = 0; s < 4; ++s) xv[u][s] = load_x16(xrow, c0 + 16 * s, k, in && has_tok, VEC);
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
   const float gamma = *gamma_p;
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
-  __syncthreads();
+  lds_barrier();
   for (int r = wave; r < 4; r += WAVES) {
     int v = 0;
 #pragma unroll
