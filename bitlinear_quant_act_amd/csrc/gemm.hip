@@ -24,9 +24,12 @@
 // stores fp32.
 //
 // Main path (k % 16 == 0, 16-byte aligned codes): an S-stage ring of LDS
-// buffers filled by direct-to-LDS copies (global_load_lds_dwordx4), S - 1
+// buffers filled by buffer-to-LDS copies (buffer_load_dwordx4 ... lds), S - 1
 // steps in flight, one barrier per step; see gemm_dma_kernel.  Otherwise a
 // register-staged two-stage variant (gemm_kernel) handles any k.
+//
+// The per-token output scale gamma * a'[t] / 127 is computed once per
+// workgroup into LDS, so the epilogue is stores only.
 //
 // Workgroup order is XCD-aware: hardware deals workgroups to the 8 XCDs
 // round-robin, so the linear id is remapped to give each XCD a contiguous
@@ -146,6 +149,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
   const int b_row = wn * TN + l32;                              // + nb * 32
   const int b_off = (b_row >> 4) * kTileBytes + (b_row & 15) * 16;  // + nb * 2 KiB + g * 256
 
+  __shared__ float scale_s[BM];
+  if (tid < BM) {
+    const int64_t t = m0 + tid;
+    scale_s[tid] = t < m ? *gamma_p * amax[t] / 127.0f : 0.0f;
+  }
+
   load_global(0);
   store_lds(0);
   __syncthreads();
@@ -183,14 +192,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
   }
 
   // 32 x 32 block layout: element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
-  const float gamma = *gamma_p;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t t = m0 + wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int tl = wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int64_t t = m0 + tl;
       if (t >= m) continue;
-      const float scale = gamma * amax[t] / 127.0f;
+      const float scale = scale_s[tl];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int64_t j = n0 + wn * TN + nb * 32 + l32;
@@ -205,21 +214,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
 }
 
 // ---------------------------------------------------------------------------
-// S-stage pipeline with direct-to-LDS loads (k % 16 == 0, codes 16-byte aligned)
+// S-stage pipeline with buffer-to-LDS loads (k % 16 == 0, codes 16-byte aligned)
 // ---------------------------------------------------------------------------
 //
-// global_load_lds_dwordx4 moves 16 bytes per lane straight into LDS (64
+// buffer_load_dwordx4 ... lds moves 16 bytes per lane straight into LDS (64
 // lanes -> 1 KiB contiguous), so no registers stage the tiles and S - 1 tiles
 // can be in flight while one is consumed.  Each stage is its own LDS array so
 // the compiler tracks the outstanding copies per stage; a wave waits for its
 // own copies of the tile it is about to read (s_waitcnt vmcnt), then a plain
 // s_barrier (no memory fence, which would drain every copy) publishes them.
+// The buffer (MUBUF) form rather than the global (FLAT) one keeps the
+// compiler's LDS-read waits exact: a pending FLAT operation forces every
+// lgkmcnt wait to zero.
+//
+// Each workgroup addresses its operands through two buffer descriptors: its
+// BM token rows of codes and its BN / 16 weight row blocks.  Reads past a
+// descriptor's byte count return zeros, which covers token rows past m and
+// row blocks past n; columns past k (inside the last token row) meet zero
+// weight padding.
 //
 // The activation tile has no padding; instead the 16 chunks of 16 bytes in
 // a 256-byte row are stored XOR-swizzled by (row % 16), which keeps the 32
-// token rows of one MFMA operand read on distinct banks.  Rows past m and
-// columns past k read valid memory (row m-1, column 0): they only meet
-// discarded output rows or zero weights.
+// token rows of one MFMA operand read on distinct banks.
 
 #define BITLINEAR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -235,10 +251,11 @@ struct DmaShape {
 
 constexpr int DmaStageBytes(int bm, int bn) { return bm * kTileCols + (bn / kTileRows) * kTileBytes; }
 
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+
 template <int BM, int BN>
-__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* __restrict__ packed_b,
-                                           const int8_t* __restrict__ xq, int64_t m0, int64_t m, int64_t k,
-                                           int64_t rb0, int64_t rb_count, int kt_count, int kt, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(uint8_t* stage, __amdgpu_buffer_rsrc_t a_rsrc, __amdgpu_buffer_rsrc_t b_rsrc,
+                                           int k, int kt_count, int kt, int wave, int lane) {
   using DS = DmaShape<BM, BN>;
   const int ktc = kt < kt_count ? kt : 0;  // tiles past the end re-read tile 0 into an unused stage
 #pragma unroll
@@ -246,20 +263,14 @@ __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* __rest
     const int blk = wave * DS::kADma + i;  // 1 KiB = 4 rows
     const int row = 4 * blk + (lane >> 4);
     const int chunk = (lane & 15) ^ (row & 15);
-    int64_t grow = m0 + row;
-    grow = grow < m ? grow : m - 1;
-    int64_t col = static_cast<int64_t>(ktc) * kTileCols + chunk * 16;
-    col = col < k ? col : 0;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + grow * k + col), BITLINEAR_LDS(stage + blk * 1024),
-                                     16, 0, 0);
+    const int off = row * k + ktc * kTileCols + chunk * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, BITLINEAR_LDS(stage + blk * 1024), 16, off, 0, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < DS::kBDma; ++i) {
     const int rbl = wave * DS::kBDma + i;
-    int64_t rbg = rb0 + rbl;
-    rbg = rbg < rb_count ? rbg : rb_count - 1;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(packed_b + (rbg * kt_count + ktc) * kTileBytes + lane * 16),
-                                     BITLINEAR_LDS(stage + DS::kABytes + rbl * 1024), 16, 0, 0);
+    const int off = (rbl * kt_count + ktc) * kTileBytes + lane * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, BITLINEAR_LDS(stage + DS::kABytes + rbl * 1024), 16, off, 0, 0, 0);
   }
 }
 
@@ -318,42 +329,89 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   const int b_row = wn * TN + l32;                                    // + nb * 32
   const int b_off = DS::kABytes + (b_row >> 4) * kTileBytes + (b_row & 15) * 16;  // + nb * 2 KiB + g * 256
 
-  auto compute = [&](const uint8_t* st) {
+  // operands of one 64-column group: NB weight slots and 2 x MB activation chunks
+  struct Ops {
+    uint4 slot[NB];
+    v4i a[2][MB];
+  };
+  auto read_ops = [&](const uint8_t* st, int g, Ops& o) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint4 slot[NB];
+    for (int nb = 0; nb < NB; ++nb) o.slot[nb] = *reinterpret_cast<const uint4*>(st + b_off + nb * 2 * kTileBytes + g * 256);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) slot[nb] = *reinterpret_cast<const uint4*>(st + b_off + nb * 2 * kTileBytes + g * 256);
+    for (int half = 0; half < 2; ++half) {
+      const int chunk = (4 * g + 2 * half) ^ a_x;  // logical chunk 4g + 2 half + h, swizzled by row % 16
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        v4i b[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const uint32_t word = half == 0 ? (h == 0 ? slot[nb].x : slot[nb].y) : (h == 0 ? slot[nb].z : slot[nb].w);
-          b[nb] = expand_ternary(word);
-        }
-        const int chunk = (4 * g + 2 * half) ^ a_x;  // logical chunk 4g + 2 half + h, swizzled by row % 16
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const v4i a = *reinterpret_cast<const v4i*>(st + (a_row0 + mb * 32) * kTileCols + chunk * 16);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[nb], acc[mb][nb], 0, 0, 0);
-        }
-      }
+      for (int mb = 0; mb < MB; ++mb)
+        o.a[half][mb] = *reinterpret_cast<const v4i*>(st + (a_row0 + mb * 32) * kTileCols + chunk * 16);
     }
   };
+  auto math = [&](const Ops& o) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      v4i b[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        // words h (columns 64g + 16h + [0,16)) and 2 + h (columns 64g + 32 + 16h + [0,16))
+        const uint32_t word = half == 0 ? (h == 0 ? o.slot[nb].x : o.slot[nb].y) : (h == 0 ? o.slot[nb].z : o.slot[nb].w);
+        b[nb] = expand_ternary(word);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[half][mb], b[nb], acc[mb][nb], 0, 0, 0);
+    }
+  };
+  // software-pipelined over the tile's four 64-column groups: the operands
+  // of group g + 1 are read from LDS while group g is on the matrix cores
+  // (scheduling barriers keep that order)
+  auto compute = [&](const uint8_t* st) {
+    Ops o0, o1;
+    read_ops(st, 0, o0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_ops(st, 1, o1);
+    __builtin_amdgcn_sched_barrier(0);
+    math(o0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_ops(st, 2, o0);
+    __builtin_amdgcn_sched_barrier(0);
+    math(o1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_ops(st, 3, o1);
+    __builtin_amdgcn_sched_barrier(0);
+    math(o0);
+    __builtin_amdgcn_sched_barrier(0);
+    math(o1);
+  };
+
+  // per-token output scale gamma * a'[t] / 127, staged once
+  __shared__ float scale_s[BM];
+  if (tid < BM) {
+    const int64_t t = m0 + tid;
+    scale_s[tid] = t < m ? *gamma_p * amax[t] / 127.0f : 0.0f;
+  }
+  lds_barrier();
+
+  // operand descriptors: this workgroup's token rows and weight row blocks
+  const int64_t rows_here = m - m0 < BM ? m - m0 : BM;
+  const int64_t rbs_here = rb_count - rb0 < BN / kTileRows ? rb_count - rb0 : BN / kTileRows;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(xq + m0 * k), 0, static_cast<int>(rows_here * k), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed_b + rb0 * kt_count * kTileBytes), 0,
+      static_cast<int>(rbs_here * kt_count * kTileBytes), kBufferWord3);
+  const int k32 = static_cast<int>(k);
 
   // prologue: tiles 0 .. S-2 in flight
-  issue_tile<BM, BN>(st0, packed_b, xq, m0, m, k, rb0, rb_count, kt_count, 0, wave, lane);
-  if (S > 2) issue_tile<BM, BN>(st1, packed_b, xq, m0, m, k, rb0, rb_count, kt_count, 1, wave, lane);
-  if (S > 3) issue_tile<BM, BN>(st2, packed_b, xq, m0, m, k, rb0, rb_count, kt_count, 2, wave, lane);
+  issue_tile<BM, BN>(st0, a_rsrc, b_rsrc, k32, kt_count, 0, wave, lane);
+  if (S > 2) issue_tile<BM, BN>(st1, a_rsrc, b_rsrc, k32, kt_count, 1, wave, lane);
+  if (S > 3) issue_tile<BM, BN>(st2, a_rsrc, b_rsrc, k32, kt_count, 2, wave, lane);
 
   // one pipeline step: tile kt sits in stage `cur`; tile kt + S - 1 goes to `nxt`
   auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
     wait_vmcnt<(S - 2) * DS::kDma>();
     __builtin_amdgcn_s_barrier();
-    issue_tile<BM, BN>(nxt, packed_b, xq, m0, m, k, rb0, rb_count, kt_count, kt + S - 1, wave, lane);
+    issue_tile<BM, BN>(nxt, a_rsrc, b_rsrc, k32, kt_count, kt + S - 1, wave, lane);
     compute(cur);
   };
   for (int kt = 0; kt < kt_count; kt += S) {
@@ -364,14 +422,14 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   }
   wait_vmcnt<0>();
 
-  const float gamma = *gamma_p;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t t = m0 + wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int tl = wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int64_t t = m0 + tl;
       if (t >= m) continue;
-      const float scale = gamma * amax[t] / 127.0f;
+      const float scale = scale_s[tl];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int64_t j = n0 + wn * TN + nb * 32 + l32;
@@ -432,6 +490,9 @@ template <int BM, int BN, int WM, int WN, int S, int OCC>
 hipError_t launch_dma(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                       const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   static_assert(S * DmaStageBytes(BM, BN) <= 163840, "LDS per workgroup");  // OCC: register-budget hint
+  // 32-bit buffer offsets: BM rows of at most 2^18 codes, BN / 16 row blocks of at most 1024 tiles
+  static_assert(static_cast<int64_t>(BM) << 18 <= 0x7fffffff && static_cast<int64_t>(BN / kTileRows) * 1024 * kTileBytes <= 0x7fffffff,
+                "buffer offsets fit 31 bits");
   const int kt = static_cast<int>(k_tiles(k));
   const int64_t mt = (m + BM - 1) / BM;
   const int64_t ntl = (n + BN - 1) / BN;

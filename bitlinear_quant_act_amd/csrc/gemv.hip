@@ -55,7 +55,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 #ifndef BITLINEAR_GEMV_MAX_GROUPS
-#define BITLINEAR_GEMV_MAX_GROUPS 1024
+#define BITLINEAR_GEMV_MAX_GROUPS 512
 #endif
 #ifndef BITLINEAR_GEMV_WAVES
 #define BITLINEAR_GEMV_WAVES 8
