@@ -60,6 +60,12 @@ def _load():
     lib.oracle_contract_pairs.restype = _ct.c_int
     lib.oracle_dequant.argtypes = [_p, _i64, _i64, _ct.c_float, _p, _p]
     lib.oracle_dequant.restype = None
+    lib.oracle_quant_act_f32.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.oracle_quant_act_f32.restype = None
+    lib.oracle_rmsnorm_quant_act.argtypes = [_p, _p, _ct.c_float, _i64, _i64, _p, _p, _p]
+    lib.oracle_rmsnorm_quant_act.restype = None
+    lib.oracle_swiglu.argtypes = [_p, _p, _i64, _p]
+    lib.oracle_swiglu.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = _ct.c_int
     _lib = lib
@@ -136,6 +142,49 @@ def quant_act(x_bits: np.ndarray):
     amax = np.empty(m, dtype=np.float32)
     _load().oracle_quant_act(_ptr(x), m, k, _ptr(xq), _ptr(amax))
     return xq, amax
+
+
+def quant_act_f32(x: np.ndarray):
+    """(xq int8 [m][k], a' fp32 [m]) from fp32 activations [m][k]."""
+    x = _c(x, np.float32)
+    m, k = x.shape
+    xq = np.empty((m, k), dtype=np.int8)
+    amax = np.empty(m, dtype=np.float32)
+    _load().oracle_quant_act_f32(_ptr(x), m, k, _ptr(xq), _ptr(amax))
+    return xq, amax
+
+
+# torch's nn.RMSNorm default eps for binary32 inputs (the machine epsilon)
+RMS_EPS = float(np.finfo(np.float32).eps)
+
+
+def rmsnorm_quant_act(x_bits: np.ndarray, w=None, eps: float = RMS_EPS):
+    """RMSNorm (optional gain w [k]) then per-token quantization.
+    Returns (xq int8 [m][k], a' fp32 [m], r fp32 [m])."""
+    x = _c(x_bits, np.uint16)
+    m, k = x.shape
+    wp = None
+    if w is not None:
+        w = _c(w, np.float32)
+        if w.shape != (k,):
+            raise OracleError("gain must have k entries")
+        wp = _ptr(w)
+    xq = np.empty((m, k), dtype=np.int8)
+    amax = np.empty(m, dtype=np.float32)
+    rr = np.empty(m, dtype=np.float32)
+    _load().oracle_rmsnorm_quant_act(_ptr(x), wp, float(np.float32(eps)), m, k, _ptr(xq), _ptr(amax), _ptr(rr))
+    return xq, amax, rr
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = silu(g) * u elementwise (binary64, rounded once to binary32)."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    if g.shape != u.shape:
+        raise OracleError("gate and up shapes differ")
+    h = np.empty(g.shape, dtype=np.float32)
+    _load().oracle_swiglu(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
 
 
 def contract(xq: np.ndarray, q: np.ndarray) -> np.ndarray:

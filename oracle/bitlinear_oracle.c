@@ -29,6 +29,24 @@
  *   - de-quantization y = acc * gamma * a' / 127 evaluated in binary64 and
  *     rounded once to binary32.
  *
+ * Beyond the four steps (the steps on either side of the contraction):
+ *   [P4] the "bit_linear.py" listing normalises the BitLinear input with
+ *        nn.RMSNorm(in_features) before activation_quant;
+ *   [P5] "BitNet 1-bit LLM Inference Framework", section "A Deep Look at the
+ *        BitNet Architecture", the ffn of the transformer block:
+ *        down_proj(silu(gate_proj(x)) * up_proj(x)).
+ * Readings taken there:
+ *   - RMSNorm: r = 1 / sqrt(mean_k x^2 + eps) per token (binary64), times an
+ *     optional per-channel gain w.  Absmax quantization is invariant under a
+ *     positive per-token factor, so the codes are those of v = x * w (one
+ *     binary32 multiply) and r is carried by the scale instead:
+ *     a' = max(max_k |v| * r, 1e-8) (binary64 product, rounded once).  An
+ *     all-zero v gives codes 0 and a' = 1e-8;
+ *   - SwiGLU: h = silu(g) * u = g * u / (1 + exp(-g)) in binary64, rounded
+ *     once to binary32, from the two de-quantized BitLinear outputs;
+ *   - h is requantized for the next BitLinear from binary32 with the same
+ *     per-token rule as the bf16 activations.
+ *
  * Build: gcc -O2 -fopenmp -fno-fast-math -ffp-contract=off (see build.py).
  * OpenMP is used over independent output rows only.
  */
@@ -208,6 +226,73 @@ void oracle_quant_act(const uint16_t *x, int64_t m, int64_t k, int8_t *xq, float
     }
 }
 
+/* Same rule from binary32 activations (x: fp32 [m][k]). */
+void oracle_quant_act_f32(const float *x, int64_t m, int64_t k, int8_t *xq, float *amax)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r) {
+        float a = 0.0f;
+        for (int64_t c = 0; c < k; ++c) {
+            float v = fabsf(x[r * k + c]);
+            if (v > a)
+                a = v;
+        }
+        if (a < 1e-8f)
+            a = 1e-8f;
+        const float s = 127.0f / a;
+        for (int64_t c = 0; c < k; ++c) {
+            float t = x[r * k + c] * s;
+            xq[r * k + c] = (int8_t)clip(round_half_even(t), -127.0, 127.0);
+        }
+        amax[r] = a;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* RMSNorm ahead of the activation quantization                        */
+/*   [P4, "bit_linear.py": x_norm = rms_norm(x); activation_quant(x_norm)]*/
+/* ------------------------------------------------------------------ */
+
+/* x: bf16 bits [m][k]; w: per-channel gain [k] (NULL: all ones); eps added to
+ * the mean square.  Codes quantize v = x * w; the factor r = 1/sqrt(mean x^2 +
+ * eps), which cancels in the codes, is folded into a'.  rms_out (may be NULL)
+ * receives r rounded to binary32. */
+void oracle_rmsnorm_quant_act(const uint16_t *x, const float *w, float eps, int64_t m, int64_t k,
+                              int8_t *xq, float *amax, float *rms_out)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < m; ++r) {
+        double ss = 0.0;
+        float a = 0.0f;
+        for (int64_t c = 0; c < k; ++c) {
+            const float xv = bf16_to_f32(x[r * k + c]);
+            ss += (double)xv * (double)xv;
+            const float v = fabsf(w ? xv * w[c] : xv);
+            if (v > a)
+                a = v;
+        }
+        const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);
+        if (rms_out)
+            rms_out[r] = (float)rr;
+        if (a == 0.0f) {
+            for (int64_t c = 0; c < k; ++c)
+                xq[r * k + c] = 0;
+            amax[r] = 1e-8f;
+            continue;
+        }
+        const float s = 127.0f / a;
+        for (int64_t c = 0; c < k; ++c) {
+            const float xv = bf16_to_f32(x[r * k + c]);
+            const float v = w ? xv * w[c] : xv;
+            xq[r * k + c] = (int8_t)clip(round_half_even(v * s), -127.0, 127.0);
+        }
+        float ap = (float)((double)a * rr);
+        amax[r] = ap < 1e-8f ? 1e-8f : ap;
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* O6: ternary x int8 contraction by add / skip / subtract              */
 /*     [P4, Mathematical Mechanism, item 3; P5, How the LUT Kernel Works]*/
@@ -293,6 +378,22 @@ void oracle_dequant(const int32_t *acc, int64_t m, int64_t n, float gamma, const
         for (int64_t j = 0; j < n; ++j)
             y[i * n + j] =
                 (float)((double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* SwiGLU between gate+up and down  [P5, Deep Look: the block's ffn]    */
+/* ------------------------------------------------------------------ */
+
+/* h[i] = silu(g[i]) * u[i] with silu(g) = g / (1 + exp(-g)), in binary64,
+ * rounded once to binary32.  g, u, h: fp32, count values each. */
+void oracle_swiglu(const float *g, const float *u, int64_t count, float *h)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < count; ++i) {
+        const double gd = (double)g[i];
+        h[i] = (float)(gd * (double)u[i] / (1.0 + exp(-gd)));
     }
 }
 

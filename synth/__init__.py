@@ -126,6 +126,13 @@ def activations_bf16(seed, m: int, k: int, outlier_frac: float = 0.0,
     return fp32_to_bf16_bits(x)
 
 
+def norm_gain(seed, k: int) -> np.ndarray:
+    """fp32 [k] per-channel RMSNorm gains: 1 + 0.1 * N(0,1), a synthetic
+    stand-in for trained gains (initialised to one)."""
+    rng = _rng(seed)
+    return (np.float32(1.0) + np.float32(0.1) * rng.standard_normal(k, dtype=np.float32)).astype(np.float32)
+
+
 def iter_layer_matrices(wl: Workload) -> Iterator[Tuple[int, int, Matrix]]:
     """(layer, matrix index, Matrix) in layer order."""
     for layer in range(wl.layers):

@@ -36,6 +36,20 @@ MUTATIONS = {
                               "(double)acc[i * n + j] * (double)gamma * (double)amax[i]"),
     "dequant uses token 0 scale": ("(double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0",
                                    "(double)acc[i * n + j] * (double)gamma * (double)amax[0] / 127.0"),
+    "rmsnorm eps dropped": ("const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);",
+                            "const double rr = 1.0 / sqrt(ss / (double)k);"),
+    "rmsnorm sum, not mean": ("const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);",
+                              "const double rr = 1.0 / sqrt(ss + (double)eps);"),
+    "rmsnorm sqrt dropped": ("const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);",
+                             "const double rr = 1.0 / (ss / (double)k + (double)eps);"),
+    "rmsnorm gain ignored in max": ("const float v = fabsf(w ? xv * w[c] : xv);", "const float v = fabsf(xv);"),
+    "rmsnorm gain ignored in codes": ("const float v = w ? xv * w[c] : xv;", "const float v = xv;"),
+    "rmsnorm r not folded into a'": ("float ap = (float)((double)a * rr);", "float ap = a;"),
+    "f32 quant max of x, not |x|": ("float v = fabsf(x[r * k + c]);", "float v = (x[r * k + c]);"),
+    "silu with exp(+g)": ("h[i] = (float)(gd * (double)u[i] / (1.0 + exp(-gd)));",
+                          "h[i] = (float)(gd * (double)u[i] / (1.0 + exp(gd)));"),
+    "swiglu drops up": ("h[i] = (float)(gd * (double)u[i] / (1.0 + exp(-gd)));",
+                        "h[i] = (float)(gd / (1.0 + exp(-gd)));"),
     "dequant drops gamma": ("(double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0",
                             "(double)acc[i * n + j] * (double)amax[i] / 127.0"),
 }

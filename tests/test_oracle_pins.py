@@ -457,3 +457,149 @@ def test_golden_end_to_end(oracle_mod):
         assert r["acc"].tolist() == ex["acc"], ex["name"]
         y = np.array([[f32_nearest(Fraction(v)) for v in row] for row in ex["y"]], np.float32)
         assert ulp_diff(r["y"], y).max() <= 1, ex["name"]
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm ahead of the quantization ("BitNet b1.58 in Production", listing
+# "bit_linear.py": x_norm = nn.RMSNorm(in_features)(x), then activation_quant)
+# ---------------------------------------------------------------------------
+
+RMS_EPS = float(np.finfo(np.float32).eps)
+
+
+def _r_exact(x_bits_row, eps):
+    """1 / sqrt(mean x^2 + eps) from the exact rational mean square."""
+    xs = synth.bf16_bits_to_fp32(x_bits_row).astype(np.float64)
+    ms = sum(Fraction(float(v)) ** 2 for v in xs) / len(xs) + Fraction(float(np.float32(eps)))
+    return 1.0 / math.sqrt(float(ms))
+
+
+def test_rmsnorm_unit_gain_keeps_codes(oracle_mod):
+    x = synth.activations_bf16(11, 5, 384, 0.01)
+    xq0, a0 = oracle_mod.quant_act(x)
+    for w in (None, np.ones(384, dtype=np.float32)):
+        xq, a, r = oracle_mod.rmsnorm_quant_act(x, w)
+        assert np.array_equal(xq, xq0)           # a positive per-token factor cancels
+        for t in range(5):
+            ref = np.float32(float(a0[t]) * _r_exact(x[t], RMS_EPS))
+            assert abs(int(ulp_diff(a[t], ref))) <= 1
+
+
+def test_rmsnorm_vs_torch_rms_norm(oracle_mod):
+    torch = pytest.importorskip("torch")
+    x = synth.activations_bf16(12, 6, 512, 0.01)
+    w = synth.norm_gain(13, 512)
+    xq, a, r = oracle_mod.rmsnorm_quant_act(x, w)
+    xf = torch.from_numpy(synth.bf16_bits_to_fp32(x).astype(np.float64))
+    xn = torch.nn.functional.rms_norm(xf, (512,), torch.from_numpy(w.astype(np.float64)), RMS_EPS).numpy()
+    amax_ref = np.abs(xn).max(axis=1)
+    assert np.allclose(a, amax_ref, rtol=2e-7, atol=0)
+    # literal quantization of the normalized activations in binary64: equal
+    # codes except where the value sits within rounding distance of a tie
+    lit = xn * (127.0 / amax_ref[:, None])
+    codes = np.clip(np.round(lit), -127, 127)
+    diff = codes - xq.astype(np.float64)
+    near_tie = np.abs(np.abs(lit - np.floor(lit)) - 0.5) < 1e-4
+    assert np.all(np.abs(diff) <= 1)
+    assert np.all(near_tie[diff != 0])
+
+
+def test_rmsnorm_invariances(oracle_mod):
+    x = synth.activations_bf16(14, 4, 256)
+    w = synth.norm_gain(15, 256)
+    xq, a, _ = oracle_mod.rmsnorm_quant_act(x, w, eps=0.0)
+    # power-of-two scaling of x (exact in bf16): same codes and, with eps = 0, same a'
+    xs = bits(synth.bf16_bits_to_fp32(x) * np.float32(8.0))
+    xq2, a2, _ = oracle_mod.rmsnorm_quant_act(xs, w, eps=0.0)
+    assert np.array_equal(xq, xq2) and np.array_equal(a, a2)
+    # negated gain: negated codes, same a'
+    xq3, a3, _ = oracle_mod.rmsnorm_quant_act(x, -w, eps=0.0)
+    assert np.array_equal(xq3, -xq) and np.array_equal(a3, a)
+    assert np.abs(xq).max() == 127
+
+
+def test_rmsnorm_closed_forms(oracle_mod):
+    k = 64
+    # constant token c: every code is sign(c) * 127, a' = |c| / sqrt(c^2 + eps)
+    for c in (0.75, -3.0, 40.0):
+        x = bits(np.full((1, k), c, dtype=np.float32))
+        xq, a, r = oracle_mod.rmsnorm_quant_act(x)
+        assert np.all(xq == np.sign(c) * 127)
+        ref = np.float32(abs(c) / math.sqrt(c * c + float(np.float32(RMS_EPS))))
+        assert abs(int(ulp_diff(a[0], ref))) <= 1
+    # eps dominates a tiny token: r ~ 1 / sqrt(eps)
+    tiny = 2.0 ** -20
+    x = bits(np.full((1, k), tiny, dtype=np.float32))
+    _, a, r = oracle_mod.rmsnorm_quant_act(x)
+    ref = tiny / math.sqrt(tiny * tiny + float(np.float32(RMS_EPS)))
+    assert abs(float(a[0]) - ref) <= 1e-6 * ref
+    # all-zero token, or a gain of zero: codes 0, a' at its floor, no NaN
+    z = np.zeros((1, k), dtype=np.uint16)
+    xq, a, r = oracle_mod.rmsnorm_quant_act(z)
+    assert np.all(xq == 0) and a[0] == np.float32(1e-8) and np.isfinite(r[0])
+    x = synth.activations_bf16(16, 1, k)
+    xq, a, _ = oracle_mod.rmsnorm_quant_act(x, np.zeros(k, dtype=np.float32))
+    assert np.all(xq == 0) and a[0] == np.float32(1e-8)
+
+
+# ---------------------------------------------------------------------------
+# quantization from binary32 (the SwiGLU output feeding the next BitLinear)
+# ---------------------------------------------------------------------------
+
+def test_quant_f32_matches_bf16_rule_on_bf16_values(oracle_mod):
+    x = synth.activations_bf16(17, 7, 300, 0.01)
+    xq0, a0 = oracle_mod.quant_act(x)
+    xq, a = oracle_mod.quant_act_f32(synth.bf16_bits_to_fp32(x))
+    assert np.array_equal(xq, xq0) and np.array_equal(a, a0)
+
+
+def test_quant_f32_vs_torch_listing_expression(oracle_mod):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(18)
+    x = (rng.standard_normal((9, 777)) * 3).astype(np.float32)
+    x[3] = 0.0
+    xq, a = oracle_mod.quant_act_f32(x)
+    xt = torch.from_numpy(x)
+    scale = xt.abs().max(dim=-1, keepdim=True)[0].clamp(min=1e-8)
+    ref = torch.clamp(torch.round(xt * (127.0 / scale)), -127, 127).to(torch.int8).numpy()
+    assert np.array_equal(xq, ref)
+    assert np.array_equal(a, scale[:, 0].numpy())
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU ("BitNet 1-bit LLM Inference Framework", section "A Deep Look at the
+# BitNet Architecture": down_proj(silu(gate_proj(x)) * up_proj(x)))
+# ---------------------------------------------------------------------------
+
+def test_swiglu_known_values_and_limits(oracle_mod):
+    sig1 = 0.7310585786300049  # logistic(1)
+    g = np.array([0.0, 1.0, -1.0, 40.0, -40.0, 2.0, 0.0], dtype=np.float32)
+    u = np.array([5.0, 1.0, 1.0, 3.0, 3.0, 0.0, -2.0], dtype=np.float32)
+    h = oracle_mod.swiglu(g, u)
+    assert h[0] == 0.0 and h[5] == 0.0 and h[6] == 0.0
+    assert h[1] == np.float32(sig1)
+    assert h[2] == np.float32(sig1 - 1.0)
+    assert h[3] == np.float32(120.0)            # sigmoid(40) rounds to 1
+    assert abs(float(h[4])) < 1e-15
+
+
+def test_swiglu_identities(oracle_mod):
+    rng = np.random.default_rng(19)
+    g = (rng.standard_normal(5000) * 3).astype(np.float32)
+    u = rng.standard_normal(5000).astype(np.float32)
+    one = np.ones_like(g)
+    # silu(g) - silu(-g) = g
+    d = oracle_mod.swiglu(g, one).astype(np.float64) - oracle_mod.swiglu(-g, one).astype(np.float64)
+    assert np.allclose(d, g, rtol=2e-7, atol=1e-7)
+    # linear in u: power-of-two scaling is exact
+    assert np.array_equal(oracle_mod.swiglu(g, u * np.float32(4.0)), oracle_mod.swiglu(g, u) * np.float32(4.0))
+
+
+def test_swiglu_vs_torch_silu(oracle_mod):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(20)
+    g = (rng.standard_normal((13, 257)) * 4).astype(np.float32)
+    u = rng.standard_normal((13, 257)).astype(np.float32)
+    h = oracle_mod.swiglu(g, u)
+    ref = (torch.nn.functional.silu(torch.from_numpy(g.astype(np.float64))) * torch.from_numpy(u.astype(np.float64))).numpy()
+    assert np.all(np.abs(ulp_diff(h, ref.astype(np.float32))) <= 1)
