@@ -17,7 +17,10 @@ MUTATIONS = {
     "weight epsilon dropped": ("const float denom = gamma + 1e-5f;", "const float denom = gamma;"),
     "round half away from zero": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;",
                                   "return td > 0 ? fl + 1.0 : fl;"),
-    "Q_b = 128": ("const float s = 127.0f / a;", "const float s = 128.0f / a;"),
+    "Q_b = 128": ("const float s = 127.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = bf16_to_f32",
+                  "const float s = 128.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = bf16_to_f32"),
+    "f32 quant Q_b = 128": ("const float s = 127.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = x[r * k + c] * s;",
+                            "const float s = 128.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = x[r * k + c] * s;"),
     "ternary clip missing": ("q[r * k + c] = (int8_t)clip(round_half_even(t), -1.0, 1.0);",
                              "q[r * k + c] = (int8_t)round_half_even(t);"),
     "gamma of W, not |W|": ("s += fabs((double)row[c]);", "s += ((double)row[c]);"),
@@ -25,7 +28,10 @@ MUTATIONS = {
                                 "double mean = abs_sum / ((double)n);"),
     "act max of x, not |x|": ("float v = fabsf(bf16_to_f32(x[r * k + c]));",
                               "float v = (bf16_to_f32(x[r * k + c]));"),
-    "act floor dropped": ("if (a < 1e-8f)\n            a = 1e-8f;", ""),
+    "act floor dropped": ("if (a < 1e-8f)\n            a = 1e-8f;\n        const float s = 127.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = bf16_to_f32",
+                          "const float s = 127.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = bf16_to_f32"),
+    "f32 quant floor dropped": ("if (a < 1e-8f)\n            a = 1e-8f;\n        const float s = 127.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = x[r * k + c] * s;",
+                                "const float s = 127.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = x[r * k + c] * s;"),
     "pack field order reversed": ("byte |= code << (2 * i);", "byte |= code << (6 - 2 * i);"),
     "codes +1/-1 swapped": ("code = (v == 1) ? 1u : (v == -1) ? 2u : 0u;",
                             "code = (v == 1) ? 2u : (v == -1) ? 1u : 0u;"),
