@@ -30,7 +30,10 @@ BITLINEAR_E_ALIGN = -3
 BITLINEAR_E_UNSUPPORTED = -4
 BITLINEAR_E_SIZE = -5
 BITLINEAR_E_HIP = -6
+BITLINEAR_E_VALUE = -7
 BITLINEAR_FORWARD_MAX_M = 16
+# nn.RMSNorm's default eps for binary32 inputs (the machine epsilon)
+RMS_EPS = 1.1920928955078125e-07
 
 _lib = None
 _i64 = _ct.c_int64
@@ -82,6 +85,12 @@ def load_library(path: str = LIB_PATH):
     lib.bitlinear_quant_forward.restype = _ct.c_int
     lib.bitlinear_quant_forward_supported.argtypes = [_i64, _i64]
     lib.bitlinear_quant_forward_supported.restype = _ct.c_int
+    lib.bitlinear_rmsnorm_quant_act.argtypes = [_p, _p, _ct.c_float, _i64, _i64, _p, _p, _p]
+    lib.bitlinear_rmsnorm_quant_act.restype = _ct.c_int
+    lib.bitlinear_rmsnorm_quant_forward.argtypes = [_p, _p, _i64, _i64, _p, _p, _ct.c_float, _i64, _p, _p, _p, _p, _p]
+    lib.bitlinear_rmsnorm_quant_forward.restype = _ct.c_int
+    lib.bitlinear_quant_act_f32.argtypes = [_p, _i64, _i64, _p, _p, _p]
+    lib.bitlinear_quant_act_f32.restype = _ct.c_int
     for name in ("bitlinear_forward", "bitlinear_forward_batched"):
         fn = getattr(lib, name)
         fn.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
@@ -197,6 +206,43 @@ def bitlinear_quant_act(x, xq=None, x_absmax=None, stream=None):
     return xq, x_absmax
 
 
+def bitlinear_rmsnorm_quant_act(x, gain=None, eps: float = RMS_EPS, xq=None, x_absmax=None, stream=None):
+    """RMSNorm (optional gain fp32 [k]) then per-token quantisation of
+    x bf16 [m][k] -> (xq int8 [m][k], a' fp32 [m]); a' carries 1/rms."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be [m][k]")
+    m, k = x.shape
+    if xq is None:
+        xq = _torch.empty((m, k), dtype=_torch.int8, device=x.device)
+    if x_absmax is None:
+        x_absmax = _torch.empty(m, dtype=_torch.float32, device=x.device)
+    rc = lib.bitlinear_rmsnorm_quant_act(
+        _dev(x, "x", (_torch.bfloat16, _torch.int16, _torch.uint16)),
+        None if gain is None else _dev(gain, "gain", (_torch.float32,), k), float(eps), m, k,
+        _dev(xq, "xq", (_torch.int8,), m * k), _dev(x_absmax, "x_absmax", (_torch.float32,), m),
+        _stream_handle(stream))
+    _check(rc, "bitlinear_rmsnorm_quant_act")
+    return xq, x_absmax
+
+
+def bitlinear_quant_act_f32(x, xq=None, x_absmax=None, stream=None):
+    """x: fp32 [m][k] -> (xq int8 [m][k], a' fp32 [m])."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be [m][k]")
+    m, k = x.shape
+    if xq is None:
+        xq = _torch.empty((m, k), dtype=_torch.int8, device=x.device)
+    if x_absmax is None:
+        x_absmax = _torch.empty(m, dtype=_torch.float32, device=x.device)
+    rc = lib.bitlinear_quant_act_f32(_dev(x, "x", (_torch.float32,)), m, k,
+                                     _dev(xq, "xq", (_torch.int8,), m * k),
+                                     _dev(x_absmax, "x_absmax", (_torch.float32,), m), _stream_handle(stream))
+    _check(rc, "bitlinear_quant_act_f32")
+    return xq, x_absmax
+
+
 def _forward(fname, packed, gamma, n, k, xq, x_absmax, y, acc, stream):
     lib = load_library()
     m = xq.shape[0]
@@ -252,6 +298,31 @@ def bitlinear_quant_forward(packed, gamma, n: int, k: int, x, y=None, acc=None, 
         None if x_absmax is None else _dev(x_absmax, "x_absmax", (_torch.float32,), m),
         _stream_handle(stream))
     _check(rc, "bitlinear_quant_forward")
+    return y
+
+
+def bitlinear_rmsnorm_quant_forward(packed, gamma, n: int, k: int, x, gain=None, eps: float = RMS_EPS, y=None,
+                                    acc=None, xq=None, x_absmax=None, stream=None):
+    """Fused RMSNorm + activation quantisation + decode forward (the support
+    rule of bitlinear_quant_forward).  Returns y fp32 [m][n]."""
+    lib = load_library()
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m][k]")
+    m = x.shape[0]
+    if packed.numel() * packed.element_size() < bitlinear_packed_bytes(n, k):
+        raise BitlinearError(BITLINEAR_E_SIZE, "bitlinear_rmsnorm_quant_forward")
+    if y is None:
+        y = _torch.empty((m, n), dtype=_torch.float32, device=x.device)
+    rc = lib.bitlinear_rmsnorm_quant_forward(
+        _dev(packed, "packed", (_torch.uint8,)), _dev(gamma, "gamma", (_torch.float32,), 1), n, k,
+        _dev(x, "x", (_torch.bfloat16, _torch.int16, _torch.uint16)),
+        None if gain is None else _dev(gain, "gain", (_torch.float32,), k), float(eps), m,
+        _dev(y, "y", (_torch.float32,), m * n),
+        None if acc is None else _dev(acc, "acc", (_torch.int32,), m * n),
+        None if xq is None else _dev(xq, "xq", (_torch.int8,), m * k),
+        None if x_absmax is None else _dev(x_absmax, "x_absmax", (_torch.float32,), m),
+        _stream_handle(stream))
+    _check(rc, "bitlinear_rmsnorm_quant_forward")
     return y
 
 

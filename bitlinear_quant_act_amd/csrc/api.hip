@@ -5,6 +5,8 @@
 // device; then it enqueues its kernels on the caller's stream and returns
 // without synchronising.  No device memory is allocated here.
 #include "bitlinear.h"
+#include <cmath>
+
 #include "bitlinear_internal.hpp"
 
 namespace {
@@ -48,6 +50,7 @@ const char* bitlinear_status_string(int status) {
     case BITLINEAR_E_UNSUPPORTED: return "valid arguments not handled by this entry point";
     case BITLINEAR_E_SIZE: return "a caller-provided buffer is too small";
     case BITLINEAR_E_HIP: return "the HIP runtime reported a launch error";
+    case BITLINEAR_E_VALUE: return "a scalar argument is outside its allowed range";
     default: return "unknown status";
   }
 }
@@ -122,6 +125,40 @@ int bitlinear_forward_batched(const void* packed, const float* gamma, int64_t n,
   if (m > kMaxBatchedM) return BITLINEAR_E_UNSUPPORTED;
   return status_of(bitlinear::launch_gemm(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_rmsnorm_quant_act(const uint16_t* x, const float* gain_or_null, float eps, int64_t m, int64_t k,
+                                int8_t* xq, float* x_absmax, void* stream) {
+  if (!x || !xq || !x_absmax) return BITLINEAR_E_NULL;
+  if (m < 1 || m > kMaxRows || k < 1 || k > kMaxK) return BITLINEAR_E_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return BITLINEAR_E_VALUE;
+  if (!aligned(x, 2) || !aligned(x_absmax, 4) || (gain_or_null && !aligned(gain_or_null, 4))) return BITLINEAR_E_ALIGN;
+  return status_of(bitlinear::launch_rmsnorm_quant_act(x, gain_or_null, eps, m, k, xq, x_absmax,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_rmsnorm_quant_forward(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
+                                    const float* gain_or_null, float eps, int64_t m, float* y, int32_t* acc_or_null,
+                                    int8_t* xq_or_null, float* x_absmax_or_null, void* stream) {
+  if (!packed || !gamma || !x || !y) return BITLINEAR_E_NULL;
+  if (int rc = check_nk(n, k)) return rc;
+  if (m < 1 || m > kMaxRows) return BITLINEAR_E_SHAPE;
+  if ((xq_or_null == nullptr) != (x_absmax_or_null == nullptr)) return BITLINEAR_E_NULL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return BITLINEAR_E_VALUE;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(x, 2) || !aligned(y, 4) ||
+      (gain_or_null && !aligned(gain_or_null, 4)) || (acc_or_null && !aligned(acc_or_null, 4)) ||
+      (x_absmax_or_null && !aligned(x_absmax_or_null, 4)))
+    return BITLINEAR_E_ALIGN;
+  if (m > BITLINEAR_FORWARD_MAX_M || !bitlinear::gemv_fits_lds(m, k)) return BITLINEAR_E_UNSUPPORTED;
+  return status_of(bitlinear::launch_norm_quant_gemv(packed, gamma, n, k, x, gain_or_null, eps, m, y, acc_or_null,
+                                                     xq_or_null, x_absmax_or_null, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quant_act_f32(const float* x, int64_t m, int64_t k, int8_t* xq, float* x_absmax, void* stream) {
+  if (!x || !xq || !x_absmax) return BITLINEAR_E_NULL;
+  if (m < 1 || m > kMaxRows || k < 1 || k > kMaxK) return BITLINEAR_E_SHAPE;
+  if (!aligned(x, 4) || !aligned(x_absmax, 4)) return BITLINEAR_E_ALIGN;
+  return status_of(bitlinear::launch_quant_act_f32(x, m, k, xq, x_absmax, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

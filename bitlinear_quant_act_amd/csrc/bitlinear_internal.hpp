@@ -56,6 +56,12 @@ __device__ __forceinline__ expand_v4i expand_ternary(uint32_t word) {
 constexpr int kPackPartials = 1024;  // fp64 partial sums of |W| (max)
 
 // ---- launchers (return the hipGetLastError of their launches) --------------
+hipError_t launch_rmsnorm_quant_act(const uint16_t* x, const float* gain, float eps, int64_t m, int64_t k, int8_t* xq,
+                                    float* amax, hipStream_t s);
+hipError_t launch_quant_act_f32(const float* x, int64_t m, int64_t k, int8_t* xq, float* amax, hipStream_t s);
+hipError_t launch_norm_quant_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
+                                  const float* gain, float eps, int64_t m, float* y, int32_t* acc, int8_t* xq_out,
+                                  float* amax_out, hipStream_t s);
 hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* amax,
                             hipStream_t s);
 

@@ -23,7 +23,11 @@
 //   * kFromBf16:  computed from the bf16 activations -- the activation
 //     quantisation fused into the GEMV: per-token max|x| as integer bit
 //     patterns, a' = max(., 1e-8), s = 127 / a' (IEEE divide), code =
-//     clamp(rint(x * s)), bit-identical to bitlinear_quant_act.
+//     clamp(rint(x * s)), bit-identical to bitlinear_quant_act;
+//   * kFromBf16Norm: RMSNorm fused as well ("bit_linear.py" listing: the
+//     BitLinear input passes nn.RMSNorm first): codes of v = x * gain, and
+//     a' = max|v| / sqrt(mean x^2 + eps) (the per-token factor cancels in
+//     the codes), bit-identical to bitlinear_rmsnorm_quant_act.
 // The activations are requested before the first weight tiles: vector-memory
 // results are waited for in issue order, so the prologue then runs while the
 // weights are still in flight.
@@ -66,7 +70,7 @@ constexpr int kWaves = BITLINEAR_GEMV_WAVES;                        // waves per
 constexpr int kMaxLdsBytes = 65536 - kWaves * 4 * 64 * 4 - 512;
 constexpr int kCachedChunks = 4;  // activation chunks per thread held in registers by the prologue
 
-enum Source { kFromCodes = 0, kFromBf16 = 1 };
+enum Source { kFromCodes = 0, kFromBf16 = 1, kFromBf16Norm = 2 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -274,6 +278,141 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
   if (write_out && threadIdx.x < m) amax_out[threadIdx.x] = amax_s[threadIdx.x];
 }
 
+// RMSNorm + quantisation, any token count: per-token max|x * gain| (LDS
+// atomics on the fp32 bit patterns) and fp64 sum of x^2 (LDS fp64 atomics);
+// quant_s receives the quantisation scale 127 / max|v|, amax_s the
+// de-quantisation a' = max|v| * r.
+__device__ __forceinline__ void norm_values(const uint4& xc, const float* __restrict__ gain8, float (&v)[8],
+                                            float (&xv)[8]) {
+  const uint32_t w[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    xv[2 * q] = __uint_as_float(w[q] << 16);
+    xv[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+  }
+  if (gain8) {
+    const float4 g0 = *reinterpret_cast<const float4*>(gain8);
+    const float4 g1 = *reinterpret_cast<const float4*>(gain8 + 4);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = xv[i] * gv[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = xv[i];
+  }
+}
+
+__device__ __forceinline__ uint32_t norm_code(float v, float s) {
+  float r = rintf(v * s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
+}
+
+__device__ void stage_bf16_norm(int8_t* xs, int pitch, float* amax_s, float* quant_s, unsigned* max_s, double* ss_s,
+                                const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x,
+                                const float* __restrict__ gain, float eps, int m, int64_t k, int kpad, bool vec,
+                                int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
+  const int nthreads = blockDim.x;
+  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
+  if (threadIdx.x < m) {
+    max_s[threadIdx.x] = 0u;
+    ss_s[threadIdx.x] = 0.0;
+  }
+  lds_barrier();
+  if (vec) {  // k % 8 == 0, x and gain 16-byte aligned: chunks of 8 values
+    const int cpr = static_cast<int>(k / 8);
+    const int total = m * cpr;
+    int cur_t = -1;
+    unsigned cur = 0;
+    double cur_ss = 0.0;
+    int j = 0;
+    for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+      const int t = c / cpr, cc = c - t * cpr;
+      if (t != cur_t) {
+        if (cur_t >= 0) {
+          atomicMax(&max_s[cur_t], cur);
+          atomicAdd(&ss_s[cur_t], cur_ss);
+        }
+        cur_t = t;
+        cur = 0;
+        cur_ss = 0.0;
+      }
+      float v[8], xv[8];
+      norm_values(j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
+                  gain ? gain + cc * 8 : nullptr, v, xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        cur_ss += static_cast<double>(xv[i]) * static_cast<double>(xv[i]);
+        cur = max(cur, __float_as_uint(fabsf(v[i])));
+      }
+    }
+    if (cur_t >= 0) {
+      atomicMax(&max_s[cur_t], cur);
+      atomicAdd(&ss_s[cur_t], cur_ss);
+    }
+  } else {
+    for (int t = 0; t < m; ++t) {
+      unsigned cur = 0;
+      double cur_ss = 0.0;
+      for (int64_t i = threadIdx.x; i < k; i += nthreads) {
+        const float xv = __uint_as_float(static_cast<uint32_t>(x[t * k + i]) << 16);
+        const float v = gain ? xv * gain[i] : xv;
+        cur_ss += static_cast<double>(xv) * static_cast<double>(xv);
+        cur = max(cur, __float_as_uint(fabsf(v)));
+      }
+      atomicMax(&max_s[t], cur);
+      atomicAdd(&ss_s[t], cur_ss);
+    }
+  }
+  lds_barrier();
+  if (threadIdx.x < m) {
+    const float av = __uint_as_float(max_s[threadIdx.x]);
+    const double r = 1.0 / sqrt(ss_s[threadIdx.x] / static_cast<double>(k) + static_cast<double>(eps));
+    const float ap = static_cast<float>(static_cast<double>(av) * r);
+    amax_s[threadIdx.x] = av > 0.0f ? fmaxf(ap, 1e-8f) : 1e-8f;
+    quant_s[threadIdx.x] = av > 0.0f ? 127.0f / av : 0.0f;  // all-zero v: every code is 0
+  }
+  lds_barrier();
+  if (vec) {
+    const int cpr = static_cast<int>(k / 8);
+    const int total = m * cpr;
+    int j = 0;
+    for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+      const int t = c / cpr, cc = c - t * cpr;
+      float v[8], xv[8];
+      norm_values(j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
+                  gain ? gain + cc * 8 : nullptr, v, xv);
+      const float qs = quant_s[t];
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= norm_code(v[i], qs) << (8 * i);
+        hi |= norm_code(v[4 + i], qs) << (8 * i);
+      }
+      const uint2 q = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(xs + t * pitch + cc * 8) = q;
+      if (write_out) *reinterpret_cast<uint2*>(xq_out + t * k + cc * 8) = q;
+    }
+    const int padc = (kpad - static_cast<int>(k)) / 8;
+    for (int c = threadIdx.x; c < m * padc; c += nthreads) {
+      const int t = c / padc, cc = c - t * padc;
+      *reinterpret_cast<uint2*>(xs + t * pitch + static_cast<int>(k) + cc * 8) = make_uint2(0, 0);
+    }
+  } else {
+    for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
+      const int t = c / kpad, col = c - t * kpad;
+      int8_t q = 0;
+      if (col < k) {
+        const float xv = __uint_as_float(static_cast<uint32_t>(x[t * k + col]) << 16);
+        q = static_cast<int8_t>(norm_code(gain ? xv * gain[col] : xv, quant_s[t]));
+        if (write_out) xq_out[t * k + col] = q;
+      }
+      xs[t * pitch + col] = q;
+    }
+  }
+  if (write_out && threadIdx.x < m) amax_out[threadIdx.x] = amax_s[threadIdx.x];
+}
+
 // ---------------------------------------------------------------------------
 // main kernel: activation codes in LDS, persistent over row blocks
 // ---------------------------------------------------------------------------
@@ -300,10 +439,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
                                                               const float* __restrict__ amax_in, int m,
                                                               float* __restrict__ y, int32_t* __restrict__ acc_out,
                                                               int8_t* __restrict__ xq_out,
-                                                              float* __restrict__ amax_out) {
+                                                              float* __restrict__ amax_out,
+                                                              const float* __restrict__ gain, float eps) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ int red[WAVES * 4 * 64];
   __shared__ float amax_s[16];
+  __shared__ float quant_s[SRC == kFromBf16Norm ? 16 : 1];
+  __shared__ double ss_s[SRC == kFromBf16Norm ? 16 : 1];
   __shared__ unsigned max_s[16];
   __shared__ unsigned wmax_s[WAVES];
 
@@ -331,6 +473,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   if (SRC == kFromCodes) {
     stage_codes(xs, pitch, cache, static_cast<const int8_t*>(xsrc), m, k, kpad, VEC);
     if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x];
+  } else if (SRC == kFromBf16Norm) {
+    stage_bf16_norm(xs, pitch, amax_s, quant_s, max_s, ss_s, cache, static_cast<const uint16_t*>(xsrc), gain, eps, m, k,
+                    kpad, VEC, xq_out, amax_out);
   } else if (VEC && m == 1) {
     stage_bf16_single<WAVES>(xs, amax_s, wmax_s, cache, static_cast<const uint16_t*>(xsrc), k, kpad, xq_out,
                              amax_out);
@@ -474,7 +619,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
 template <int SRC, int WAVES, int U>
 hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
                       const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
-                      hipStream_t s, bool vec) {
+                      const float* gain, float eps, hipStream_t s, bool vec) {
   const int kt = static_cast<int>(k_tiles(k));
   const int64_t rbs = row_blocks(n);
   // balanced persistent grid: every workgroup takes the same number of row blocks (+-1)
@@ -484,10 +629,12 @@ hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t
   const uint4* p = static_cast<const uint4*>(packed);
   if (vec)
     gemv_lds_kernel<WAVES, U, SRC, true><<<grid, WAVES * 64, lds, s>>>(p, gamma, n, k, kt, rbs, xsrc, amax_in,
-                                                                       static_cast<int>(m), y, acc, xq_out, amax_out);
+                                                                       static_cast<int>(m), y, acc, xq_out, amax_out,
+                                                                       gain, eps);
   else
     gemv_lds_kernel<WAVES, U, SRC, false><<<grid, WAVES * 64, lds, s>>>(p, gamma, n, k, kt, rbs, xsrc, amax_in,
-                                                                        static_cast<int>(m), y, acc, xq_out, amax_out);
+                                                                        static_cast<int>(m), y, acc, xq_out, amax_out,
+                                                                        gain, eps);
   return hipGetLastError();
 }
 
@@ -496,15 +643,15 @@ hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t
 template <int SRC>
 hipError_t dispatch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
                         const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
-                        hipStream_t s, bool vec) {
+                        const float* gain, float eps, hipStream_t s, bool vec) {
   const int64_t kt = k_tiles(k);
   if (kt <= kWaves)
-    return launch_lds<SRC, kWaves, 1>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+    return launch_lds<SRC, kWaves, 1>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
   if (kt <= 2 * kWaves)
-    return launch_lds<SRC, kWaves, 2>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+    return launch_lds<SRC, kWaves, 2>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
   if (kt <= 4 * kWaves)
-    return launch_lds<SRC, kWaves, 4>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
-  return launch_lds<SRC, kWaves, 8>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, s, vec);
+    return launch_lds<SRC, kWaves, 4>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
+  return launch_lds<SRC, kWaves, 8>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
 }
 
 }  // namespace
@@ -515,7 +662,7 @@ hipError_t launch_gemv(const void* packed, const float* gamma, int64_t n, int64_
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
   if (gemv_fits_lds(m, k))
-    return dispatch_lds<kFromCodes>(packed, gamma, n, k, xq, amax, m, y, acc, nullptr, nullptr, s, vec);
+    return dispatch_lds<kFromCodes>(packed, gamma, n, k, xq, amax, m, y, acc, nullptr, nullptr, nullptr, 0.0f, s, vec);
   const int kt = static_cast<int>(k_tiles(k));
   const dim3 grid(static_cast<unsigned>(row_blocks(n)));
   const uint4* p = static_cast<const uint4*>(packed);
@@ -530,7 +677,16 @@ hipError_t launch_quant_gemv(const void* packed, const float* gamma, int64_t n, 
                              int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s) {
   const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 8 == 0);
-  return dispatch_lds<kFromBf16>(packed, gamma, n, k, x, nullptr, m, y, acc, xq_out, amax_out, s, vec);
+  return dispatch_lds<kFromBf16>(packed, gamma, n, k, x, nullptr, m, y, acc, xq_out, amax_out, nullptr, 0.0f, s, vec);
+}
+
+hipError_t launch_norm_quant_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
+                                  const float* gain, float eps, int64_t m, float* y, int32_t* acc, int8_t* xq_out,
+                                  float* amax_out, hipStream_t s) {
+  const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (gain == nullptr || reinterpret_cast<uintptr_t>(gain) % 16 == 0) &&
+                   (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 8 == 0);
+  return dispatch_lds<kFromBf16Norm>(packed, gamma, n, k, x, nullptr, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
 }
 
 }  // namespace bitlinear

@@ -1,0 +1,300 @@
+// Activation quantisation variants on either side of the BitLinear
+// contraction.
+//
+// RMSNorm then per-token quantisation: "BitNet b1.58 in Production: 1-Bit
+// LLMs and Energy Benchmarks", listing "bit_linear.py" (the BitLinear input
+// passes nn.RMSNorm before activation_quant).  RMSNorm multiplies token t by
+// r_t = 1 / sqrt(mean_k x^2 + eps) and channel c by a gain w_c.  Per-token
+// absmax quantisation is invariant under the positive factor r_t, so the
+// codes are those of v = x * w (one fp32 multiply per value) and r_t is
+// folded into the de-quantisation scale: a'_t = max_c |v| * r_t, with the
+// mean square accumulated in fp64 and the product rounded once to fp32.  A
+// token whose v is all zero gets codes 0 and a' = 1e-8.
+//
+// Quantisation from fp32: the same per-token rule as the bf16 kernel
+// (section "The Mathematical Mechanism", item 2), for activations produced in
+// fp32 on the GPU -- the SwiGLU output feeding the down projection.
+//
+// One workgroup per token; rows are read with 16-byte loads, the max is
+// reduced as fp32 bit patterns (non-negative floats order like their bits)
+// and the mean square as fp64, across the wave with shuffles and across the
+// four waves in LDS.
+#include "bitlinear_internal.hpp"
+
+namespace bitlinear {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t code_of(float v, float s) {
+  float r = rintf(v * s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm + quantisation
+// ---------------------------------------------------------------------------
+
+// 8 consecutive values of one token: x (one 16-byte bf16 chunk), gain (two
+// float4, or none) -> v = x * gain
+__device__ __forceinline__ void chunk_values(const uint4& xc, const float* __restrict__ gain8, float (&v)[8],
+                                             float (&xv)[8]) {
+  const uint32_t w[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    xv[2 * q] = bf16_lo(w[q]);
+    xv[2 * q + 1] = bf16_hi(w[q]);
+  }
+  if (gain8) {
+    const float4 g0 = *reinterpret_cast<const float4*>(gain8);
+    const float4 g1 = *reinterpret_cast<const float4*>(gain8 + 4);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = xv[i] * g[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = xv[i];
+  }
+}
+
+// Vector path: k % 8 == 0, x and gain 16-byte aligned, xq 8-byte aligned;
+// the row fits in CPT chunks per thread (kept in registers between passes).
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void rmsnorm_quant_vec(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ gain, float eps, int k,
+                                                              int8_t* __restrict__ xq, float* __restrict__ amax) {
+  __shared__ uint32_t red_max[kWaves];
+  __shared__ double red_ss[kWaves];
+  const int64_t row = blockIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * k);
+  const int chunks = k >> 3;
+  uint4 c[CPT];
+  uint32_t mx = 0;
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < chunks) {
+      c[i] = xr[idx];
+      float v[8], xv[8];
+      chunk_values(c[i], gain ? gain + idx * 8 : nullptr, v, xv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ss += static_cast<double>(xv[j]) * static_cast<double>(xv[j]);
+        mx = max(mx, __float_as_uint(fabsf(v[j])));
+      }
+    }
+  }
+  mx = wave_max_u(mx);
+  ss = wave_sum_d(ss);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red_max[wave] = mx;
+    red_ss[wave] = ss;
+  }
+  __syncthreads();
+  uint32_t mall = red_max[0];
+  double sall = red_ss[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    mall = max(mall, red_max[w]);
+    sall += red_ss[w];
+  }
+  const float av = __uint_as_float(mall);
+  const float s = av > 0.0f ? 127.0f / av : 0.0f;  // all-zero v: every code is 0
+  uint2* out = reinterpret_cast<uint2*>(xq + row * k);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < chunks) {
+      float v[8], xv[8];
+      chunk_values(c[i], gain ? gain + idx * 8 : nullptr, v, xv);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo |= code_of(v[j], s) << (8 * j);
+        hi |= code_of(v[4 + j], s) << (8 * j);
+      }
+      out[idx] = make_uint2(lo, hi);
+    }
+  }
+  if (threadIdx.x == 0) {
+    const double r = 1.0 / sqrt(sall / static_cast<double>(k) + static_cast<double>(eps));
+    const float ap = static_cast<float>(static_cast<double>(av) * r);
+    amax[row] = av > 0.0f ? fmaxf(ap, 1e-8f) : 1e-8f;
+  }
+}
+
+// General path: any k and alignment; two passes over the row with scalar loads.
+__global__ __launch_bounds__(kThreads) void rmsnorm_quant_any(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ gain, float eps, int64_t k,
+                                                              int8_t* __restrict__ xq, float* __restrict__ amax) {
+  __shared__ uint32_t red_max[kWaves];
+  __shared__ double red_ss[kWaves];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * k;
+  uint32_t mx = 0;
+  double ss = 0.0;
+  for (int64_t i = threadIdx.x; i < k; i += kThreads) {
+    const float xv = __uint_as_float(static_cast<uint32_t>(xr[i]) << 16);
+    const float v = gain ? xv * gain[i] : xv;
+    ss += static_cast<double>(xv) * static_cast<double>(xv);
+    mx = max(mx, __float_as_uint(fabsf(v)));
+  }
+  mx = wave_max_u(mx);
+  ss = wave_sum_d(ss);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red_max[wave] = mx;
+    red_ss[wave] = ss;
+  }
+  __syncthreads();
+  uint32_t mall = red_max[0];
+  double sall = red_ss[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    mall = max(mall, red_max[w]);
+    sall += red_ss[w];
+  }
+  const float av = __uint_as_float(mall);
+  const float s = av > 0.0f ? 127.0f / av : 0.0f;
+  int8_t* out = xq + row * k;
+  for (int64_t i = threadIdx.x; i < k; i += kThreads) {
+    const float xv = __uint_as_float(static_cast<uint32_t>(xr[i]) << 16);
+    const float v = gain ? xv * gain[i] : xv;
+    out[i] = static_cast<int8_t>(code_of(v, s));
+  }
+  if (threadIdx.x == 0) {
+    const double r = 1.0 / sqrt(sall / static_cast<double>(k) + static_cast<double>(eps));
+    const float ap = static_cast<float>(static_cast<double>(av) * r);
+    amax[row] = av > 0.0f ? fmaxf(ap, 1e-8f) : 1e-8f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// quantisation from fp32
+// ---------------------------------------------------------------------------
+
+// Vector path: k % 4 == 0, x 16-byte aligned, xq 4-byte aligned.
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void quant_f32_vec(const float* __restrict__ x, int k, int8_t* __restrict__ xq,
+                                                          float* __restrict__ amax) {
+  __shared__ uint32_t red_max[kWaves];
+  const int64_t row = blockIdx.x;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * k);
+  const int chunks = k >> 2;
+  float4 c[CPT];
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < chunks) {
+      c[i] = xr[idx];
+      mx = max(max(mx, max(__float_as_uint(fabsf(c[i].x)), __float_as_uint(fabsf(c[i].y)))),
+               max(__float_as_uint(fabsf(c[i].z)), __float_as_uint(fabsf(c[i].w))));
+    }
+  }
+  mx = wave_max_u(mx);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red_max[wave] = mx;
+  __syncthreads();
+  uint32_t mall = red_max[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) mall = max(mall, red_max[w]);
+  const float a = fmaxf(__uint_as_float(mall), 1e-8f);
+  const float s = 127.0f / a;
+  uint32_t* out = reinterpret_cast<uint32_t*>(xq + row * k);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    if (idx < chunks)
+      out[idx] = code_of(c[i].x, s) | (code_of(c[i].y, s) << 8) | (code_of(c[i].z, s) << 16) | (code_of(c[i].w, s) << 24);
+  }
+  if (threadIdx.x == 0) amax[row] = a;
+}
+
+__global__ __launch_bounds__(kThreads) void quant_f32_any(const float* __restrict__ x, int64_t k,
+                                                          int8_t* __restrict__ xq, float* __restrict__ amax) {
+  __shared__ uint32_t red_max[kWaves];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * k;
+  uint32_t mx = 0;
+  for (int64_t i = threadIdx.x; i < k; i += kThreads) mx = max(mx, __float_as_uint(fabsf(xr[i])));
+  mx = wave_max_u(mx);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red_max[wave] = mx;
+  __syncthreads();
+  uint32_t mall = red_max[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) mall = max(mall, red_max[w]);
+  const float a = fmaxf(__uint_as_float(mall), 1e-8f);
+  const float s = 127.0f / a;
+  int8_t* out = xq + row * k;
+  for (int64_t i = threadIdx.x; i < k; i += kThreads) out[i] = static_cast<int8_t>(code_of(xr[i], s));
+  if (threadIdx.x == 0) amax[row] = a;
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_quant_act(const uint16_t* x, const float* gain, float eps, int64_t m, int64_t k, int8_t* xq,
+                                    float* amax, hipStream_t s) {
+  const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (gain == nullptr || reinterpret_cast<uintptr_t>(gain) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(xq) % 8 == 0);
+  const int64_t per_thread = (k / 8 + kThreads - 1) / kThreads;
+  const dim3 grid(static_cast<unsigned>(m));
+  const int ki = static_cast<int>(k);
+  if (vec && per_thread <= 1)
+    rmsnorm_quant_vec<1><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+  else if (vec && per_thread <= 2)
+    rmsnorm_quant_vec<2><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+  else if (vec && per_thread <= 4)
+    rmsnorm_quant_vec<4><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+  else if (vec && per_thread <= 8)
+    rmsnorm_quant_vec<8><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+  else if (vec && per_thread <= 16)
+    rmsnorm_quant_vec<16><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+  else
+    rmsnorm_quant_any<<<grid, kThreads, 0, s>>>(x, gain, eps, k, xq, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_f32(const float* x, int64_t m, int64_t k, int8_t* xq, float* amax, hipStream_t s) {
+  const bool vec = (k % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(xq) % 4 == 0);
+  const int64_t per_thread = (k / 4 + kThreads - 1) / kThreads;
+  const dim3 grid(static_cast<unsigned>(m));
+  const int ki = static_cast<int>(k);
+  if (vec && per_thread <= 1)
+    quant_f32_vec<1><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else if (vec && per_thread <= 2)
+    quant_f32_vec<2><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else if (vec && per_thread <= 4)
+    quant_f32_vec<4><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else if (vec && per_thread <= 8)
+    quant_f32_vec<8><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else if (vec && per_thread <= 16)
+    quant_f32_vec<16><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
+  else
+    quant_f32_any<<<grid, kThreads, 0, s>>>(x, k, xq, amax);
+  return hipGetLastError();
+}
+
+}  // namespace bitlinear

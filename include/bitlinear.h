@@ -58,7 +58,8 @@ typedef enum {
     BITLINEAR_E_ALIGN = -3,       /* a pointer breaks its alignment rule      */
     BITLINEAR_E_UNSUPPORTED = -4, /* valid, but not handled by this entry     */
     BITLINEAR_E_SIZE = -5,        /* a caller buffer is smaller than required */
-    BITLINEAR_E_HIP = -6          /* the HIP runtime reported a launch error  */
+    BITLINEAR_E_HIP = -6,         /* the HIP runtime reported a launch error  */
+    BITLINEAR_E_VALUE = -7        /* a scalar argument is outside its range   */
 } bitlinear_status;
 
 /* Version of this ABI and of the device weight layout (BITLINEAR_ABI_VERSION). */
@@ -170,6 +171,49 @@ int bitlinear_quant_forward_supported(int64_t m, int64_t k);
 int bitlinear_forward_batched(const void *packed, const float *gamma, int64_t n, int64_t k,
                               const int8_t *xq, const float *x_absmax, int64_t m,
                               float *y, int32_t *acc_or_null, void *stream);
+
+/*
+ * RMSNorm ahead of the activation quantisation ("BitNet b1.58 in
+ * Production", listing "bit_linear.py": the BitLinear input passes
+ * nn.RMSNorm before activation_quant).  Per token r = 1 / sqrt(mean_k x^2 +
+ * eps), and the normalised input is x * r * gain.  Absmax quantisation is
+ * invariant under the positive per-token factor r, so the codes are computed
+ * from v = x * gain (one fp32 multiply per value; gain = 1 when NULL) by the
+ * rule of bitlinear_quant_act, and r is carried by the scale:
+ *   s = 127 / max_k |v| (IEEE fp32 divide); x_q = Clip(Round(v * s), -127, 127);
+ *   a' = max(max_k |v| * r, 1e-8), mean square in fp64, product rounded once;
+ * y = acc * gamma * a' / 127 then de-quantises the normalised input.  A
+ * token whose v is all zero gets codes 0 and a' = 1e-8.
+ *   x             in   bf16 bit patterns [m][k], 2-byte aligned
+ *   gain_or_null  in   fp32 [k] per-channel gain, 4-byte aligned, or NULL
+ *   eps           in   finite and >= 0 (nn.RMSNorm's default for fp32 input
+ *                      is FLT_EPSILON), else BITLINEAR_E_VALUE
+ *   xq, x_absmax  out  int8 [m][k] and fp32 [m] (a')
+ */
+int bitlinear_rmsnorm_quant_act(const uint16_t *x, const float *gain_or_null, float eps,
+                                int64_t m, int64_t k, int8_t *xq, float *x_absmax, void *stream);
+
+/*
+ * RMSNorm and quantisation fused into the decode forward: one launch that
+ * computes exactly bitlinear_rmsnorm_quant_act followed by bitlinear_forward.
+ * Arguments as bitlinear_quant_forward plus gain_or_null and eps as above;
+ * the same (m, k) support rule (bitlinear_quant_forward_supported).
+ */
+int bitlinear_rmsnorm_quant_forward(const void *packed, const float *gamma, int64_t n, int64_t k,
+                                    const uint16_t *x, const float *gain_or_null, float eps, int64_t m,
+                                    float *y, int32_t *acc_or_null,
+                                    int8_t *xq_or_null, float *x_absmax_or_null, void *stream);
+
+/*
+ * Per-token quantisation of fp32 activations: the rule of bitlinear_quant_act
+ * applied to binary32 inputs, for activations produced on the device in fp32
+ * (such as the SwiGLU output of the feed-forward block, which feeds the down
+ * projection).
+ *   x             in   fp32 [m][k], 4-byte aligned
+ *   xq, x_absmax  out  int8 [m][k] and fp32 [m] (a')
+ */
+int bitlinear_quant_act_f32(const float *x, int64_t m, int64_t k,
+                            int8_t *xq, float *x_absmax, void *stream);
 
 #ifdef __cplusplus
 }

@@ -126,6 +126,12 @@ def activations_bf16(seed, m: int, k: int, outlier_frac: float = 0.0,
     return fp32_to_bf16_bits(x)
 
 
+def activations_f32(seed, m: int, k: int, scale: float = 1.0) -> np.ndarray:
+    """fp32 [m][k]: scale * N(0,1), for inputs produced in fp32 on the device."""
+    rng = _rng(seed)
+    return (np.float32(scale) * rng.standard_normal((m, k), dtype=np.float32)).astype(np.float32)
+
+
 def norm_gain(seed, k: int) -> np.ndarray:
     """fp32 [k] per-channel RMSNorm gains: 1 + 0.1 * N(0,1), a synthetic
     stand-in for trained gains (initialised to one)."""

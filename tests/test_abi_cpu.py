@@ -50,7 +50,7 @@ def test_single_hip_runtime_mapped(blq):
 
 def test_version_and_status_strings(blq):
     assert blq.bitlinear_abi_version() == 2
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         assert blq.bitlinear_status_string(s) not in ("", "unknown status")
     assert blq.bitlinear_status_string(12345) == "unknown status"
 
@@ -174,3 +174,39 @@ def test_quant_forward_validation(blq):
         for k in (1, 255, 256, 4096, 6912, 14336, 28672, 40000):
             if lib.bitlinear_quant_forward_supported(m, k):
                 assert m * (((k + 255) // 256) * 256 + 16) <= 65536
+
+
+def test_norm_and_f32_quant_validation(blq):
+    lib = blq.load_library()
+    E = blq
+    f = lib.bitlinear_rmsnorm_quant_act
+    assert f(None, None, 1e-6, 1, 8, A16, A16, None) == E.BITLINEAR_E_NULL
+    assert f(A16, None, 1e-6, 1, 8, None, A16, None) == E.BITLINEAR_E_NULL
+    assert f(A16, None, 1e-6, 1, 8, A16, None, None) == E.BITLINEAR_E_NULL
+    assert f(A16, None, 1e-6, 0, 8, A16, A16, None) == E.BITLINEAR_E_SHAPE
+    assert f(A16, None, 1e-6, 1, (1 << 18) + 1, A16, A16, None) == E.BITLINEAR_E_SHAPE
+    assert f(A16, None, -1.0, 1, 8, A16, A16, None) == E.BITLINEAR_E_VALUE
+    assert f(A16, None, float("inf"), 1, 8, A16, A16, None) == E.BITLINEAR_E_VALUE
+    assert f(A16, None, float("nan"), 1, 8, A16, A16, None) == E.BITLINEAR_E_VALUE
+    assert f(A16 + 1, None, 1e-6, 1, 8, A16, A16, None) == E.BITLINEAR_E_ALIGN
+    assert f(A16, A2, 1e-6, 1, 8, A16, A16, None) == E.BITLINEAR_E_ALIGN
+    g = lib.bitlinear_quant_act_f32
+    assert g(None, 1, 8, A16, A16, None) == E.BITLINEAR_E_NULL
+    assert g(A16, 0, 8, A16, A16, None) == E.BITLINEAR_E_SHAPE
+    assert g(A2, 1, 8, A16, A16, None) == E.BITLINEAR_E_ALIGN
+    h = lib.bitlinear_rmsnorm_quant_forward
+    ok = dict(packed=A16, gamma=A16, n=64, k=512, x=A16, gain=None, eps=1e-6, m=1, y=A16, acc=None, xq=None, amax=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return h(a["packed"], a["gamma"], a["n"], a["k"], a["x"], a["gain"], a["eps"], a["m"], a["y"], a["acc"],
+                 a["xq"], a["amax"], None)
+
+    for key in ("packed", "gamma", "x", "y"):
+        assert call(**{key: None}) == E.BITLINEAR_E_NULL, key
+    assert call(xq=A16) == E.BITLINEAR_E_NULL
+    assert call(n=0) == E.BITLINEAR_E_SHAPE
+    assert call(eps=-2.0) == E.BITLINEAR_E_VALUE
+    assert call(gain=A2) == E.BITLINEAR_E_ALIGN
+    assert call(packed=A8) == E.BITLINEAR_E_ALIGN
+    assert call(m=17) == E.BITLINEAR_E_UNSUPPORTED

@@ -1,0 +1,169 @@
+"""GPU parity of the steps on either side of the contraction, against the CPU
+oracle on the same seeded inputs:
+
+  * RMSNorm ahead of the activation quantisation ("BitNet b1.58 in
+    Production", listing "bit_linear.py"), standalone and fused into the
+    decode forward;
+  * per-token quantisation from fp32 (the SwiGLU output feeding the down
+    projection).
+
+Bar: int8 codes and int32 accumulators bit-exact; a' of the RMSNorm path
+within one fp32 ulp (the mean square is an fp64 sum whose order differs
+between the two sides, and a' = max|v| * r is one rounding of an fp64
+product, so the two can land on different sides of a rounding boundary);
+a' of the fp32 quantisation bit-exact (a max of exact values); y within
+1e-5 relative and exactly 0 where the oracle's is 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import compare_y, host, log, to_dev, to_dev_bits, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def blq():
+    torch_mod()
+    import bitlinear_quant_act_amd as m
+    m.load_library()
+    return m
+
+
+def assert_within_ulps(a, b, ulps, tag):
+    a = np.asarray(a, dtype=np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, dtype=np.float32).view(np.int32).astype(np.int64)
+    d = np.abs(a - b)
+    assert d.max(initial=0) <= ulps, (tag, int(d.max()))
+
+
+def gain_of(kind, seed, k):
+    if kind == "none":
+        return None
+    g = synth.norm_gain(seed, k)
+    return -g if kind == "negated" else g
+
+
+NORM_SHAPES = [(1, 8), (1, 2560), (3, 4096), (5, 6912), (2, 1000), (4, 1003), (7, 28672), (16, 2048),
+               (2, 40000), (1, 1)]
+
+
+@pytest.mark.parametrize("m,k", NORM_SHAPES)
+@pytest.mark.parametrize("gain_kind", ["none", "synthetic", "negated"])
+def test_rmsnorm_quant_parity(blq, m, k, gain_kind):
+    tag = "rmsnorm m=%d k=%d gain=%s" % (m, k, gain_kind)
+    log("case", tag)
+    x = synth.activations_bf16((101, m, k), m, k, 0.01)
+    w = gain_of(gain_kind, (102, k), k)
+    xq_d, a_d = blq.bitlinear_rmsnorm_quant_act(to_dev_bits(x), gain=None if w is None else to_dev(w))
+    xq_o, a_o, _ = oracle.rmsnorm_quant_act(x, w)
+    assert np.array_equal(host(xq_d), xq_o), tag
+    assert_within_ulps(host(a_d), a_o, 1, tag)
+
+
+def test_rmsnorm_quant_degenerate(blq):
+    k = 512
+    x = synth.activations_bf16((103,), 6, k)
+    x[1] = 0                                     # all-zero token
+    x[2] = synth.fp32_to_bf16_bits(np.full(k, 2.0 ** -20, dtype=np.float32))  # eps dominates
+    x[3, 1:] = 0                                 # one non-zero value
+    w = synth.norm_gain((104,), k)
+    for gain, eps in ((None, oracle.RMS_EPS), (w, 0.0), (w, 1.0), (np.zeros(k, dtype=np.float32), oracle.RMS_EPS)):
+        tag = "degenerate gain=%s eps=%r" % ("none" if gain is None else "set", eps)
+        log("case", tag)
+        xq_d, a_d = blq.bitlinear_rmsnorm_quant_act(to_dev_bits(x), gain=None if gain is None else to_dev(gain), eps=eps)
+        xq_o, a_o, _ = oracle.rmsnorm_quant_act(x, gain, eps=eps)
+        assert np.array_equal(host(xq_d), xq_o), tag
+        assert_within_ulps(host(a_d), a_o, 1, tag)
+        assert np.all(np.isfinite(host(a_d))), tag
+
+
+def test_rmsnorm_quant_misaligned(blq):
+    torch = torch_mod()
+    m, k = 3, 1024
+    x = synth.activations_bf16((105,), m, k + 1)
+    w = synth.norm_gain((106,), k + 1)
+    xd = to_dev_bits(x)[:, 1:].contiguous()      # fresh buffer, aligned
+    base = to_dev_bits(x).view(-1)[1:1 + m * k].view(m, k)   # 2-byte aligned view
+    wd = to_dev(w)[1:]                            # 4-byte aligned view
+    for xin, xh in ((xd, x[:, 1:]), (base, x.reshape(-1)[1:1 + m * k].reshape(m, k))):
+        xq_d, a_d = blq.bitlinear_rmsnorm_quant_act(xin, gain=wd)
+        xq_o, a_o, _ = oracle.rmsnorm_quant_act(np.ascontiguousarray(xh), w[1:])
+        assert np.array_equal(host(xq_d), xq_o)
+        assert_within_ulps(host(a_d), a_o, 1, "misaligned")
+    torch.cuda.synchronize()
+
+
+def test_rmsnorm_quant_rejects_bad_eps(blq):
+    x = to_dev_bits(synth.activations_bf16((107,), 1, 64))
+    for eps in (-1.0, float("inf"), float("nan")):
+        with pytest.raises(blq.BitlinearError) as e:
+            blq.bitlinear_rmsnorm_quant_act(x, eps=eps)
+        assert e.value.status == blq.BITLINEAR_E_VALUE
+
+
+# ---------------------------------------------------------------------------
+# fused RMSNorm + quantisation + decode forward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(2560, 2560), (700, 1000), (3840, 2560), (2560, 6912), (64, 14336), (33, 1003)])
+@pytest.mark.parametrize("m", [1, 3, 16])
+@pytest.mark.parametrize("gain_kind", ["none", "synthetic"])
+def test_rmsnorm_quant_forward_parity(blq, n, k, m, gain_kind):
+    if not blq.bitlinear_quant_forward_supported(m, k):
+        pytest.skip("m*k codes beyond the on-chip budget of the fused path")
+    torch = torch_mod()
+    tag = "rmsnorm_quant_forward n=%d k=%d m=%d gain=%s" % (n, k, m, gain_kind)
+    log("case", tag)
+    w = synth.latent_weights((108, n, k), n, k)
+    x = synth.activations_bf16((109, m, k), m, k, 0.01)
+    gn = gain_of(gain_kind, (110, k), k)
+    packed, gamma = blq.bitlinear_pack_weights(to_dev(w))
+    acc_d = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    xq_d = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    a_d = torch.empty(m, dtype=torch.float32, device="cuda")
+    y_d = blq.bitlinear_rmsnorm_quant_forward(packed, gamma, n, k, to_dev_bits(x), gain=None if gn is None else to_dev(gn),
+                                              acc=acc_d, xq=xq_d, x_absmax=a_d)
+    g = np.float32(host(gamma)[0])
+    codes = host(blq.bitlinear_unpack_weights(packed, n, k))
+    assert np.array_equal(codes, oracle.ternarize(w, g)), tag   # same gamma: codes decided identically
+    xq_o, a_o, _ = oracle.rmsnorm_quant_act(x, gn)
+    assert np.array_equal(host(xq_d), xq_o), tag
+    assert_within_ulps(host(a_d), a_o, 1, tag)
+    acc_o = oracle.contract(xq_o, codes)
+    assert np.array_equal(host(acc_d), acc_o), tag
+    compare_y(host(y_d), oracle.dequant(acc_o, g, host(a_d)), tag)
+    # the fused prologue computes exactly the standalone kernel's codes and a'
+    xq_s, a_s = blq.bitlinear_rmsnorm_quant_act(to_dev_bits(x), gain=None if gn is None else to_dev(gn))
+    assert np.array_equal(host(xq_s), host(xq_d)) and np.array_equal(host(a_s), host(a_d)), tag
+
+
+# ---------------------------------------------------------------------------
+# quantisation from fp32
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,k", [(1, 1), (1, 7), (3, 1023), (2, 1024), (5, 13824), (1, 28672), (64, 6912),
+                                 (3, 40000), (16, 14336)])
+def test_quant_act_f32_parity(blq, m, k):
+    tag = "quant_f32 m=%d k=%d" % (m, k)
+    log("case", tag)
+    x = synth.activations_f32((111, m, k), m, k, 3.0)
+    if m > 1:
+        x[m // 2] = 0.0
+    xq_d, a_d = blq.bitlinear_quant_act_f32(to_dev(x))
+    xq_o, a_o = oracle.quant_act_f32(x)
+    assert np.array_equal(host(xq_d), xq_o), tag
+    assert np.array_equal(host(a_d), a_o), tag
+
+
+def test_quant_act_f32_misaligned(blq):
+    m, k = 4, 2048
+    x = synth.activations_f32((112,), m, k + 1)
+    base = to_dev(x).view(-1)[1:1 + m * k].view(m, k)    # 4-byte aligned view
+    xq_d, a_d = blq.bitlinear_quant_act_f32(base)
+    xq_o, a_o = oracle.quant_act_f32(x.reshape(-1)[1:1 + m * k].reshape(m, k))
+    assert np.array_equal(host(xq_d), xq_o) and np.array_equal(host(a_d), a_o)
