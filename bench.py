@@ -69,10 +69,11 @@ def quant_bytes(m: int, k: int) -> int:
 
 
 class Mat:
-    __slots__ = ("layer", "j", "n", "k", "packed", "gamma", "x", "xq", "amax", "y", "q_or", "g_or", "x_np")
+    __slots__ = ("layer", "j", "n", "k", "packed", "gamma", "x", "xq", "amax", "y", "q_or", "g_or", "x_np",
+                 "gain", "gain_np")
 
 
-def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod):
+def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"):
     """Generate, upload and pack every matrix; returns replicas x [Mat]."""
     dev = torch.device("cuda")
     mats = []
@@ -107,6 +108,9 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod):
             mat.xq = torch.empty((m, mt.k), dtype=torch.int8, device=dev)
             mat.amax = torch.empty(m, dtype=torch.float32, device=dev)
             mat.y = torch.empty((m, mt.n), dtype=torch.float32, device=dev)
+            mat.gain_np = (synth.norm_gain(synth.seed_for(wl, layer, j, synth.ROLE_GAIN), mt.k)
+                           if variant == "rmsnorm" else None)
+            mat.gain = None if mat.gain_np is None else torch.from_numpy(mat.gain_np).to(dev)
             if keep_oracle_codes:
                 mat.g_or = oracle_mod.gamma(w)
                 mat.q_or = oracle_mod.ternarize(w, mat.g_or)
@@ -131,15 +135,29 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod):
     return reps, {"seconds": t_pack, "bytes": pack_bytes}
 
 
+def _quant(blq, mat, stream):
+    if mat.gain is not None:  # RMSNorm ahead of the quantisation
+        blq.bitlinear_rmsnorm_quant_act(mat.x, mat.gain, xq=mat.xq, x_absmax=mat.amax, stream=stream)
+    else:
+        blq.bitlinear_quant_act(mat.x, mat.xq, mat.amax, stream=stream)
+
+
+def _fused(blq, mat, stream):
+    if mat.gain is not None:
+        blq.bitlinear_rmsnorm_quant_forward(mat.packed, mat.gamma, mat.n, mat.k, mat.x, mat.gain, y=mat.y, stream=stream)
+    else:
+        blq.bitlinear_quant_forward(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
+
+
 def launch_step(blq, mats, m, stream, fused):
     """One pass of the per-token path over every matrix, in layer order."""
     if fused:
         for mat in mats:
-            blq.bitlinear_quant_forward(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
+            _fused(blq, mat, stream)
         return
     fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
     for mat in mats:
-        blq.bitlinear_quant_act(mat.x, mat.xq, mat.amax, stream=stream)
+        _quant(blq, mat, stream)
         fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
 
 
@@ -148,11 +166,11 @@ def launch_kernel_only(blq, mats, m, stream, which):
     fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
     for mat in mats:
         if which == "quant":
-            blq.bitlinear_quant_act(mat.x, mat.xq, mat.amax, stream=stream)
+            _quant(blq, mat, stream)
         elif which == "forward":
             fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
         else:
-            blq.bitlinear_quant_forward(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
+            _fused(blq, mat, stream)
 
 
 def fused_bytes(m: int, n: int, k: int) -> int:
@@ -192,7 +210,10 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s):
     nmat = 0
     for mat in mats:
         t0 = time.perf_counter()
-        xq, amax = oracle_mod.quant_act(mat.x_np)
+        if mat.gain_np is not None:
+            xq, amax, _ = oracle_mod.rmsnorm_quant_act(mat.x_np, mat.gain_np)
+        else:
+            xq, amax = oracle_mod.quant_act(mat.x_np)
         if m * mat.n * mat.k <= 2e10:
             acc = oracle_mod.contract(xq, mat.q_or)
             y = oracle_mod.dequant(acc, mat.g_or, amax)
@@ -231,6 +252,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
+    ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm"),
+                    help="rmsnorm: every BitLinear normalises its input first (per-channel gains)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bound)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -295,7 +318,8 @@ def main():
             oracle_quota += 1
             if macs > args.cpu_budget * 3e9:
                 break
-    reps, pack = setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod)
+    reps, pack = setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, args.variant)
+    norm = args.variant == "rmsnorm"
     log("setup %.1f s" % (time.time() - t0))
 
     mats0 = reps[0]
@@ -363,7 +387,7 @@ def main():
     q_ms = time_graph(torch, stream, all_reps("quant"), replays) / len(reps)
     q_avg_us = q_ms / len(mats0) * 1e3
     per_call = fused_bytes if fused else forward_bytes
-    fw_bytes = sum(per_call(m, mt.n, mt.k) for mt in mats0)
+    fw_bytes = sum(per_call(m, mt.n, mt.k) + (4 * mt.k if norm and fused else 0) for mt in mats0)
     fw_ops = step_ops
     fw_ms = dom_ms
     if batched:
@@ -379,15 +403,16 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof["kernel"] = ("bitlinear_forward_batched (gemm_kernel)" if batched else
-                      "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)" if fused else
+                      ("bitlinear_rmsnorm_quant_forward (gemv_lds_kernel, RMSNorm + bf16 prologue)" if norm else
+                       "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)") if fused else
                       "bitlinear_forward (gemv kernel)")
     roof["avg_launch_us"] = round(fw_avg_us, 3)
     roof["launches_timed"] = nlaunch
     roof["per_launch"] = "mean over the workload's matrices of %s" % (
-        "2*M*N*K" if batched else "ceil(N*K/4)+2*M*K+4+4*M*N bytes" if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
+        "2*M*N*K" if batched else ("ceil(N*K/4)+2*M*K+4K+4+4*M*N bytes" if norm else "ceil(N*K/4)+2*M*K+4+4*M*N bytes") if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
     roof["timing"] = "HIP events around %d graph replays of the kernel's %d launches" % (replays, len(mats0) * len(reps))
     roof["traffic"] = None
-    prof = os.path.join(ROOT, "profiles", "counters_%s_m%d.json" % (wl.key, m))
+    prof = os.path.join(ROOT, "profiles", "counters_%s_m%d%s.json" % (wl.key, m, "_rmsnorm" if norm else ""))
     if os.path.exists(prof):
         with open(prof) as f:
             c = json.load(f)
@@ -414,8 +439,10 @@ def main():
             "layers": wl.layers,
             "matrices_per_step": len(mats0),
             "shapes_kxn": ["%dx%d" % (mt.k, mt.n) for mt in wl.matrices],
-            "entry_points": ("bitlinear_quant_forward" if fused else
-                             "bitlinear_quant_act + " + ("bitlinear_forward_batched" if batched else "bitlinear_forward")),
+            "variant": args.variant,
+            "entry_points": (("bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward") if fused else
+                             ("bitlinear_rmsnorm_quant_act + " if norm else "bitlinear_quant_act + ") +
+                             ("bitlinear_forward_batched" if batched else "bitlinear_forward")),
             "launch": ("hip graph, %d kernels per step" % ((1 if fused else 2) * len(mats0))
                        if not args.eager else "eager"),
             "cold_cache": "weights %.0f MB per step x %d replica(s)" % (total_packed / 1e6, len(reps)),

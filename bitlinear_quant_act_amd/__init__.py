@@ -91,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.bitlinear_rmsnorm_quant_forward.restype = _ct.c_int
     lib.bitlinear_quant_act_f32.argtypes = [_p, _i64, _i64, _p, _p, _p]
     lib.bitlinear_quant_act_f32.restype = _ct.c_int
+    lib.bitlinear_forward_swiglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
+    lib.bitlinear_forward_swiglu.restype = _ct.c_int
     for name in ("bitlinear_forward", "bitlinear_forward_batched"):
         fn = getattr(lib, name)
         fn.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
@@ -264,6 +266,30 @@ def _forward(fname, packed, gamma, n, k, xq, x_absmax, y, acc, stream):
 def bitlinear_forward(packed, gamma, n: int, k: int, xq, x_absmax, y=None, acc=None, stream=None):
     """Decode path (1 <= m <= 16): y fp32 [m][n]; optional exact int32 acc [m][n]."""
     return _forward("bitlinear_forward", packed, gamma, n, k, xq, x_absmax, y, acc, stream)
+
+
+def bitlinear_forward_swiglu(packed_gate, gamma_gate, packed_up, gamma_up, f: int, k: int, xq, x_absmax,
+                             h=None, acc=None, stream=None):
+    """Gate and up projections with h = silu(y_gate) * y_up fused into the
+    epilogue: h fp32 [m][f]; optional exact int32 acc [m][2f] (gate, up)."""
+    lib = load_library()
+    m = xq.shape[0]
+    if xq.dim() != 2 or xq.shape[1] != k:
+        raise ValueError("xq must be [m][k]")
+    nb = bitlinear_packed_bytes(f, k)
+    for name, pk in (("packed_gate", packed_gate), ("packed_up", packed_up)):
+        if pk.numel() * pk.element_size() < nb:
+            raise BitlinearError(BITLINEAR_E_SIZE, "bitlinear_forward_swiglu (%s)" % name)
+    if h is None:
+        h = _torch.empty((m, f), dtype=_torch.float32, device=xq.device)
+    rc = lib.bitlinear_forward_swiglu(
+        _dev(packed_gate, "packed_gate", (_torch.uint8,)), _dev(gamma_gate, "gamma_gate", (_torch.float32,), 1),
+        _dev(packed_up, "packed_up", (_torch.uint8,)), _dev(gamma_up, "gamma_up", (_torch.float32,), 1), f, k,
+        _dev(xq, "xq", (_torch.int8,)), _dev(x_absmax, "x_absmax", (_torch.float32,), m), m,
+        _dev(h, "h", (_torch.float32,), m * f),
+        None if acc is None else _dev(acc, "acc", (_torch.int32,), 2 * m * f), _stream_handle(stream))
+    _check(rc, "bitlinear_forward_swiglu")
+    return h
 
 
 def bitlinear_forward_batched(packed, gamma, n: int, k: int, xq, x_absmax, y=None, acc=None, stream=None):

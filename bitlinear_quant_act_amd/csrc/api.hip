@@ -161,4 +161,20 @@ int bitlinear_quant_act_f32(const float* x, int64_t m, int64_t k, int8_t* xq, fl
   return status_of(bitlinear::launch_quant_act_f32(x, m, k, xq, x_absmax, static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_forward_swiglu(const void* packed_gate, const float* gamma_gate, const void* packed_up,
+                             const float* gamma_up, int64_t f, int64_t k, const int8_t* xq, const float* x_absmax,
+                             int64_t m, float* h, int32_t* acc_or_null, void* stream) {
+  if (!packed_up || !gamma_up) return BITLINEAR_E_NULL;
+  if (int rc = check_forward(packed_gate, gamma_gate, f, k, xq, x_absmax, m, h, acc_or_null)) return rc;
+  if (!aligned(packed_up, 16) || !aligned(gamma_up, 4)) return BITLINEAR_E_ALIGN;
+  if (m > kMaxBatchedM) return BITLINEAR_E_UNSUPPORTED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m <= BITLINEAR_FORWARD_MAX_M && bitlinear::gemv_fits_lds(m, k))
+    return status_of(bitlinear::launch_gemv_swiglu(packed_gate, gamma_gate, packed_up, gamma_up, f, k, xq, x_absmax, m,
+                                                   h, acc_or_null, st));
+  if (!bitlinear::gemm_swiglu_supported(k, xq)) return BITLINEAR_E_UNSUPPORTED;
+  return status_of(bitlinear::launch_gemm_swiglu(packed_gate, gamma_gate, packed_up, gamma_up, f, k, xq, x_absmax, m,
+                                                 h, acc_or_null, st));
+}
+
 }  // extern "C"

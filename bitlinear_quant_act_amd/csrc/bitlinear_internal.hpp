@@ -62,6 +62,13 @@ hipError_t launch_quant_act_f32(const float* x, int64_t m, int64_t k, int8_t* xq
 hipError_t launch_norm_quant_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
                                   const float* gain, float eps, int64_t m, float* y, int32_t* acc, int8_t* xq_out,
                                   float* amax_out, hipStream_t s);
+hipError_t launch_gemv_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
+                              int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
+                              int32_t* acc, hipStream_t s);
+bool gemm_swiglu_supported(int64_t k, const int8_t* xq);
+hipError_t launch_gemm_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
+                              int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
+                              int32_t* acc, hipStream_t s);
 hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* amax,
                             hipStream_t s);
 

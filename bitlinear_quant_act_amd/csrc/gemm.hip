@@ -253,9 +253,14 @@ constexpr int DmaStageBytes(int bm, int bn) { return bm * kTileCols + (bn / kTil
 
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
 
-template <int BM, int BN>
+// With SWIGLU the BN weight rows of a stage come from two matrices, gate and
+// up, in alternating 32-row blocks over BN / 2 features: 32-row block v holds
+// rows 32 * (v / 2) + [0, 32) of the workgroup's features, from gate for even
+// v and from up for odd v (b_rsrc / u_rsrc).
+template <int BM, int BN, bool SWIGLU = false>
 __device__ __forceinline__ void issue_tile(uint8_t* stage, __amdgpu_buffer_rsrc_t a_rsrc, __amdgpu_buffer_rsrc_t b_rsrc,
-                                           int k, int kt_count, int kt, int wave, int lane) {
+                                           __amdgpu_buffer_rsrc_t u_rsrc, int k, int kt_count, int kt, int wave,
+                                           int lane) {
   using DS = DmaShape<BM, BN>;
   const int ktc = kt < kt_count ? kt : 0;  // tiles past the end re-read tile 0 into an unused stage
 #pragma unroll
@@ -269,8 +274,15 @@ __device__ __forceinline__ void issue_tile(uint8_t* stage, __amdgpu_buffer_rsrc_
 #pragma unroll
   for (int i = 0; i < DS::kBDma; ++i) {
     const int rbl = wave * DS::kBDma + i;
-    const int off = (rbl * kt_count + ktc) * kTileBytes + lane * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, BITLINEAR_LDS(stage + DS::kABytes + rbl * 1024), 16, off, 0, 0, 0);
+    if (SWIGLU) {
+      const int src = ((rbl >> 2) << 1) | (rbl & 1);  // row block of the features
+      const int off = (src * kt_count + ktc) * kTileBytes + lane * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((rbl & 2) ? u_rsrc : b_rsrc,
+                                               BITLINEAR_LDS(stage + DS::kABytes + rbl * 1024), 16, off, 0, 0, 0);
+    } else {
+      const int off = (rbl * kt_count + ktc) * kTileBytes + lane * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, BITLINEAR_LDS(stage + DS::kABytes + rbl * 1024), 16, off, 0, 0, 0);
+    }
   }
 }
 
@@ -282,19 +294,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int BM, int BN, int WM, int WN, int S, int OCC>
+// SWIGLU: packed_b / gamma_p are the gate projection, packed_u / gamma_u the
+// up projection (same [n][k] shape, n = features); the workgroup covers
+// BN / 2 features and writes h = silu(y_gate) * y_up to y [m][n] (acc_out, if
+// set, is [m][2n]: gate accumulators, then up accumulators).
+template <int BM, int BN, int WM, int WN, int S, int OCC, bool SWIGLU = false>
 __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* __restrict__ packed_b,
                                                                const float* __restrict__ gamma_p, int64_t n,
                                                                int64_t k, int kt_count, const int8_t* __restrict__ xq,
                                                                const float* __restrict__ amax, int64_t m,
                                                                int mt_count, int nt_count, float* __restrict__ y,
-                                                               int32_t* __restrict__ acc_out) {
+                                                               int32_t* __restrict__ acc_out,
+                                                               const uint8_t* __restrict__ packed_u,
+                                                               const float* __restrict__ gamma_u) {
   static_assert(WM * WN == kThreads / 64, "4 waves");
   static_assert(S >= 2 && S <= 4, "2..4 stages");
   using DS = DmaShape<BM, BN>;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;
   static_assert(MB >= 1 && NB >= 1 && TM % 32 == 0 && TN % 32 == 0 && BN % 64 == 0, "tile shape");
+  static_assert(!SWIGLU || NB % 2 == 0, "gate and up blocks pair up inside a wave");
+  constexpr int FB = SWIGLU ? BN / 2 : BN;  // output columns (features) per workgroup
 
   __shared__ __attribute__((aligned(1024))) uint8_t st0[DS::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[DS::kStage];
@@ -313,7 +333,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
   const int nt = id / mt_count, mt = id - nt * mt_count;
   const int64_t m0 = static_cast<int64_t>(mt) * BM;
-  const int64_t n0 = static_cast<int64_t>(nt) * BN;
+  const int64_t n0 = static_cast<int64_t>(nt) * FB;
   const int64_t rb0 = n0 / kTileRows;
   const int64_t rb_count = row_blocks(n);
 
@@ -384,34 +404,39 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
     math(o1);
   };
 
-  // per-token output scale gamma * a'[t] / 127, staged once
+  // per-token output scale gamma * a'[t] / 127, staged once (one per matrix)
   __shared__ float scale_s[BM];
+  __shared__ float scale_u[SWIGLU ? BM : 1];
   if (tid < BM) {
     const int64_t t = m0 + tid;
     scale_s[tid] = t < m ? *gamma_p * amax[t] / 127.0f : 0.0f;
+    if (SWIGLU) scale_u[tid] = t < m ? *gamma_u * amax[t] / 127.0f : 0.0f;
   }
   lds_barrier();
 
   // operand descriptors: this workgroup's token rows and weight row blocks
   const int64_t rows_here = m - m0 < BM ? m - m0 : BM;
-  const int64_t rbs_here = rb_count - rb0 < BN / kTileRows ? rb_count - rb0 : BN / kTileRows;
+  const int64_t rbs_here = rb_count - rb0 < FB / kTileRows ? rb_count - rb0 : FB / kTileRows;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(xq + m0 * k), 0, static_cast<int>(rows_here * k), kBufferWord3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(packed_b + rb0 * kt_count * kTileBytes), 0,
       static_cast<int>(rbs_here * kt_count * kTileBytes), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t u_rsrc = SWIGLU ? __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed_u + rb0 * kt_count * kTileBytes), 0,
+      static_cast<int>(rbs_here * kt_count * kTileBytes), kBufferWord3) : b_rsrc;
   const int k32 = static_cast<int>(k);
 
   // prologue: tiles 0 .. S-2 in flight
-  issue_tile<BM, BN>(st0, a_rsrc, b_rsrc, k32, kt_count, 0, wave, lane);
-  if (S > 2) issue_tile<BM, BN>(st1, a_rsrc, b_rsrc, k32, kt_count, 1, wave, lane);
-  if (S > 3) issue_tile<BM, BN>(st2, a_rsrc, b_rsrc, k32, kt_count, 2, wave, lane);
+  issue_tile<BM, BN, SWIGLU>(st0, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 0, wave, lane);
+  if (S > 2) issue_tile<BM, BN, SWIGLU>(st1, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 1, wave, lane);
+  if (S > 3) issue_tile<BM, BN, SWIGLU>(st2, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 2, wave, lane);
 
   // one pipeline step: tile kt sits in stage `cur`; tile kt + S - 1 goes to `nxt`
   auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
     wait_vmcnt<(S - 2) * DS::kDma>();
     __builtin_amdgcn_s_barrier();
-    issue_tile<BM, BN>(nxt, a_rsrc, b_rsrc, k32, kt_count, kt + S - 1, wave, lane);
+    issue_tile<BM, BN, SWIGLU>(nxt, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, kt + S - 1, wave, lane);
     compute(cur);
   };
   for (int kt = 0; kt < kt_count; kt += S) {
@@ -422,6 +447,36 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   }
   wait_vmcnt<0>();
 
+  if (SWIGLU) {
+    // blocks nb (gate) and nb + 1 (up) hold the same 32 features; the lane's
+    // elements line up, so h = silu(g) * u is formed in registers
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tl = wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t t = m0 + tl;
+        if (t >= m) continue;
+        const float sg = scale_s[tl], su = scale_u[tl];
+#pragma unroll
+        for (int nb = 0; nb < NB; nb += 2) {
+          const int64_t j = n0 + 16 * (wn * NB + nb) + l32;
+          if (j < n) {
+            const int vg = acc[mb][nb][r] >> kWeightShift;
+            const int vu = acc[mb][nb + 1][r] >> kWeightShift;
+            const float g = static_cast<float>(vg) * sg;
+            const float u = static_cast<float>(vu) * su;
+            y[t * n + j] = g * u / (1.0f + expf(-g));
+            if (acc_out) {
+              acc_out[t * 2 * n + j] = vg;
+              acc_out[t * 2 * n + n + j] = vu;
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -499,7 +554,24 @@ hipError_t launch_dma(const void* packed, const float* gamma, int64_t n, int64_t
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
   gemm_dma_kernel<BM, BN, WM, WN, S, OCC><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
       static_cast<const uint8_t*>(packed), gamma, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl),
-      y, acc);
+      y, acc, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int S, int OCC>
+hipError_t launch_dma_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
+                             int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
+                             int32_t* acc, hipStream_t s) {
+  static_assert(S * DmaStageBytes(BM, BN) <= 163840, "LDS per workgroup");
+  static_assert(static_cast<int64_t>(BM) << 18 <= 0x7fffffff && static_cast<int64_t>(BN / kTileRows) * 1024 * kTileBytes <= 0x7fffffff,
+                "buffer offsets fit 31 bits");
+  const int kt = static_cast<int>(k_tiles(k));
+  const int64_t mt = (m + BM - 1) / BM;
+  const int64_t ntl = (f + BN / 2 - 1) / (BN / 2);
+  if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
+  gemm_dma_kernel<BM, BN, WM, WN, S, OCC, true><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+      static_cast<const uint8_t*>(packed_g), gamma_g, f, k, kt, xq, amax, m, static_cast<int>(mt),
+      static_cast<int>(ntl), h, acc, static_cast<const uint8_t*>(packed_u), gamma_u);
   return hipGetLastError();
 }
 
@@ -523,6 +595,19 @@ DmaConfig choose_dma(int64_t m, int64_t n) {
 }
 
 }  // namespace
+
+bool gemm_swiglu_supported(int64_t k, const int8_t* xq) {
+  return (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
+}
+
+hipError_t launch_gemm_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
+                              int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
+                              int32_t* acc, hipStream_t s) {
+  if (!gemm_swiglu_supported(k, xq)) return hipErrorInvalidValue;
+  if (f >= 8192)
+    return launch_dma_swiglu<64, 256, 2, 2, 2, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
+  return launch_dma_swiglu<64, 128, 2, 2, 2, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
+}
 
 hipError_t launch_gemm(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {

@@ -420,18 +420,27 @@ __device__ void stage_bf16_norm(int8_t* xs, int pitch, float* amax_s, float* qua
 // Work items of a workgroup: its row blocks rb = blockIdx.x + i * gridDim.x,
 // each cut into chunks of U * WAVES tiles (one chunk unless k is long).  A
 // wave's share of item (rb, c) is tiles c*U*WAVES + wave + u*WAVES, u < U.
-template <int WAVES, int U>
-__device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict__ packed, int64_t rb, int c,
-                                          int kt_count, int wave, int lane, bool valid) {
+// With an up matrix (SwiGLU) an item walks 2 * kt_count tiles: the row
+// block's gate tiles, then its up tiles.
+template <int WAVES, int U, bool SWIGLU>
+__device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict__ packed,
+                                          const uint4* __restrict__ packed_u, int64_t rb, int c, int kt_count,
+                                          int wave, int lane, bool valid) {
+  const int kt_items = SWIGLU ? 2 * kt_count : kt_count;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int kt = c * U * WAVES + wave + u * WAVES;
-    w[u] = (valid && kt < kt_count) ? load_weights_nt(packed + (rb * kt_count + kt) * 64 + lane)
+    const int kv = c * U * WAVES + wave + u * WAVES;
+    const bool up = SWIGLU && kv >= kt_count;
+    const int kt = up ? kv - kt_count : kv;
+    w[u] = (valid && kv < kt_items) ? load_weights_nt((up ? packed_u : packed) + (rb * kt_count + kt) * 64 + lane)
                                     : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
   }
 }
 
-template <int WAVES, int U, int SRC, bool VEC>
+// SWIGLU: packed / gamma_p are the gate projection, packed_u / gamma_u the up
+// projection; y receives h = silu(y_gate) * y_up [m][n] and acc_out (if set)
+// the gate then the up accumulators, [m][2n].
+template <int WAVES, int U, int SRC, bool VEC, bool SWIGLU = false>
 __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __restrict__ packed,
                                                               const float* __restrict__ gamma_p, int64_t n,
                                                               int64_t k, int kt_count, int64_t rb_count,
@@ -440,7 +449,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
                                                               float* __restrict__ y, int32_t* __restrict__ acc_out,
                                                               int8_t* __restrict__ xq_out,
                                                               float* __restrict__ amax_out,
-                                                              const float* __restrict__ gain, float eps) {
+                                                              const float* __restrict__ gain, float eps,
+                                                              const uint4* __restrict__ packed_u,
+                                                              const float* __restrict__ gamma_u) {
+  static_assert(!SWIGLU || WAVES >= 4, "one token group per wave in the SwiGLU epilogue");
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ int red[WAVES * 4 * 64];
   __shared__ float amax_s[16];
@@ -456,7 +468,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   const bool has_tok = tok < m;
   const int pitch = static_cast<int>(lds_pitch(kt_count));
   const int kpad = kt_count * kTileCols;
-  const int nchunks = (kt_count + U * WAVES - 1) / (U * WAVES);
+  const int kt_items = SWIGLU ? 2 * kt_count : kt_count;  // tiles per item
+  const int nchunks = (kt_items + U * WAVES - 1) / (U * WAVES);
 
   int64_t rb = blockIdx.x;
   int c = 0;
@@ -468,7 +481,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
       prefetch_bf16(cache, static_cast<const uint16_t*>(xsrc), m, k);
   }
   uint4 wcur[U];
-  load_item<WAVES, U>(wcur, packed, rb, c, kt_count, wave, lane, rb < rb_count);
+  load_item<WAVES, U, SWIGLU>(wcur, packed, packed_u, rb, c, kt_count, wave, lane, rb < rb_count);
 
   if (SRC == kFromCodes) {
     stage_codes(xs, pitch, cache, static_cast<const int8_t*>(xsrc), m, k, kpad, VEC);
@@ -486,9 +499,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   lds_barrier();
 
   const float gamma = *gamma_p;
+  const float gamma_up = SWIGLU ? *gamma_u : 0.0f;
   const v4i zero4 = {0, 0, 0, 0};
   const int8_t* xrow = xs + (has_tok ? tok : 0) * pitch + g * 64;
   v4i acc = zero4;
+  v4i acc_u = zero4;  // SwiGLU: the up projection's partial sums
   while (rb < rb_count) {
     int64_t rbn = rb;
     int cn = c + 1;
@@ -497,20 +512,65 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
       rbn = rb + gridDim.x;
     }
     uint4 wnext[U];
-    load_item<WAVES, U>(wnext, packed, rbn, cn, kt_count, wave, lane, rbn < rb_count);
+    load_item<WAVES, U, SWIGLU>(wnext, packed, packed_u, rbn, cn, kt_count, wave, lane, rbn < rb_count);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kt = c * U * WAVES + wave + u * WAVES;
-      if (kt < kt_count) {
+      const int kv = c * U * WAVES + wave + u * WAVES;
+      if (kv < kt_items) {
+        const bool up = SWIGLU && kv >= kt_count;
+        const int kt = up ? kv - kt_count : kv;
         const uint32_t words[4] = {wcur[u].x, wcur[u].y, wcur[u].z, wcur[u].w};
+        if (up) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const v4i a = has_tok ? *reinterpret_cast<const v4i*>(xrow + kt * kTileCols + 16 * s) : zero4;
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_ternary(words[s]), acc, 0, 0, 0);
+          for (int s = 0; s < 4; ++s) {
+            const v4i a = has_tok ? *reinterpret_cast<const v4i*>(xrow + kt * kTileCols + 16 * s) : zero4;
+            acc_u = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_ternary(words[s]), acc_u, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const v4i a = has_tok ? *reinterpret_cast<const v4i*>(xrow + kt * kTileCols + 16 * s) : zero4;
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_ternary(words[s]), acc, 0, 0, 0);
+          }
         }
       }
     }
-    if (c == nchunks - 1) {
+    if (SWIGLU && c == nchunks - 1) {
+      // gate partials through LDS, then up partials; a wave < 4 owns token group r = wave
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
+      lds_barrier();
+      int vg = 0;
+      if (wave < 4) {
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) vg += red[(w * 4 + wave) * 64 + lane];
+      }
+      lds_barrier();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc_u[r];
+      lds_barrier();
+      const int64_t row = rb * kTileRows + tok;
+      if (wave < 4) {
+        int vu = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) vu += red[(w * 4 + wave) * 64 + lane];
+        const int t = 4 * g + wave;
+        if (t < m && row < n) {
+          vg >>= kWeightShift;  // exact: the sums are multiples of 64
+          vu >>= kWeightShift;
+          const float gv = static_cast<float>(vg) * (gamma * amax_s[t] / 127.0f);
+          const float uv = static_cast<float>(vu) * (gamma_up * amax_s[t] / 127.0f);
+          y[t * n + row] = gv * uv / (1.0f + expf(-gv));
+          if (acc_out) {
+            acc_out[t * 2 * n + row] = vg;
+            acc_out[t * 2 * n + n + row] = vu;
+          }
+        }
+      }
+      lds_barrier();
+      acc = zero4;
+      acc_u = zero4;
+    } else if (c == nchunks - 1) {
       // lane holds 64 * acc for tokens 4g + r (r = 0..3) of weight row 16 rb + tok
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
@@ -616,10 +676,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
   }
 }
 
-template <int SRC, int WAVES, int U>
+template <int SRC, int WAVES, int U, bool SWIGLU = false>
 hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
                       const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
-                      const float* gain, float eps, hipStream_t s, bool vec) {
+                      const float* gain, float eps, hipStream_t s, bool vec, const void* packed_u = nullptr,
+                      const float* gamma_u = nullptr) {
   const int kt = static_cast<int>(k_tiles(k));
   const int64_t rbs = row_blocks(n);
   // balanced persistent grid: every workgroup takes the same number of row blocks (+-1)
@@ -627,14 +688,13 @@ hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t
   const dim3 grid(static_cast<unsigned>((rbs + per - 1) / per));
   const size_t lds = lds_bytes(m, kt);
   const uint4* p = static_cast<const uint4*>(packed);
+  const uint4* pu = static_cast<const uint4*>(packed_u);
   if (vec)
-    gemv_lds_kernel<WAVES, U, SRC, true><<<grid, WAVES * 64, lds, s>>>(p, gamma, n, k, kt, rbs, xsrc, amax_in,
-                                                                       static_cast<int>(m), y, acc, xq_out, amax_out,
-                                                                       gain, eps);
+    gemv_lds_kernel<WAVES, U, SRC, true, SWIGLU><<<grid, WAVES * 64, lds, s>>>(
+        p, gamma, n, k, kt, rbs, xsrc, amax_in, static_cast<int>(m), y, acc, xq_out, amax_out, gain, eps, pu, gamma_u);
   else
-    gemv_lds_kernel<WAVES, U, SRC, false><<<grid, WAVES * 64, lds, s>>>(p, gamma, n, k, kt, rbs, xsrc, amax_in,
-                                                                        static_cast<int>(m), y, acc, xq_out, amax_out,
-                                                                        gain, eps);
+    gemv_lds_kernel<WAVES, U, SRC, false, SWIGLU><<<grid, WAVES * 64, lds, s>>>(
+        p, gamma, n, k, kt, rbs, xsrc, amax_in, static_cast<int>(m), y, acc, xq_out, amax_out, gain, eps, pu, gamma_u);
   return hipGetLastError();
 }
 
@@ -657,6 +717,27 @@ hipError_t dispatch_lds(const void* packed, const float* gamma, int64_t n, int64
 }  // namespace
 
 bool gemv_fits_lds(int64_t m, int64_t k) { return lds_bytes(m, k_tiles(k)) <= kMaxLdsBytes; }
+
+// SwiGLU decode path: codes staged in LDS; an item's tiles are the gate row
+// block followed by the up row block, so U is chosen for 2 * kt tiles.
+hipError_t launch_gemv_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
+                              int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
+                              int32_t* acc, hipStream_t s) {
+  if (!gemv_fits_lds(m, k)) return hipErrorInvalidValue;
+  const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
+  const int64_t items = 2 * k_tiles(k);
+  if (items <= kWaves)
+    return launch_lds<kFromCodes, kWaves, 1, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr,
+                                                   nullptr, 0.0f, s, vec, packed_u, gamma_u);
+  if (items <= 2 * kWaves)
+    return launch_lds<kFromCodes, kWaves, 2, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr,
+                                                   nullptr, 0.0f, s, vec, packed_u, gamma_u);
+  if (items <= 4 * kWaves)
+    return launch_lds<kFromCodes, kWaves, 4, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr,
+                                                   nullptr, 0.0f, s, vec, packed_u, gamma_u);
+  return launch_lds<kFromCodes, kWaves, 8, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr,
+                                                 nullptr, 0.0f, s, vec, packed_u, gamma_u);
+}
 
 hipError_t launch_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {

@@ -215,6 +215,34 @@ int bitlinear_rmsnorm_quant_forward(const void *packed, const float *gamma, int6
 int bitlinear_quant_act_f32(const float *x, int64_t m, int64_t k,
                             int8_t *xq, float *x_absmax, void *stream);
 
+/*
+ * Gate and up projections of the feed-forward block with the SwiGLU between
+ * them fused into the epilogue ("BitNet 1-bit LLM Inference Framework",
+ * section "A Deep Look at the BitNet Architecture": the block's ffn is
+ * down_proj(silu(gate_proj(x)) * up_proj(x))).  For every token t and
+ * feature j:
+ *   y_g = acc_g * gamma_gate * a'[t] / 127,  y_u = acc_u * gamma_up * a'[t] / 127
+ *   h[t][j] = y_g * y_u / (1 + exp(-y_g))     (fp32)
+ * from one pass over the activation codes; the [m][2f] projections are never
+ * written.  The gate and up matrices are packed separately (each with its own
+ * gamma) or are the two halves of one packed [2f][k] matrix (f % 16 == 0:
+ * the up half starts bitlinear_packed_bytes(f, k) bytes in).
+ *   packed_gate, packed_up  in   from bitlinear_pack_weights(f, k), 16-byte aligned
+ *   gamma_gate, gamma_up    in   1 fp32 each (device)
+ *   xq, x_absmax            in   codes [m][k] and a' [m] of the block input
+ *   h                       out  fp32 [m][f], 4-byte aligned
+ *   acc_or_null             out  optional int32 [m][2f]: per token the f gate
+ *                                accumulators, then the f up accumulators
+ * 1 <= m <= 2^21.  Up to BITLINEAR_FORWARD_MAX_M tokens whose codes fit the
+ * decode path's on-chip budget use the streaming decode kernel; otherwise the
+ * matrix-core kernel, which needs k % 16 == 0 and 16-byte aligned codes
+ * (else BITLINEAR_E_UNSUPPORTED).
+ */
+int bitlinear_forward_swiglu(const void *packed_gate, const float *gamma_gate,
+                             const void *packed_up, const float *gamma_up,
+                             int64_t f, int64_t k, const int8_t *xq, const float *x_absmax, int64_t m,
+                             float *h, int32_t *acc_or_null, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,7 @@ BY_KEY = {w.key: w for w in WORKLOADS}
 
 ROLE_WEIGHT = 0
 ROLE_ACT = 1
+ROLE_GAIN = 2
 
 
 def seed_for(wl: Workload, layer: int, mat: int, role: int, extra: int = 0):

@@ -210,3 +210,24 @@ def test_norm_and_f32_quant_validation(blq):
     assert call(gain=A2) == E.BITLINEAR_E_ALIGN
     assert call(packed=A8) == E.BITLINEAR_E_ALIGN
     assert call(m=17) == E.BITLINEAR_E_UNSUPPORTED
+
+
+def test_swiglu_validation(blq):
+    fn = blq.load_library().bitlinear_forward_swiglu
+    E = blq
+    ok = dict(pg=A16, gg=A16, pu=A16, gu=A16, f=64, k=512, xq=A16, amax=A16, m=1, h=A16, acc=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return fn(a["pg"], a["gg"], a["pu"], a["gu"], a["f"], a["k"], a["xq"], a["amax"], a["m"], a["h"], a["acc"], None)
+
+    for key in ("pg", "gg", "pu", "gu", "xq", "amax", "h"):
+        assert call(**{key: None}) == E.BITLINEAR_E_NULL, key
+    assert call(f=0) == E.BITLINEAR_E_SHAPE
+    assert call(m=0) == E.BITLINEAR_E_SHAPE
+    assert call(k=(1 << 18) + 1) == E.BITLINEAR_E_SHAPE
+    assert call(pu=A8) == E.BITLINEAR_E_ALIGN
+    assert call(pg=A8) == E.BITLINEAR_E_ALIGN
+    assert call(gu=A2) == E.BITLINEAR_E_ALIGN
+    assert call(h=A2) == E.BITLINEAR_E_ALIGN
+    assert call(m=(1 << 21) + 1) == E.BITLINEAR_E_UNSUPPORTED

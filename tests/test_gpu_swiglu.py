@@ -1,0 +1,136 @@
+"""GPU parity of the gate and up projections with the SwiGLU fused into the
+epilogue ("BitNet 1-bit LLM Inference Framework", section "A Deep Look at the
+BitNet Architecture": down_proj(silu(gate_proj(x)) * up_proj(x))), against
+the CPU oracle on the same seeded inputs.
+
+Bar: the gate and up int32 accumulators bit-exact; h within 1e-5 relative of
+the oracle's silu(y_g) * y_u (binary64 from the oracle's fp32 y_g, y_u) and
+exactly 0 where the oracle's is 0.  Derivation of the bound: the GPU's y_g,
+y_u are each within ~2 fp32 roundings of the oracle's (acc exact, scale
+gamma * a' / 127 in fp32); h = silu(g) * u has relative condition number
+1 + g * (1 - sigmoid(g)) in g and 1 in u, plus one expf (~1 ulp) and three
+fp32 operations, so the relative error stays below ~(4 + |g|) * 1.2e-7,
+under 1e-5 for the |g| < 40 that these inputs produce (|y| of order 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import compare_y, host, log, to_dev, to_dev_bits, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def blq():
+    torch_mod()
+    import bitlinear_quant_act_amd as m
+    m.load_library()
+    return m
+
+
+def reference(blq, packed, gamma, f, k, xq_o, a_o):
+    codes = host(blq.bitlinear_unpack_weights(packed, f, k))
+    g = np.float32(host(gamma)[0])
+    return codes, g
+
+
+def check(blq, pg, gg, pu, gu, f, k, x, tag):
+    torch = torch_mod()
+    m = x.shape[0]
+    xq_d, a_d = blq.bitlinear_quant_act(to_dev_bits(x))
+    acc_d = torch.empty((m, 2 * f), dtype=torch.int32, device="cuda")
+    h_d = blq.bitlinear_forward_swiglu(pg, gg, pu, gu, f, k, xq_d, a_d, acc=acc_d)
+    xq_o, a_o = oracle.quant_act(x)
+    assert np.array_equal(host(xq_d), xq_o), tag
+    cg, g_g = reference(blq, pg, gg, f, k, xq_o, a_o)
+    cu, g_u = reference(blq, pu, gu, f, k, xq_o, a_o)
+    acc_g = oracle.contract(xq_o, cg)
+    acc_u = oracle.contract(xq_o, cu)
+    acc = host(acc_d)
+    assert np.array_equal(acc[:, :f], acc_g), tag
+    assert np.array_equal(acc[:, f:], acc_u), tag
+    h_o = oracle.swiglu(oracle.dequant(acc_g, g_g, a_o), oracle.dequant(acc_u, g_u, a_o))
+    compare_y(host(h_d), h_o, tag)
+    # without the optional accumulators: same h bits
+    h2 = blq.bitlinear_forward_swiglu(pg, gg, pu, gu, f, k, xq_d, a_d)
+    assert np.array_equal(host(h2), host(h_d)), tag
+    return h_d
+
+
+CASES = [(64, 256), (200, 1000), (2560, 2560), (6912, 2560), (1000, 4096), (96, 14336)]
+
+
+@pytest.mark.parametrize("f,k", CASES)
+@pytest.mark.parametrize("m", [1, 3, 16, 17, 64, 130])
+def test_swiglu_separate_matrices(blq, f, k, m):
+    tag = "swiglu f=%d k=%d m=%d" % (f, k, m)
+    if m > blq.BITLINEAR_FORWARD_MAX_M and k % 16:
+        pytest.skip("matrix-core path needs k % 16 == 0 (E_UNSUPPORTED is tested below)")
+    log("case", tag)
+    wg = synth.latent_weights((201, f, k), f, k)
+    wu = synth.latent_weights((202, f, k), f, k) * np.float32(1.5)   # a different gamma
+    x = synth.activations_bf16((203, m, k), m, k, 0.01)
+    pg, gg = blq.bitlinear_pack_weights(to_dev(wg))
+    pu, gu = blq.bitlinear_pack_weights(to_dev(wu))
+    check(blq, pg, gg, pu, gu, f, k, x, tag)
+
+
+@pytest.mark.parametrize("f,k,m", [(6912, 2560, 1), (6912, 2560, 512), (14336, 4096, 8), (1024, 4096, 64)])
+def test_swiglu_halves_of_one_matrix(blq, f, k, m):
+    """The gate+up matrix of the block, packed once as [2f][k] with one gamma."""
+    tag = "swiglu halves f=%d k=%d m=%d" % (f, k, m)
+    log("case", tag)
+    w = synth.latent_weights((204, f, k), 2 * f, k)
+    x = synth.activations_bf16((205, m, k), m, k, 0.005)
+    packed, gamma = blq.bitlinear_pack_weights(to_dev(w))
+    half = blq.bitlinear_packed_bytes(f, k)
+    assert 2 * half == blq.bitlinear_packed_bytes(2 * f, k)
+    check(blq, packed[:half], gamma, packed[half:], gamma, f, k, x, tag)
+
+
+def test_swiglu_feeds_the_down_projection(blq):
+    """h -> per-token quantisation from fp32 -> down projection, against the
+    oracle's chain on the same inputs."""
+    torch = torch_mod()
+    f, k, m = 6912, 2560, 4
+    w_gu = synth.latent_weights((206,), 2 * f, k)
+    w_dn = synth.latent_weights((207,), k, f)
+    x = synth.activations_bf16((208,), m, k)
+    p_gu, g_gu = blq.bitlinear_pack_weights(to_dev(w_gu))
+    p_dn, g_dn = blq.bitlinear_pack_weights(to_dev(w_dn))
+    half = blq.bitlinear_packed_bytes(f, k)
+    xq_d, a_d = blq.bitlinear_quant_act(to_dev_bits(x))
+    h_d = blq.bitlinear_forward_swiglu(p_gu[:half], g_gu, p_gu[half:], g_gu, f, k, xq_d, a_d)
+    hq_d, ha_d = blq.bitlinear_quant_act_f32(h_d)
+    acc_d = torch.empty((m, k), dtype=torch.int32, device="cuda")
+    y_d = blq.bitlinear_forward(p_dn, g_dn, k, f, hq_d, ha_d, acc=acc_d)
+    # oracle chain (the GPU's h is not an input to it)
+    xq_o, a_o = oracle.quant_act(x)
+    c_gu = host(blq.bitlinear_unpack_weights(p_gu, 2 * f, k))
+    gg = np.float32(host(g_gu)[0])
+    acc_gu = oracle.contract(xq_o, c_gu)
+    h_o = oracle.swiglu(oracle.dequant(acc_gu[:, :f], gg, a_o), oracle.dequant(acc_gu[:, f:], gg, a_o))
+    compare_y(host(h_d), h_o, "chain h")
+    # the requantisation of h: codes decided from values equal up to the h
+    # tolerance, so a code may differ by one at a rounding tie; compare the
+    # codes of the GPU's own h exactly, and the chain's y within the bound
+    hq_o, ha_o = oracle.quant_act_f32(host(h_d))
+    assert np.array_equal(host(hq_d), hq_o) and np.array_equal(host(ha_d), ha_o)
+    c_dn = host(blq.bitlinear_unpack_weights(p_dn, k, f))
+    acc_dn = oracle.contract(hq_o, c_dn)
+    assert np.array_equal(host(acc_d), acc_dn)
+    compare_y(host(y_d), oracle.dequant(acc_dn, np.float32(host(g_dn)[0]), ha_o), "chain y")
+
+
+def test_swiglu_unsupported_batched_k(blq):
+    f, k, m = 64, 1000, 40
+    w = synth.latent_weights((209,), f, k)
+    packed, gamma = blq.bitlinear_pack_weights(to_dev(w))
+    xq_d, a_d = blq.bitlinear_quant_act(to_dev_bits(synth.activations_bf16((210,), m, k)))
+    with pytest.raises(blq.BitlinearError) as e:
+        blq.bitlinear_forward_swiglu(packed, gamma, packed, gamma, f, k, xq_d, a_d)
+    assert e.value.status == blq.BITLINEAR_E_UNSUPPORTED
