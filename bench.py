@@ -70,7 +70,7 @@ def quant_bytes(m: int, k: int) -> int:
 
 class Mat:
     __slots__ = ("layer", "j", "n", "k", "packed", "gamma", "x", "xq", "amax", "y", "q_or", "g_or", "x_np",
-                 "gain", "gain_np")
+                 "gain", "gain_np", "name", "h")
 
 
 def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"):
@@ -99,6 +99,7 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             pack_bytes += 4 * mt.n * mt.k + (mt.n * mt.k + 3) // 4
             mat = Mat()
             mat.layer, mat.j, mat.n, mat.k = layer, j, mt.n, mt.k
+            mat.name = mt.name
             mat.packed, mat.gamma = packed, gamma
             x = synth.activations_bf16(synth.seed_for(wl, layer, j, synth.ROLE_ACT, extra=m), m, mt.k,
                                        wl.outlier_frac)
@@ -111,6 +112,9 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             mat.gain_np = (synth.norm_gain(synth.seed_for(wl, layer, j, synth.ROLE_GAIN), mt.k)
                            if variant == "rmsnorm" else None)
             mat.gain = None if mat.gain_np is None else torch.from_numpy(mat.gain_np).to(dev)
+            # SwiGLU variant: the gate+up BitLinear writes h [m][n/2] instead of y
+            mat.h = (torch.empty((m, mt.n // 2), dtype=torch.float32, device=dev)
+                     if variant == "swiglu" and mt.name == "gate_up" else None)
             if keep_oracle_codes:
                 mat.g_or = oracle_mod.gamma(w)
                 mat.q_or = oracle_mod.ternarize(w, mat.g_or)
@@ -129,6 +133,7 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
                 setattr(c, s, getattr(mat, s))
             c.packed = mat.packed.clone()
             c.x, c.xq, c.amax, c.y = mat.x.clone(), torch.empty_like(mat.xq), torch.empty_like(mat.amax), torch.empty_like(mat.y)
+            c.h = None if mat.h is None else torch.empty_like(mat.h)
             c.q_or = None
             cp.append(c)
         reps.append(cp)
@@ -149,8 +154,40 @@ def _fused(blq, mat, stream):
         blq.bitlinear_quant_forward(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
 
 
-def launch_step(blq, mats, m, stream, fused):
+def _swiglu(blq, mat, stream):
+    """gate+up BitLinear (the two halves of one packed matrix) with the SwiGLU
+    in its epilogue: h = silu(y_gate) * y_up."""
+    f = mat.n // 2
+    half = blq.bitlinear_packed_bytes(f, mat.k)
+    blq.bitlinear_forward_swiglu(mat.packed[:half], mat.gamma, mat.packed[half:], mat.gamma, f, mat.k, mat.xq,
+                                 mat.amax, h=mat.h, stream=stream)
+
+
+def launch_step_swiglu(blq, mats, m, stream, fused):
+    """Feed-forward block as the pages' transformer block computes it: the
+    down projection consumes its own layer's SwiGLU output h (quantised from
+    fp32); the attention projections run as in the plain step."""
+    fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
+    h = None
+    for mat in mats:
+        if mat.name == "gate_up":
+            _quant(blq, mat, stream)
+            _swiglu(blq, mat, stream)
+            h = mat.h
+        elif mat.name == "down":
+            blq.bitlinear_quant_act_f32(h, mat.xq, mat.amax, stream=stream)
+            fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+        elif fused:
+            _fused(blq, mat, stream)
+        else:
+            _quant(blq, mat, stream)
+            fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+
+
+def launch_step(blq, mats, m, stream, fused, variant="plain"):
     """One pass of the per-token path over every matrix, in layer order."""
+    if variant == "swiglu":
+        return launch_step_swiglu(blq, mats, m, stream, fused)
     if fused:
         for mat in mats:
             _fused(blq, mat, stream)
@@ -165,12 +202,21 @@ def launch_kernel_only(blq, mats, m, stream, which):
     """Launches of one kernel over every matrix ('quant', 'forward', 'fused')."""
     fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
     for mat in mats:
-        if which == "quant":
+        if which == "swiglu":
+            if mat.name == "gate_up":
+                _swiglu(blq, mat, stream)
+        elif which == "quant":
             _quant(blq, mat, stream)
         elif which == "forward":
             fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
         else:
             _fused(blq, mat, stream)
+
+
+def swiglu_bytes(m: int, f: int, k: int) -> int:
+    """Algorithmic bytes of one gate+up call with the SwiGLU epilogue: both
+    packed halves, int8 codes, a', two gammas, fp32 h [m][f]."""
+    return 2 * ((f * k + 3) // 4) + m * k + 4 * m + 8 + 4 * m * f
 
 
 def fused_bytes(m: int, n: int, k: int) -> int:
@@ -198,47 +244,68 @@ def time_graph(torch, stream, fn, replays):
     return e0.elapsed_time(e1) / replays
 
 
-def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s):
-    """The oracle (quant + contraction + dequant) over the workload's matrices
-    in layer order, on the host cores, until the sample is done or the time
-    budget is spent.  Also checks the GPU outputs of the same matrices."""
+def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
+    """The oracle (quant + contraction + dequant; with the SwiGLU variant the
+    gate+up -> SwiGLU -> fp32 quant -> down chain) over the workload's
+    matrices in layer order, on the host cores, until the sample is done or
+    the time budget is spent.  Also checks the GPU outputs of the same
+    matrices against the oracle's."""
     mats = [mt for mt in reps_mats if mt.q_or is not None]
     done_bytes = 0
     done_ops = 0
     t_total = 0.0
     worst = 0.0
+    chain_ok = True
     nmat = 0
+    h_prev = None
+    rows_used = m
     for mat in mats:
         t0 = time.perf_counter()
-        if mat.gain_np is not None:
-            xq, amax, _ = oracle_mod.rmsnorm_quant_act(mat.x_np, mat.gain_np)
+        rows = m if m * mat.n * mat.k <= 2e10 else max(1, int(2e10 // (mat.n * mat.k)))
+        if variant == "swiglu" and mat.name == "down":
+            if h_prev is None:
+                break
+            rows = h_prev.shape[0]  # the tokens the gate+up sample produced
+            xq, amax = oracle_mod.quant_act_f32(h_prev)
+        elif mat.gain_np is not None:
+            xq, amax, _ = oracle_mod.rmsnorm_quant_act(mat.x_np[:rows], mat.gain_np)
         else:
-            xq, amax = oracle_mod.quant_act(mat.x_np)
-        if m * mat.n * mat.k <= 2e10:
-            acc = oracle_mod.contract(xq, mat.q_or)
+            xq, amax = oracle_mod.quant_act(mat.x_np[:rows])
+        acc = oracle_mod.contract(xq, mat.q_or)
+        if variant == "swiglu" and mat.name == "gate_up":
+            f = mat.n // 2
+            y = oracle_mod.swiglu(oracle_mod.dequant(acc[:, :f], mat.g_or, amax),
+                                  oracle_mod.dequant(acc[:, f:], mat.g_or, amax))
+            h_prev = y
+        else:
             y = oracle_mod.dequant(acc, mat.g_or, amax)
-            t_total += time.perf_counter() - t0
-            rows_used = m
-        else:  # a bounded slice of tokens for the very large batched case
-            sl = max(1, int(2e10 // (mat.n * mat.k)))
-            acc = oracle_mod.contract(xq[:sl], mat.q_or)
-            y = oracle_mod.dequant(acc, mat.g_or, amax[:sl])
-            t_total += time.perf_counter() - t0
-            rows_used = sl
-        done_bytes += forward_bytes(rows_used, mat.n, mat.k)
-        done_ops += 2 * rows_used * mat.n * mat.k
-        yg = mat.y[:rows_used].cpu().numpy().astype(np.float64)
+        t_total += time.perf_counter() - t0
+        rows_used = rows
+        done_bytes += (swiglu_bytes(rows, mat.n // 2, mat.k) if variant == "swiglu" and mat.name == "gate_up"
+                       else forward_bytes(rows, mat.n, mat.k))
+        done_ops += 2 * rows * mat.n * mat.k
+        out = mat.h if mat.h is not None else mat.y
+        yg = out[:rows].cpu().numpy().astype(np.float64)
         yo = y.astype(np.float64)
-        nz = yo != 0
-        if (yg[~nz] != 0).any():
-            worst = float("inf")
-        if nz.any():
-            worst = max(worst, float((np.abs(yg[nz] - yo[nz]) / np.abs(yo[nz])).max()))
+        if variant == "swiglu" and mat.name == "down":
+            # the GPU quantises its own h, equal to the oracle's within 1e-5:
+            # a code may sit one step away where the oracle's h * s is within
+            # that bound of a rounding tie; allow those codes' weight per token
+            t = h_prev.astype(np.float64) * (127.0 / amax.astype(np.float64))[:, None]
+            ties = (np.abs(np.abs(t - np.floor(t)) - 0.5) <= 1e-5 * np.abs(t) + 1e-6).sum(axis=1)
+            allow = ties[:, None] * float(mat.g_or) * amax.astype(np.float64)[:, None] / 127.0
+            chain_ok &= bool(np.all(np.abs(yg - yo) <= 1e-5 * np.abs(yo) + allow * (1 + 1e-5) + 1e-30))
+        else:
+            nz = yo != 0
+            if (yg[~nz] != 0).any():
+                worst = float("inf")
+            if nz.any():
+                worst = max(worst, float((np.abs(yg[nz] - yo[nz]) / np.abs(yo[nz])).max()))
         nmat += 1
-        if t_total > budget_s:
+        if t_total > budget_s and not (variant == "swiglu" and mat.name == "gate_up"):
             break
     return {"seconds": t_total, "bytes": done_bytes, "ops": done_ops, "matrices": nmat, "rows": rows_used,
-            "max_rel_err": worst}
+            "max_rel_err": worst, "chain_ok": chain_ok}
 
 
 def main():
@@ -252,8 +319,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
-    ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm"),
-                    help="rmsnorm: every BitLinear normalises its input first (per-channel gains)")
+    ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu"),
+                    help="rmsnorm: every BitLinear normalises its input first (per-channel gains); "
+                         "swiglu: gate+up with the SwiGLU fused, down fed by its output")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bound)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -320,10 +388,18 @@ def main():
                 break
     reps, pack = setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, args.variant)
     norm = args.variant == "rmsnorm"
+    sw = args.variant == "swiglu"
     log("setup %.1f s" % (time.time() - t0))
 
     mats0 = reps[0]
-    step_bytes = sum(forward_bytes(m, mt.n, mt.k) for mt in mats0)
+    if sw and not any(mt.name == "gate_up" for mt in mats0):
+        print("bench.py: --variant swiglu needs a workload with a gate+up matrix", file=sys.stderr)
+        sys.exit(2)
+
+    def call_bytes(mt):
+        return swiglu_bytes(m, mt.n // 2, mt.k) if sw and mt.name == "gate_up" else forward_bytes(m, mt.n, mt.k)
+
+    step_bytes = sum(call_bytes(mt) for mt in mats0)
     step_quant_bytes = sum(quant_bytes(m, mt.k) for mt in mats0)
     step_ops = sum(2 * m * mt.n * mt.k for mt in mats0)
 
@@ -337,7 +413,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for mats in reps:
-                launch_step(blq, mats, m, torch.cuda.current_stream(), fused)
+                launch_step(blq, mats, m, torch.cuda.current_stream(), fused, args.variant)
         torch.cuda.synchronize()
     per_run = len(reps)
 
@@ -345,7 +421,7 @@ def main():
         if args.eager:
             with torch.cuda.stream(stream):
                 for mats in reps:
-                    launch_step(blq, mats, m, stream, fused)
+                    launch_step(blq, mats, m, stream, fused, args.variant)
         else:
             graph.replay()
 
@@ -376,19 +452,24 @@ def main():
             launch_kernel_only(blq, mats0, m, stream, "quant")
         torch.cuda.synchronize()
     replays = max(2, min(10, args.steps))
-    dom = "fused" if fused else "forward"
+    dom = "swiglu" if sw else "fused" if fused else "forward"
+    dom_mats = [mt for mt in mats0 if mt.name == "gate_up"] if sw else mats0
 
     def all_reps(which):
         return lambda st: [launch_kernel_only(blq, mats, m, st, which) for mats in reps]
 
     dom_ms = time_graph(torch, stream, all_reps(dom), replays) / len(reps)
-    nlaunch = len(mats0) * replays * len(reps)
-    fw_avg_us = dom_ms / len(mats0) * 1e3
+    nlaunch = len(dom_mats) * replays * len(reps)
+    fw_avg_us = dom_ms / len(dom_mats) * 1e3
     q_ms = time_graph(torch, stream, all_reps("quant"), replays) / len(reps)
     q_avg_us = q_ms / len(mats0) * 1e3
     per_call = fused_bytes if fused else forward_bytes
-    fw_bytes = sum(per_call(m, mt.n, mt.k) + (4 * mt.k if norm and fused else 0) for mt in mats0)
-    fw_ops = step_ops
+    if sw:
+        fw_bytes = sum(swiglu_bytes(m, mt.n // 2, mt.k) for mt in dom_mats)
+        fw_ops = sum(2 * m * mt.n * mt.k for mt in dom_mats)
+    else:
+        fw_bytes = sum(per_call(m, mt.n, mt.k) + (4 * mt.k if norm and fused else 0) for mt in mats0)
+        fw_ops = step_ops
     fw_ms = dom_ms
     if batched:
         value = step_ops / (ms_per_step * 1e-3) / 1e12
@@ -402,17 +483,24 @@ def main():
         achieved = fw_bytes / (fw_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = ("bitlinear_forward_batched (gemm_kernel)" if batched else
+    roof["kernel"] = ("bitlinear_forward_swiglu (%s, SwiGLU epilogue)" % ("gemm_dma_kernel" if batched else "gemv_lds_kernel")
+                      if sw else "bitlinear_forward_batched (gemm_kernel)" if batched else
                       ("bitlinear_rmsnorm_quant_forward (gemv_lds_kernel, RMSNorm + bf16 prologue)" if norm else
                        "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)") if fused else
                       "bitlinear_forward (gemv kernel)")
     roof["avg_launch_us"] = round(fw_avg_us, 3)
     roof["launches_timed"] = nlaunch
-    roof["per_launch"] = "mean over the workload's matrices of %s" % (
-        "2*M*N*K" if batched else ("ceil(N*K/4)+2*M*K+4K+4+4*M*N bytes" if norm else "ceil(N*K/4)+2*M*K+4+4*M*N bytes") if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
-    roof["timing"] = "HIP events around %d graph replays of the kernel's %d launches" % (replays, len(mats0) * len(reps))
+    if sw:
+        roof["per_launch"] = "mean over the gate+up matrices of %s" % (
+            "2*M*2F*K" if batched else "2*ceil(F*K/4)+M*K+4M+8+4*M*F bytes")
+    else:
+        roof["per_launch"] = "mean over the workload's matrices of %s" % (
+            "2*M*N*K" if batched else ("ceil(N*K/4)+2*M*K+4K+4+4*M*N bytes" if norm else "ceil(N*K/4)+2*M*K+4+4*M*N bytes")
+            if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
+    roof["timing"] = "HIP events around %d graph replays of the kernel's %d launches" % (replays, len(dom_mats) * len(reps))
     roof["traffic"] = None
-    prof = os.path.join(ROOT, "profiles", "counters_%s_m%d%s.json" % (wl.key, m, "_rmsnorm" if norm else ""))
+    prof = os.path.join(ROOT, "profiles", "counters_%s_m%d%s.json" % (
+        wl.key, m, "" if args.variant == "plain" else "_" + args.variant))
     if os.path.exists(prof):
         with open(prof) as f:
             c = json.load(f)
@@ -440,7 +528,10 @@ def main():
             "matrices_per_step": len(mats0),
             "shapes_kxn": ["%dx%d" % (mt.k, mt.n) for mt in wl.matrices],
             "variant": args.variant,
-            "entry_points": (("bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward") if fused else
+            "entry_points": ("gate+up: bitlinear_quant_act + bitlinear_forward_swiglu; down: bitlinear_quant_act_f32 + "
+                             + ("bitlinear_forward_batched" if batched else "bitlinear_forward") + "; others as plain"
+                             if sw else
+                             ("bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward") if fused else
                              ("bitlinear_rmsnorm_quant_act + " if norm else "bitlinear_quant_act + ") +
                              ("bitlinear_forward_batched" if batched else "bitlinear_forward")),
             "launch": ("hip graph, %d kernels per step" % ((1 if fused else 2) * len(mats0))
@@ -459,7 +550,7 @@ def main():
 
     if want_cpu:
         log("cpu baseline (oracle) ...")
-        cb = cpu_baseline(oracle_mod, mats0, m, wl, args.cpu_budget)
+        cb = cpu_baseline(oracle_mod, mats0, m, wl, args.cpu_budget, args.variant)
         cores = oracle_mod.num_threads()
         if batched:
             v = cb["ops"] / cb["seconds"] / 1e12
@@ -474,7 +565,9 @@ def main():
             "cpu": _cpu_model(),
         }
         out["parity_vs_oracle"] = {"matrices": cb["matrices"], "max_rel_err_y": cb["max_rel_err"],
-                                   "ok": bool(cb["max_rel_err"] <= 1e-5)}
+                                   "ok": bool(cb["max_rel_err"] <= 1e-5 and cb["chain_ok"])}
+        if sw:
+            out["parity_vs_oracle"]["down_chain_ok"] = cb["chain_ok"]
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

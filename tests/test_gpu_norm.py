@@ -21,7 +21,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import compare_y, host, log, to_dev, to_dev_bits, torch_mod
+from tests.gpu_util import check_gamma, compare_codes, compare_y, host, log, to_dev, to_dev_bits, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -128,15 +128,17 @@ def test_rmsnorm_quant_forward_parity(blq, n, k, m, gain_kind):
     a_d = torch.empty(m, dtype=torch.float32, device="cuda")
     y_d = blq.bitlinear_rmsnorm_quant_forward(packed, gamma, n, k, to_dev_bits(x), gain=None if gn is None else to_dev(gn),
                                               acc=acc_d, xq=xq_d, x_absmax=a_d)
-    g = np.float32(host(gamma)[0])
-    codes = host(blq.bitlinear_unpack_weights(packed, n, k))
-    assert np.array_equal(codes, oracle.ternarize(w, g)), tag   # same gamma: codes decided identically
+    g_or = oracle.gamma(w)
+    q_or = oracle.ternarize(w, g_or)
+    same = check_gamma(host(gamma)[0], g_or, tag)
+    bad_rows = compare_codes(host(blq.bitlinear_unpack_weights(packed, n, k)), q_or, w, g_or, same, tag)
+    keep = np.setdiff1d(np.arange(n), bad_rows)
     xq_o, a_o, _ = oracle.rmsnorm_quant_act(x, gn)
     assert np.array_equal(host(xq_d), xq_o), tag
     assert_within_ulps(host(a_d), a_o, 1, tag)
-    acc_o = oracle.contract(xq_o, codes)
-    assert np.array_equal(host(acc_d), acc_o), tag
-    compare_y(host(y_d), oracle.dequant(acc_o, g, host(a_d)), tag)
+    acc_o = oracle.contract(xq_o, q_or)
+    assert np.array_equal(host(acc_d)[:, keep], acc_o[:, keep]), tag
+    compare_y(host(y_d)[:, keep], oracle.dequant(acc_o, g_or, a_o)[:, keep], tag)
     # the fused prologue computes exactly the standalone kernel's codes and a'
     xq_s, a_s = blq.bitlinear_rmsnorm_quant_act(to_dev_bits(x), gain=None if gn is None else to_dev(gn))
     assert np.array_equal(host(xq_s), host(xq_d)) and np.array_equal(host(a_s), host(a_d)), tag
