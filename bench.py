@@ -110,7 +110,7 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             mat.amax = torch.empty(m, dtype=torch.float32, device=dev)
             mat.y = torch.empty((m, mt.n), dtype=torch.float32, device=dev)
             mat.gain_np = (synth.norm_gain(synth.seed_for(wl, layer, j, synth.ROLE_GAIN), mt.k)
-                           if variant == "rmsnorm" else None)
+                           if variant == "rmsnorm" or (variant == "swiglu" and mt.name == "gate_up") else None)
             mat.gain = None if mat.gain_np is None else torch.from_numpy(mat.gain_np).to(dev)
             # SwiGLU variant: the gate+up BitLinear writes h [m][n/2] instead of y
             mat.h = (torch.empty((m, mt.n // 2), dtype=torch.float32, device=dev)
@@ -154,29 +154,40 @@ def _fused(blq, mat, stream):
         blq.bitlinear_quant_forward(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
 
 
-def _swiglu(blq, mat, stream):
+def _swiglu(blq, mat, stream, fused):
     """gate+up BitLinear (the two halves of one packed matrix) with the SwiGLU
-    in its epilogue: h = silu(y_gate) * y_up."""
+    in its epilogue: h = silu(y_gate) * y_up.  fused: the block input's
+    RMSNorm and quantisation run in the same launch."""
     f = mat.n // 2
     half = blq.bitlinear_packed_bytes(f, mat.k)
-    blq.bitlinear_forward_swiglu(mat.packed[:half], mat.gamma, mat.packed[half:], mat.gamma, f, mat.k, mat.xq,
-                                 mat.amax, h=mat.h, stream=stream)
+    if fused:
+        blq.bitlinear_rmsnorm_quant_forward_swiglu(mat.packed[:half], mat.gamma, mat.packed[half:], mat.gamma, f,
+                                                   mat.k, mat.x, mat.gain, h=mat.h, stream=stream)
+    else:
+        blq.bitlinear_forward_swiglu(mat.packed[:half], mat.gamma, mat.packed[half:], mat.gamma, f, mat.k, mat.xq,
+                                     mat.amax, h=mat.h, stream=stream)
 
 
 def launch_step_swiglu(blq, mats, m, stream, fused):
-    """Feed-forward block as the pages' transformer block computes it: the
-    down projection consumes its own layer's SwiGLU output h (quantised from
-    fp32); the attention projections run as in the plain step."""
+    """Feed-forward block as one unit, as the pages' transformer block
+    computes it: RMSNorm of the block input, gate+up with the SwiGLU fused,
+    and the down projection fed by its own layer's h (quantised from fp32).
+    With one token each half is one launch.  The attention projections run as
+    in the plain step."""
     fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
     h = None
     for mat in mats:
         if mat.name == "gate_up":
-            _quant(blq, mat, stream)
-            _swiglu(blq, mat, stream)
+            if not fused:
+                _quant(blq, mat, stream)
+            _swiglu(blq, mat, stream, fused)
             h = mat.h
         elif mat.name == "down":
-            blq.bitlinear_quant_act_f32(h, mat.xq, mat.amax, stream=stream)
-            fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+            if fused:
+                blq.bitlinear_quant_forward_f32(mat.packed, mat.gamma, mat.n, mat.k, h, y=mat.y, stream=stream)
+            else:
+                blq.bitlinear_quant_act_f32(h, mat.xq, mat.amax, stream=stream)
+                fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
         elif fused:
             _fused(blq, mat, stream)
         else:
@@ -198,13 +209,14 @@ def launch_step(blq, mats, m, stream, fused, variant="plain"):
         fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
 
 
-def launch_kernel_only(blq, mats, m, stream, which):
-    """Launches of one kernel over every matrix ('quant', 'forward', 'fused')."""
+def launch_kernel_only(blq, mats, m, stream, which, fused=False):
+    """Launches of one kernel over every matrix ('quant', 'forward', 'fused',
+    'swiglu': the gate+up launches of the SwiGLU variant)."""
     fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
     for mat in mats:
         if which == "swiglu":
             if mat.name == "gate_up":
-                _swiglu(blq, mat, stream)
+                _swiglu(blq, mat, stream, fused)
         elif which == "quant":
             _quant(blq, mat, stream)
         elif which == "forward":
@@ -321,7 +333,8 @@ def main():
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
     ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu"),
                     help="rmsnorm: every BitLinear normalises its input first (per-channel gains); "
-                         "swiglu: gate+up with the SwiGLU fused, down fed by its output")
+                         "swiglu: the feed-forward block as a unit (RMSNorm, gate+up with the SwiGLU fused, "
+                         "down fed by h)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bound)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -397,7 +410,9 @@ def main():
         sys.exit(2)
 
     def call_bytes(mt):
-        return swiglu_bytes(m, mt.n // 2, mt.k) if sw and mt.name == "gate_up" else forward_bytes(m, mt.n, mt.k)
+        if sw and mt.name == "gate_up":
+            return swiglu_bytes(m, mt.n // 2, mt.k)
+        return forward_bytes(m, mt.n, mt.k)
 
     step_bytes = sum(call_bytes(mt) for mt in mats0)
     step_quant_bytes = sum(quant_bytes(m, mt.k) for mt in mats0)
@@ -456,7 +471,7 @@ def main():
     dom_mats = [mt for mt in mats0 if mt.name == "gate_up"] if sw else mats0
 
     def all_reps(which):
-        return lambda st: [launch_kernel_only(blq, mats, m, st, which) for mats in reps]
+        return lambda st: [launch_kernel_only(blq, mats, m, st, which, fused) for mats in reps]
 
     dom_ms = time_graph(torch, stream, all_reps(dom), replays) / len(reps)
     nlaunch = len(dom_mats) * replays * len(reps)
@@ -465,7 +480,9 @@ def main():
     q_avg_us = q_ms / len(mats0) * 1e3
     per_call = fused_bytes if fused else forward_bytes
     if sw:
-        fw_bytes = sum(swiglu_bytes(m, mt.n // 2, mt.k) for mt in dom_mats)
+        # fused: bf16 input and gains instead of codes and a'
+        fw_bytes = sum(swiglu_bytes(m, mt.n // 2, mt.k) + ((m * mt.k + 4 * mt.k - 4 * m) if fused else 0)
+                       for mt in dom_mats)
         fw_ops = sum(2 * m * mt.n * mt.k for mt in dom_mats)
     else:
         fw_bytes = sum(per_call(m, mt.n, mt.k) + (4 * mt.k if norm and fused else 0) for mt in mats0)
@@ -483,7 +500,9 @@ def main():
         achieved = fw_bytes / (fw_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = ("bitlinear_forward_swiglu (%s, SwiGLU epilogue)" % ("gemm_dma_kernel" if batched else "gemv_lds_kernel")
+    roof["kernel"] = (("bitlinear_rmsnorm_quant_forward_swiglu (gemv_lds_kernel, RMSNorm prologue, SwiGLU epilogue)"
+                       if fused else "bitlinear_forward_swiglu (%s, SwiGLU epilogue)" % (
+                           "gemm_dma_kernel" if batched else "gemv_lds_kernel"))
                       if sw else "bitlinear_forward_batched (gemm_kernel)" if batched else
                       ("bitlinear_rmsnorm_quant_forward (gemv_lds_kernel, RMSNorm + bf16 prologue)" if norm else
                        "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)") if fused else
@@ -492,7 +511,8 @@ def main():
     roof["launches_timed"] = nlaunch
     if sw:
         roof["per_launch"] = "mean over the gate+up matrices of %s" % (
-            "2*M*2F*K" if batched else "2*ceil(F*K/4)+M*K+4M+8+4*M*F bytes")
+            "2*M*2F*K" if batched else "2*ceil(F*K/4)+2*M*K+4K+8+4*M*F bytes" if fused else
+            "2*ceil(F*K/4)+M*K+4M+8+4*M*F bytes")
     else:
         roof["per_launch"] = "mean over the workload's matrices of %s" % (
             "2*M*N*K" if batched else ("ceil(N*K/4)+2*M*K+4K+4+4*M*N bytes" if norm else "ceil(N*K/4)+2*M*K+4+4*M*N bytes")
@@ -528,8 +548,11 @@ def main():
             "matrices_per_step": len(mats0),
             "shapes_kxn": ["%dx%d" % (mt.k, mt.n) for mt in wl.matrices],
             "variant": args.variant,
-            "entry_points": ("gate+up: bitlinear_quant_act + bitlinear_forward_swiglu; down: bitlinear_quant_act_f32 + "
-                             + ("bitlinear_forward_batched" if batched else "bitlinear_forward") + "; others as plain"
+            "entry_points": (("gate+up: bitlinear_rmsnorm_quant_forward_swiglu; down: bitlinear_quant_forward_f32; "
+                              "others: bitlinear_quant_forward") if sw and fused else
+                             "gate+up: bitlinear_rmsnorm_quant_act + bitlinear_forward_swiglu; down: "
+                             "bitlinear_quant_act_f32 + " + ("bitlinear_forward_batched" if batched else
+                                                             "bitlinear_forward") + "; others as plain"
                              if sw else
                              ("bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward") if fused else
                              ("bitlinear_rmsnorm_quant_act + " if norm else "bitlinear_quant_act + ") +

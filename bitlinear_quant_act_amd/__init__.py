@@ -91,6 +91,11 @@ def load_library(path: str = LIB_PATH):
     lib.bitlinear_rmsnorm_quant_forward.restype = _ct.c_int
     lib.bitlinear_quant_act_f32.argtypes = [_p, _i64, _i64, _p, _p, _p]
     lib.bitlinear_quant_act_f32.restype = _ct.c_int
+    lib.bitlinear_rmsnorm_quant_forward_swiglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p, _ct.c_float, _i64,
+                                                           _p, _p, _p, _p, _p]
+    lib.bitlinear_rmsnorm_quant_forward_swiglu.restype = _ct.c_int
+    lib.bitlinear_quant_forward_f32.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
+    lib.bitlinear_quant_forward_f32.restype = _ct.c_int
     lib.bitlinear_forward_swiglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
     lib.bitlinear_forward_swiglu.restype = _ct.c_int
     for name in ("bitlinear_forward", "bitlinear_forward_batched"):
@@ -349,6 +354,58 @@ def bitlinear_rmsnorm_quant_forward(packed, gamma, n: int, k: int, x, gain=None,
         None if x_absmax is None else _dev(x_absmax, "x_absmax", (_torch.float32,), m),
         _stream_handle(stream))
     _check(rc, "bitlinear_rmsnorm_quant_forward")
+    return y
+
+
+def bitlinear_rmsnorm_quant_forward_swiglu(packed_gate, gamma_gate, packed_up, gamma_up, f: int, k: int, x,
+                                           gain=None, eps: float = RMS_EPS, h=None, acc=None, xq=None,
+                                           x_absmax=None, stream=None):
+    """RMSNorm + quantisation + gate/up projections + SwiGLU in one decode
+    launch (m <= 16 within the on-chip budget).  Returns h fp32 [m][f]."""
+    lib = load_library()
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m][k]")
+    m = x.shape[0]
+    nb = bitlinear_packed_bytes(f, k)
+    for name, pk in (("packed_gate", packed_gate), ("packed_up", packed_up)):
+        if pk.numel() * pk.element_size() < nb:
+            raise BitlinearError(BITLINEAR_E_SIZE, "bitlinear_rmsnorm_quant_forward_swiglu (%s)" % name)
+    if h is None:
+        h = _torch.empty((m, f), dtype=_torch.float32, device=x.device)
+    rc = lib.bitlinear_rmsnorm_quant_forward_swiglu(
+        _dev(packed_gate, "packed_gate", (_torch.uint8,)), _dev(gamma_gate, "gamma_gate", (_torch.float32,), 1),
+        _dev(packed_up, "packed_up", (_torch.uint8,)), _dev(gamma_up, "gamma_up", (_torch.float32,), 1), f, k,
+        _dev(x, "x", (_torch.bfloat16, _torch.int16, _torch.uint16)),
+        None if gain is None else _dev(gain, "gain", (_torch.float32,), k), float(eps), m,
+        _dev(h, "h", (_torch.float32,), m * f),
+        None if acc is None else _dev(acc, "acc", (_torch.int32,), 2 * m * f),
+        None if xq is None else _dev(xq, "xq", (_torch.int8,), m * k),
+        None if x_absmax is None else _dev(x_absmax, "x_absmax", (_torch.float32,), m),
+        _stream_handle(stream))
+    _check(rc, "bitlinear_rmsnorm_quant_forward_swiglu")
+    return h
+
+
+def bitlinear_quant_forward_f32(packed, gamma, n: int, k: int, x, y=None, acc=None, xq=None, x_absmax=None,
+                                stream=None):
+    """Quantisation of fp32 activations [m][k] fused into the decode forward.
+    Returns y fp32 [m][n]."""
+    lib = load_library()
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m][k]")
+    m = x.shape[0]
+    if packed.numel() * packed.element_size() < bitlinear_packed_bytes(n, k):
+        raise BitlinearError(BITLINEAR_E_SIZE, "bitlinear_quant_forward_f32")
+    if y is None:
+        y = _torch.empty((m, n), dtype=_torch.float32, device=x.device)
+    rc = lib.bitlinear_quant_forward_f32(
+        _dev(packed, "packed", (_torch.uint8,)), _dev(gamma, "gamma", (_torch.float32,), 1), n, k,
+        _dev(x, "x", (_torch.float32,)), m, _dev(y, "y", (_torch.float32,), m * n),
+        None if acc is None else _dev(acc, "acc", (_torch.int32,), m * n),
+        None if xq is None else _dev(xq, "xq", (_torch.int8,), m * k),
+        None if x_absmax is None else _dev(x_absmax, "x_absmax", (_torch.float32,), m),
+        _stream_handle(stream))
+    _check(rc, "bitlinear_quant_forward_f32")
     return y
 
 

@@ -177,4 +177,39 @@ int bitlinear_forward_swiglu(const void* packed_gate, const float* gamma_gate, c
                                                  h, acc_or_null, st));
 }
 
+int bitlinear_rmsnorm_quant_forward_swiglu(const void* packed_gate, const float* gamma_gate, const void* packed_up,
+                                           const float* gamma_up, int64_t f, int64_t k, const uint16_t* x,
+                                           const float* gain_or_null, float eps, int64_t m, float* h,
+                                           int32_t* acc_or_null, int8_t* xq_or_null, float* x_absmax_or_null,
+                                           void* stream) {
+  if (!packed_gate || !gamma_gate || !packed_up || !gamma_up || !x || !h) return BITLINEAR_E_NULL;
+  if (int rc = check_nk(f, k)) return rc;
+  if (m < 1 || m > kMaxRows) return BITLINEAR_E_SHAPE;
+  if ((xq_or_null == nullptr) != (x_absmax_or_null == nullptr)) return BITLINEAR_E_NULL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return BITLINEAR_E_VALUE;
+  if (!aligned(packed_gate, 16) || !aligned(packed_up, 16) || !aligned(gamma_gate, 4) || !aligned(gamma_up, 4) ||
+      !aligned(x, 2) || !aligned(h, 4) || (gain_or_null && !aligned(gain_or_null, 4)) ||
+      (acc_or_null && !aligned(acc_or_null, 4)) || (x_absmax_or_null && !aligned(x_absmax_or_null, 4)))
+    return BITLINEAR_E_ALIGN;
+  if (m > BITLINEAR_FORWARD_MAX_M || !bitlinear::gemv_fits_lds(m, k)) return BITLINEAR_E_UNSUPPORTED;
+  return status_of(bitlinear::launch_norm_quant_gemv_swiglu(packed_gate, gamma_gate, packed_up, gamma_up, f, k, x,
+                                                            gain_or_null, eps, m, h, acc_or_null, xq_or_null,
+                                                            x_absmax_or_null, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quant_forward_f32(const void* packed, const float* gamma, int64_t n, int64_t k, const float* x, int64_t m,
+                                float* y, int32_t* acc_or_null, int8_t* xq_or_null, float* x_absmax_or_null,
+                                void* stream) {
+  if (!packed || !gamma || !x || !y) return BITLINEAR_E_NULL;
+  if (int rc = check_nk(n, k)) return rc;
+  if (m < 1 || m > kMaxRows) return BITLINEAR_E_SHAPE;
+  if ((xq_or_null == nullptr) != (x_absmax_or_null == nullptr)) return BITLINEAR_E_NULL;
+  if (!aligned(packed, 16) || !aligned(gamma, 4) || !aligned(x, 4) || !aligned(y, 4) ||
+      (acc_or_null && !aligned(acc_or_null, 4)) || (x_absmax_or_null && !aligned(x_absmax_or_null, 4)))
+    return BITLINEAR_E_ALIGN;
+  if (m > BITLINEAR_FORWARD_MAX_M || !bitlinear::gemv_fits_lds(m, k)) return BITLINEAR_E_UNSUPPORTED;
+  return status_of(bitlinear::launch_quant_gemv_f32(packed, gamma, n, k, x, m, y, acc_or_null, xq_or_null,
+                                                    x_absmax_or_null, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

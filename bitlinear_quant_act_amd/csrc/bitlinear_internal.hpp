@@ -36,6 +36,48 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Wave-wide reductions on DPP row operations (register moves, no trip through
+// the LDS unit): an inclusive scan inside each row of 16 lanes (row_shr 1, 2,
+// 4, 8), then the row totals carried across rows (row_bcast 15 into rows 1
+// and 3, row_bcast 31 into rows 2 and 3); lane 63 ends with the result, which
+// is returned to every lane.  Lanes without a source keep the identity.
+#define BITLINEAR_DPP_MAX(V, CTRL, ROWS) \
+  V = max(V, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(V), static_cast<int>(V), CTRL, ROWS, 0xf, false)))
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  BITLINEAR_DPP_MAX(v, 0x111, 0xf);  // row_shr:1
+  BITLINEAR_DPP_MAX(v, 0x112, 0xf);  // row_shr:2
+  BITLINEAR_DPP_MAX(v, 0x114, 0xf);  // row_shr:4
+  BITLINEAR_DPP_MAX(v, 0x118, 0xf);  // row_shr:8
+  BITLINEAR_DPP_MAX(v, 0x142, 0xa);  // row_bcast:15 into rows 1, 3
+  BITLINEAR_DPP_MAX(v, 0x143, 0xc);  // row_bcast:31 into rows 2, 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+#undef BITLINEAR_DPP_MAX
+
+// one scan step of a 64-bit value: lanes without a source add 0
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, ROWS, 0xf, false);
+  return v + __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                                        static_cast<uint32_t>(lo)));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = dpp_add_f64<0x111, 0xf>(v);
+  v = dpp_add_f64<0x112, 0xf>(v);
+  v = dpp_add_f64<0x114, 0xf>(v);
+  v = dpp_add_f64<0x118, 0xf>(v);
+  v = dpp_add_f64<0x142, 0xa>(v);
+  v = dpp_add_f64<0x143, 0xc>(v);
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), 63));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), 63));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
 // 16-byte streaming load of packed weights: read once, so marked
 // non-temporal to keep them from displacing reused data in the caches.
 __device__ __forceinline__ uint4 load_weights_nt(const uint4* p) {
@@ -65,6 +107,12 @@ hipError_t launch_norm_quant_gemv(const void* packed, const float* gamma, int64_
 hipError_t launch_gemv_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
                               int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
                               int32_t* acc, hipStream_t s);
+hipError_t launch_norm_quant_gemv_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u,
+                                         const float* gamma_u, int64_t f, int64_t k, const uint16_t* x,
+                                         const float* gain, float eps, int64_t m, float* h, int32_t* acc,
+                                         int8_t* xq_out, float* amax_out, hipStream_t s);
+hipError_t launch_quant_gemv_f32(const void* packed, const float* gamma, int64_t n, int64_t k, const float* x,
+                                 int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s);
 bool gemm_swiglu_supported(int64_t k, const int8_t* xq);
 hipError_t launch_gemm_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
                               int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,

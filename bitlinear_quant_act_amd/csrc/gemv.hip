@@ -27,7 +27,10 @@
 //   * kFromBf16Norm: RMSNorm fused as well ("bit_linear.py" listing: the
 //     BitLinear input passes nn.RMSNorm first): codes of v = x * gain, and
 //     a' = max|v| / sqrt(mean x^2 + eps) (the per-token factor cancels in
-//     the codes), bit-identical to bitlinear_rmsnorm_quant_act.
+//     the codes), equal to bitlinear_rmsnorm_quant_act's (a' within one ulp:
+//     the mean square is an fp64 sum in another order);
+//   * kFromF32: computed from fp32 activations, bit-identical to
+//     bitlinear_quant_act_f32.
 // The activations are requested before the first weight tiles: vector-memory
 // results are waited for in issue order, so the prologue then runs while the
 // weights are still in flight.
@@ -70,7 +73,7 @@ constexpr int kWaves = BITLINEAR_GEMV_WAVES;                        // waves per
 constexpr int kMaxLdsBytes = 65536 - kWaves * 4 * 64 * 4 - 512;
 constexpr int kCachedChunks = 4;  // activation chunks per thread held in registers by the prologue
 
-enum Source { kFromCodes = 0, kFromBf16 = 1, kFromBf16Norm = 2 };
+enum Source { kFromCodes = 0, kFromBf16 = 1, kFromBf16Norm = 2, kFromF32 = 3 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -102,11 +105,7 @@ __device__ __forceinline__ unsigned chunk_absmax(const uint4& v) {
   return mx;
 }
 
-__device__ __forceinline__ unsigned wave_max(unsigned v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));
-  return v;
-}
+__device__ __forceinline__ unsigned wave_max(unsigned v) { return wave_max_u32(v); }
 
 // LDS row pitch of the staged codes: the padded k extent plus 16 bytes, so
 // consecutive token rows start 4 banks apart.
@@ -308,80 +307,122 @@ __device__ __forceinline__ uint32_t norm_code(float v, float s) {
   return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
 }
 
-__device__ void stage_bf16_norm(int8_t* xs, int pitch, float* amax_s, float* quant_s, unsigned* max_s, double* ss_s,
-                                const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x,
-                                const float* __restrict__ gain, float eps, int m, int64_t k, int kpad, bool vec,
-                                int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
+__device__ __forceinline__ double wave_sum_d(double v) { return wave_sum_f64(v); }
+
+// a' and the quantisation scale of one token from max|v| and the sum of x^2
+__device__ __forceinline__ void norm_scales(unsigned mx, double ss, int64_t k, float eps, float* amax_dst,
+                                            float* quant_dst) {
+  const float av = __uint_as_float(mx);
+  const double r = 1.0 / sqrt(ss / static_cast<double>(k) + static_cast<double>(eps));
+  const float ap = static_cast<float>(static_cast<double>(av) * r);
+  *amax_dst = av > 0.0f ? fmaxf(ap, 1e-8f) : 1e-8f;
+  *quant_dst = av > 0.0f ? 127.0f / av : 0.0f;  // all-zero v: every code is 0
+}
+
+// Single token, vector path: wave shuffles and one LDS slot per wave for both
+// reductions (no atomics, a fixed summation order).
+template <int WAVES>
+__device__ void stage_bf16_norm_single(int8_t* xs, float* amax_s, float* quant_s, unsigned* wmax_s, double* wss_s,
+                                       const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x,
+                                       const float* __restrict__ gain, float eps, int64_t k, int kpad,
+                                       int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
   const int nthreads = blockDim.x;
   const bool write_out = xq_out != nullptr && blockIdx.x == 0;
-  if (threadIdx.x < m) {
-    max_s[threadIdx.x] = 0u;
-    ss_s[threadIdx.x] = 0.0;
-  }
-  lds_barrier();
-  if (vec) {  // k % 8 == 0, x and gain 16-byte aligned: chunks of 8 values
-    const int cpr = static_cast<int>(k / 8);
-    const int total = m * cpr;
-    int cur_t = -1;
-    unsigned cur = 0;
-    double cur_ss = 0.0;
-    int j = 0;
-    for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
-      const int t = c / cpr, cc = c - t * cpr;
-      if (t != cur_t) {
-        if (cur_t >= 0) {
-          atomicMax(&max_s[cur_t], cur);
-          atomicAdd(&ss_s[cur_t], cur_ss);
-        }
-        cur_t = t;
-        cur = 0;
-        cur_ss = 0.0;
-      }
-      float v[8], xv[8];
-      norm_values(j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
-                  gain ? gain + cc * 8 : nullptr, v, xv);
+  const int total = static_cast<int>(k / 8);
+  unsigned mx = 0;
+  double ss = 0.0;
+  int j = 0;
+  for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+    float v[8], xv[8];
+    norm_values(j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
+                gain ? gain + c * 8 : nullptr, v, xv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        cur_ss += static_cast<double>(xv[i]) * static_cast<double>(xv[i]);
-        cur = max(cur, __float_as_uint(fabsf(v[i])));
-      }
-    }
-    if (cur_t >= 0) {
-      atomicMax(&max_s[cur_t], cur);
-      atomicAdd(&ss_s[cur_t], cur_ss);
-    }
-  } else {
-    for (int t = 0; t < m; ++t) {
-      unsigned cur = 0;
-      double cur_ss = 0.0;
-      for (int64_t i = threadIdx.x; i < k; i += nthreads) {
-        const float xv = __uint_as_float(static_cast<uint32_t>(x[t * k + i]) << 16);
-        const float v = gain ? xv * gain[i] : xv;
-        cur_ss += static_cast<double>(xv) * static_cast<double>(xv);
-        cur = max(cur, __float_as_uint(fabsf(v)));
-      }
-      atomicMax(&max_s[t], cur);
-      atomicAdd(&ss_s[t], cur_ss);
+    for (int i = 0; i < 8; ++i) {
+      ss += static_cast<double>(xv[i]) * static_cast<double>(xv[i]);
+      mx = max(mx, __float_as_uint(fabsf(v[i])));
     }
   }
-  lds_barrier();
-  if (threadIdx.x < m) {
-    const float av = __uint_as_float(max_s[threadIdx.x]);
-    const double r = 1.0 / sqrt(ss_s[threadIdx.x] / static_cast<double>(k) + static_cast<double>(eps));
-    const float ap = static_cast<float>(static_cast<double>(av) * r);
-    amax_s[threadIdx.x] = av > 0.0f ? fmaxf(ap, 1e-8f) : 1e-8f;
-    quant_s[threadIdx.x] = av > 0.0f ? 127.0f / av : 0.0f;  // all-zero v: every code is 0
+  mx = wave_max(mx);
+  ss = wave_sum_d(ss);
+  if ((threadIdx.x & 63) == 0) {
+    wmax_s[threadIdx.x >> 6] = mx;
+    wss_s[threadIdx.x >> 6] = ss;
   }
   lds_barrier();
+  unsigned mall = wmax_s[0];
+  double sall = wss_s[0];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) {
+    mall = max(mall, wmax_s[w]);
+    sall += wss_s[w];
+  }
+  float ap, qs;
+  norm_scales(mall, sall, k, eps, &ap, &qs);
+  if (threadIdx.x == 0) {
+    amax_s[0] = ap;
+    quant_s[0] = qs;
+    if (write_out) amax_out[0] = ap;
+  }
+  j = 0;
+  for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+    float v[8], xv[8];
+    norm_values(j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
+                gain ? gain + c * 8 : nullptr, v, xv);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= norm_code(v[i], qs) << (8 * i);
+      hi |= norm_code(v[4 + i], qs) << (8 * i);
+    }
+    const uint2 q = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(xs + c * 8) = q;
+    if (write_out) *reinterpret_cast<uint2*>(xq_out + c * 8) = q;
+  }
+  for (int c = total + threadIdx.x; c < kpad / 8; c += nthreads) *reinterpret_cast<uint2*>(xs + c * 8) = make_uint2(0, 0);
+}
+
+// Any token count: token t belongs to wave t % WAVES, whose lanes reduce it
+// with shuffles (a fixed order, no atomics).  vec: k % 8 == 0, x and gain
+// 16-byte aligned.
+template <int WAVES>
+__device__ void stage_bf16_norm(int8_t* xs, int pitch, float* amax_s, float* quant_s, const uint16_t* __restrict__ x,
+                                const float* __restrict__ gain, float eps, int m, int64_t k, int kpad, bool vec,
+                                int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
+  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < m; t += WAVES) {
+    const uint16_t* xr = x + t * k;
+    unsigned mx = 0;
+    double ss = 0.0;
+    if (vec) {
+      for (int cc = lane; cc < k / 8; cc += 64) {
+        float v[8], xv[8];
+        norm_values(*reinterpret_cast<const uint4*>(xr + cc * 8), gain ? gain + cc * 8 : nullptr, v, xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ss += static_cast<double>(xv[i]) * static_cast<double>(xv[i]);
+          mx = max(mx, __float_as_uint(fabsf(v[i])));
+        }
+      }
+    } else {
+      for (int64_t i = lane; i < k; i += 64) {
+        const float xv = __uint_as_float(static_cast<uint32_t>(xr[i]) << 16);
+        ss += static_cast<double>(xv) * static_cast<double>(xv);
+        mx = max(mx, __float_as_uint(fabsf(gain ? xv * gain[i] : xv)));
+      }
+    }
+    mx = wave_max(mx);
+    ss = wave_sum_d(ss);
+    if (lane == 0) norm_scales(mx, ss, k, eps, &amax_s[t], &quant_s[t]);
+  }
+  lds_barrier();
+  const int nthreads = blockDim.x;
   if (vec) {
     const int cpr = static_cast<int>(k / 8);
-    const int total = m * cpr;
-    int j = 0;
-    for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+    for (int c = threadIdx.x; c < m * cpr; c += nthreads) {
       const int t = c / cpr, cc = c - t * cpr;
       float v[8], xv[8];
-      norm_values(j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
-                  gain ? gain + cc * 8 : nullptr, v, xv);
+      norm_values(*reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8), gain ? gain + cc * 8 : nullptr, v, xv);
       const float qs = quant_s[t];
       uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -411,6 +452,83 @@ __device__ void stage_bf16_norm(int8_t* xs, int pitch, float* amax_s, float* qua
     }
   }
   if (write_out && threadIdx.x < m) amax_out[threadIdx.x] = amax_s[threadIdx.x];
+}
+
+// fp32 activations, any token count: per-token max|x| (LDS atomics on the bit
+// patterns), a' = max(., 1e-8), codes clamp(rint(x * (127 / a'))).  vec:
+// k % 4 == 0 and x 16-byte aligned (chunks of 4 values).
+__device__ void stage_f32(int8_t* xs, int pitch, float* amax_s, unsigned* max_s, const uint4 (&cache)[kCachedChunks],
+                          const float* __restrict__ x, int m, int64_t k, int kpad, bool vec,
+                          int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
+  const int nthreads = blockDim.x;
+  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
+  if (threadIdx.x < m) max_s[threadIdx.x] = 0u;
+  lds_barrier();
+  if (vec) {
+    const int cpr = static_cast<int>(k / 4);
+    const int total = m * cpr;
+    int cur_t = -1;
+    unsigned cur = 0;
+    int j = 0;
+    for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+      const int t = c / cpr;
+      if (t != cur_t) {
+        if (cur_t >= 0) atomicMax(&max_s[cur_t], cur);
+        cur_t = t;
+        cur = 0;
+      }
+      const uint4 v = j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 4);
+      cur = max(cur, max(max(v.x & 0x7fffffffu, v.y & 0x7fffffffu), max(v.z & 0x7fffffffu, v.w & 0x7fffffffu)));
+    }
+    if (cur_t >= 0) atomicMax(&max_s[cur_t], cur);
+    lds_barrier();
+    if (threadIdx.x < m) amax_s[threadIdx.x] = fmaxf(__uint_as_float(max_s[threadIdx.x]), 1e-8f);
+    lds_barrier();
+    j = 0;
+    for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
+      const int t = c / cpr, cc = c - t * cpr;
+      const uint4 v = j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 4);
+      const float s = 127.0f / amax_s[t];
+      const uint32_t q = norm_code(__uint_as_float(v.x), s) | (norm_code(__uint_as_float(v.y), s) << 8) |
+                         (norm_code(__uint_as_float(v.z), s) << 16) | (norm_code(__uint_as_float(v.w), s) << 24);
+      *reinterpret_cast<uint32_t*>(xs + t * pitch + cc * 4) = q;
+      if (write_out) *reinterpret_cast<uint32_t*>(xq_out + t * k + cc * 4) = q;
+    }
+    const int padc = (kpad - static_cast<int>(k)) / 4;
+    for (int c = threadIdx.x; c < m * padc; c += nthreads) {
+      const int t = c / padc, cc = c - t * padc;
+      *reinterpret_cast<uint32_t*>(xs + t * pitch + static_cast<int>(k) + cc * 4) = 0u;
+    }
+  } else {
+    for (int t = 0; t < m; ++t) {
+      unsigned cur = 0;
+      for (int64_t i = threadIdx.x; i < k; i += nthreads) cur = max(cur, __float_as_uint(fabsf(x[t * k + i])));
+      atomicMax(&max_s[t], cur);
+    }
+    lds_barrier();
+    if (threadIdx.x < m) amax_s[threadIdx.x] = fmaxf(__uint_as_float(max_s[threadIdx.x]), 1e-8f);
+    lds_barrier();
+    for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
+      const int t = c / kpad, col = c - t * kpad;
+      int8_t q = 0;
+      if (col < k) {
+        q = static_cast<int8_t>(norm_code(x[t * k + col], 127.0f / amax_s[t]));
+        if (write_out) xq_out[t * k + col] = q;
+      }
+      xs[t * pitch + col] = q;
+    }
+  }
+  if (write_out && threadIdx.x < m) amax_out[threadIdx.x] = amax_s[threadIdx.x];
+}
+
+__device__ __forceinline__ void prefetch_f32(uint4 (&cache)[kCachedChunks], const float* __restrict__ x, int m,
+                                             int64_t k) {
+  const int total = m * static_cast<int>(k / 4);
+#pragma unroll
+  for (int j = 0; j < kCachedChunks; ++j) {
+    const int c = threadIdx.x + j * static_cast<int>(blockDim.x);
+    cache[j] = c < total ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 4) : make_uint4(0, 0, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -457,7 +575,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   __shared__ int red[WAVES * 4 * 64];
   __shared__ float amax_s[16];
   __shared__ float quant_s[SRC == kFromBf16Norm ? 16 : 1];
-  __shared__ double ss_s[SRC == kFromBf16Norm ? 16 : 1];
+  __shared__ double wss_s[SRC == kFromBf16Norm ? WAVES : 1];
   __shared__ unsigned max_s[16];
   __shared__ unsigned wmax_s[WAVES];
 
@@ -477,7 +595,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   if (VEC) {
     if (SRC == kFromCodes)
       prefetch_codes(cache, static_cast<const int8_t*>(xsrc), m, k, kpad);
-    else
+    else if (SRC == kFromF32)
+      prefetch_f32(cache, static_cast<const float*>(xsrc), m, k);
+    else if (SRC == kFromBf16 || m == 1)
       prefetch_bf16(cache, static_cast<const uint16_t*>(xsrc), m, k);
   }
   uint4 wcur[U];
@@ -486,9 +606,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   if (SRC == kFromCodes) {
     stage_codes(xs, pitch, cache, static_cast<const int8_t*>(xsrc), m, k, kpad, VEC);
     if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x];
+  } else if (SRC == kFromBf16Norm && VEC && m == 1) {
+    stage_bf16_norm_single<WAVES>(xs, amax_s, quant_s, wmax_s, wss_s, cache, static_cast<const uint16_t*>(xsrc), gain,
+                                  eps, k, kpad, xq_out, amax_out);
   } else if (SRC == kFromBf16Norm) {
-    stage_bf16_norm(xs, pitch, amax_s, quant_s, max_s, ss_s, cache, static_cast<const uint16_t*>(xsrc), gain, eps, m, k,
-                    kpad, VEC, xq_out, amax_out);
+    stage_bf16_norm<WAVES>(xs, pitch, amax_s, quant_s, static_cast<const uint16_t*>(xsrc), gain, eps, m, k, kpad, VEC,
+                           xq_out, amax_out);
+  } else if (SRC == kFromF32) {
+    stage_f32(xs, pitch, amax_s, max_s, cache, static_cast<const float*>(xsrc), m, k, kpad, VEC, xq_out, amax_out);
   } else if (VEC && m == 1) {
     stage_bf16_single<WAVES>(xs, amax_s, wmax_s, cache, static_cast<const uint16_t*>(xsrc), k, kpad, xq_out,
                              amax_out);
@@ -700,18 +825,24 @@ hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t
 
 // U = tiles per wave per item: one item covers a row block of up to
 // 8 * WAVES tiles; longer rows are walked in chunks of that many tiles.
-template <int SRC>
+// SWIGLU items hold 2 * kt tiles (gate then up), so U follows the item size.
+template <int SRC, bool SWIGLU = false>
 hipError_t dispatch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
                         const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
-                        const float* gain, float eps, hipStream_t s, bool vec) {
-  const int64_t kt = k_tiles(k);
+                        const float* gain, float eps, hipStream_t s, bool vec, const void* packed_u = nullptr,
+                        const float* gamma_u = nullptr) {
+  const int64_t kt = (SWIGLU ? 2 : 1) * k_tiles(k);
   if (kt <= kWaves)
-    return launch_lds<SRC, kWaves, 1>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
+    return launch_lds<SRC, kWaves, 1, SWIGLU>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps,
+                                              s, vec, packed_u, gamma_u);
   if (kt <= 2 * kWaves)
-    return launch_lds<SRC, kWaves, 2>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
+    return launch_lds<SRC, kWaves, 2, SWIGLU>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps,
+                                              s, vec, packed_u, gamma_u);
   if (kt <= 4 * kWaves)
-    return launch_lds<SRC, kWaves, 4>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
-  return launch_lds<SRC, kWaves, 8>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
+    return launch_lds<SRC, kWaves, 4, SWIGLU>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps,
+                                              s, vec, packed_u, gamma_u);
+  return launch_lds<SRC, kWaves, 8, SWIGLU>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps,
+                                            s, vec, packed_u, gamma_u);
 }
 
 }  // namespace
@@ -719,24 +850,32 @@ hipError_t dispatch_lds(const void* packed, const float* gamma, int64_t n, int64
 bool gemv_fits_lds(int64_t m, int64_t k) { return lds_bytes(m, k_tiles(k)) <= kMaxLdsBytes; }
 
 // SwiGLU decode path: codes staged in LDS; an item's tiles are the gate row
-// block followed by the up row block, so U is chosen for 2 * kt tiles.
+// block followed by the up row block.
 hipError_t launch_gemv_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
                               int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
                               int32_t* acc, hipStream_t s) {
   if (!gemv_fits_lds(m, k)) return hipErrorInvalidValue;
   const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
-  const int64_t items = 2 * k_tiles(k);
-  if (items <= kWaves)
-    return launch_lds<kFromCodes, kWaves, 1, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr,
-                                                   nullptr, 0.0f, s, vec, packed_u, gamma_u);
-  if (items <= 2 * kWaves)
-    return launch_lds<kFromCodes, kWaves, 2, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr,
-                                                   nullptr, 0.0f, s, vec, packed_u, gamma_u);
-  if (items <= 4 * kWaves)
-    return launch_lds<kFromCodes, kWaves, 4, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr,
-                                                   nullptr, 0.0f, s, vec, packed_u, gamma_u);
-  return launch_lds<kFromCodes, kWaves, 8, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr,
-                                                 nullptr, 0.0f, s, vec, packed_u, gamma_u);
+  return dispatch_lds<kFromCodes, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr, nullptr, 0.0f,
+                                        s, vec, packed_u, gamma_u);
+}
+
+hipError_t launch_norm_quant_gemv_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u,
+                                         const float* gamma_u, int64_t f, int64_t k, const uint16_t* x,
+                                         const float* gain, float eps, int64_t m, float* h, int32_t* acc,
+                                         int8_t* xq_out, float* amax_out, hipStream_t s) {
+  const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (gain == nullptr || reinterpret_cast<uintptr_t>(gain) % 16 == 0) &&
+                   (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 8 == 0);
+  return dispatch_lds<kFromBf16Norm, true>(packed_g, gamma_g, f, k, x, nullptr, m, h, acc, xq_out, amax_out, gain, eps,
+                                           s, vec, packed_u, gamma_u);
+}
+
+hipError_t launch_quant_gemv_f32(const void* packed, const float* gamma, int64_t n, int64_t k, const float* x,
+                                 int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s) {
+  const bool vec = (k % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 4 == 0);
+  return dispatch_lds<kFromF32>(packed, gamma, n, k, x, nullptr, m, y, acc, xq_out, amax_out, nullptr, 0.0f, s, vec);
 }
 
 hipError_t launch_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,

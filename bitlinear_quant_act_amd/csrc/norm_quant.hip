@@ -18,7 +18,7 @@
 // One workgroup per token; rows are read with 16-byte loads, the max is
 // reduced as fp32 bit patterns (non-negative floats order like their bits)
 // and the mean square as fp64, across the wave with shuffles and across the
-// four waves in LDS.
+// four waves in LDS (the in-wave steps on DPP row operations).
 #include "bitlinear_internal.hpp"
 
 namespace bitlinear {
@@ -36,17 +36,8 @@ __device__ __forceinline__ uint32_t code_of(float v, float s) {
   return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
 }
 
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) { return wave_max_u32(v); }
+__device__ __forceinline__ double wave_sum_d(double v) { return wave_sum_f64(v); }
 
 // ---------------------------------------------------------------------------
 // RMSNorm + quantisation

@@ -7,7 +7,7 @@
 // One workgroup per token.  The token's bf16 row is read once with 16-byte
 // loads and kept in registers; |x| is reduced as integer bit patterns (for
 // finite non-negative floats the bit order is the numeric order), first
-// across the wave with cross-lane shuffles, then across the four waves in
+// across the wave with DPP row operations, then across the four waves in
 // LDS.  The scale is one IEEE fp32 divide (127 / a'); every code is one fp32
 // multiply followed by v_rndne_f32 (round half to even) and a clamp, so the
 // result is bit-identical to any other evaluation of the same two roundings.
@@ -36,8 +36,7 @@ __device__ __forceinline__ uint32_t abs_max2(uint32_t word) {
 
 // max over the workgroup; every thread receives the result
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  v = wave_max_u32(v);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();

@@ -243,6 +243,32 @@ int bitlinear_forward_swiglu(const void *packed_gate, const float *gamma_gate,
                              int64_t f, int64_t k, const int8_t *xq, const float *x_absmax, int64_t m,
                              float *h, int32_t *acc_or_null, void *stream);
 
+/*
+ * The feed-forward block's first half in one launch for the decode path:
+ * RMSNorm + quantisation of the block input (as bitlinear_rmsnorm_quant_act)
+ * fused into the gate / up projections with the SwiGLU epilogue (as
+ * bitlinear_forward_swiglu).  Arguments as those two entry points; xq_or_null
+ * and x_absmax_or_null (both or neither) receive the codes and a'.  Supported
+ * for the (m, k) of bitlinear_quant_forward_supported, else
+ * BITLINEAR_E_UNSUPPORTED.
+ */
+int bitlinear_rmsnorm_quant_forward_swiglu(const void *packed_gate, const float *gamma_gate,
+                                           const void *packed_up, const float *gamma_up,
+                                           int64_t f, int64_t k, const uint16_t *x,
+                                           const float *gain_or_null, float eps, int64_t m,
+                                           float *h, int32_t *acc_or_null,
+                                           int8_t *xq_or_null, float *x_absmax_or_null, void *stream);
+
+/*
+ * Quantisation of fp32 activations fused into the decode forward: exactly
+ * bitlinear_quant_act_f32 followed by bitlinear_forward, in one launch (the
+ * down projection fed by the SwiGLU output h).  x: fp32 [m][k], 4-byte
+ * aligned; other arguments and the support rule as bitlinear_quant_forward.
+ */
+int bitlinear_quant_forward_f32(const void *packed, const float *gamma, int64_t n, int64_t k,
+                                const float *x, int64_t m, float *y, int32_t *acc_or_null,
+                                int8_t *xq_or_null, float *x_absmax_or_null, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

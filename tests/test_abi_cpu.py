@@ -231,3 +231,39 @@ def test_swiglu_validation(blq):
     assert call(gu=A2) == E.BITLINEAR_E_ALIGN
     assert call(h=A2) == E.BITLINEAR_E_ALIGN
     assert call(m=(1 << 21) + 1) == E.BITLINEAR_E_UNSUPPORTED
+
+
+def test_fused_ffn_entry_validation(blq):
+    lib = blq.load_library()
+    E = blq
+    f = lib.bitlinear_rmsnorm_quant_forward_swiglu
+    ok = dict(pg=A16, gg=A16, pu=A16, gu=A16, f=64, k=512, x=A16, gain=None, eps=1e-6, m=1, h=A16, acc=None,
+              xq=None, amax=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["pg"], a["gg"], a["pu"], a["gu"], a["f"], a["k"], a["x"], a["gain"], a["eps"], a["m"], a["h"],
+                 a["acc"], a["xq"], a["amax"], None)
+
+    for key in ("pg", "gg", "pu", "gu", "x", "h"):
+        assert call(**{key: None}) == E.BITLINEAR_E_NULL, key
+    assert call(amax=A16) == E.BITLINEAR_E_NULL
+    assert call(f=0) == E.BITLINEAR_E_SHAPE
+    assert call(eps=-1.0) == E.BITLINEAR_E_VALUE
+    assert call(pu=A8) == E.BITLINEAR_E_ALIGN
+    assert call(x=A16 + 1) == E.BITLINEAR_E_ALIGN
+    assert call(m=17) == E.BITLINEAR_E_UNSUPPORTED
+    g = lib.bitlinear_quant_forward_f32
+    ok2 = dict(packed=A16, gamma=A16, n=64, k=512, x=A16, m=1, y=A16, acc=None, xq=None, amax=None)
+
+    def call2(**kw):
+        a = dict(ok2, **kw)
+        return g(a["packed"], a["gamma"], a["n"], a["k"], a["x"], a["m"], a["y"], a["acc"], a["xq"], a["amax"], None)
+
+    for key in ("packed", "gamma", "x", "y"):
+        assert call2(**{key: None}) == E.BITLINEAR_E_NULL, key
+    assert call2(xq=A16) == E.BITLINEAR_E_NULL
+    assert call2(m=0) == E.BITLINEAR_E_SHAPE
+    assert call2(x=A2) == E.BITLINEAR_E_ALIGN
+    assert call2(m=17) == E.BITLINEAR_E_UNSUPPORTED
+    assert call2(m=16, k=14336) == E.BITLINEAR_E_UNSUPPORTED

@@ -159,6 +159,42 @@ def test_swiglu_feeds_the_down_projection(blq):
     assert np.all(np.abs(yg - y_o) <= 1e-5 * np.abs(y_o) + allow * (1 + 1e-5) + 1e-30), "chain y"
 
 
+@pytest.mark.parametrize("f,k,m", [(6912, 2560, 1), (14336, 4096, 1), (1000, 4096, 3), (200, 1003, 2), (2560, 2560, 16)])
+def test_rmsnorm_quant_forward_swiglu(blq, f, k, m):
+    """RMSNorm + quantisation + gate/up + SwiGLU in one launch, against the
+    oracle's RMSNorm quantisation, contraction and SwiGLU."""
+    if not blq.bitlinear_quant_forward_supported(m, k):
+        pytest.skip("m*k codes beyond the on-chip budget of the fused path")
+    torch = torch_mod()
+    tag = "rmsnorm_quant_forward_swiglu f=%d k=%d m=%d" % (f, k, m)
+    log("case", tag)
+    wg = synth.latent_weights((211, f, k), f, k)
+    wu = synth.latent_weights((212, f, k), f, k)
+    gain = synth.norm_gain((213, k), k)
+    x = synth.activations_bf16((214, m, k), m, k, 0.005)
+    pg, gg = blq.bitlinear_pack_weights(to_dev(wg))
+    pu, gu = blq.bitlinear_pack_weights(to_dev(wu))
+    acc_d = torch.empty((m, 2 * f), dtype=torch.int32, device="cuda")
+    xq_d = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    a_d = torch.empty(m, dtype=torch.float32, device="cuda")
+    h_d = blq.bitlinear_rmsnorm_quant_forward_swiglu(pg, gg, pu, gu, f, k, to_dev_bits(x), gain=to_dev(gain),
+                                                     acc=acc_d, xq=xq_d, x_absmax=a_d)
+    xq_o, a_o, _ = oracle.rmsnorm_quant_act(x, gain)
+    assert np.array_equal(host(xq_d), xq_o), tag
+    ad = host(a_d).view(np.int32).astype(np.int64)
+    assert np.abs(ad - a_o.view(np.int32).astype(np.int64)).max() <= 1, tag
+    g_g, q_g, bad_g = oracle_codes(blq, pg, gg, wg, f, k, tag + " gate")
+    g_u, q_u, bad_u = oracle_codes(blq, pu, gu, wu, f, k, tag + " up")
+    keep = np.setdiff1d(np.arange(f), np.union1d(bad_g, bad_u))
+    acc_g = oracle.contract(xq_o, q_g)
+    acc_u = oracle.contract(xq_o, q_u)
+    acc = host(acc_d)
+    assert np.array_equal(acc[:, :f][:, keep], acc_g[:, keep]), tag
+    assert np.array_equal(acc[:, f:][:, keep], acc_u[:, keep]), tag
+    h_o = oracle.swiglu(oracle.dequant(acc_g, g_g, a_o), oracle.dequant(acc_u, g_u, a_o))
+    compare_y(host(h_d)[:, keep], h_o[:, keep], tag)
+
+
 def test_swiglu_unsupported_batched_k(blq):
     f, k, m = 64, 1000, 40
     w = synth.latent_weights((209,), f, k)
