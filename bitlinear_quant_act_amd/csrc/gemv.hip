@@ -301,6 +301,44 @@ __device__ __forceinline__ void norm_values(const uint4& xc, const float* __rest
   }
 }
 
+// the same from two float4 gains already in registers
+__device__ __forceinline__ void norm_values_reg(const uint4& xc, const float4& g0, const float4& g1, bool has_gain,
+                                                float (&v)[8], float (&xv)[8]) {
+  const uint32_t w[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    xv[2 * q] = __uint_as_float(w[q] << 16);
+    xv[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+  }
+  const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = has_gain ? xv[i] * gv[i] : xv[i];
+}
+
+// gains of the chunks whose activations prefetch_bf16 requests (single token)
+__device__ __forceinline__ void prefetch_gain(float4 (&gc)[kCachedChunks][2], const float* __restrict__ gain,
+                                              int64_t k) {
+  const int total = static_cast<int>(k / 8);
+#pragma unroll
+  for (int j = 0; j < kCachedChunks; ++j) {
+    const int c = threadIdx.x + j * static_cast<int>(blockDim.x);
+    if (gain && c < total) {
+      gc[j][0] = *reinterpret_cast<const float4*>(gain + c * 8);
+      gc[j][1] = *reinterpret_cast<const float4*>(gain + c * 8 + 4);
+    } else {
+      gc[j][0] = gc[j][1] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    }
+  }
+}
+
+__device__ __forceinline__ float4 cached_gain(const float4 (&gc)[kCachedChunks][2], int j, int half) {
+  float4 v = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+#pragma unroll
+  for (int q = 0; q < kCachedChunks; ++q)
+    if (q == j) v = gc[q][half];
+  return v;
+}
+
 __device__ __forceinline__ uint32_t norm_code(float v, float s) {
   float r = rintf(v * s);
   r = fminf(fmaxf(r, -127.0f), 127.0f);
@@ -323,19 +361,28 @@ __device__ __forceinline__ void norm_scales(unsigned mx, double ss, int64_t k, f
 // reductions (no atomics, a fixed summation order).
 template <int WAVES>
 __device__ void stage_bf16_norm_single(int8_t* xs, float* amax_s, float* quant_s, unsigned* wmax_s, double* wss_s,
-                                       const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x,
-                                       const float* __restrict__ gain, float eps, int64_t k, int kpad,
-                                       int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
+                                       const uint4 (&cache)[kCachedChunks], const float4 (&gcache)[kCachedChunks][2],
+                                       const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
+                                       int64_t k, int kpad, int8_t* __restrict__ xq_out,
+                                       float* __restrict__ amax_out) {
   const int nthreads = blockDim.x;
   const bool write_out = xq_out != nullptr && blockIdx.x == 0;
   const int total = static_cast<int>(k / 8);
+  const bool has_gain = gain != nullptr;
   unsigned mx = 0;
   double ss = 0.0;
   int j = 0;
+  // chunks j < kCachedChunks come from registers (activations and gains were
+  // requested before the weight tiles); later ones are read here
+  auto values = [&](int c, int jj, float (&v)[8], float (&xv)[8]) {
+    if (jj < kCachedChunks)
+      norm_values_reg(cached(cache, jj), cached_gain(gcache, jj, 0), cached_gain(gcache, jj, 1), has_gain, v, xv);
+    else
+      norm_values(*reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8), gain ? gain + c * 8 : nullptr, v, xv);
+  };
   for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
     float v[8], xv[8];
-    norm_values(j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
-                gain ? gain + c * 8 : nullptr, v, xv);
+    values(c, j, v, xv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       ss += static_cast<double>(xv[i]) * static_cast<double>(xv[i]);
@@ -366,8 +413,7 @@ __device__ void stage_bf16_norm_single(int8_t* xs, float* amax_s, float* quant_s
   j = 0;
   for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
     float v[8], xv[8];
-    norm_values(j < kCachedChunks ? cached(cache, j) : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
-                gain ? gain + c * 8 : nullptr, v, xv);
+    values(c, j, v, xv);
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -592,6 +638,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   int64_t rb = blockIdx.x;
   int c = 0;
   uint4 cache[kCachedChunks];
+  float4 gcache[kCachedChunks][2];
+  if (SRC == kFromBf16Norm && VEC && m == 1) prefetch_gain(gcache, gain, k);
   if (VEC) {
     if (SRC == kFromCodes)
       prefetch_codes(cache, static_cast<const int8_t*>(xsrc), m, k, kpad);
@@ -607,8 +655,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
     stage_codes(xs, pitch, cache, static_cast<const int8_t*>(xsrc), m, k, kpad, VEC);
     if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x];
   } else if (SRC == kFromBf16Norm && VEC && m == 1) {
-    stage_bf16_norm_single<WAVES>(xs, amax_s, quant_s, wmax_s, wss_s, cache, static_cast<const uint16_t*>(xsrc), gain,
-                                  eps, k, kpad, xq_out, amax_out);
+    stage_bf16_norm_single<WAVES>(xs, amax_s, quant_s, wmax_s, wss_s, cache, gcache, static_cast<const uint16_t*>(xsrc),
+                                  gain, eps, k, kpad, xq_out, amax_out);
   } else if (SRC == kFromBf16Norm) {
     stage_bf16_norm<WAVES>(xs, pitch, amax_s, quant_s, static_cast<const uint16_t*>(xsrc), gain, eps, m, k, kpad, VEC,
                            xq_out, amax_out);
