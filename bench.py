@@ -43,6 +43,7 @@ MALL_BYTES = 256 << 20         # last-level (Infinity) cache
 COLD_BYTES = 1 << 30           # walk at least this many weight bytes between reuses
 # sources of the dominant kernel: the counters in profiles/ are used only while these are unchanged
 DECODE_SOURCES = ("gemv.hip", "bitlinear_internal.hpp")
+LUT_SOURCES = ("gemv_lut.hip", "bitlinear_internal.hpp")
 BATCHED_SOURCES = ("gemm.hip", "bitlinear_internal.hpp")
 
 
@@ -195,6 +196,12 @@ def launch_step_swiglu(blq, mats, m, stream, fused):
             fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
 
 
+def _forward_fn(blq, m, variant):
+    if variant == "lut":
+        return blq.bitlinear_forward_lut
+    return blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
+
+
 def launch_step(blq, mats, m, stream, fused, variant="plain"):
     """One pass of the per-token path over every matrix, in layer order."""
     if variant == "swiglu":
@@ -203,16 +210,16 @@ def launch_step(blq, mats, m, stream, fused, variant="plain"):
         for mat in mats:
             _fused(blq, mat, stream)
         return
-    fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
+    fwd = _forward_fn(blq, m, variant)
     for mat in mats:
         _quant(blq, mat, stream)
         fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
 
 
-def launch_kernel_only(blq, mats, m, stream, which, fused=False):
+def launch_kernel_only(blq, mats, m, stream, which, fused=False, variant="plain"):
     """Launches of one kernel over every matrix ('quant', 'forward', 'fused',
     'swiglu': the gate+up launches of the SwiGLU variant)."""
-    fwd = blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
+    fwd = _forward_fn(blq, m, variant)
     for mat in mats:
         if which == "swiglu":
             if mat.name == "gate_up":
@@ -331,18 +338,23 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
-    ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu"),
+    ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu", "lut"),
                     help="rmsnorm: every BitLinear normalises its input first (per-channel gains); "
                          "swiglu: the feed-forward block as a unit (RMSNorm, gate+up with the SwiGLU fused, "
-                         "down fed by h)")
+                         "down fed by h); lut: quant + the table-lookup decode forward")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bound)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--compare-counters", nargs="+", metavar="ARG",
+                    help="CPU only: side-by-side SQ counter table of kernels (see compare_counters())")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
                     help="CPU only: write profiles/ summaries from rocprofv3 CSVs (see summarize())")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.compare_counters:
+        compare_counters(args.compare_counters)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -372,7 +384,13 @@ def main():
     batched = m > blq.BITLINEAR_FORWARD_MAX_M
     # the fused entry point re-quantises the tokens in every workgroup, which
     # pays off for a single token; several tokens go through quant + forward
-    fused = (m == 1 and not args.unfused and
+    lut = args.variant == "lut"
+    if lut and (m > blq.BITLINEAR_FORWARD_MAX_M or
+                not all(blq.bitlinear_forward_lut_supported(mt.k) for mt in wl.matrices)):
+        print("bench.py: --variant lut needs m <= %d and every k within the on-chip table "
+              "(k <= 9984)" % blq.BITLINEAR_FORWARD_MAX_M, file=sys.stderr)
+        sys.exit(2)
+    fused = (m == 1 and not args.unfused and not lut and
              all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
     want_cpu = not args.no_cpu_baseline
     oracle_mod = None
@@ -471,7 +489,7 @@ def main():
     dom_mats = [mt for mt in mats0 if mt.name == "gate_up"] if sw else mats0
 
     def all_reps(which):
-        return lambda st: [launch_kernel_only(blq, mats, m, st, which, fused) for mats in reps]
+        return lambda st: [launch_kernel_only(blq, mats, m, st, which, fused, args.variant) for mats in reps]
 
     dom_ms = time_graph(torch, stream, all_reps(dom), replays) / len(reps)
     nlaunch = len(dom_mats) * replays * len(reps)
@@ -506,7 +524,7 @@ def main():
                       if sw else "bitlinear_forward_batched (gemm_kernel)" if batched else
                       ("bitlinear_rmsnorm_quant_forward (gemv_lds_kernel, RMSNorm + bf16 prologue)" if norm else
                        "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)") if fused else
-                      "bitlinear_forward (gemv kernel)")
+                      "bitlinear_forward_lut (gemv_lut_kernel)" if lut else "bitlinear_forward (gemv kernel)")
     roof["avg_launch_us"] = round(fw_avg_us, 3)
     roof["launches_timed"] = nlaunch
     if sw:
@@ -524,7 +542,8 @@ def main():
     if os.path.exists(prof):
         with open(prof) as f:
             c = json.load(f)
-        if c.get("kernel_source_hash") == kernel_source_hash(BATCHED_SOURCES if batched else DECODE_SOURCES):
+        if c.get("kernel_source_hash") == kernel_source_hash(
+                BATCHED_SOURCES if batched else LUT_SOURCES if lut else DECODE_SOURCES):
             roof["traffic"] = c.get("hbm_bytes_per_launch")
 
     out = {
@@ -556,7 +575,8 @@ def main():
                              if sw else
                              ("bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward") if fused else
                              ("bitlinear_rmsnorm_quant_act + " if norm else "bitlinear_quant_act + ") +
-                             ("bitlinear_forward_batched" if batched else "bitlinear_forward")),
+                             ("bitlinear_forward_batched" if batched else
+                              "bitlinear_forward_lut" if lut else "bitlinear_forward")),
             "launch": ("hip graph, %d kernels per step" % ((1 if fused else 2) * len(mats0))
                        if not args.eager else "eager"),
             "cold_cache": "weights %.0f MB per step x %d replica(s)" % (total_packed / 1e6, len(reps)),
@@ -615,11 +635,65 @@ def _counter_avg_kib(path, kernel_pat):
     return sum(vals.values()) / len(vals), len(vals)
 
 
+def _counters_per_dispatch(paths, kernel_pat):
+    """Mean per-dispatch value of every counter in rocprofv3 counter CSVs,
+    over dispatches whose kernel name contains kernel_pat."""
+    out = {}
+    for path in paths:
+        per = {}
+        for r in _read_csv(path):
+            if kernel_pat in r["Kernel_Name"]:
+                d = per.setdefault(r["Counter_Name"], {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        for name, d in per.items():
+            out[name] = (sum(d.values()) / len(d), len(d))
+    return out
+
+
+def compare_counters(args):
+    """Side-by-side counter table of kernels on one workload (CPU only).
+
+    --compare-counters OUT_MD KEY M LABEL=PATTERN=CSV[,CSV...] ... CMDS CMD...
+    Every counter is averaged per dispatch of the kernels whose name holds
+    PATTERN.  Derived rows divide by the mean weights per launch (N*K over the
+    workload's matrices): wave instructions x 64 lanes per weight."""
+    out_md, key, m = args[0], args[1], int(args[2])
+    sep = args.index("CMDS") if "CMDS" in args else len(args)
+    specs = [a.split("=", 2) for a in args[3:sep]]
+    cmds = " ".join(args[sep + 1:])
+    wl = synth.BY_KEY[key]
+    weights = sum(mt.n * mt.k for mt in wl.matrices) / len(wl.matrices)
+    cols = []
+    for label, pat, csvs in specs:
+        cols.append((label, pat, _counters_per_dispatch(csvs.split(","), pat)))
+    names = sorted(set().union(*[c[2].keys() for c in cols]))
+    lines = ["# Counter comparison: %s, m=%d" % (wl.title, m), "",
+             "Commands (run from the repository root on one MI355X):", "", "```", cmds, "```", "",
+             "Mean per dispatch over every launch of the kernel in the run (mean weights per launch: %.0f)." % weights,
+             "", "| counter | " + " | ".join("%s (`%s`)" % (c[0], c[1]) for c in cols) + " |",
+             "|---|" + "---|" * len(cols)]
+    for name in names:
+        lines.append("| %s | " % name + " | ".join(
+            "%.4g" % c[2][name][0] if name in c[2] else "-" for c in cols) + " |")
+    for name in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_SALU"):
+        if all(name in c[2] for c in cols):
+            lines.append("| %s x 64 per weight | " % name + " | ".join(
+                "%.3f" % (c[2][name][0] * 64 / weights) for c in cols) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize(args):
     """Write profiles/ summaries from rocprofv3 output (CPU only).
 
-    --summarize KEY M STATS_CSV FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB KERNEL_PAT CMD..."""
+    --summarize KEY[:VARIANT] M STATS_CSV FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB KERNEL_PAT CMD...
+    The algorithmic bytes are those of the dominant kernel bench.py times for
+    that workload and variant (fused quant + forward at m = 1 unless the
+    variant is lut)."""
     key, m, stats, fetch, write, cfetch, cwrite, copy_mib, pat = args[:9]
+    key, _, variant = key.partition(":")
+    variant = variant or "plain"
     cmds = " ".join(args[9:])
     m = int(m)
     copy_kib = float(copy_mib) * 1024.0
@@ -633,19 +707,29 @@ def summarize(args):
     rows = [r for r in _read_csv(stats)]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     wl = synth.BY_KEY[key]
-    alg = sum((fused_bytes if m == 1 else forward_bytes)(m, mt.n, mt.k) for mt in wl.matrices) / len(wl.matrices)
+    if variant == "swiglu":
+        mats = [mt for mt in wl.matrices if mt.name == "gate_up"]
+        alg = sum(swiglu_bytes(m, mt.n // 2, mt.k) + ((m * mt.k + 4 * mt.k - 4 * m) if m == 1 else 0)
+                  for mt in mats) / len(mats)
+    else:
+        per = fused_bytes if (m == 1 and variant != "lut") else forward_bytes
+        alg = sum(per(m, mt.n, mt.k) + (4 * mt.k if variant == "rmsnorm" and m == 1 else 0)
+                  for mt in wl.matrices) / len(wl.matrices)
+    suffix = "" if variant == "plain" else "_" + variant
+    sources = LUT_SOURCES if variant == "lut" else DECODE_SOURCES if m <= 16 else BATCHED_SOURCES
     out = {
-        "workload": key, "m": m, "kernel_pattern": pat,
-        "kernel_source_hash": kernel_source_hash(DECODE_SOURCES if m <= 16 else BATCHED_SOURCES),
+        "workload": key, "m": m, "variant": variant, "kernel_pattern": pat,
+        "kernel_source_hash": kernel_source_hash(sources),
         "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": [nf, nw],
         "copy_calibration": {"copy_mib": float(copy_mib), "fetch_kib": cf, "write_kib": cw,
                              "fetch_factor": f_fetch, "write_factor": f_write},
         "hbm_bytes_per_launch": round(traffic), "algorithmic_bytes_per_launch": round(alg),
         "commands": cmds,
     }
-    with open(os.path.join(ROOT, "profiles", "counters_%s_m%d.json" % (key, m)), "w") as f:
+    with open(os.path.join(ROOT, "profiles", "counters_%s_m%d%s.json" % (key, m, suffix)), "w") as f:
         json.dump(out, f, indent=1)
-    lines = ["# rocprofv3 kernel statistics: %s, m=%d" % (wl.title, m), "",
+    lines = ["# rocprofv3 kernel statistics: %s, m=%d%s" % (wl.title, m, "" if variant == "plain" else
+                                                           ", variant " + variant), "",
              "Commands (run from the repository root on one MI355X):", "", "```", cmds, "```", "",
              "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -660,7 +744,7 @@ def summarize(args):
               "device copy of %s MiB measured the same way (factors %.4f / %.4f): %.0f bytes per launch vs "
               "%.0f algorithmic bytes per launch (mean over the workload's matrices)." % (
                   pat, copy_mib, f_fetch, f_write, traffic, alg)]
-    with open(os.path.join(ROOT, "profiles", "%s_m%d_kernels.md" % (key, m)), "w") as f:
+    with open(os.path.join(ROOT, "profiles", "%s_m%d%s_kernels.md" % (key, m, suffix)), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(out))
 

@@ -98,7 +98,9 @@ def load_library(path: str = LIB_PATH):
     lib.bitlinear_quant_forward_f32.restype = _ct.c_int
     lib.bitlinear_forward_swiglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
     lib.bitlinear_forward_swiglu.restype = _ct.c_int
-    for name in ("bitlinear_forward", "bitlinear_forward_batched"):
+    lib.bitlinear_forward_lut_supported.argtypes = [_i64]
+    lib.bitlinear_forward_lut_supported.restype = _ct.c_int
+    for name in ("bitlinear_forward", "bitlinear_forward_batched", "bitlinear_forward_lut"):
         fn = getattr(lib, name)
         fn.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         fn.restype = _ct.c_int
@@ -295,6 +297,15 @@ def bitlinear_forward_swiglu(packed_gate, gamma_gate, packed_up, gamma_up, f: in
         None if acc is None else _dev(acc, "acc", (_torch.int32,), 2 * m * f), _stream_handle(stream))
     _check(rc, "bitlinear_forward_swiglu")
     return h
+
+
+def bitlinear_forward_lut_supported(k: int) -> bool:
+    return bool(load_library().bitlinear_forward_lut_supported(k))
+
+
+def bitlinear_forward_lut(packed, gamma, n: int, k: int, xq, x_absmax, y=None, acc=None, stream=None):
+    """Table-lookup decode forward; same arguments and result as bitlinear_forward."""
+    return _forward("bitlinear_forward_lut", packed, gamma, n, k, xq, x_absmax, y, acc, stream)
 
 
 def bitlinear_forward_batched(packed, gamma, n: int, k: int, xq, x_absmax, y=None, acc=None, stream=None):

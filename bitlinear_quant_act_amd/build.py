@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "quant_act.hip", "norm_quant.hip", "pack.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quant_act.hip", "norm_quant.hip", "pack.hip", "gemv.hip", "gemv_lut.hip", "gemm.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-fno-fast-math", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",

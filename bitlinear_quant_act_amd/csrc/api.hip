@@ -119,6 +119,19 @@ int bitlinear_quant_forward_supported(int64_t m, int64_t k) {
   return bitlinear::gemv_fits_lds(m, k) ? 1 : 0;
 }
 
+int bitlinear_forward_lut(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+                          const float* x_absmax, int64_t m, float* y, int32_t* acc_or_null, void* stream) {
+  if (int rc = check_forward(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null)) return rc;
+  if (m > BITLINEAR_FORWARD_MAX_M || !bitlinear::gemv_lut_supported(k)) return BITLINEAR_E_UNSUPPORTED;
+  return status_of(bitlinear::launch_gemv_lut(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_lut_supported(int64_t k) {
+  if (k < 1 || k > kMaxK) return 0;
+  return bitlinear::gemv_lut_supported(k) ? 1 : 0;
+}
+
 int bitlinear_forward_batched(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                               const float* x_absmax, int64_t m, float* y, int32_t* acc_or_null, void* stream) {
   if (int rc = check_forward(packed, gamma, n, k, xq, x_absmax, m, y, acc_or_null)) return rc;

@@ -113,6 +113,9 @@ hipError_t launch_norm_quant_gemv_swiglu(const void* packed_g, const float* gamm
                                          int8_t* xq_out, float* amax_out, hipStream_t s);
 hipError_t launch_quant_gemv_f32(const void* packed, const float* gamma, int64_t n, int64_t k, const float* x,
                                  int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s);
+bool gemv_lut_supported(int64_t k);
+hipError_t launch_gemv_lut(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+                           const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s);
 bool gemm_swiglu_supported(int64_t k, const int8_t* xq);
 hipError_t launch_gemm_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
                               int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,

@@ -269,6 +269,27 @@ int bitlinear_quant_forward_f32(const void *packed, const float *gamma, int64_t 
                                 const float *x, int64_t m, float *y, int32_t *acc_or_null,
                                 int8_t *xq_or_null, float *x_absmax_or_null, void *stream);
 
+/*
+ * Table-lookup decode forward ("BitNet 1-bit LLM Inference Framework",
+ * "How the LUT Kernel Works": every ternary weight is -1, 0 or +1, so the
+ * product of a weight group with the activations takes one of a few values
+ * that can be looked up instead of multiplied).  Same arguments and the same
+ * result, bit for bit, as bitlinear_forward: each workgroup builds in on-chip
+ * memory the 16 partial sums of every pair of int8 codes that share a 4-bit
+ * nibble of the packed layout and adds one table entry per weight pair.  The
+ * table takes 16 bytes per activation column (k rounded up to 256), so
+ * 1 <= m <= BITLINEAR_FORWARD_MAX_M and bitlinear_forward_lut_supported(k)
+ * are required, else BITLINEAR_E_UNSUPPORTED.  Each token streams the weights
+ * once: the entry is meant for m = 1 and is kept as the measured counterpart
+ * of the matrix-core decode kernel.
+ */
+int bitlinear_forward_lut(const void *packed, const float *gamma, int64_t n, int64_t k,
+                          const int8_t *xq, const float *x_absmax, int64_t m,
+                          float *y, int32_t *acc_or_null, void *stream);
+
+/* 1 if bitlinear_forward_lut's table for k fits on chip, else 0.  Pure host function. */
+int bitlinear_forward_lut_supported(int64_t k);
+
 #ifdef __cplusplus
 }
 #endif
