@@ -16,6 +16,17 @@ section in the C file):
   contract            -- item 3 (add / skip / subtract) and the LUT section's
                          scalar loop;
   dequant             -- item 4 (gamma * max|x| / Q_b).
+Variant modes:
+  quant_act_tensor, dequant_tensor, contract_q128
+                      -- "BitNet 1-bit LLM Inference Framework", the BitLinear
+                         class under "The Core Structure of BitNet b1.58"
+                         (one activation scale per tensor, Q_b = 128);
+  row_scales, ternarize_rows, dequant_rows, f32_to_f16_bits
+                      -- "BitNet-2B-4T: Inside the 2B-Parameter, 4T-Token 1-Bit
+                         LLM", "Weight Representation: Ternary + Scale, Not
+                         Pure Binary" (one FP16 scale per output channel);
+  binarize            -- "BitNet's 1-Bit Transformer: Architecture Breakdown",
+                         "Binary Weight Matrices with Learnable Scaling".
 All of them are pinned by tests in tests/test_oracle_*.py.
 """
 from __future__ import annotations
@@ -66,6 +77,24 @@ def _load():
     lib.oracle_rmsnorm_quant_act.restype = None
     lib.oracle_swiglu.argtypes = [_p, _p, _i64, _p]
     lib.oracle_swiglu.restype = None
+    lib.oracle_quant_act_tensor.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.oracle_quant_act_tensor.restype = None
+    lib.oracle_dequant_tensor.argtypes = [_p, _i64, _i64, _ct.c_float, _ct.c_float, _p]
+    lib.oracle_dequant_tensor.restype = None
+    lib.oracle_contract_q128.argtypes = [_p, _p, _i64, _i64, _i64, _p]
+    lib.oracle_contract_q128.restype = _ct.c_int
+    lib.oracle_f32_to_f16.argtypes = [_ct.c_float]
+    lib.oracle_f32_to_f16.restype = _ct.c_uint16
+    lib.oracle_f16_to_f32.argtypes = [_ct.c_uint16]
+    lib.oracle_f16_to_f32.restype = _ct.c_float
+    lib.oracle_row_scales.argtypes = [_p, _i64, _i64, _p]
+    lib.oracle_row_scales.restype = None
+    lib.oracle_ternarize_rows.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.oracle_ternarize_rows.restype = None
+    lib.oracle_dequant_rows.argtypes = [_p, _i64, _i64, _p, _p, _p]
+    lib.oracle_dequant_rows.restype = None
+    lib.oracle_binarize.argtypes = [_p, _i64, _i64, _p]
+    lib.oracle_binarize.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = _ct.c_int
     _lib = lib
@@ -242,6 +271,130 @@ def forward(x_bits: np.ndarray, w: np.ndarray, g=None) -> dict:
     acc = contract(xq, q)
     y = dequant(acc, gm, amax)
     return {"gamma": gm, "q": q, "xq": xq, "amax": amax, "acc": acc, "y": y}
+
+
+# ---------------------------------------------------------------------------
+# variant modes
+# ---------------------------------------------------------------------------
+
+def quant_act_tensor(x_bits: np.ndarray):
+    """V1: (xq int8 [m][k] in [-128, 127], g fp32) with one scale for the
+    whole tensor: code = round(clamp((x * 128) / (g + 1e-8), -128, 127)),
+    g = max |x| over every element."""
+    x = _c(x_bits, np.uint16)
+    m, k = x.shape
+    xq = np.empty((m, k), dtype=np.int8)
+    g = np.empty(1, dtype=np.float32)
+    _load().oracle_quant_act_tensor(_ptr(x), m, k, _ptr(xq), _ptr(g))
+    return xq, g[0]
+
+
+def dequant_tensor(acc: np.ndarray, g_w, g_x) -> np.ndarray:
+    """V1: fp32 [m][n] = acc * gamma * g / 2^7 (binary64, rounded once)."""
+    acc = _c(acc, np.int32)
+    m, n = acc.shape
+    y = np.empty((m, n), dtype=np.float32)
+    _load().oracle_dequant_tensor(_ptr(acc), m, n, float(np.float32(g_w)), float(np.float32(g_x)), _ptr(y))
+    return y
+
+
+def contract_q128(xq: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """contract() for codes in [-128, 127] (bound 128 * K)."""
+    xq = _c(xq, np.int8)
+    q = _c(q, np.int8)
+    m, k = xq.shape
+    n, k2 = q.shape
+    if k != k2:
+        raise OracleError("inner sizes differ")
+    acc = np.empty((m, n), dtype=np.int32)
+    rc = _load().oracle_contract_q128(_ptr(xq), _ptr(q), m, n, k, _ptr(acc))
+    if rc == -1:
+        raise OracleError("accumulator bound |acc| <= 128*K violated")
+    if rc == -2:
+        raise OracleError("weight code outside {-1, 0, 1}")
+    return acc
+
+
+def f32_to_f16_bits(v) -> np.ndarray:
+    """binary16 bits (round to nearest even) of binary32 values, element-wise."""
+    a = np.asarray(v, dtype=np.float32)
+    lib = _load()
+    return np.array([lib.oracle_f32_to_f16(float(t)) for t in a.ravel()], dtype=np.uint16).reshape(a.shape)
+
+
+def f16_bits_to_f32(b) -> np.ndarray:
+    a = np.asarray(b, dtype=np.uint16)
+    lib = _load()
+    return np.array([lib.oracle_f16_to_f32(int(t)) for t in a.ravel()], dtype=np.float32).reshape(a.shape)
+
+
+def row_scales(w: np.ndarray) -> np.ndarray:
+    """V2: binary16 bits [n] of each row's absmean (binary64 mean, rounded
+    to binary32, then to binary16)."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    s16 = np.empty(n, dtype=np.uint16)
+    _load().oracle_row_scales(_ptr(w), n, k, _ptr(s16))
+    return s16
+
+
+def ternarize_rows(w: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """V2: int8 [n][k] = Clip(Round(W / (s_row + 1e-5)), -1, 1)."""
+    w = _c(w, np.float32)
+    s16 = _c(s16, np.uint16)
+    n, k = w.shape
+    if s16.shape != (n,):
+        raise OracleError("one scale per row")
+    q = np.empty((n, k), dtype=np.int8)
+    _load().oracle_ternarize_rows(_ptr(w), n, k, _ptr(s16), _ptr(q))
+    return q
+
+
+def dequant_rows(acc: np.ndarray, s16: np.ndarray, amax: np.ndarray) -> np.ndarray:
+    """V2: fp32 [m][n] = acc * s_n * a'_m / 127 (binary64, rounded once)."""
+    acc = _c(acc, np.int32)
+    s16 = _c(s16, np.uint16)
+    amax = _c(amax, np.float32)
+    m, n = acc.shape
+    y = np.empty((m, n), dtype=np.float32)
+    _load().oracle_dequant_rows(_ptr(acc), m, n, _ptr(s16), _ptr(amax), _ptr(y))
+    return y
+
+
+def binarize(w: np.ndarray) -> np.ndarray:
+    """V3: int8 [n][k] = -1 where W < 0, else +1."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    b = np.empty((n, k), dtype=np.int8)
+    _load().oracle_binarize(_ptr(w), n, k, _ptr(b))
+    return b
+
+
+def forward_tensor_act(x_bits: np.ndarray, w: np.ndarray) -> dict:
+    """V1 path: main-path gamma and codes, per-tensor Q_b = 128 activations."""
+    gm = gamma(w)
+    q = ternarize(w, gm)
+    xq, gx = quant_act_tensor(x_bits)
+    acc = contract_q128(xq, q)
+    return {"gamma": gm, "q": q, "xq": xq, "gx": gx, "acc": acc, "y": dequant_tensor(acc, gm, gx)}
+
+
+def forward_rowscale(x_bits: np.ndarray, w: np.ndarray) -> dict:
+    """V2 path: per-row FP16 scales and codes, per-token activations."""
+    s16 = row_scales(w)
+    q = ternarize_rows(w, s16)
+    xq, amax = quant_act(x_bits)
+    acc = contract(xq, q)
+    return {"s16": s16, "q": q, "xq": xq, "amax": amax, "acc": acc, "y": dequant_rows(acc, s16, amax)}
+
+
+def forward_binary(x_bits: np.ndarray, w: np.ndarray, s) -> dict:
+    """V3 path: sign(W) (zero -> +1) with the given per-layer scale s,
+    per-token activations."""
+    b = binarize(w)
+    xq, amax = quant_act(x_bits)
+    acc = contract(xq, b)
+    return {"b": b, "xq": xq, "amax": amax, "acc": acc, "y": dequant(acc, np.float32(s), amax)}
 
 
 def num_threads() -> int:

@@ -47,6 +47,23 @@
  *   - h is requantized for the next BitLinear from binary32 with the same
  *     per-token rule as the bf16 activations.
  *
+ * Variant modes (each its own functions, V1-V3 below):
+ *   V1 [P5] "BitNet 1-bit LLM Inference Framework", the BitLinear class
+ *      under "The Core Structure of BitNet b1.58": one activation scale per
+ *      tensor, Q_b = 2^7 = 128, codes in
+ *      [-128, 127] (clamp, then round), de-quantization by gamma * g / 2^7.
+ *      The same listing's weight epsilon (1e-8) is not taken: the variant
+ *      changes the activation side only, weights follow O1-O3;
+ *   V2 [P2] "BitNet-2B-4T: Inside the 2B-Parameter, 4T-Token 1-Bit LLM",
+ *      section "Weight Representation: Ternary + Scale, Not Pure Binary":
+ *      one FP16 scale per output channel.  Reading: the scale is that row's
+ *      absmean (as gamma, per row), rounded to binary32 then to binary16, and
+ *      the row is ternarized and de-quantized with the stored value;
+ *   V3 [P1] "BitNet's 1-Bit Transformer: Architecture Breakdown", section
+ *      "Binary Weight Matrices with Learnable Scaling": W_bit = s * sign(W),
+ *      s one learned scalar per layer (an input here).  Reading: sign(0) is
+ *      +1; the activations take the main path's per-token int8 codes.
+ *
  * Build: gcc -O2 -fopenmp -fno-fast-math -ffp-contract=off (see build.py).
  * OpenMP is used over independent output rows only.
  */
@@ -131,16 +148,20 @@ float oracle_gamma_from_sum(double abs_sum, int64_t n, int64_t k)
 
 /* q = Clip(Round(W / (gamma + eps)), -1, 1) with eps = 1e-5 added in binary32
  * and one IEEE binary32 divide per weight. */
+static int8_t ternary_code(float w, float denom)
+{
+    const float t = w / denom;
+    return (int8_t)clip(round_half_even(t), -1.0, 1.0);
+}
+
 void oracle_ternarize(const float *w, int64_t n, int64_t k, float gamma, int8_t *q)
 {
     const float denom = gamma + 1e-5f;
     int64_t r;
 #pragma omp parallel for schedule(static)
     for (r = 0; r < n; ++r) {
-        for (int64_t c = 0; c < k; ++c) {
-            float t = w[r * k + c] / denom;
-            q[r * k + c] = (int8_t)clip(round_half_even(t), -1.0, 1.0);
-        }
+        for (int64_t c = 0; c < k; ++c)
+            q[r * k + c] = ternary_code(w[r * k + c], denom);
     }
 }
 
@@ -300,14 +321,15 @@ void oracle_rmsnorm_quant_act(const uint16_t *x, const float *w, float eps, int6
 
 /* acc[i][j] = sum_k xq[i][k] * q[j][k], computed as: +x where the weight is
  * +1, nothing where it is 0, -x where it is -1.  The sum is kept in int64 and
- * checked against the bound |acc| <= 127 * k before it is stored as int32.
+ * checked against the bound |acc| <= 127 * k (128 * k for the V1 codes, which
+ * reach -128) before it is stored as int32.
  * Returns 0, or -1 if the bound (or int32 range) is violated, or -2 if a
  * weight is not in {-1, 0, 1}. */
-int oracle_contract(const int8_t *xq, const int8_t *q, int64_t m, int64_t n, int64_t k,
-                    int32_t *acc)
+static int contract_bounded(const int8_t *xq, const int8_t *q, int64_t m, int64_t n, int64_t k,
+                            int64_t qmax, int32_t *acc)
 {
     int bad = 0;
-    const int64_t bound = 127 * k;
+    const int64_t bound = qmax * k;
     int64_t i;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (i = 0; i < m * n; ++i) {
@@ -330,6 +352,12 @@ int oracle_contract(const int8_t *xq, const int8_t *q, int64_t m, int64_t n, int
     if (bad & 2)
         return -2;
     return (bad & 1) ? -1 : 0;
+}
+
+int oracle_contract(const int8_t *xq, const int8_t *q, int64_t m, int64_t n, int64_t k,
+                    int32_t *acc)
+{
+    return contract_bounded(xq, q, m, n, k, 127, acc);
 }
 
 /* Same contraction for an explicit list of (row, col) output positions, for
@@ -395,6 +423,178 @@ void oracle_swiglu(const float *g, const float *u, int64_t count, float *h)
         const double gd = (double)g[i];
         h[i] = (float)(gd * (double)u[i] / (1.0 + exp(-gd)));
     }
+}
+
+/* ================================================================== */
+/* Variant modes the pages describe beside the main path               */
+/* ================================================================== */
+
+/* ------------------------------------------------------------------ */
+/* V1: per-tensor activation quantization, Q_b = 128                    */
+/*   [P5, "BitNet 1-bit LLM Inference Framework", "A Deep Look at the    */
+/*    BitNet Architecture", "The Core Structure of BitNet b1.58": the    */
+/*    BitLinear class's activation_quantize and its de-quantization]    */
+/* ------------------------------------------------------------------ */
+
+/* One scale for the whole [m][k] tensor: g = max |x| over every element;
+ * each code is the binary32 value (x * 128) / (g + 1e-8) (one multiply, one
+ * IEEE divide; 1e-8 added to g in binary32), clamped to [-128, 127] first
+ * and then rounded half to even.  gx receives g itself (the listing returns
+ * the max, without the epsilon, as the de-quantization scale). */
+void oracle_quant_act_tensor(const uint16_t *x, int64_t m, int64_t k, int8_t *xq, float *gx)
+{
+    float g = 0.0f;
+    for (int64_t i = 0; i < m * k; ++i) {
+        const float v = fabsf(bf16_to_f32(x[i]));
+        if (v > g)
+            g = v;
+    }
+    const float d = g + 1e-8f;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < m * k; ++i) {
+        const float t = (bf16_to_f32(x[i]) * 128.0f) / d;
+        xq[i] = (int8_t)round_half_even((float)clip((double)t, -128.0, 127.0));
+    }
+    *gx = g;
+}
+
+/* y = acc * gamma * g / 2^7 (the listing's de-quantization), binary64,
+ * rounded once to binary32. */
+void oracle_dequant_tensor(const int32_t *acc, int64_t m, int64_t n, float gamma, float gx, float *y)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < m * n; ++i)
+        y[i] = (float)((double)acc[i] * (double)gamma * (double)gx / 128.0);
+}
+
+/* Contraction of codes in [-128, 127] (the V1 range): as oracle_contract,
+ * with the bound |acc| <= 128 * k. */
+int oracle_contract_q128(const int8_t *xq, const int8_t *q, int64_t m, int64_t n, int64_t k,
+                         int32_t *acc)
+{
+    return contract_bounded(xq, q, m, n, k, 128, acc);
+}
+
+/* ------------------------------------------------------------------ */
+/* V2: per-output-channel FP16 scales                                  */
+/*   [P2, "BitNet-2B-4T: Inside the 2B-Parameter, 4T-Token 1-Bit LLM",   */
+/*    "Weight Representation: Ternary + Scale, Not Pure Binary": W_bit   */
+/*    times s with one FP16 scale per output channel]                    */
+/* ------------------------------------------------------------------ */
+
+/* Ties-to-even rounding of a binary64 value below 2^52 (written out from
+ * the definition, as round_half_even). */
+static double rne_double(double v)
+{
+    const double below = floor(v);
+    const double rest = v - below; /* exact */
+    if (rest != 0.5)
+        return rest < 0.5 ? below : below + 1.0;
+    return fmod(below, 2.0) != 0.0 ? below + 1.0 : below; /* tie: even neighbour */
+}
+
+/* IEEE 754 binary16 encoding of a binary32 value, round to nearest, ties to
+ * even: 1 sign, 5 exponent (bias 15) and 10 fraction bits; subnormals are
+ * multiples of 2^-24; magnitudes from 65520 (halfway between the largest
+ * finite 65504 and 2^16) round to infinity. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7E00u);
+    const double a = fabs((double)f);
+    if (a >= 65520.0)
+        return (uint16_t)(sign | 0x7C00u);
+    if (a < 6.103515625e-05) { /* below 2^-14: subnormal quantum 2^-24 */
+        const double q = rne_double(a * 16777216.0);
+        return (uint16_t)(sign | (uint16_t)q); /* q = 1024 encodes 2^-14 itself */
+    }
+    int e;
+    (void)frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): unbiased exponent e - 1 */
+    e -= 1;
+    double q = rne_double(ldexp(a, 10 - e)); /* 1024 .. 2048 */
+    if (q >= 2048.0) {
+        q = 1024.0;
+        e += 1;
+    }
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
+/* Decode binary16 bits (exact in binary32). */
+float oracle_f16_to_f32(uint16_t h)
+{
+    const int e = (h >> 10) & 31;
+    const int frac = h & 1023;
+    double v;
+    if (e == 31)
+        v = frac ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)frac, -24);
+    else
+        v = ldexp((double)(frac + 1024), e - 25);
+    return (float)((h & 0x8000u) ? -v : v);
+}
+
+/* Reading: the scale of output channel r is that row's absmean (the main
+ * path's gamma rule applied to one row: binary64 sum left to right, divided
+ * by k, rounded once to binary32), stored as binary16. */
+void oracle_row_scales(const float *w, int64_t n, int64_t k, uint16_t *s16)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r) {
+        double s = 0.0;
+        for (int64_t c = 0; c < k; ++c)
+            s += fabs((double)w[r * k + c]);
+        s16[r] = oracle_f32_to_f16((float)(s / (double)k));
+    }
+}
+
+/* Row r is ternarized with its stored scale: q = Clip(Round(W / (s_r + 1e-5)),
+ * -1, 1), s_r the binary16 value widened to binary32, eps added in binary32,
+ * one binary32 divide per weight. */
+void oracle_ternarize_rows(const float *w, int64_t n, int64_t k, const uint16_t *s16, int8_t *q)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r) {
+        const float denom = oracle_f16_to_f32(s16[r]) + 1e-5f;
+        for (int64_t c = 0; c < k; ++c)
+            q[r * k + c] = ternary_code(w[r * k + c], denom);
+    }
+}
+
+/* y[i][j] = acc[i][j] * s_j * a'_i / 127 (binary64, rounded once). */
+void oracle_dequant_rows(const int32_t *acc, int64_t m, int64_t n, const uint16_t *s16,
+                         const float *amax, float *y)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j)
+            y[i * n + j] = (float)((double)acc[i * n + j] * (double)oracle_f16_to_f32(s16[j]) *
+                                   (double)amax[i] / 127.0);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* V3: binary +-1 weights with a per-layer scale                        */
+/*   [P1, "BitNet's 1-Bit Transformer: Architecture Breakdown", "Binary  */
+/*    Weight Matrices with Learnable Scaling": W_bit = s * sign(W)]      */
+/* ------------------------------------------------------------------ */
+
+/* b = sign(W) with zero taken as +1 (a reading: one bit per weight leaves no
+ * code for 0), i.e. -1 exactly where W < 0.  The scale s is learned, not
+ * derived from W; it enters only the de-quantization (oracle_dequant with
+ * gamma = s). */
+void oracle_binarize(const float *w, int64_t n, int64_t k, int8_t *b)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n * k; ++i)
+        b[i] = (int8_t)(w[i] < 0.0f ? -1 : 1);
 }
 
 /* Number of OpenMP threads the oracle runs with (reported by the benchmark). */

@@ -21,8 +21,8 @@ MUTATIONS = {
                   "const float s = 128.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = bf16_to_f32"),
     "f32 quant Q_b = 128": ("const float s = 127.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = x[r * k + c] * s;",
                             "const float s = 128.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float t = x[r * k + c] * s;"),
-    "ternary clip missing": ("q[r * k + c] = (int8_t)clip(round_half_even(t), -1.0, 1.0);",
-                             "q[r * k + c] = (int8_t)round_half_even(t);"),
+    "ternary clip missing": ("return (int8_t)clip(round_half_even(t), -1.0, 1.0);",
+                             "return (int8_t)round_half_even(t);"),
     "gamma of W, not |W|": ("s += fabs((double)row[c]);", "s += ((double)row[c]);"),
     "gamma divides by n only": ("double mean = abs_sum / ((double)n * (double)k);",
                                 "double mean = abs_sum / ((double)n);"),
@@ -56,6 +56,28 @@ MUTATIONS = {
                           "h[i] = (float)(gd * (double)u[i] / (1.0 + exp(gd)));"),
     "swiglu drops up": ("h[i] = (float)(gd * (double)u[i] / (1.0 + exp(-gd)));",
                         "h[i] = (float)(gd / (1.0 + exp(-gd)));"),
+    "tensor quant Q_b = 127": ("const float t = (bf16_to_f32(x[i]) * 128.0f) / d;",
+                               "const float t = (bf16_to_f32(x[i]) * 127.0f) / d;"),
+    "tensor quant symmetric clamp": ("clip((double)t, -128.0, 127.0)", "clip((double)t, -127.0, 127.0)"),
+    "tensor quant epsilon dropped": ("const float d = g + 1e-8f;", "const float d = g;"),
+    "tensor quant max of x, not |x|": ("const float v = fabsf(bf16_to_f32(x[i]));", "const float v = bf16_to_f32(x[i]);"),
+    "tensor dequant by 127": ("(double)gx / 128.0", "(double)gx / 127.0"),
+    "q128 bound is 127 * k": ("return contract_bounded(xq, q, m, n, k, 128, acc);",
+                              "return contract_bounded(xq, q, m, n, k, 127, acc);"),
+    "tensor dequant drops g": ("(double)acc[i] * (double)gamma * (double)gx / 128.0",
+                               "(double)acc[i] * (double)gamma / 128.0"),
+    "f16 ties away from zero": ("return fmod(below, 2.0) != 0.0 ? below + 1.0 : below;", "return below + 1.0;"),
+    "f16 exponent bias 16": ("((e + 15) << 10)", "((e + 16) << 10)"),
+    "f16 subnormal quantum 2^-23": ("rne_double(a * 16777216.0)", "rne_double(a * 8388608.0)"),
+    "f16 overflow from 65504": ("if (a >= 65520.0)", "if (a > 65504.0)"),
+    "row scale divides by n": ("oracle_f32_to_f16((float)(s / (double)k))", "oracle_f32_to_f16((float)(s / (double)n))"),
+    "row scale kept in binary32": ("s16[r] = oracle_f32_to_f16((float)(s / (double)k));",
+                                   "s16[r] = oracle_f32_to_f16((float)(s / (double)k));\n        if (s16[r] == 0x3ACD) s16[r] = 0x3ACC;"),
+    "row ternarize epsilon dropped": ("const float denom = oracle_f16_to_f32(s16[r]) + 1e-5f;",
+                                      "const float denom = oracle_f16_to_f32(s16[r]);"),
+    "row dequant uses row 0 scale": ("(double)oracle_f16_to_f32(s16[j])", "(double)oracle_f16_to_f32(s16[0])"),
+    "binary sign of zero is -1": ("b[i] = (int8_t)(w[i] < 0.0f ? -1 : 1);", "b[i] = (int8_t)(w[i] <= 0.0f ? -1 : 1);"),
+    "binary uses the sign bit": ("b[i] = (int8_t)(w[i] < 0.0f ? -1 : 1);", "b[i] = (int8_t)(signbit(w[i]) ? -1 : 1);"),
     "dequant drops gamma": ("(double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0",
                             "(double)acc[i * n + j] * (double)amax[i] / 127.0"),
 }

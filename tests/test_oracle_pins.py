@@ -603,3 +603,160 @@ def test_swiglu_vs_torch_silu(oracle_mod):
     h = oracle_mod.swiglu(g, u)
     ref = (torch.nn.functional.silu(torch.from_numpy(g.astype(np.float64))) * torch.from_numpy(u.astype(np.float64))).numpy()
     assert np.all(np.abs(ulp_diff(h, ref.astype(np.float32))) <= 1)
+
+
+# ---------------------------------------------------------------------------
+# variant modes
+# ---------------------------------------------------------------------------
+# V1 "BitNet 1-bit LLM Inference Framework", "The Core Structure of BitNet
+#    b1.58": the BitLinear class quantizes activations with one max over the
+#    whole tensor, Q_b = 2^7, x * Q_b / (max + 1e-8) clamped to [-Q_b, Q_b - 1]
+#    and then rounded, and de-quantizes by w_scale * x_scale / 2^7.
+# V2 "BitNet-2B-4T: Inside the 2B-Parameter, 4T-Token 1-Bit LLM", "Weight
+#    Representation: Ternary + Scale, Not Pure Binary": one FP16 scale per
+#    output channel.
+# V3 "BitNet's 1-Bit Transformer: Architecture Breakdown", "Binary Weight
+#    Matrices with Learnable Scaling": W_bit = s * sign(W).
+
+def test_v1_tensor_quant_hand_values():
+    """g = 1, and 1 + 1e-8 rounds to 1 in binary32 (its ulp is 2^-23), so each
+    code is round(clamp(128 x)): 128 -> 127 (clamp), -128 kept, 0.75 -> 96,
+    2.5/128 -> tie 2.5 -> 2 (even), 0.5 -> 64, -0.25 -> -32; 0.1 is the bf16
+    value 0.10009765625, 128 of it is 12.8125 -> 13."""
+    import oracle
+    x = bits([[1.0, -1.0, 0.75, 2.5 / 128], [0.5, 0.0, -0.25, 0.1]])
+    xq, g = oracle.quant_act_tensor(x)
+    assert g == np.float32(1.0)
+    assert xq.tolist() == [[127, -128, 96, 2], [64, 0, -32, 13]]
+
+
+def test_v1_one_scale_for_the_tensor():
+    """The max is over |x| of every token: g = 4 from token 0's -4, so token
+    1's 1 and -0.5 give 32 and -16 (per token they would be 127 and -64),
+    and token 0's -4 gives -128 (Q_b = 128, not 127)."""
+    import oracle
+    xq, g = oracle.quant_act_tensor(bits([[-4.0, 1.0], [1.0, -0.5]]))
+    assert g == np.float32(4.0)
+    assert xq.tolist() == [[-128, 32], [32, -16]]
+
+
+def test_v1_ties_and_epsilon():
+    """Ties go to even on both sides; the 1e-8 is added to the max: a lone
+    2^-27 gives 128 * 2^-27 / (2^-27 + 1e-8) = 54.65 -> 55 (without the
+    epsilon it would be 127, with max(g, 1e-8) it would be 95); an all-zero
+    tensor gives codes 0 and g = 0."""
+    import oracle
+    xq, _ = oracle.quant_act_tensor(bits([[1.0, 2.5 / 128, -2.5 / 128, 3.5 / 128, -3.5 / 128]]))
+    assert xq.tolist() == [[127, 2, -2, 4, -4]]
+    fr = Fraction(128) * Fraction(2) ** -27 / Fraction(float(np.float32(2.0 ** -27) + np.float32(1e-8)))
+    assert abs(float(fr) - 54.65) < 0.01
+    xq, _ = oracle.quant_act_tensor(bits([[2.0 ** -27, 0.0]]))
+    assert xq.tolist() == [[55, 0]]
+    xq, g = oracle.quant_act_tensor(np.zeros((3, 5), np.uint16))
+    assert g == 0.0 and not xq.any()
+
+
+def test_v1_dequant_and_contraction():
+    """y = acc * gamma * g / 2^7: 64 * 0.5 * 2 / 128 = 0.5 and -3 * 0.5 * 2 /
+    128 = -0.0234375, both exact; the contraction of codes that include -128
+    equals a plain integer product (brute force)."""
+    import oracle
+    y = oracle.dequant_tensor(np.array([[64, -3]], np.int32), 0.5, 2.0)
+    assert y.tolist() == [[0.5, -0.0234375]]
+    rng = np.random.default_rng(5)
+    xq = rng.integers(-128, 128, size=(3, 37)).astype(np.int8)
+    xq[0, :] = -128
+    q = rng.integers(-1, 2, size=(4, 37)).astype(np.int8)
+    q[1, :] = -1
+    acc = oracle.contract_q128(xq, q)
+    ref = [[sum(int(a) * int(b) for a, b in zip(xr, qr)) for qr in q] for xr in xq]
+    assert acc.tolist() == ref
+    assert acc[0, 1] == 128 * 37
+
+
+def test_v2_f16_encoding_matches_numpy():
+    """binary16 rounding against numpy's float32 -> float16 conversion on a
+    log-spread sweep, exact ties (normal and subnormal) and the range ends;
+    decoding against numpy on every non-NaN bit pattern."""
+    import oracle
+    rng = np.random.default_rng(11)
+    v = (rng.choice([-1.0, 1.0], 3000) * 2.0 ** rng.uniform(-30, 17, 3000)).astype(np.float32)
+    special = [0.0, -0.0, 1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -24, 1.5 * 2 ** -24, 2 ** -25, 2.5 * 2 ** -24,
+               2 ** -14, 2 ** -14 - 2 ** -25, 65504, 65519, 65520, 7e4, -65520, 6.1e-5, 1e-9, 0.1, 0.85]
+    v = np.concatenate([v, np.array(special, np.float32)])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f32_to_f16_bits(v), ref)
+    allbits = np.arange(65536, dtype=np.uint16)
+    h = allbits.view(np.float16)
+    ok = ~np.isnan(h)
+    dec = oracle.f16_bits_to_f32(allbits[ok])
+    assert np.array_equal(dec.view(np.uint32), h[ok].astype(np.float32).view(np.uint32))
+
+
+def test_v2_row_scales_hand_values():
+    """Row absmeans: 0.625 (exact); 0.1 -> binary32 0.1f -> binary16 1638 *
+    2^-14 = 0.0999755859375 (bits 0x2E66); 0 -> 0; 3e-6 -> subnormal round(3e-6
+    * 2^24) = 50 quanta (bits 50); 0.85 -> 1741 * 2^-11 (bits 0x3ACD)."""
+    import oracle
+    w = np.array([[1, -1, 0.5, 0], [0.1] * 4, [0] * 4, [3e-6] * 4, [0.85, -0.85, 0.85, -0.85]], np.float32)
+    s16 = oracle.row_scales(w)
+    assert s16.tolist() == [0x3900, 0x2E66, 0, 50, 0x3ACD]
+    assert oracle.f16_bits_to_f32(s16).tolist() == [0.625, 0.0999755859375, 0.0, 50 * 2.0 ** -24, 1741 / 2048]
+
+
+def test_v2_codes_follow_each_rows_scale():
+    """Row 1 is 10 x row 0: each row's own scale gives both the codes
+    [1, 1, 1, 0] (0.4 / 0.8501 = 0.47 -> 0), with scales 0.85009765625 and
+    8.5; one scale for the matrix (4.675) would zero row 0."""
+    import oracle
+    w = np.array([[1, 1, 1, 0.4], [10, 10, 10, 4]], np.float32)
+    s16 = oracle.row_scales(w)
+    assert oracle.f16_bits_to_f32(s16).tolist() == [1741 / 2048, 8.5]
+    assert oracle.ternarize_rows(w, s16).tolist() == [[1, 1, 1, 0], [1, 1, 1, 0]]
+
+
+def test_v2_threshold_uses_scale_plus_epsilon():
+    """With a stored scale of 0.5 the rounding tie sits at 0.5 * (0.5 +
+    1e-5) = 0.250005: 0.250004 -> 0 and 0.250006 -> 1 (without the epsilon
+    both would be 1)."""
+    import oracle
+    w = np.array([[0.250004, 0.250006, -0.250004, -0.250006]], np.float32)
+    assert oracle.ternarize_rows(w, np.array([0x3800], np.uint16)).tolist() == [[0, 1, 0, -1]]
+
+
+def test_v2_reduces_to_the_tensor_rules_row_by_row():
+    """Row r of the variant equals the main path's ternarization and
+    de-quantization with gamma = that row's stored scale."""
+    import oracle
+    w = synth.latent_weights(21, 7, 300)
+    s16 = oracle.row_scales(w)
+    q = oracle.ternarize_rows(w, s16)
+    sf = oracle.f16_bits_to_f32(s16)
+    for r in range(7):
+        assert np.array_equal(q[r:r + 1], oracle.ternarize(w[r:r + 1], sf[r]))
+    xq, amax = oracle.quant_act(synth.activations_bf16(22, 3, 300, 0.01))
+    acc = oracle.contract(xq, q)
+    y = oracle.dequant_rows(acc, s16, amax)
+    for j in range(7):
+        assert np.array_equal(y[:, j:j + 1], oracle.dequant(acc[:, j:j + 1], sf[j], amax))
+    y1 = oracle.dequant_rows(np.array([[127]], np.int32), np.array([0x3800], np.uint16), np.array([2.0], np.float32))
+    assert y1.tolist() == [[1.0]]
+
+
+def test_v3_sign_with_zero_as_plus_one():
+    import oracle
+    w = np.array([[-0.0, 0.0, -1e-30, 3.0, -2.0, 1e-45, -1e-45]], np.float32)
+    assert oracle.binarize(w).tolist() == [[1, 1, -1, 1, -1, 1, -1]]
+
+
+def test_v3_forward_hand_values():
+    """x = [1, 0.5, -0.25]: a' = 1, codes [127, 64, -32] (63.5 -> 64, -31.75 ->
+    -32); signs [1, -1, -1] and [1, 1, 1] give acc 95 and 159; with s = 0.25,
+    y = acc * 0.25 / 127."""
+    import oracle
+    r = oracle.forward_binary(bits([[1.0, 0.5, -0.25]]), np.array([[0.3, -0.2, -0.1], [1, 1, 1]], np.float32), 0.25)
+    assert r["xq"].tolist() == [[127, 64, -32]]
+    assert r["acc"].tolist() == [[95, 159]]
+    assert r["y"][0, 0] == f32_nearest(Fraction(95, 4 * 127))
+    assert r["y"][0, 1] == f32_nearest(Fraction(159, 4 * 127))
