@@ -98,9 +98,26 @@ def load_library(path: str = LIB_PATH):
     lib.bitlinear_quant_forward_f32.restype = _ct.c_int
     lib.bitlinear_forward_swiglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
     lib.bitlinear_forward_swiglu.restype = _ct.c_int
+    lib.bitlinear_quant_act_tensor_workspace_bytes.argtypes = [_i64, _i64]
+    lib.bitlinear_quant_act_tensor_workspace_bytes.restype = _ct.c_size_t
+    lib.bitlinear_quant_act_tensor.argtypes = [_p, _i64, _i64, _p, _p, _p, _ct.c_size_t, _p]
+    lib.bitlinear_quant_act_tensor.restype = _ct.c_int
+    lib.bitlinear_pack_weights_rowscale.argtypes = [_p, _i64, _i64, _p, _ct.c_size_t, _p, _p]
+    lib.bitlinear_pack_weights_rowscale.restype = _ct.c_int
+    lib.bitlinear_packed_bytes_binary.argtypes = [_i64, _i64]
+    lib.bitlinear_packed_bytes_binary.restype = _ct.c_size_t
+    lib.bitlinear_pack_binary.argtypes = [_p, _i64, _i64, _p, _ct.c_size_t, _p]
+    lib.bitlinear_pack_binary.restype = _ct.c_int
+    lib.bitlinear_unpack_binary.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.bitlinear_unpack_binary.restype = _ct.c_int
+    lib.bitlinear_quant_forward_binary.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
+    lib.bitlinear_quant_forward_binary.restype = _ct.c_int
+    lib.bitlinear_quant_forward_binary_supported.argtypes = [_i64, _i64]
+    lib.bitlinear_quant_forward_binary_supported.restype = _ct.c_int
     lib.bitlinear_forward_lut_supported.argtypes = [_i64]
     lib.bitlinear_forward_lut_supported.restype = _ct.c_int
-    for name in ("bitlinear_forward", "bitlinear_forward_batched", "bitlinear_forward_lut"):
+    for name in ("bitlinear_forward", "bitlinear_forward_batched", "bitlinear_forward_lut",
+                 "bitlinear_forward_tensor_act", "bitlinear_forward_rowscale", "bitlinear_forward_binary"):
         fn = getattr(lib, name)
         fn.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         fn.restype = _ct.c_int
@@ -297,6 +314,157 @@ def bitlinear_forward_swiglu(packed_gate, gamma_gate, packed_up, gamma_up, f: in
         None if acc is None else _dev(acc, "acc", (_torch.int32,), 2 * m * f), _stream_handle(stream))
     _check(rc, "bitlinear_forward_swiglu")
     return h
+
+
+# ---------------------------------------------------------------------------
+# variant modes
+# ---------------------------------------------------------------------------
+
+def _variant_forward(fname, packed, packed_bytes, wscale, wscale_dtype, wscale_n, n, k, xq, ascale, ascale_n, y, acc,
+                     stream):
+    lib = load_library()
+    if xq.dim() != 2 or xq.shape[1] != k:
+        raise ValueError("xq must be [m][k]")
+    m = xq.shape[0]
+    if packed.numel() * packed.element_size() < packed_bytes:
+        raise BitlinearError(BITLINEAR_E_SIZE, fname)
+    if y is None:
+        y = _torch.empty((m, n), dtype=_torch.float32, device=xq.device)
+    rc = getattr(lib, fname)(
+        _dev(packed, "packed", (_torch.uint8,)), _dev(wscale, "weight scale", wscale_dtype, wscale_n), n, k,
+        _dev(xq, "xq", (_torch.int8,), m * k), _dev(ascale, "activation scale", (_torch.float32,), ascale_n), m,
+        _dev(y, "y", (_torch.float32,), m * n),
+        None if acc is None else _dev(acc, "acc", (_torch.int32,), m * n), _stream_handle(stream))
+    _check(rc, fname)
+    return y
+
+
+def bitlinear_quant_act_tensor_workspace_bytes(m: int, k: int) -> int:
+    return int(load_library().bitlinear_quant_act_tensor_workspace_bytes(m, k))
+
+
+def bitlinear_quant_act_tensor(x, xq=None, x_scale=None, workspace=None, stream=None):
+    """Per-tensor Q_b = 128 quantisation: x bf16 [m][k] -> (xq int8 [m][k] in
+    [-128, 127], g fp32 [1] = max |x| over the tensor)."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be [m][k]")
+    m, k = x.shape
+    if xq is None:
+        xq = _torch.empty((m, k), dtype=_torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = _torch.empty(1, dtype=_torch.float32, device=x.device)
+    if workspace is None:
+        workspace = _torch.empty(max(bitlinear_quant_act_tensor_workspace_bytes(m, k), 4), dtype=_torch.uint8,
+                                 device=x.device)
+    rc = lib.bitlinear_quant_act_tensor(_dev(x, "x", (_torch.bfloat16, _torch.int16, _torch.uint16)), m, k,
+                                        _dev(xq, "xq", (_torch.int8,), m * k),
+                                        _dev(x_scale, "x_scale", (_torch.float32,), 1),
+                                        _dev(workspace, "workspace", (_torch.uint8, _torch.int32)),
+                                        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(rc, "bitlinear_quant_act_tensor")
+    return xq, x_scale
+
+
+def bitlinear_forward_tensor_act(packed, gamma, n: int, k: int, xq, x_scale, y=None, acc=None, stream=None):
+    """Forward of per-tensor codes: y = acc * gamma * g / 128 (any m)."""
+    return _variant_forward("bitlinear_forward_tensor_act", packed, bitlinear_packed_bytes(n, k), gamma,
+                            (_torch.float32,), 1, n, k, xq, x_scale, 1, y, acc, stream)
+
+
+def bitlinear_pack_weights_rowscale(w, packed=None, scales=None, stream=None):
+    """w fp32 [n][k] -> (packed uint8, binary16 scales [n] as int16 bit patterns)."""
+    lib = load_library()
+    if w.dim() != 2:
+        raise ValueError("w must be [n][k]")
+    n, k = w.shape
+    nbytes = bitlinear_packed_bytes(n, k)
+    if nbytes == 0:
+        raise BitlinearError(BITLINEAR_E_SHAPE, "bitlinear_pack_weights_rowscale")
+    if packed is None:
+        packed = _torch.empty(nbytes, dtype=_torch.uint8, device=w.device)
+    if scales is None:
+        scales = _torch.empty(n, dtype=_torch.int16, device=w.device)
+    rc = lib.bitlinear_pack_weights_rowscale(
+        _dev(w, "w", (_torch.float32,)), n, k, _dev(packed, "packed", (_torch.uint8,)),
+        packed.numel() * packed.element_size(),
+        _dev(scales, "scales", (_torch.int16, _torch.uint16, _torch.float16), n), _stream_handle(stream))
+    _check(rc, "bitlinear_pack_weights_rowscale")
+    return packed, scales
+
+
+def bitlinear_forward_rowscale(packed, scales, n: int, k: int, xq, x_absmax, y=None, acc=None, stream=None):
+    """Forward with one binary16 scale per output row: y = acc * s_row * a' / 127 (any m)."""
+    m = xq.shape[0]
+    return _variant_forward("bitlinear_forward_rowscale", packed, bitlinear_packed_bytes(n, k), scales,
+                            (_torch.int16, _torch.uint16, _torch.float16), n, n, k, xq, x_absmax, m, y, acc, stream)
+
+
+def bitlinear_packed_bytes_binary(n: int, k: int) -> int:
+    return int(load_library().bitlinear_packed_bytes_binary(n, k))
+
+
+def bitlinear_pack_binary(w, packed=None, stream=None):
+    """w fp32 [n][k] -> packed sign bits (uint8 tensor)."""
+    lib = load_library()
+    if w.dim() != 2:
+        raise ValueError("w must be [n][k]")
+    n, k = w.shape
+    nbytes = bitlinear_packed_bytes_binary(n, k)
+    if nbytes == 0:
+        raise BitlinearError(BITLINEAR_E_SHAPE, "bitlinear_pack_binary")
+    if packed is None:
+        packed = _torch.empty(nbytes, dtype=_torch.uint8, device=w.device)
+    rc = lib.bitlinear_pack_binary(_dev(w, "w", (_torch.float32,)), n, k, _dev(packed, "packed", (_torch.uint8,)),
+                                   packed.numel() * packed.element_size(), _stream_handle(stream))
+    _check(rc, "bitlinear_pack_binary")
+    return packed
+
+
+def bitlinear_unpack_binary(packed, n: int, k: int, codes=None, stream=None):
+    lib = load_library()
+    if codes is None:
+        codes = _torch.empty((n, k), dtype=_torch.int8, device=packed.device)
+    if packed.numel() * packed.element_size() < bitlinear_packed_bytes_binary(n, k):
+        raise BitlinearError(BITLINEAR_E_SIZE, "bitlinear_unpack_binary")
+    rc = lib.bitlinear_unpack_binary(_dev(packed, "packed", (_torch.uint8,)), n, k,
+                                     _dev(codes, "codes", (_torch.int8,), n * k), _stream_handle(stream))
+    _check(rc, "bitlinear_unpack_binary")
+    return codes
+
+
+def bitlinear_forward_binary(packed, scale, n: int, k: int, xq, x_absmax, y=None, acc=None, stream=None):
+    """Binary-weight forward: y = acc * s * a' / 127 (any m); scale fp32 [1]."""
+    m = xq.shape[0]
+    return _variant_forward("bitlinear_forward_binary", packed, bitlinear_packed_bytes_binary(n, k), scale,
+                            (_torch.float32,), 1, n, k, xq, x_absmax, m, y, acc, stream)
+
+
+def bitlinear_quant_forward_binary_supported(m: int, k: int) -> bool:
+    return bool(load_library().bitlinear_quant_forward_binary_supported(m, k))
+
+
+def bitlinear_quant_forward_binary(packed, scale, n: int, k: int, x, y=None, acc=None, xq=None, x_absmax=None,
+                                   stream=None):
+    """Fused quantisation + binary-weight decode forward (as bitlinear_quant_forward)."""
+    lib = load_library()
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m][k]")
+    m = x.shape[0]
+    if packed.numel() * packed.element_size() < bitlinear_packed_bytes_binary(n, k):
+        raise BitlinearError(BITLINEAR_E_SIZE, "bitlinear_quant_forward_binary")
+    if y is None:
+        y = _torch.empty((m, n), dtype=_torch.float32, device=x.device)
+    rc = lib.bitlinear_quant_forward_binary(
+        _dev(packed, "packed", (_torch.uint8,)), _dev(scale, "scale", (_torch.float32,), 1), n, k,
+        _dev(x, "x", (_torch.bfloat16, _torch.int16, _torch.uint16)), m,
+        _dev(y, "y", (_torch.float32,), m * n),
+        None if acc is None else _dev(acc, "acc", (_torch.int32,), m * n),
+        None if xq is None else _dev(xq, "xq", (_torch.int8,), m * k),
+        None if x_absmax is None else _dev(x_absmax, "x_absmax", (_torch.float32,), m),
+        _stream_handle(stream))
+    _check(rc, "bitlinear_quant_forward_binary")
+    return y
 
 
 def bitlinear_forward_lut_supported(k: int) -> bool:

@@ -23,6 +23,15 @@ constexpr uint32_t kZeroCode = 0u;  // w = 0
 constexpr uint32_t kZeroWord = 0u;  // sixteen zero weights
 constexpr int kWeightShift = 6;     // expanded weight bytes are 64 * w
 
+// ---- packed binary layout (sign bits, one per weight) ----------------------
+// A binary tile is 16 rows x 256 columns = 512 bytes (the same columns as a
+// ternary tile, half the bytes): 64 slots of 8 bytes.  Slot l: row (l % 16),
+// columns 64*(l/16) + [0, 64); word s (0, 1) of a slot covers 32 of them,
+// column c at bit 8*(c%4) + 7 - c/4, set for -1 and clear for +1.  Then
+// ((word << i) & 0x80808080) | 0x40404040 yields columns 4i..4i+3 in order as
+// four int8 bytes equal to 64 * w, the ternary expansion's scale.
+constexpr int kBinTileBytes = 512;
+
 __host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kTileRows - 1) / kTileRows; }
 __host__ __device__ inline int64_t k_tiles(int64_t k) { return (k + kTileCols - 1) / kTileCols; }
 
@@ -86,6 +95,12 @@ __device__ __forceinline__ uint4 load_weights_nt(const uint4* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+__device__ __forceinline__ uint2 load_weights_nt2(const uint2* p) {
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  const v2u t = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+  return make_uint2(t.x, t.y);
+}
+
 // One packed word (16 weights) -> the 16-byte int8 operand 64 * w of one
 // 16x16x64 MFMA, columns in order: three shifts and four masks.
 typedef int expand_v4i __attribute__((ext_vector_type(4)));
@@ -94,6 +109,33 @@ __device__ __forceinline__ expand_v4i expand_ternary(uint32_t word) {
   return expand_v4i{static_cast<int>((word << 6) & m), static_cast<int>((word << 4) & m),
                     static_cast<int>((word << 2) & m), static_cast<int>(word & m)};
 }
+
+// Half o (columns 16o .. 16o+15) of a binary word -> the 16-byte int8
+// operand 64 * w, columns in order: one shift and one and-or per 4 weights.
+__device__ __forceinline__ expand_v4i expand_binary(uint32_t word, int o) {
+  const int i0 = 4 * o;
+  return expand_v4i{static_cast<int>(((word << i0) & 0x80808080u) | 0x40404040u),
+                    static_cast<int>(((word << (i0 + 1)) & 0x80808080u) | 0x40404040u),
+                    static_cast<int>(((word << (i0 + 2)) & 0x80808080u) | 0x40404040u),
+                    static_cast<int>(((word << (i0 + 3)) & 0x80808080u) | 0x40404040u)};
+}
+
+// binary16 bit pattern -> binary32 (exact)
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// How the forward kernels turn an int32 accumulator into y:
+//   y[t][j] = acc * (w_scale * a[t * astride] / qdiv)
+// w_scale is the tensor's gamma, or the binary16 scale of row j when
+// row_scale is set.  The main path: per-token a', qdiv 127.  The per-tensor
+// activation variant: one a (astride 0), qdiv 128.
+struct Dequant {
+  const uint16_t* row_scale;
+  float qdiv;
+  int astride;
+};
+constexpr Dequant kTokenDequant = {nullptr, 127.0f, 1};
 
 constexpr int kPackPartials = 1024;  // fp64 partial sums of |W| (max)
 
@@ -137,5 +179,21 @@ hipError_t launch_quant_gemv(const void* packed, const float* gamma, int64_t n, 
 hipError_t launch_gemm(const void* packed, const float* gamma, int64_t n, int64_t k,
                        const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc,
                        hipStream_t s);
+
+// ---- variant modes ------------------------------------------------------------
+// forward with a de-quantization mode and a weight format (binary: sign-bit tiles)
+hipError_t launch_gemv_ex(const void* packed, bool binary, const float* gamma, Dequant dq, int64_t n, int64_t k,
+                          const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s);
+hipError_t launch_quant_gemv_binary(const void* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                                    int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s);
+bool gemv_binary_fits_lds(int64_t m, int64_t k);
+hipError_t launch_gemm_ex(const void* packed, bool binary, const float* gamma, Dequant dq, int64_t n, int64_t k,
+                          const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s);
+int quant_tensor_partial_count(int64_t m, int64_t k);
+hipError_t launch_quant_act_tensor(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* gx,
+                                   uint32_t* partials, hipStream_t s);
+hipError_t launch_pack_rowscale(const float* w, int64_t n, int64_t k, void* packed, uint16_t* scales, hipStream_t s);
+hipError_t launch_pack_binary(const float* w, int64_t n, int64_t k, void* packed, hipStream_t s);
+hipError_t launch_unpack_binary(const void* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t s);
 
 }  // namespace bitlinear

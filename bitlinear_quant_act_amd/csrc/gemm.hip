@@ -64,17 +64,60 @@ __device__ __forceinline__ uint4 load_a16(const int8_t* __restrict__ xq, int64_t
   return r;
 }
 
-template <int BM, int BN>
+// WB: 2 = ternary 1 KiB tiles, 1 = binary 512-byte tiles (same 256 columns)
+template <int WB>
+constexpr int wtile_bytes() {
+  return WB == 1 ? kBinTileBytes : kTileBytes;
+}
+
+// The lane's weight slot of 64-column group g and its operand for step
+// `half` (columns 64g + 32 half + 16h + [0, 16)): ternary slots are 16 bytes
+// (word 2 half + h); binary slots 8 bytes (half h of word `half`).
+template <int WB>
+__device__ __forceinline__ uint4 read_slot(const uint8_t* p) {
+  if (WB == 1) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return make_uint4(v.x, v.y, 0, 0);
+  }
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <int WB>
+__device__ __forceinline__ v4i slot_operand(uint4 slot, int half, int h) {
+  const uint32_t lo = half == 0 ? slot.x : slot.z;  // half is a compile-time constant at every call
+  const uint32_t hi = half == 0 ? slot.y : slot.w;
+  if (WB == 1) return expand_binary(half == 0 ? slot.x : slot.y, h);
+  return expand_ternary(h == 0 ? lo : hi);
+}
+
+template <int WB>
+__device__ __forceinline__ int slot_offset(int b_row) {  // + nb * 2 tiles + g * (slot bytes * 16)
+  return WB == 1 ? (b_row >> 4) * kBinTileBytes + (b_row & 15) * 8 : (b_row >> 4) * kTileBytes + (b_row & 15) * 16;
+}
+
+// Output scale of token t (LDS-staged): gamma * a / qdiv, or a alone when the
+// scale is per weight row (then applied in the epilogue).
+__device__ __forceinline__ float token_scale(const float* gamma_p, Dequant dq, const float* amax, int64_t t) {
+  const float a = amax[t * dq.astride];
+  return dq.row_scale ? a : *gamma_p * a / dq.qdiv;
+}
+
+__device__ __forceinline__ float out_scale(Dequant dq, float staged, int64_t j) {
+  return dq.row_scale ? half_bits_to_float(dq.row_scale[j]) * staged / dq.qdiv : staged;
+}
+
+template <int BM, int BN, int WB = 2>
 struct TileShape {
   static constexpr int kABytes = BM * kAPitch;
-  static constexpr int kBBytes = (BN / kTileRows) * kTileBytes;
+  static constexpr int kBBytes = (BN / kTileRows) * wtile_bytes<WB>();
   static constexpr int kStage = kABytes + kBBytes;
   static constexpr int kLds = 2 * kStage;
 };
 
-template <int BM, int BN, int WM, int WN, bool VEC>
+template <int BM, int BN, int WM, int WN, bool VEC, int WB = 2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restrict__ packed,
-                                                           const float* __restrict__ gamma_p, int64_t n, int64_t k,
+                                                           const float* __restrict__ gamma_p, Dequant dq, int64_t n,
+                                                           int64_t k,
                                                            int kt_count, const int8_t* __restrict__ xq,
                                                            const float* __restrict__ amax, int64_t m, int mt_count,
                                                            int nt_count, float* __restrict__ y,
@@ -83,9 +126,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;  // 32 x 32 output blocks per wave
   constexpr int A_PER = BM * 16 / kThreads;  // 16-byte activation chunks per thread per step
-  constexpr int B_CHUNKS = (BN / kTileRows) * 64;
+  constexpr int TB = wtile_bytes<WB>();
+  constexpr int CPT = TB / 16;  // 16-byte chunks per weight tile
+  constexpr int B_CHUNKS = (BN / kTileRows) * CPT;
   constexpr int B_PER = (B_CHUNKS + kThreads - 1) / kThreads;
-  using TS = TileShape<BM, BN>;
+  using TS = TileShape<BM, BN, WB>;
   static_assert(A_PER >= 1 && MB >= 1 && NB >= 1 && TM % 32 == 0 && TN % 32 == 0, "tile too small");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -118,8 +163,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
       const int c = tid + kThreads * i;
-      const int64_t rbg = rb0 + (c >> 6);
-      breg[i] = (c < B_CHUNKS && rbg < rb_count) ? packed[(rbg * kt_count + kt) * 64 + (c & 63)]
+      const int64_t rbg = rb0 + c / CPT;
+      breg[i] = (c < B_CHUNKS && rbg < rb_count) ? packed[(rbg * kt_count + kt) * CPT + c % CPT]
                                                  : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
     }
   };
@@ -146,13 +191,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
 
   // per-lane LDS offsets: A row (token), B slot of the lane's weight row
   const int a_off = (wm * TM + l32) * kAPitch + 16 * h;
-  const int b_row = wn * TN + l32;                              // + nb * 32
-  const int b_off = (b_row >> 4) * kTileBytes + (b_row & 15) * 16;  // + nb * 2 KiB + g * 256
+  const int b_row = wn * TN + l32;           // + nb * 32
+  const int b_off = slot_offset<WB>(b_row);  // + nb * 2 tiles + g * 16 slots
 
   __shared__ float scale_s[BM];
   if (tid < BM) {
     const int64_t t = m0 + tid;
-    scale_s[tid] = t < m ? *gamma_p * amax[t] / 127.0f : 0.0f;
+    scale_s[tid] = t < m ? token_scale(gamma_p, dq, amax, t) : 0.0f;
   }
 
   load_global(0);
@@ -169,15 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
       // + [0,16)) and 2 + h (columns 64g + 32 + 16h + [0,16))
       uint4 slot[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) slot[nb] = *reinterpret_cast<const uint4*>(Bs + b_off + nb * 2 * kTileBytes + g * 256);
+      for (int nb = 0; nb < NB; ++nb) slot[nb] = read_slot<WB>(Bs + b_off + nb * 2 * TB + g * (TB / 4));
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         v4i b[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const uint32_t word = half == 0 ? (h == 0 ? slot[nb].x : slot[nb].y) : (h == 0 ? slot[nb].z : slot[nb].w);
-          b[nb] = expand_ternary(word);
-        }
+        for (int nb = 0; nb < NB; ++nb) b[nb] = slot_operand<WB>(slot[nb], half, h);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const v4i a = *reinterpret_cast<const v4i*>(As + a_off + mb * 32 * kAPitch + g * 64 + half * 32);
@@ -199,13 +241,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
       const int tl = wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       const int64_t t = m0 + tl;
       if (t >= m) continue;
-      const float scale = scale_s[tl];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int64_t j = n0 + wn * TN + nb * 32 + l32;
         if (j < n) {
           const int v = acc[mb][nb][r] >> kWeightShift;  // exact: multiples of 64
-          y[t * n + j] = static_cast<float>(v) * scale;
+          y[t * n + j] = static_cast<float>(v) * out_scale(dq, scale_s[tl], j);
           if (acc_out) acc_out[t * n + j] = v;
         }
       }
@@ -239,37 +280,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
 
 #define BITLINEAR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int BM, int BN>
+template <int BM, int BN, int WB = 2>
 struct DmaShape {
   static constexpr int kABytes = BM * kTileCols;
-  static constexpr int kBBytes = (BN / kTileRows) * kTileBytes;
+  static constexpr int kBBytes = (BN / kTileRows) * wtile_bytes<WB>();
   static constexpr int kStage = kABytes + kBBytes;
   static constexpr int kADma = BM / 16;   // 1 KiB copies per wave for the activation tile
-  static constexpr int kBDma = BN / 64;   // 1 KiB copies per wave for the weight tiles
+  static constexpr int kBDma = BN / 64;   // 1 KiB copies per wave for the (ternary) weight tiles
   static constexpr int kDma = kADma + kBDma;
 };
 
-constexpr int DmaStageBytes(int bm, int bn) { return bm * kTileCols + (bn / kTileRows) * kTileBytes; }
+constexpr int DmaStageBytes(int bm, int bn, int wb = 2) {
+  return bm * kTileCols + (bn / kTileRows) * (wb == 1 ? kBinTileBytes : kTileBytes);
+}
 
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+constexpr int kPastDescriptor = 0x7fffff00;  // byte offset beyond any descriptor's range (reads return 0)
 
 // With SWIGLU the BN weight rows of a stage come from two matrices, gate and
 // up, in alternating 32-row blocks over BN / 2 features: 32-row block v holds
 // rows 32 * (v / 2) + [0, 32) of the workgroup's features, from gate for even
 // v and from up for odd v (b_rsrc / u_rsrc).
-template <int BM, int BN, bool SWIGLU = false>
+//
+// Binary weights (WB = 1): one 1 KiB copy carries the 512-byte tiles of two
+// row blocks (lanes 0-31 the first, 32-63 the second); the BN / 32 copies of
+// a stage are dealt to the waves round-robin, so waves may issue different
+// counts (the binary kernel runs two stages and waits for all copies).
+template <int BM, int BN, bool SWIGLU = false, int WB = 2>
 __device__ __forceinline__ void issue_tile(uint8_t* stage, __amdgpu_buffer_rsrc_t a_rsrc, __amdgpu_buffer_rsrc_t b_rsrc,
                                            __amdgpu_buffer_rsrc_t u_rsrc, int k, int kt_count, int kt, int wave,
                                            int lane) {
-  using DS = DmaShape<BM, BN>;
+  using DS = DmaShape<BM, BN, WB>;
   const int ktc = kt < kt_count ? kt : 0;  // tiles past the end re-read tile 0 into an unused stage
 #pragma unroll
   for (int i = 0; i < DS::kADma; ++i) {
     const int blk = wave * DS::kADma + i;  // 1 KiB = 4 rows
     const int row = 4 * blk + (lane >> 4);
     const int chunk = (lane & 15) ^ (row & 15);
-    const int off = row * k + ktc * kTileCols + chunk * 16;
+    int off = row * k + ktc * kTileCols + chunk * 16;
+    // binary padding weights are +1, not 0: columns past k must read as zero
+    // codes, so their chunk is sent past the descriptor (which returns zeros)
+    // instead of into the next token's row
+    if (WB == 1 && ktc * kTileCols + chunk * 16 >= k) off = kPastDescriptor;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, BITLINEAR_LDS(stage + blk * 1024), 16, off, 0, 0, 0);
+  }
+  if (WB == 1) {
+    for (int i = wave; i < BN / 32; i += kThreads / 64) {
+      const int rbl = 2 * i + (lane >> 5);
+      const int off = (rbl * kt_count + ktc) * kBinTileBytes + (lane & 31) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, BITLINEAR_LDS(stage + DS::kABytes + i * 1024), 16, off, 0, 0, 0);
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < DS::kBDma; ++i) {
@@ -298,9 +359,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // up projection (same [n][k] shape, n = features); the workgroup covers
 // BN / 2 features and writes h = silu(y_gate) * y_up to y [m][n] (acc_out, if
 // set, is [m][2n]: gate accumulators, then up accumulators).
-template <int BM, int BN, int WM, int WN, int S, int OCC, bool SWIGLU = false>
+template <int BM, int BN, int WM, int WN, int S, int OCC, bool SWIGLU = false, int WB = 2>
 __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* __restrict__ packed_b,
-                                                               const float* __restrict__ gamma_p, int64_t n,
+                                                               const float* __restrict__ gamma_p, Dequant dq, int64_t n,
                                                                int64_t k, int kt_count, const int8_t* __restrict__ xq,
                                                                const float* __restrict__ amax, int64_t m,
                                                                int mt_count, int nt_count, float* __restrict__ y,
@@ -309,7 +370,9 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
                                                                const float* __restrict__ gamma_u) {
   static_assert(WM * WN == kThreads / 64, "4 waves");
   static_assert(S >= 2 && S <= 4, "2..4 stages");
-  using DS = DmaShape<BM, BN>;
+  static_assert(WB == 2 || (S == 2 && !SWIGLU), "binary weights: two stages, plain epilogue");
+  using DS = DmaShape<BM, BN, WB>;
+  constexpr int TB = wtile_bytes<WB>();
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = TM / 32, NB = TN / 32;
   static_assert(MB >= 1 && NB >= 1 && TM % 32 == 0 && TN % 32 == 0 && BN % 64 == 0, "tile shape");
@@ -347,7 +410,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   const int a_row0 = wm * TM + l32;                                   // + mb * 32; row % 16 == l32 % 16
   const int a_x = (l32 & 15) ^ h;                                     // swizzle key with the lane's half folded in
   const int b_row = wn * TN + l32;                                    // + nb * 32
-  const int b_off = DS::kABytes + (b_row >> 4) * kTileBytes + (b_row & 15) * 16;  // + nb * 2 KiB + g * 256
+  const int b_off = DS::kABytes + slot_offset<WB>(b_row);              // + nb * 2 tiles + g * 16 slots
 
   // operands of one 64-column group: NB weight slots and 2 x MB activation chunks
   struct Ops {
@@ -356,7 +419,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   };
   auto read_ops = [&](const uint8_t* st, int g, Ops& o) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o.slot[nb] = *reinterpret_cast<const uint4*>(st + b_off + nb * 2 * kTileBytes + g * 256);
+    for (int nb = 0; nb < NB; ++nb) o.slot[nb] = read_slot<WB>(st + b_off + nb * 2 * TB + g * (TB / 4));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int chunk = (4 * g + 2 * half) ^ a_x;  // logical chunk 4g + 2 half + h, swizzled by row % 16
@@ -370,11 +433,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
     for (int half = 0; half < 2; ++half) {
       v4i b[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // words h (columns 64g + 16h + [0,16)) and 2 + h (columns 64g + 32 + 16h + [0,16))
-        const uint32_t word = half == 0 ? (h == 0 ? o.slot[nb].x : o.slot[nb].y) : (h == 0 ? o.slot[nb].z : o.slot[nb].w);
-        b[nb] = expand_ternary(word);
-      }
+      for (int nb = 0; nb < NB; ++nb) b[nb] = slot_operand<WB>(o.slot[nb], half, h);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -409,7 +468,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   __shared__ float scale_u[SWIGLU ? BM : 1];
   if (tid < BM) {
     const int64_t t = m0 + tid;
-    scale_s[tid] = t < m ? *gamma_p * amax[t] / 127.0f : 0.0f;
+    scale_s[tid] = t < m ? token_scale(gamma_p, dq, amax, t) : 0.0f;
     if (SWIGLU) scale_u[tid] = t < m ? *gamma_u * amax[t] / 127.0f : 0.0f;
   }
   lds_barrier();
@@ -420,23 +479,22 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(xq + m0 * k), 0, static_cast<int>(rows_here * k), kBufferWord3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(packed_b + rb0 * kt_count * kTileBytes), 0,
-      static_cast<int>(rbs_here * kt_count * kTileBytes), kBufferWord3);
+      const_cast<uint8_t*>(packed_b + rb0 * kt_count * TB), 0, static_cast<int>(rbs_here * kt_count * TB), kBufferWord3);
   const __amdgpu_buffer_rsrc_t u_rsrc = SWIGLU ? __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(packed_u + rb0 * kt_count * kTileBytes), 0,
       static_cast<int>(rbs_here * kt_count * kTileBytes), kBufferWord3) : b_rsrc;
   const int k32 = static_cast<int>(k);
 
   // prologue: tiles 0 .. S-2 in flight
-  issue_tile<BM, BN, SWIGLU>(st0, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 0, wave, lane);
-  if (S > 2) issue_tile<BM, BN, SWIGLU>(st1, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 1, wave, lane);
-  if (S > 3) issue_tile<BM, BN, SWIGLU>(st2, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 2, wave, lane);
+  issue_tile<BM, BN, SWIGLU, WB>(st0, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 0, wave, lane);
+  if (S > 2) issue_tile<BM, BN, SWIGLU, WB>(st1, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 1, wave, lane);
+  if (S > 3) issue_tile<BM, BN, SWIGLU, WB>(st2, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 2, wave, lane);
 
   // one pipeline step: tile kt sits in stage `cur`; tile kt + S - 1 goes to `nxt`
   auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
     wait_vmcnt<(S - 2) * DS::kDma>();
     __builtin_amdgcn_s_barrier();
-    issue_tile<BM, BN, SWIGLU>(nxt, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, kt + S - 1, wave, lane);
+    issue_tile<BM, BN, SWIGLU, WB>(nxt, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, kt + S - 1, wave, lane);
     compute(cur);
   };
   for (int kt = 0; kt < kt_count; kt += S) {
@@ -484,13 +542,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
       const int tl = wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       const int64_t t = m0 + tl;
       if (t >= m) continue;
-      const float scale = scale_s[tl];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int64_t j = n0 + wn * TN + nb * 32 + l32;
         if (j < n) {
           const int v = acc[mb][nb][r] >> kWeightShift;
-          y[t * n + j] = static_cast<float>(v) * scale;
+          y[t * n + j] = static_cast<float>(v) * out_scale(dq, scale_s[tl], j);
           if (acc_out) acc_out[t * n + j] = v;
         }
       }
@@ -498,28 +555,28 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+template <int BM, int BN, int WM, int WN, int WB>
+hipError_t launch(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
                   const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s, bool vec) {
   const int kt = static_cast<int>(k_tiles(k));
   const int64_t mt = (m + BM - 1) / BM;
   const int64_t ntl = (n + BN - 1) / BN;
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;  // beyond one grid dimension
   const dim3 grid(static_cast<unsigned>(mt * ntl));
-  constexpr int lds = TileShape<BM, BN>::kLds;
+  constexpr int lds = TileShape<BM, BN, WB>::kLds;
   const uint4* p = static_cast<const uint4*>(packed);
   if (vec) {
-    static const bool attr = lds <= 65536 || hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, true>),
+    static const bool attr = lds <= 65536 || hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, true, WB>),
                                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
     (void)attr;
-    gemm_kernel<BM, BN, WM, WN, true><<<grid, kThreads, lds, s>>>(p, gamma, n, k, kt, xq, amax, m, static_cast<int>(mt),
-                                                                  static_cast<int>(ntl), y, acc);
+    gemm_kernel<BM, BN, WM, WN, true, WB><<<grid, kThreads, lds, s>>>(p, gamma, dq, n, k, kt, xq, amax, m,
+                                                                      static_cast<int>(mt), static_cast<int>(ntl), y, acc);
   } else {
-    static const bool attr = lds <= 65536 || hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, false>),
+    static const bool attr = lds <= 65536 || hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<BM, BN, WM, WN, false, WB>),
                                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
     (void)attr;
-    gemm_kernel<BM, BN, WM, WN, false><<<grid, kThreads, lds, s>>>(p, gamma, n, k, kt, xq, amax, m, static_cast<int>(mt),
-                                                                   static_cast<int>(ntl), y, acc);
+    gemm_kernel<BM, BN, WM, WN, false, WB><<<grid, kThreads, lds, s>>>(p, gamma, dq, n, k, kt, xq, amax, m,
+                                                                       static_cast<int>(mt), static_cast<int>(ntl), y, acc);
   }
   return hipGetLastError();
 }
@@ -541,10 +598,10 @@ Cand choose(int64_t m, int64_t /*n*/) {
 
 // ---- direct-to-LDS pipeline configurations ---------------------------------
 
-template <int BM, int BN, int WM, int WN, int S, int OCC>
-hipError_t launch_dma(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+template <int BM, int BN, int WM, int WN, int S, int OCC, int WB = 2>
+hipError_t launch_dma(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
                       const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
-  static_assert(S * DmaStageBytes(BM, BN) <= 163840, "LDS per workgroup");  // OCC: register-budget hint
+  static_assert(S * DmaStageBytes(BM, BN, WB) <= 163840, "LDS per workgroup");  // OCC: register-budget hint
   // 32-bit buffer offsets: BM rows of at most 2^18 codes, BN / 16 row blocks of at most 1024 tiles
   static_assert(static_cast<int64_t>(BM) << 18 <= 0x7fffffff && static_cast<int64_t>(BN / kTileRows) * 1024 * kTileBytes <= 0x7fffffff,
                 "buffer offsets fit 31 bits");
@@ -552,8 +609,8 @@ hipError_t launch_dma(const void* packed, const float* gamma, int64_t n, int64_t
   const int64_t mt = (m + BM - 1) / BM;
   const int64_t ntl = (n + BN - 1) / BN;
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
-  gemm_dma_kernel<BM, BN, WM, WN, S, OCC><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
-      static_cast<const uint8_t*>(packed), gamma, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl),
+  gemm_dma_kernel<BM, BN, WM, WN, S, OCC, false, WB><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+      static_cast<const uint8_t*>(packed), gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl),
       y, acc, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -570,7 +627,7 @@ hipError_t launch_dma_swiglu(const void* packed_g, const float* gamma_g, const v
   const int64_t ntl = (f + BN / 2 - 1) / (BN / 2);
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
   gemm_dma_kernel<BM, BN, WM, WN, S, OCC, true><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
-      static_cast<const uint8_t*>(packed_g), gamma_g, f, k, kt, xq, amax, m, static_cast<int>(mt),
+      static_cast<const uint8_t*>(packed_g), gamma_g, kTokenDequant, f, k, kt, xq, amax, m, static_cast<int>(mt),
       static_cast<int>(ntl), h, acc, static_cast<const uint8_t*>(packed_u), gamma_u);
   return hipGetLastError();
 }
@@ -609,24 +666,37 @@ hipError_t launch_gemm_swiglu(const void* packed_g, const float* gamma_g, const 
   return launch_dma_swiglu<64, 128, 2, 2, 2, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
 }
 
-hipError_t launch_gemm(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
-                       const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
+hipError_t launch_gemm_ex(const void* packed, bool binary, const float* gamma, Dequant dq, int64_t n, int64_t k,
+                          const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
+  if (vec && binary) {  // two stages: the binary tiles' copies are not the same count on every wave
+    switch (choose_dma(m, n)) {
+      case kWide: return launch_dma<64, 256, 2, 2, 2, 2, 1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+      case kMid: return launch_dma<64, 192, 2, 2, 2, 2, 1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+      case kSmall: return launch_dma<64, 64, 2, 2, 2, 3, 1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+    }
+  }
   if (vec) {
     switch (choose_dma(m, n)) {
-      case kWide: return launch_dma<64, 256, 2, 2, 2, 2>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      case kMid: return launch_dma<64, 192, 2, 2, 2, 2>(packed, gamma, n, k, xq, amax, m, y, acc, s);
-      case kSmall: return launch_dma<64, 64, 2, 2, 3, 3>(packed, gamma, n, k, xq, amax, m, y, acc, s);
+      case kWide: return launch_dma<64, 256, 2, 2, 2, 2>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+      case kMid: return launch_dma<64, 192, 2, 2, 2, 2>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+      case kSmall: return launch_dma<64, 64, 2, 2, 3, 3>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
     }
   }
   const Cand c = choose(m, n);
-#define BITLINEAR_GEMM_CASE(BM_, BN_, WM_, WN_)                 \
-  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_) \
-    return launch<BM_, BN_, WM_, WN_>(packed, gamma, n, k, xq, amax, m, y, acc, s, vec);
+#define BITLINEAR_GEMM_CASE(BM_, BN_, WM_, WN_)                                                            \
+  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_)                                            \
+    return binary ? launch<BM_, BN_, WM_, WN_, 1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s, vec)    \
+                  : launch<BM_, BN_, WM_, WN_, 2>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s, vec);
   BITLINEAR_GEMM_CASE(128, 128, 2, 2)
   BITLINEAR_GEMM_CASE(64, 64, 2, 2)
 #undef BITLINEAR_GEMM_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
+                       const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
+  return launch_gemm_ex(packed, false, gamma, kTokenDequant, n, k, xq, amax, m, y, acc, s);
 }
 
 }  // namespace bitlinear

@@ -586,14 +586,29 @@ __device__ __forceinline__ void prefetch_f32(uint4 (&cache)[kCachedChunks], cons
 // wave's share of item (rb, c) is tiles c*U*WAVES + wave + u*WAVES, u < U.
 // With an up matrix (SwiGLU) an item walks 2 * kt_count tiles: the row
 // block's gate tiles, then its up tiles.
-template <int WAVES, int U, bool SWIGLU>
+//
+// Binary weights (WB = 1): an item is a pair of 512-byte tiles (512 columns),
+// loaded as two 8-byte-per-lane reads into one register quad (tile 2i in
+// x, y; tile 2i + 1 in z, w); kt_count is then the tile count rounded up to
+// even and kt_real the stored tile count of a row block.
+template <int WAVES, int U, bool SWIGLU, int WB = 2>
 __device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict__ packed,
                                           const uint4* __restrict__ packed_u, int64_t rb, int c, int kt_count,
-                                          int wave, int lane, bool valid) {
-  const int kt_items = SWIGLU ? 2 * kt_count : kt_count;
+                                          int kt_real, int wave, int lane, bool valid) {
+  const int kt_items = WB == 1 ? kt_count / 2 : SWIGLU ? 2 * kt_count : kt_count;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int kv = c * U * WAVES + wave + u * WAVES;
+    if (WB == 1) {
+      w[u] = make_uint4(0, 0, 0, 0);
+      if (valid && kv < kt_items) {
+        const uint2* t = reinterpret_cast<const uint2*>(packed) + (rb * kt_real + 2 * kv) * 64 + lane;
+        const uint2 lo = load_weights_nt2(t);
+        const uint2 hi = 2 * kv + 1 < kt_real ? load_weights_nt2(t + 64) : make_uint2(0, 0);
+        w[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+      continue;
+    }
     const bool up = SWIGLU && kv >= kt_count;
     const int kt = up ? kv - kt_count : kv;
     w[u] = (valid && kv < kt_items) ? load_weights_nt((up ? packed_u : packed) + (rb * kt_count + kt) * 64 + lane)
@@ -601,13 +616,27 @@ __device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict
   }
 }
 
+// Operand j of an item: its activation column offset (inside the lane's
+// 64-column group) and its expanded weight bytes.  Ternary: word j of the
+// tile's slot, 16 columns each.  Binary: tile j / 4 of the pair, word
+// (j / 2) % 2 of its slot, half j % 2 of the word.
+template <int WB>
+__device__ __forceinline__ int item_col(int item, int j) {
+  return WB == 1 ? item * 512 + (j >> 2) * kTileCols + ((j >> 1) & 1) * 32 + (j & 1) * 16 : item * kTileCols + 16 * j;
+}
+
+template <int WB>
+__device__ __forceinline__ v4i item_weights(const uint32_t (&words)[4], int j) {
+  return WB == 1 ? expand_binary(words[j >> 1], j & 1) : expand_ternary(words[j]);
+}
+
 // SWIGLU: packed / gamma_p are the gate projection, packed_u / gamma_u the up
 // projection; y receives h = silu(y_gate) * y_up [m][n] and acc_out (if set)
 // the gate then the up accumulators, [m][2n].
-template <int WAVES, int U, int SRC, bool VEC, bool SWIGLU = false>
+template <int WAVES, int U, int SRC, bool VEC, bool SWIGLU = false, int WB = 2>
 __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __restrict__ packed,
-                                                              const float* __restrict__ gamma_p, int64_t n,
-                                                              int64_t k, int kt_count, int64_t rb_count,
+                                                              const float* __restrict__ gamma_p, Dequant dq, int64_t n,
+                                                              int64_t k, int kt_count, int kt_real, int64_t rb_count,
                                                               const void* __restrict__ xsrc,
                                                               const float* __restrict__ amax_in, int m,
                                                               float* __restrict__ y, int32_t* __restrict__ acc_out,
@@ -617,6 +646,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
                                                               const uint4* __restrict__ packed_u,
                                                               const float* __restrict__ gamma_u) {
   static_assert(!SWIGLU || WAVES >= 4, "one token group per wave in the SwiGLU epilogue");
+  static_assert(WB == 2 || !SWIGLU, "binary weights: plain epilogue only");
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ int red[WAVES * 4 * 64];
   __shared__ float amax_s[16];
@@ -632,8 +662,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   const bool has_tok = tok < m;
   const int pitch = static_cast<int>(lds_pitch(kt_count));
   const int kpad = kt_count * kTileCols;
-  const int kt_items = SWIGLU ? 2 * kt_count : kt_count;  // tiles per item
+  const int kt_items = WB == 1 ? kt_count / 2 : SWIGLU ? 2 * kt_count : kt_count;  // items per row block
   const int nchunks = (kt_items + U * WAVES - 1) / (U * WAVES);
+  constexpr int kOps = WB == 1 ? 8 : 4;  // MFMA operands per item
 
   int64_t rb = blockIdx.x;
   int c = 0;
@@ -649,11 +680,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
       prefetch_bf16(cache, static_cast<const uint16_t*>(xsrc), m, k);
   }
   uint4 wcur[U];
-  load_item<WAVES, U, SWIGLU>(wcur, packed, packed_u, rb, c, kt_count, wave, lane, rb < rb_count);
+  load_item<WAVES, U, SWIGLU, WB>(wcur, packed, packed_u, rb, c, kt_count, kt_real, wave, lane, rb < rb_count);
 
   if (SRC == kFromCodes) {
     stage_codes(xs, pitch, cache, static_cast<const int8_t*>(xsrc), m, k, kpad, VEC);
-    if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x];
+    if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x * dq.astride];
   } else if (SRC == kFromBf16Norm && VEC && m == 1) {
     stage_bf16_norm_single<WAVES>(xs, amax_s, quant_s, wmax_s, wss_s, cache, gcache, static_cast<const uint16_t*>(xsrc),
                                   gain, eps, k, kpad, xq_out, amax_out);
@@ -671,7 +702,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   }
   lds_barrier();
 
-  const float gamma = *gamma_p;
+  const float gamma = dq.row_scale ? 0.0f : *gamma_p;  // no tensor scale with per-row scales
   const float gamma_up = SWIGLU ? *gamma_u : 0.0f;
   const v4i zero4 = {0, 0, 0, 0};
   const int8_t* xrow = xs + (has_tok ? tok : 0) * pitch + g * 64;
@@ -685,7 +716,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
       rbn = rb + gridDim.x;
     }
     uint4 wnext[U];
-    load_item<WAVES, U, SWIGLU>(wnext, packed, packed_u, rbn, cn, kt_count, wave, lane, rbn < rb_count);
+    load_item<WAVES, U, SWIGLU, WB>(wnext, packed, packed_u, rbn, cn, kt_count, kt_real, wave, lane, rbn < rb_count);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kv = c * U * WAVES + wave + u * WAVES;
@@ -701,9 +732,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
           }
         } else {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const v4i a = has_tok ? *reinterpret_cast<const v4i*>(xrow + kt * kTileCols + 16 * s) : zero4;
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_ternary(words[s]), acc, 0, 0, 0);
+          for (int j = 0; j < kOps; ++j) {
+            const v4i a = has_tok ? *reinterpret_cast<const v4i*>(xrow + item_col<WB>(kt, j)) : zero4;
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, item_weights<WB>(words, j), acc, 0, 0, 0);
           }
         }
       }
@@ -756,7 +787,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
         const int t = 4 * g + r;
         if (t < m && row < n) {
           v >>= kWeightShift;  // exact: the sum is a multiple of 64
-          const float scale = gamma * amax_s[t] / 127.0f;
+          const float ws = dq.row_scale ? half_bits_to_float(dq.row_scale[row]) : gamma;
+          const float scale = ws * amax_s[t] / dq.qdiv;
           y[t * n + row] = static_cast<float>(v) * scale;
           if (acc_out) acc_out[t * n + row] = v;
         }
@@ -791,10 +823,10 @@ __device__ __forceinline__ v4i load_x16(const int8_t* __restrict__ row, int64_t 
   return r;
 }
 
-template <int WAVES, int U, bool VEC>
+template <int WAVES, int U, bool VEC, int WB = 2>
 __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __restrict__ packed,
-                                                                 const float* __restrict__ gamma_p, int64_t n,
-                                                                 int64_t k, int kt_count,
+                                                                 const float* __restrict__ gamma_p, Dequant dq,
+                                                                 int64_t n, int64_t k, int kt_count, int kt_real,
                                                                  const int8_t* __restrict__ xq,
                                                                  const float* __restrict__ amax, int m,
                                                                  float* __restrict__ y, int32_t* __restrict__ acc_out) {
@@ -805,33 +837,41 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
   const int g = lane >> 4;
   const int tok = lane & 15;
   const bool has_tok = tok < m;
-  const uint4* tiles = packed + rb * kt_count * 64 + lane;
   const int8_t* xrow = xq + static_cast<int64_t>(has_tok ? tok : 0) * k;
+  constexpr int kOps = WB == 1 ? 8 : 4;
+  const int items = WB == 1 ? kt_count / 2 : kt_count;
 
   v4i acc = {0, 0, 0, 0};
-  for (int kt0 = wave; kt0 < kt_count; kt0 += WAVES * U) {
+  for (int i0 = wave; i0 < items; i0 += WAVES * U) {
     uint4 wv[U];
-    v4i xv[U][4];
+    v4i xv[U][kOps];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kt = kt0 + u * WAVES;
-      const bool in = kt < kt_count;
-      wv[u] = in ? load_weights_nt(tiles + static_cast<int64_t>(kt) * 64)
-                 : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
-      const int64_t c0 = static_cast<int64_t>(kt) * kTileCols + g * 64;
+      const int it = i0 + u * WAVES;
+      const bool in = it < items;
+      wv[u] = make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
+      if (in && WB == 1) {  // binary: tiles 2 it and 2 it + 1 of 512 bytes
+        const uint2* t = reinterpret_cast<const uint2*>(packed) + (rb * kt_real + 2 * it) * 64 + lane;
+        const uint2 lo = load_weights_nt2(t);
+        const uint2 hi = 2 * it + 1 < kt_real ? load_weights_nt2(t + 64) : make_uint2(0, 0);
+        wv[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else if (in) {  // ternary: item it is tile it
+        wv[u] = load_weights_nt(packed + (rb * kt_count + it) * 64 + lane);
+      }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xv[u][s] = load_x16(xrow, c0 + 16 * s, k, in && has_tok, VEC);
+      for (int j = 0; j < kOps; ++j)
+        xv[u][j] = load_x16(xrow, static_cast<int64_t>(item_col<WB>(it, j)) + g * 64, k, in && has_tok, VEC);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t words[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv[u][s], expand_ternary(words[s]), acc, 0, 0, 0);
+      for (int j = 0; j < kOps; ++j)
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv[u][j], item_weights<WB>(words, j), acc, 0, 0, 0);
     }
   }
   const int64_t row = rb * kTileRows + tok;
-  const float gamma = *gamma_p;
+  const float gamma = dq.row_scale ? 0.0f : *gamma_p;
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
   lds_barrier();
@@ -842,19 +882,28 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
     const int t = 4 * g + r;
     if (t < m && row < n) {
       v >>= kWeightShift;
-      const float scale = gamma * amax[t] / 127.0f;
+      const float ws = dq.row_scale ? half_bits_to_float(dq.row_scale[row]) : gamma;
+      const float scale = ws * amax[t * dq.astride] / dq.qdiv;
       y[t * n + row] = static_cast<float>(v) * scale;
       if (acc_out) acc_out[t * n + row] = v;
     }
   }
 }
 
-template <int SRC, int WAVES, int U, bool SWIGLU = false>
-hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
+// Binary weights (WB = 1) stage the codes over an even number of 256-column
+// tiles, since an item spans two.
+inline int64_t staged_tiles(int64_t k, int wb) {
+  const int64_t kt = k_tiles(k);
+  return wb == 1 ? kt + (kt & 1) : kt;
+}
+
+template <int SRC, int WAVES, int U, bool SWIGLU = false, int WB = 2>
+hipError_t launch_lds(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const void* xsrc,
                       const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
                       const float* gain, float eps, hipStream_t s, bool vec, const void* packed_u = nullptr,
                       const float* gamma_u = nullptr) {
-  const int kt = static_cast<int>(k_tiles(k));
+  const int kt = static_cast<int>(staged_tiles(k, WB));
+  const int kt_real = static_cast<int>(k_tiles(k));
   const int64_t rbs = row_blocks(n);
   // balanced persistent grid: every workgroup takes the same number of row blocks (+-1)
   const int64_t per = (rbs + kMaxResidentGroups - 1) / kMaxResidentGroups;
@@ -863,34 +912,53 @@ hipError_t launch_lds(const void* packed, const float* gamma, int64_t n, int64_t
   const uint4* p = static_cast<const uint4*>(packed);
   const uint4* pu = static_cast<const uint4*>(packed_u);
   if (vec)
-    gemv_lds_kernel<WAVES, U, SRC, true, SWIGLU><<<grid, WAVES * 64, lds, s>>>(
-        p, gamma, n, k, kt, rbs, xsrc, amax_in, static_cast<int>(m), y, acc, xq_out, amax_out, gain, eps, pu, gamma_u);
+    gemv_lds_kernel<WAVES, U, SRC, true, SWIGLU, WB><<<grid, WAVES * 64, lds, s>>>(
+        p, gamma, dq, n, k, kt, kt_real, rbs, xsrc, amax_in, static_cast<int>(m), y, acc, xq_out, amax_out, gain, eps,
+        pu, gamma_u);
   else
-    gemv_lds_kernel<WAVES, U, SRC, false, SWIGLU><<<grid, WAVES * 64, lds, s>>>(
-        p, gamma, n, k, kt, rbs, xsrc, amax_in, static_cast<int>(m), y, acc, xq_out, amax_out, gain, eps, pu, gamma_u);
+    gemv_lds_kernel<WAVES, U, SRC, false, SWIGLU, WB><<<grid, WAVES * 64, lds, s>>>(
+        p, gamma, dq, n, k, kt, kt_real, rbs, xsrc, amax_in, static_cast<int>(m), y, acc, xq_out, amax_out, gain, eps,
+        pu, gamma_u);
   return hipGetLastError();
 }
 
-// U = tiles per wave per item: one item covers a row block of up to
-// 8 * WAVES tiles; longer rows are walked in chunks of that many tiles.
-// SWIGLU items hold 2 * kt tiles (gate then up), so U follows the item size.
-template <int SRC, bool SWIGLU = false>
-hipError_t dispatch_lds(const void* packed, const float* gamma, int64_t n, int64_t k, const void* xsrc,
+// U = items per wave per chunk: one chunk covers a row block of up to
+// 8 * WAVES items; longer rows are walked in chunks of that many items.
+// SWIGLU items hold 2 * kt tiles (gate then up) and binary items two tiles,
+// so U follows the item count.
+template <int SRC, bool SWIGLU = false, int WB = 2>
+hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const void* xsrc,
                         const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
                         const float* gain, float eps, hipStream_t s, bool vec, const void* packed_u = nullptr,
                         const float* gamma_u = nullptr) {
-  const int64_t kt = (SWIGLU ? 2 : 1) * k_tiles(k);
-  if (kt <= kWaves)
-    return launch_lds<SRC, kWaves, 1, SWIGLU>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps,
-                                              s, vec, packed_u, gamma_u);
-  if (kt <= 2 * kWaves)
-    return launch_lds<SRC, kWaves, 2, SWIGLU>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps,
-                                              s, vec, packed_u, gamma_u);
-  if (kt <= 4 * kWaves)
-    return launch_lds<SRC, kWaves, 4, SWIGLU>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps,
-                                              s, vec, packed_u, gamma_u);
-  return launch_lds<SRC, kWaves, 8, SWIGLU>(packed, gamma, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out, gain, eps,
-                                            s, vec, packed_u, gamma_u);
+  const int64_t items = WB == 1 ? staged_tiles(k, 1) / 2 : (SWIGLU ? 2 : 1) * k_tiles(k);
+  if (items <= kWaves)
+    return launch_lds<SRC, kWaves, 1, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
+                                                  gain, eps, s, vec, packed_u, gamma_u);
+  if (items <= 2 * kWaves)
+    return launch_lds<SRC, kWaves, 2, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
+                                                  gain, eps, s, vec, packed_u, gamma_u);
+  if (items <= 4 * kWaves)
+    return launch_lds<SRC, kWaves, 4, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
+                                                  gain, eps, s, vec, packed_u, gamma_u);
+  return launch_lds<SRC, kWaves, 8, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
+                                                gain, eps, s, vec, packed_u, gamma_u);
+}
+
+template <int WB>
+hipError_t launch_global(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
+                         const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s, bool vec) {
+  const int kt = static_cast<int>(staged_tiles(k, WB));
+  const int kt_real = static_cast<int>(k_tiles(k));
+  const dim3 grid(static_cast<unsigned>(row_blocks(n)));
+  const uint4* p = static_cast<const uint4*>(packed);
+  if (vec)
+    gemv_global_kernel<4, 4, true, WB><<<grid, 256, 0, s>>>(p, gamma, dq, n, k, kt, kt_real, xq, amax,
+                                                            static_cast<int>(m), y, acc);
+  else
+    gemv_global_kernel<4, 4, false, WB><<<grid, 256, 0, s>>>(p, gamma, dq, n, k, kt, kt_real, xq, amax,
+                                                             static_cast<int>(m), y, acc);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -904,7 +972,7 @@ hipError_t launch_gemv_swiglu(const void* packed_g, const float* gamma_g, const 
                               int32_t* acc, hipStream_t s) {
   if (!gemv_fits_lds(m, k)) return hipErrorInvalidValue;
   const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
-  return dispatch_lds<kFromCodes, true>(packed_g, gamma_g, f, k, xq, amax, m, h, acc, nullptr, nullptr, nullptr, 0.0f,
+  return dispatch_lds<kFromCodes, true>(packed_g, gamma_g, kTokenDequant, f, k, xq, amax, m, h, acc, nullptr, nullptr, nullptr, 0.0f,
                                         s, vec, packed_u, gamma_u);
 }
 
@@ -915,7 +983,7 @@ hipError_t launch_norm_quant_gemv_swiglu(const void* packed_g, const float* gamm
   const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (gain == nullptr || reinterpret_cast<uintptr_t>(gain) % 16 == 0) &&
                    (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 8 == 0);
-  return dispatch_lds<kFromBf16Norm, true>(packed_g, gamma_g, f, k, x, nullptr, m, h, acc, xq_out, amax_out, gain, eps,
+  return dispatch_lds<kFromBf16Norm, true>(packed_g, gamma_g, kTokenDequant, f, k, x, nullptr, m, h, acc, xq_out, amax_out, gain, eps,
                                            s, vec, packed_u, gamma_u);
 }
 
@@ -923,29 +991,45 @@ hipError_t launch_quant_gemv_f32(const void* packed, const float* gamma, int64_t
                                  int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s) {
   const bool vec = (k % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 4 == 0);
-  return dispatch_lds<kFromF32>(packed, gamma, n, k, x, nullptr, m, y, acc, xq_out, amax_out, nullptr, 0.0f, s, vec);
+  return dispatch_lds<kFromF32>(packed, gamma, kTokenDequant, n, k, x, nullptr, m, y, acc, xq_out, amax_out, nullptr, 0.0f, s, vec);
+}
+
+hipError_t launch_gemv_ex(const void* packed, bool binary, const float* gamma, Dequant dq, int64_t n, int64_t k,
+                          const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
+  const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
+  if (binary) {
+    if (lds_bytes(m, staged_tiles(k, 1)) <= kMaxLdsBytes)
+      return dispatch_lds<kFromCodes, false, 1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, nullptr, nullptr, nullptr,
+                                                0.0f, s, vec);
+    return launch_global<1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s, vec);
+  }
+  if (gemv_fits_lds(m, k))
+    return dispatch_lds<kFromCodes>(packed, gamma, dq, n, k, xq, amax, m, y, acc, nullptr, nullptr, nullptr, 0.0f, s,
+                                    vec);
+  return launch_global<2>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s, vec);
 }
 
 hipError_t launch_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const int8_t* xq,
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
-  const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
-  if (gemv_fits_lds(m, k))
-    return dispatch_lds<kFromCodes>(packed, gamma, n, k, xq, amax, m, y, acc, nullptr, nullptr, nullptr, 0.0f, s, vec);
-  const int kt = static_cast<int>(k_tiles(k));
-  const dim3 grid(static_cast<unsigned>(row_blocks(n)));
-  const uint4* p = static_cast<const uint4*>(packed);
-  if (vec)
-    gemv_global_kernel<4, 4, true><<<grid, 256, 0, s>>>(p, gamma, n, k, kt, xq, amax, static_cast<int>(m), y, acc);
-  else
-    gemv_global_kernel<4, 4, false><<<grid, 256, 0, s>>>(p, gamma, n, k, kt, xq, amax, static_cast<int>(m), y, acc);
-  return hipGetLastError();
+  return launch_gemv_ex(packed, false, gamma, kTokenDequant, n, k, xq, amax, m, y, acc, s);
+}
+
+bool gemv_binary_fits_lds(int64_t m, int64_t k) { return lds_bytes(m, staged_tiles(k, 1)) <= kMaxLdsBytes; }
+
+hipError_t launch_quant_gemv_binary(const void* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                                    int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s) {
+  if (!gemv_binary_fits_lds(m, k)) return hipErrorInvalidValue;
+  const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 8 == 0);
+  return dispatch_lds<kFromBf16, false, 1>(packed, scale, kTokenDequant, n, k, x, nullptr, m, y, acc, xq_out,
+                                           amax_out, nullptr, 0.0f, s, vec);
 }
 
 hipError_t launch_quant_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
                              int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out, hipStream_t s) {
   const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 8 == 0);
-  return dispatch_lds<kFromBf16>(packed, gamma, n, k, x, nullptr, m, y, acc, xq_out, amax_out, nullptr, 0.0f, s, vec);
+  return dispatch_lds<kFromBf16>(packed, gamma, kTokenDequant, n, k, x, nullptr, m, y, acc, xq_out, amax_out, nullptr, 0.0f, s, vec);
 }
 
 hipError_t launch_norm_quant_gemv(const void* packed, const float* gamma, int64_t n, int64_t k, const uint16_t* x,
@@ -954,7 +1038,7 @@ hipError_t launch_norm_quant_gemv(const void* packed, const float* gamma, int64_
   const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (gain == nullptr || reinterpret_cast<uintptr_t>(gain) % 16 == 0) &&
                    (xq_out == nullptr || reinterpret_cast<uintptr_t>(xq_out) % 8 == 0);
-  return dispatch_lds<kFromBf16Norm>(packed, gamma, n, k, x, nullptr, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
+  return dispatch_lds<kFromBf16Norm>(packed, gamma, kTokenDequant, n, k, x, nullptr, m, y, acc, xq_out, amax_out, gain, eps, s, vec);
 }
 
 }  // namespace bitlinear

@@ -73,21 +73,12 @@ __device__ __forceinline__ uint32_t ternary_field(float wv, float d) {
 // position of column t (0..15) of a 16-column word
 __device__ __forceinline__ int field_shift(int t) { return 8 * (t & 3) + 2 * (t >> 2); }
 
+// Ternary words of the packed matrix, one thread per 16-column word (words of
+// a padded row are consecutive).  The denominator is gamma + 1e-5 for every
+// row, or, with row_scale set, the binary16 scale of the word's row + 1e-5.
 template <bool kVec>
-__global__ __launch_bounds__(kThreads) void ternarize_pack(const float* __restrict__ w, int64_t n,
-                                                           int64_t k, int64_t kt_count,
-                                                           const double* __restrict__ partials,
-                                                           int parts, float* __restrict__ gamma_out,
-                                                           uint32_t* __restrict__ packed) {
-  __shared__ double red[kWaves];
-  double s = 0.0;
-  for (int i = threadIdx.x; i < parts; i += kThreads) s += partials[i];
-  s = block_sum(s, red);
-  const float gamma = static_cast<float>(s / (static_cast<double>(n) * static_cast<double>(k)));
-  const float d = gamma + 1e-5f;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gamma_out = gamma;
-
-  // one thread per 16-column word; words of a (padded) row are consecutive
+__device__ void pack_ternary_words(const float* __restrict__ w, int64_t n, int64_t k, int64_t kt_count, float d_all,
+                                   const uint16_t* __restrict__ row_scale, uint32_t* __restrict__ packed) {
   const int64_t words_per_row = kt_count * 16;
   const int64_t rows = row_blocks(n) * kTileRows;
   const int64_t total = rows * words_per_row;
@@ -96,6 +87,7 @@ __global__ __launch_bounds__(kThreads) void ternarize_pack(const float* __restri
     const int64_t row = idx / words_per_row;
     const int64_t cw = idx - row * words_per_row;
     const int64_t k0 = cw * 16;
+    const float d = (row_scale && row < n) ? half_bits_to_float(row_scale[row]) + 1e-5f : d_all;
     uint32_t word = 0;
     if (row < n && k0 + 16 <= k) {
       const float* src = w + row * k + k0;
@@ -124,6 +116,102 @@ __global__ __launch_bounds__(kThreads) void ternarize_pack(const float* __restri
     const int64_t kt = cw >> 4;
     const int64_t slot = (row & 15) + 16 * ((cw & 15) >> 2);
     packed[((row >> 4) * kt_count + kt) * 256 + slot * 4 + (cw & 3)] = word;
+  }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kThreads) void ternarize_pack(const float* __restrict__ w, int64_t n,
+                                                           int64_t k, int64_t kt_count,
+                                                           const double* __restrict__ partials,
+                                                           int parts, float* __restrict__ gamma_out,
+                                                           uint32_t* __restrict__ packed) {
+  __shared__ double red[kWaves];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < parts; i += kThreads) s += partials[i];
+  s = block_sum(s, red);
+  const float gamma = static_cast<float>(s / (static_cast<double>(n) * static_cast<double>(k)));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gamma_out = gamma;
+  pack_ternary_words<kVec>(w, n, k, kt_count, gamma + 1e-5f, nullptr, packed);
+}
+
+// ---- per-output-channel binary16 scales ("BitNet-2B-4T: Inside the
+// 2B-Parameter, 4T-Token 1-Bit LLM", "Weight Representation: Ternary + Scale,
+// Not Pure Binary"): the scale of row r is its absmean -- fp64 sum of |W|,
+// divided by k, rounded to fp32, then to binary16 (round to nearest even) --
+// and the row is ternarized with that stored value.  One wave per row.
+__global__ __launch_bounds__(kThreads) void row_scale_kernel(const float* __restrict__ w, int64_t n, int64_t k,
+                                                             uint16_t* __restrict__ scales) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const int lane = threadIdx.x & 63;
+  const float* r = w + row * k;
+  double s = 0.0;
+  for (int64_t c = lane; c < k; c += 64) s += fabs(static_cast<double>(r[c]));
+  s = wave_sum_f64(s);
+  if (lane == 0) {
+    const float mean = static_cast<float>(s / static_cast<double>(k));
+    scales[row] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(mean));
+  }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kThreads) void ternarize_pack_rows(const float* __restrict__ w, int64_t n, int64_t k,
+                                                                int64_t kt_count, const uint16_t* __restrict__ scales,
+                                                                uint32_t* __restrict__ packed) {
+  pack_ternary_words<kVec>(w, n, k, kt_count, 0.0f, scales, packed);
+}
+
+// ---- binary sign bits ("BitNet's 1-Bit Transformer: Architecture
+// Breakdown", "Binary Weight Matrices with Learnable Scaling": W_bit =
+// s * sign(W)); bit set for W < 0, so zero packs as +1.  One thread per
+// 32-column word; word cw of a row is word cw % 2 of slot (row % 16) +
+// 16 * ((cw % 8) / 2) in tile (row / 16, cw / 8).
+__device__ __forceinline__ int sign_bit_pos(int c) { return 8 * (c & 3) + 7 - (c >> 2); }
+
+template <bool kVec>
+__global__ __launch_bounds__(kThreads) void pack_binary_kernel(const float* __restrict__ w, int64_t n, int64_t k,
+                                                               int64_t kt_count, uint32_t* __restrict__ packed) {
+  const int64_t words_per_row = kt_count * 8;
+  const int64_t total = row_blocks(n) * kTileRows * words_per_row;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int64_t row = idx / words_per_row;
+    const int64_t cw = idx - row * words_per_row;
+    const int64_t k0 = cw * 32;
+    uint32_t word = 0;
+    if (row < n && kVec && k0 + 32 <= k) {
+      const float4* s4 = reinterpret_cast<const float4*>(w + row * k + k0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = s4[q];
+        word |= static_cast<uint32_t>(v.x < 0.0f) << sign_bit_pos(4 * q + 0);
+        word |= static_cast<uint32_t>(v.y < 0.0f) << sign_bit_pos(4 * q + 1);
+        word |= static_cast<uint32_t>(v.z < 0.0f) << sign_bit_pos(4 * q + 2);
+        word |= static_cast<uint32_t>(v.w < 0.0f) << sign_bit_pos(4 * q + 3);
+      }
+    } else if (row < n) {
+      for (int c = 0; c < 32; ++c)
+        if (k0 + c < k) word |= static_cast<uint32_t>(w[row * k + k0 + c] < 0.0f) << sign_bit_pos(c);
+    }
+    const int64_t slot = (row & 15) + 16 * ((cw & 7) >> 1);
+    packed[((row >> 4) * kt_count + (cw >> 3)) * 128 + slot * 2 + (cw & 1)] = word;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void unpack_binary_kernel(const uint32_t* __restrict__ packed, int64_t n,
+                                                                 int64_t k, int64_t kt_count,
+                                                                 int8_t* __restrict__ codes) {
+  const int64_t words_per_row = kt_count * 8;
+  const int64_t total = n * words_per_row;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int64_t row = idx / words_per_row;
+    const int64_t cw = idx - row * words_per_row;
+    const int64_t slot = (row & 15) + 16 * ((cw & 7) >> 1);
+    const uint32_t word = packed[((row >> 4) * kt_count + (cw >> 3)) * 128 + slot * 2 + (cw & 1)];
+    const int64_t k0 = cw * 32;
+    for (int c = 0; c < 32; ++c)
+      if (k0 + c < k) codes[row * k + k0 + c] = ((word >> sign_bit_pos(c)) & 1u) ? int8_t(-1) : int8_t(1);
   }
 }
 
@@ -185,6 +273,38 @@ hipError_t launch_pack(const float* w, int64_t n, int64_t k, void* packed, float
   else
     ternarize_pack<false><<<grid_for(words), kThreads, 0, s>>>(w, n, k, kt, partials, parts, gamma,
                                                                 static_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rowscale(const float* w, int64_t n, int64_t k, void* packed, uint16_t* scales, hipStream_t s) {
+  row_scale_kernel<<<static_cast<unsigned>((n + kWaves - 1) / kWaves), kThreads, 0, s>>>(w, n, k, scales);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t kt = k_tiles(k);
+  const int64_t words = row_blocks(n) * kTileRows * kt * 16;
+  const bool vec = (reinterpret_cast<uintptr_t>(w) % 16 == 0) && (k % 4 == 0);
+  if (vec)
+    ternarize_pack_rows<true><<<grid_for(words), kThreads, 0, s>>>(w, n, k, kt, scales, static_cast<uint32_t*>(packed));
+  else
+    ternarize_pack_rows<false><<<grid_for(words), kThreads, 0, s>>>(w, n, k, kt, scales, static_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_binary(const float* w, int64_t n, int64_t k, void* packed, hipStream_t s) {
+  const int64_t kt = k_tiles(k);
+  const int64_t words = row_blocks(n) * kTileRows * kt * 8;
+  const bool vec = (reinterpret_cast<uintptr_t>(w) % 16 == 0) && (k % 4 == 0);
+  if (vec)
+    pack_binary_kernel<true><<<grid_for(words), kThreads, 0, s>>>(w, n, k, kt, static_cast<uint32_t*>(packed));
+  else
+    pack_binary_kernel<false><<<grid_for(words), kThreads, 0, s>>>(w, n, k, kt, static_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_binary(const void* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t s) {
+  const int64_t kt = k_tiles(k);
+  unpack_binary_kernel<<<grid_for(n * kt * 8), kThreads, 0, s>>>(static_cast<const uint32_t*>(packed), n, k, kt,
+                                                                 codes);
   return hipGetLastError();
 }
 

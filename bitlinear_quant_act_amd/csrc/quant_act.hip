@@ -107,7 +107,128 @@ __global__ __launch_bounds__(kThreads) void quant_act_any(const uint16_t* __rest
   if (threadIdx.x == 0) amax[row] = a;
 }
 
+// ---- per-tensor variant ("BitNet 1-bit LLM Inference Framework", "The Core
+// Structure of BitNet b1.58": the BitLinear class's activation_quantize) --
+// one g = max |x| over the whole [m][k] tensor, code = round(clamp((x * 128) /
+// (g + 1e-8), -128, 127)): one fp32 multiply (exact), one IEEE divide, clamp,
+// v_rndne.  Kernel 1 leaves one max (bf16 bit pattern without sign) per
+// workgroup of a contiguous range; kernel 2 folds them in every workgroup and
+// quantizes its range (at most 1024 ranges, so the partials take at most
+// 4 KiB).  A tensor of at most kTensorOneGroup values is done by one
+// workgroup in one launch.
+
+constexpr int64_t kTensorChunk = 16384;     // least values per workgroup range
+constexpr int64_t kTensorOneGroup = 16384;  // single-launch size
+constexpr int kTensorMaxParts = 1024;       // ranges (workgroups) at most
+
+// values per range: at least kTensorChunk, a multiple of 8, at most kTensorMaxParts ranges
+inline int64_t tensor_range(int64_t total) {
+  int64_t per = (total + kTensorMaxParts - 1) / kTensorMaxParts;
+  per = per < kTensorChunk ? kTensorChunk : per;
+  return (per + 7) & ~int64_t(7);
+}
+
+__device__ __forceinline__ uint32_t tensor_code(uint32_t bits16, float d) {
+  float t = (bf16_to_f32(bits16) * 128.0f) / d;
+  t = fminf(fmaxf(t, -128.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(rintf(t))) & 0xffu;
+}
+
+__device__ __forceinline__ uint32_t range_max(const uint16_t* __restrict__ x, int64_t begin, int64_t end, bool vec) {
+  uint32_t mx = 0;
+  if (vec) {  // begin, end multiples of 8 (end may be the tensor's end: tail below)
+    const int64_t vend = begin + ((end - begin) & ~int64_t(7));
+    for (int64_t i = begin / 8 + threadIdx.x; i < vend / 8; i += kThreads) {
+      const uint4 c = reinterpret_cast<const uint4*>(x)[i];
+      mx = max(mx, max(max(abs_max2(c.x), abs_max2(c.y)), max(abs_max2(c.z), abs_max2(c.w))));
+    }
+    for (int64_t i = vend + threadIdx.x; i < end; i += kThreads) mx = max(mx, static_cast<uint32_t>(x[i]) & 0x7fffu);
+  } else {
+    for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) mx = max(mx, static_cast<uint32_t>(x[i]) & 0x7fffu);
+  }
+  return mx;
+}
+
+__device__ __forceinline__ void range_quant(const uint16_t* __restrict__ x, int64_t begin, int64_t end, float d,
+                                            int8_t* __restrict__ xq, bool vec) {
+  if (vec) {
+    const int64_t vend = begin + ((end - begin) & ~int64_t(7));
+    for (int64_t i = begin / 8 + threadIdx.x; i < vend / 8; i += kThreads) {
+      const uint4 c = reinterpret_cast<const uint4*>(x)[i];
+      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        lo |= tensor_code(w[j] & 0xffffu, d) << (16 * j);
+        lo |= tensor_code(w[j] >> 16, d) << (16 * j + 8);
+        hi |= tensor_code(w[j + 2] & 0xffffu, d) << (16 * j);
+        hi |= tensor_code(w[j + 2] >> 16, d) << (16 * j + 8);
+      }
+      reinterpret_cast<uint2*>(xq)[i] = make_uint2(lo, hi);
+    }
+    for (int64_t i = vend + threadIdx.x; i < end; i += kThreads) xq[i] = static_cast<int8_t>(tensor_code(x[i], d));
+  } else {
+    for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) xq[i] = static_cast<int8_t>(tensor_code(x[i], d));
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void tensor_max_partial(const uint16_t* __restrict__ x, int64_t total,
+                                                               int64_t per, uint32_t* __restrict__ partials,
+                                                               bool vec) {
+  __shared__ uint32_t red[kWaves];
+  const int64_t begin = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t end = min(total, begin + per);
+  const uint32_t mx = block_max(range_max(x, begin, end, vec), red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = mx;
+}
+
+// parts == 0: one workgroup, the max of the whole tensor computed here
+__global__ __launch_bounds__(kThreads) void tensor_quant(const uint16_t* __restrict__ x, int64_t total, int64_t per,
+                                                         const uint32_t* __restrict__ partials, int parts,
+                                                         int8_t* __restrict__ xq, float* __restrict__ gx, bool vec) {
+  __shared__ uint32_t red[kWaves];
+  uint32_t mx = 0;
+  int64_t begin = 0, end = total;
+  if (parts == 0) {
+    mx = range_max(x, 0, total, vec);
+  } else {
+    for (int i = threadIdx.x; i < parts; i += kThreads) mx = max(mx, partials[i]);
+    begin = static_cast<int64_t>(blockIdx.x) * per;
+    end = min(total, begin + per);
+  }
+  mx = block_max(mx, red);
+  const float g = bf16_to_f32(mx);
+  const float d = g + 1e-8f;
+  range_quant(x, begin, end, d, xq, vec);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gx = g;
+}
+
 }  // namespace
+
+int quant_tensor_partial_count(int64_t m, int64_t k) {
+  const int64_t total = m * k;
+  if (total <= kTensorOneGroup) return 0;
+  const int64_t per = tensor_range(total);
+  return static_cast<int>((total + per - 1) / per);
+}
+
+hipError_t launch_quant_act_tensor(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* gx,
+                                   uint32_t* partials, hipStream_t s) {
+  const int64_t total = m * k;
+  const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 8 == 0);
+  const int parts = quant_tensor_partial_count(m, k);
+  if (parts > kTensorMaxParts) return hipErrorInvalidValue;
+  if (parts == 0) {
+    tensor_quant<<<1, kThreads, 0, s>>>(x, total, total, nullptr, 0, xq, gx, vec);
+    return hipGetLastError();
+  }
+  const int64_t per = tensor_range(total);
+  tensor_max_partial<<<parts, kThreads, 0, s>>>(x, total, per, partials, vec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  tensor_quant<<<parts, kThreads, 0, s>>>(x, total, per, partials, parts, xq, gx, vec);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* amax,
                             hipStream_t s) {

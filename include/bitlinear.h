@@ -290,6 +290,114 @@ int bitlinear_forward_lut(const void *packed, const float *gamma, int64_t n, int
 /* 1 if bitlinear_forward_lut's table for k fits on chip, else 0.  Pure host function. */
 int bitlinear_forward_lut_supported(int64_t k);
 
+/* ======================================================================
+ * Variant modes described by the other pages.  Each keeps the main path's
+ * contraction (int8 codes times +-1 / 0 weights, exact int32 accumulators)
+ * and changes one side of it.
+ * ====================================================================== */
+
+/*
+ * V1, activation side: one scale per tensor with Q_b = 128 ("BitNet 1-bit LLM
+ * Inference Framework", "A Deep Look at the BitNet Architecture", "The Core
+ * Structure of BitNet b1.58": the BitLinear class's activation_quantize).
+ * g = max |x| over all m * k values; every code is
+ * round_half_even(clamp((x * 128) / (g + 1e-8), -128, 127)) (fp32 multiply,
+ * one IEEE fp32 divide, g + 1e-8 in fp32), so codes span [-128, 127].
+ *   x          in   bf16 bit patterns [m][k], 2-byte aligned, finite
+ *   xq         out  int8 [m][k]
+ *   x_scale    out  1 fp32: g (without the 1e-8, the de-quantization scale)
+ *   workspace  tmp  >= bitlinear_quant_act_tensor_workspace_bytes(m, k) bytes
+ *                   (at most 4 KiB), 4-byte aligned
+ * m * k above 2^40 returns BITLINEAR_E_SHAPE.  One launch for at most 16384
+ * values, else two.
+ */
+size_t bitlinear_quant_act_tensor_workspace_bytes(int64_t m, int64_t k);
+int bitlinear_quant_act_tensor(const uint16_t *x, int64_t m, int64_t k,
+                               int8_t *xq, float *x_scale,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * V1 forward: the codes of bitlinear_quant_act_tensor against main-path
+ * weights (bitlinear_pack_weights), y = acc * (gamma * g / 128) in fp32 (the
+ * class's de-quantization by w_scale * x_scale / 2^7).  Any 1 <= m <= 2^21
+ * (decode kernel up to BITLINEAR_FORWARD_MAX_M tokens, matrix cores above);
+ * k must be below 2^18 (|acc| <= 128 k), else BITLINEAR_E_SHAPE.
+ *   x_scale  in  1 fp32 (device), from bitlinear_quant_act_tensor
+ *   other arguments as bitlinear_forward
+ */
+int bitlinear_forward_tensor_act(const void *packed, const float *gamma, int64_t n, int64_t k,
+                                 const int8_t *xq, const float *x_scale, int64_t m,
+                                 float *y, int32_t *acc_or_null, void *stream);
+
+/*
+ * V2, weight side: one binary16 scale per output channel ("BitNet-2B-4T:
+ * Inside the 2B-Parameter, 4T-Token 1-Bit LLM", "Weight Representation:
+ * Ternary + Scale, Not Pure Binary").  The page does not say how the scale
+ * is found; here s_r = binary16(fp32(mean |W[r][:]|)) (fp64 sum, one rounding
+ * to fp32, then round-to-nearest-even to binary16), and row r is ternarised
+ * as Clip(Round(W / (s_r + 1e-5)), -1, 1) with that stored value, in the
+ * same tiled 2-bit layout (bitlinear_packed_bytes).
+ *   w       in   fp32 [n][k], 4-byte aligned, finite
+ *   packed  out  >= bitlinear_packed_bytes(n, k) bytes, 16-byte aligned
+ *   scales  out  binary16 bit patterns [n], 2-byte aligned
+ * Rows whose absmean rounds above the binary16 range get an infinite scale.
+ */
+int bitlinear_pack_weights_rowscale(const float *w, int64_t n, int64_t k,
+                                    void *packed, size_t packed_bytes,
+                                    uint16_t *scales, void *stream);
+
+/*
+ * V2 forward: per-token codes (bitlinear_quant_act), y[t][j] = acc *
+ * (s_j * a'_t / 127) in fp32 with s_j widened from binary16.  Any
+ * 1 <= m <= 2^21 as bitlinear_forward_tensor_act.
+ *   scales  in  binary16 [n] (device), from bitlinear_pack_weights_rowscale
+ *   other arguments as bitlinear_forward
+ */
+int bitlinear_forward_rowscale(const void *packed, const uint16_t *scales, int64_t n, int64_t k,
+                               const int8_t *xq, const float *x_absmax, int64_t m,
+                               float *y, int32_t *acc_or_null, void *stream);
+
+/*
+ * V3, weight side: binary weights W_bit = s * sign(W) with one per-layer
+ * scale s ("BitNet's 1-Bit Transformer: Architecture Breakdown", "Binary
+ * Weight Matrices with Learnable Scaling"), one bit per weight.  sign(0) is
+ * taken as +1 (one bit has no code for 0): the bit is set exactly where
+ * W < 0.  s is learned, so it is an input of the forward, not computed here.
+ * Layout: tiles of 16 rows x 256 columns, 512 bytes each, tile (rb, kt) at
+ * byte (rb * ceil(k/256) + kt) * 512; 8-byte slot l (0..63) holds row
+ * 16*rb + (l % 16) and columns 256*kt + 64*(l / 16) + [0, 64); its 32-bit
+ * word s (0, 1) covers 32 of those columns, column c of the word in bit
+ * 8*(c % 4) + 7 - c/4 (set = -1, clear = +1).  Padding bits are clear.
+ */
+size_t bitlinear_packed_bytes_binary(int64_t n, int64_t k);
+int bitlinear_pack_binary(const float *w, int64_t n, int64_t k,
+                          void *packed, size_t packed_bytes, void *stream);
+
+/* Decode the binary layout to int8 codes in {-1, +1} [n][k] (tests, inspection). */
+int bitlinear_unpack_binary(const void *packed, int64_t n, int64_t k,
+                            int8_t *codes, void *stream);
+
+/*
+ * V3 forward: per-token codes against the sign bits, y = acc * (s * a' / 127)
+ * in fp32.  Any 1 <= m <= 2^21 as bitlinear_forward_tensor_act.
+ *   packed  in  from bitlinear_pack_binary(n, k), 16-byte aligned
+ *   scale   in  1 fp32 (device): the layer's scale s
+ *   other arguments as bitlinear_forward
+ */
+int bitlinear_forward_binary(const void *packed, const float *scale, int64_t n, int64_t k,
+                             const int8_t *xq, const float *x_absmax, int64_t m,
+                             float *y, int32_t *acc_or_null, void *stream);
+
+/*
+ * V3 decode forward with the activation quantisation fused (as
+ * bitlinear_quant_forward, binary weights).  Supported when
+ * bitlinear_quant_forward_binary_supported(m, k), else BITLINEAR_E_UNSUPPORTED.
+ */
+int bitlinear_quant_forward_binary(const void *packed, const float *scale, int64_t n, int64_t k,
+                                   const uint16_t *x, int64_t m, float *y, int32_t *acc_or_null,
+                                   int8_t *xq_or_null, float *x_absmax_or_null, void *stream);
+int bitlinear_quant_forward_binary_supported(int64_t m, int64_t k);
+
 #ifdef __cplusplus
 }
 #endif

@@ -267,3 +267,59 @@ def test_fused_ffn_entry_validation(blq):
     assert call2(x=A2) == E.BITLINEAR_E_ALIGN
     assert call2(m=17) == E.BITLINEAR_E_UNSUPPORTED
     assert call2(m=16, k=14336) == E.BITLINEAR_E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# variant modes: sizes and host-side validation (nothing reaches a launch)
+# ---------------------------------------------------------------------------
+
+def test_variant_sizes(blq):
+    # binary tiles: 16 x 256 columns in 512 bytes (one bit per weight)
+    assert blq.bitlinear_packed_bytes_binary(2048, 2048) == 2048 * 2048 // 8
+    assert blq.bitlinear_packed_bytes_binary(1, 1) == 512
+    assert blq.bitlinear_packed_bytes_binary(17, 257) == 2 * 2 * 512
+    assert blq.bitlinear_packed_bytes_binary(0, 5) == 0
+    # per-tensor quantisation: one launch (no partials) up to 16384 values, at most 1024 partials
+    assert blq.bitlinear_quant_act_tensor_workspace_bytes(1, 16384) == 4
+    assert blq.bitlinear_quant_act_tensor_workspace_bytes(2, 16384) == 8
+    assert blq.bitlinear_quant_act_tensor_workspace_bytes(4096, 28672) <= 4096
+    assert blq.bitlinear_quant_act_tensor_workspace_bytes(0, 8) == 0
+    assert blq.bitlinear_quant_forward_binary_supported(1, 28672)
+    assert not blq.bitlinear_quant_forward_binary_supported(17, 256)
+
+
+def test_variant_validation(blq):
+    lib = blq.load_library()
+    E = blq
+    ws = blq.bitlinear_quant_act_tensor_workspace_bytes(64, 512)
+    q = lib.bitlinear_quant_act_tensor
+    assert q(None, 64, 512, A16, A16, A16, ws, None) == E.BITLINEAR_E_NULL
+    assert q(A16, 64, 512, A16, A16, None, ws, None) == E.BITLINEAR_E_NULL
+    assert q(A16, 0, 512, A16, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
+    assert q(A16, 64, (1 << 18) + 1, A16, A16, A16, ws, None) == E.BITLINEAR_E_SHAPE
+    assert q(A16 + 1, 64, 512, A16, A16, A16, ws, None) == E.BITLINEAR_E_ALIGN
+    assert q(A16, 64, 512, A16, A2, A16, ws, None) == E.BITLINEAR_E_ALIGN
+    assert q(A16, 64, 512, A16, A16, A16, ws - 1, None) == E.BITLINEAR_E_SIZE
+    f = lib.bitlinear_forward_tensor_act
+    assert f(A16, A16, 64, 1 << 18, A16, A16, 1, A16, None, None) == E.BITLINEAR_E_SHAPE  # |acc| <= 128 k
+    assert f(A16, None, 64, 512, A16, A16, 1, A16, None, None) == E.BITLINEAR_E_NULL
+    assert f(A16, A16, 64, 512, A16, A16, (1 << 21) + 1, A16, None, None) == E.BITLINEAR_E_UNSUPPORTED
+    nb = blq.bitlinear_packed_bytes(64, 512)
+    p = lib.bitlinear_pack_weights_rowscale
+    assert p(A16, 64, 512, A16, nb, None, None) == E.BITLINEAR_E_NULL
+    assert p(A16, 64, 512, A16, nb, A16 + 1, None) == E.BITLINEAR_E_ALIGN
+    assert p(A16, 64, 512, A16, nb - 1, A16, None) == E.BITLINEAR_E_SIZE
+    r = lib.bitlinear_forward_rowscale
+    assert r(A16, None, 64, 512, A16, A16, 1, A16, None, None) == E.BITLINEAR_E_NULL
+    assert r(A16, A16 + 1, 64, 512, A16, A16, 1, A16, None, None) == E.BITLINEAR_E_ALIGN
+    assert r(A16, A16, 64, 512, A16, A16, 0, A16, None, None) == E.BITLINEAR_E_SHAPE
+    bb = blq.bitlinear_packed_bytes_binary(64, 512)
+    assert lib.bitlinear_pack_binary(A16, 64, 512, A16, bb - 1, None) == E.BITLINEAR_E_SIZE
+    assert lib.bitlinear_pack_binary(A16, 64, 512, A8, bb, None) == E.BITLINEAR_E_ALIGN
+    assert lib.bitlinear_unpack_binary(None, 64, 512, A16, None) == E.BITLINEAR_E_NULL
+    b = lib.bitlinear_forward_binary
+    assert b(A16, None, 64, 512, A16, A16, 1, A16, None, None) == E.BITLINEAR_E_NULL
+    assert b(A16, A16, 64, 512, A16, A16, 1, A16, A2, None) == E.BITLINEAR_E_ALIGN
+    fb = lib.bitlinear_quant_forward_binary
+    assert fb(A16, A16, 64, 512, A16, 17, A16, None, None, None, None) == E.BITLINEAR_E_UNSUPPORTED
+    assert fb(A16, A16, 64, 512, A16, 1, A16, None, A16, None, None) == E.BITLINEAR_E_NULL
