@@ -69,9 +69,26 @@ def quant_bytes(m: int, k: int) -> int:
     return 2 * m * k + m * k + 4 * m
 
 
+# Variant modes of the pages (each a forward of its own, see include/bitlinear.h):
+#   tensor128 -- per-tensor activation scale, Q_b = 128 (bitlinear_quant_act_tensor + bitlinear_forward_tensor_act)
+#   rowscale  -- one binary16 scale per output row (bitlinear_forward_rowscale)
+#   binary    -- 1-bit sign weights with a per-layer scale (bitlinear_forward_binary; fused at m = 1)
+MODES = ("tensor128", "rowscale", "binary")
+
+
+def mode_forward_bytes(variant: str, m: int, n: int, k: int, fused: bool = False) -> int:
+    """Algorithmic bytes of one forward call of a variant mode."""
+    if variant == "binary":
+        x_bytes = 2 * m * k if fused else m * k + 4 * m
+        return (n * k + 7) // 8 + x_bytes + 4 + 4 * m * n
+    if variant == "rowscale":
+        return (n * k + 3) // 4 + m * k + 4 * m + 2 * n + 4 * m * n
+    return (n * k + 3) // 4 + m * k + 4 + 4 + 4 * m * n  # tensor128: one activation scale
+
+
 class Mat:
     __slots__ = ("layer", "j", "n", "k", "packed", "gamma", "x", "xq", "amax", "y", "q_or", "g_or", "x_np",
-                 "gain", "gain_np", "name", "h")
+                 "gain", "gain_np", "name", "h", "ws", "s16_or")
 
 
 def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"):
@@ -88,16 +105,28 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
         ws = synth.generate_many([(synth.seed_for(wl, l, j, synth.ROLE_WEIGHT), mt.n, mt.k) for l, j, mt in chunk])
         for (layer, j, mt), w in zip(chunk, ws):
             wd = torch.from_numpy(w).to(dev)
-            packed = torch.empty(blq.bitlinear_packed_bytes(mt.n, mt.k), dtype=torch.uint8, device=dev)
+            nbytes = (blq.bitlinear_packed_bytes_binary(mt.n, mt.k) if variant == "binary"
+                      else blq.bitlinear_packed_bytes(mt.n, mt.k))
+            packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)
             gamma = torch.empty(1, dtype=torch.float32, device=dev)
             work = torch.empty(blq.bitlinear_pack_workspace_bytes(mt.n, mt.k), dtype=torch.uint8, device=dev)
+            s_bin = np.float32(np.abs(w).astype(np.float64).mean())  # stand-in for a learned layer scale
+            if variant == "rowscale":
+                gamma = torch.empty(mt.n, dtype=torch.int16, device=dev)  # binary16 row scales
+            elif variant == "binary":
+                gamma = torch.from_numpy(np.array([s_bin], np.float32)).to(dev)
             torch.cuda.synchronize()
             e0.record()
-            blq.bitlinear_pack_weights(wd, packed, gamma, work)
+            if variant == "rowscale":
+                blq.bitlinear_pack_weights_rowscale(wd, packed, gamma)
+            elif variant == "binary":
+                blq.bitlinear_pack_binary(wd, packed)
+            else:
+                blq.bitlinear_pack_weights(wd, packed, gamma, work)
             e1.record()
             torch.cuda.synchronize()
             t_pack += e0.elapsed_time(e1) * 1e-3
-            pack_bytes += 4 * mt.n * mt.k + (mt.n * mt.k + 3) // 4
+            pack_bytes += 4 * mt.n * mt.k + nbytes
             mat = Mat()
             mat.layer, mat.j, mat.n, mat.k = layer, j, mt.n, mt.k
             mat.name = mt.name
@@ -108,7 +137,10 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             mat.x_np = x if keep_oracle_codes else None
             mat.x = torch.from_numpy(x.view(np.int16)).to(dev)
             mat.xq = torch.empty((m, mt.k), dtype=torch.int8, device=dev)
-            mat.amax = torch.empty(m, dtype=torch.float32, device=dev)
+            mat.amax = torch.empty(1 if variant == "tensor128" else m, dtype=torch.float32, device=dev)
+            mat.ws = (torch.empty(max(4, blq.bitlinear_quant_act_tensor_workspace_bytes(m, mt.k)), dtype=torch.uint8,
+                                  device=dev) if variant == "tensor128" else None)
+            mat.s16_or = None
             mat.y = torch.empty((m, mt.n), dtype=torch.float32, device=dev)
             mat.gain_np = (synth.norm_gain(synth.seed_for(wl, layer, j, synth.ROLE_GAIN), mt.k)
                            if variant == "rmsnorm" or (variant == "swiglu" and mt.name == "gate_up") else None)
@@ -116,7 +148,14 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             # SwiGLU variant: the gate+up BitLinear writes h [m][n/2] instead of y
             mat.h = (torch.empty((m, mt.n // 2), dtype=torch.float32, device=dev)
                      if variant == "swiglu" and mt.name == "gate_up" else None)
-            if keep_oracle_codes:
+            if keep_oracle_codes and variant == "binary":
+                mat.g_or = s_bin
+                mat.q_or = oracle_mod.binarize(w)
+            elif keep_oracle_codes and variant == "rowscale":
+                mat.g_or = None
+                mat.s16_or = oracle_mod.row_scales(w)
+                mat.q_or = oracle_mod.ternarize_rows(w, mat.s16_or)
+            elif keep_oracle_codes:
                 mat.g_or = oracle_mod.gamma(w)
                 mat.q_or = oracle_mod.ternarize(w, mat.g_or)
             else:
@@ -134,6 +173,7 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
                 setattr(c, s, getattr(mat, s))
             c.packed = mat.packed.clone()
             c.x, c.xq, c.amax, c.y = mat.x.clone(), torch.empty_like(mat.xq), torch.empty_like(mat.amax), torch.empty_like(mat.y)
+            c.ws = None if mat.ws is None else torch.empty_like(mat.ws)
             c.h = None if mat.h is None else torch.empty_like(mat.h)
             c.q_or = None
             cp.append(c)
@@ -202,8 +242,36 @@ def _forward_fn(blq, m, variant):
     return blq.bitlinear_forward if m <= blq.BITLINEAR_FORWARD_MAX_M else blq.bitlinear_forward_batched
 
 
+def _mode_quant(blq, mat, stream, variant):
+    if variant == "tensor128":
+        blq.bitlinear_quant_act_tensor(mat.x, mat.xq, mat.amax, mat.ws, stream=stream)
+    else:
+        _quant(blq, mat, stream)
+
+
+def _mode_forward(blq, mat, stream, variant):
+    if variant == "tensor128":
+        blq.bitlinear_forward_tensor_act(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+    elif variant == "rowscale":
+        blq.bitlinear_forward_rowscale(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+    else:
+        blq.bitlinear_forward_binary(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+
+
+def _mode_fused(blq, mat, stream):  # binary weights, quantisation in the decode prologue
+    blq.bitlinear_quant_forward_binary(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
+
+
 def launch_step(blq, mats, m, stream, fused, variant="plain"):
     """One pass of the per-token path over every matrix, in layer order."""
+    if variant in MODES:
+        for mat in mats:
+            if fused:
+                _mode_fused(blq, mat, stream)
+            else:
+                _mode_quant(blq, mat, stream, variant)
+                _mode_forward(blq, mat, stream, variant)
+        return
     if variant == "swiglu":
         return launch_step_swiglu(blq, mats, m, stream, fused)
     if fused:
@@ -220,6 +288,15 @@ def launch_kernel_only(blq, mats, m, stream, which, fused=False, variant="plain"
     """Launches of one kernel over every matrix ('quant', 'forward', 'fused',
     'swiglu': the gate+up launches of the SwiGLU variant)."""
     fwd = _forward_fn(blq, m, variant)
+    if variant in MODES:
+        for mat in mats:
+            if which == "quant":
+                _mode_quant(blq, mat, stream, variant)
+            elif which == "forward":
+                _mode_forward(blq, mat, stream, variant)
+            else:
+                _mode_fused(blq, mat, stream)
+        return
     for mat in mats:
         if which == "swiglu":
             if mat.name == "gate_up":
@@ -288,10 +365,18 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
             xq, amax = oracle_mod.quant_act_f32(h_prev)
         elif mat.gain_np is not None:
             xq, amax, _ = oracle_mod.rmsnorm_quant_act(mat.x_np[:rows], mat.gain_np)
+        elif variant == "tensor128":
+            xq, gx = oracle_mod.quant_act_tensor(mat.x_np)  # the scale spans every token
+            xq = xq[:rows]
         else:
             xq, amax = oracle_mod.quant_act(mat.x_np[:rows])
-        acc = oracle_mod.contract(xq, mat.q_or)
-        if variant == "swiglu" and mat.name == "gate_up":
+        acc = (oracle_mod.contract_q128(xq, mat.q_or) if variant == "tensor128"
+               else oracle_mod.contract(xq, mat.q_or))
+        if variant == "tensor128":
+            y = oracle_mod.dequant_tensor(acc, mat.g_or, gx)
+        elif variant == "rowscale":
+            y = oracle_mod.dequant_rows(acc, mat.s16_or, amax)
+        elif variant == "swiglu" and mat.name == "gate_up":
             f = mat.n // 2
             y = oracle_mod.swiglu(oracle_mod.dequant(acc[:, :f], mat.g_or, amax),
                                   oracle_mod.dequant(acc[:, f:], mat.g_or, amax))
@@ -301,6 +386,7 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
         t_total += time.perf_counter() - t0
         rows_used = rows
         done_bytes += (swiglu_bytes(rows, mat.n // 2, mat.k) if variant == "swiglu" and mat.name == "gate_up"
+                       else mode_forward_bytes(variant, rows, mat.n, mat.k) if variant in MODES
                        else forward_bytes(rows, mat.n, mat.k))
         done_ops += 2 * rows * mat.n * mat.k
         out = mat.h if mat.h is not None else mat.y
@@ -338,10 +424,12 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
-    ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu", "lut"),
+    ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu", "lut") + MODES,
                     help="rmsnorm: every BitLinear normalises its input first (per-channel gains); "
                          "swiglu: the feed-forward block as a unit (RMSNorm, gate+up with the SwiGLU fused, "
-                         "down fed by h); lut: quant + the table-lookup decode forward")
+                         "down fed by h); lut: quant + the table-lookup decode forward; tensor128, rowscale, "
+                         "binary: the variant modes (per-tensor Q_b = 128 activations, fp16 row scales, "
+                         "1-bit sign weights)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (bound)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -390,8 +478,13 @@ def main():
         print("bench.py: --variant lut needs m <= %d and every k within the on-chip table "
               "(k <= 9984)" % blq.BITLINEAR_FORWARD_MAX_M, file=sys.stderr)
         sys.exit(2)
-    fused = (m == 1 and not args.unfused and not lut and
-             all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
+    mode = args.variant if args.variant in MODES else None
+    if mode == "binary":
+        fused = (m == 1 and not args.unfused and
+                 all(blq.bitlinear_quant_forward_binary_supported(m, mt.k) for mt in wl.matrices))
+    else:
+        fused = (m == 1 and not args.unfused and not lut and mode is None and
+                 all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
     want_cpu = not args.no_cpu_baseline
     oracle_mod = None
     if want_cpu:
@@ -399,6 +492,8 @@ def main():
         oracle_mod._load()
 
     total_packed = synth.packed_weight_bytes_2bit(wl)
+    if mode == "binary":
+        total_packed //= 2  # one bit per weight
     # a step that walks more than 1.5x the last-level cache evicts its own
     # weights before they come round again; smaller workloads are replicated
     # and walked in turn (the reported steps then round up to whole walks)
@@ -428,6 +523,8 @@ def main():
         sys.exit(2)
 
     def call_bytes(mt):
+        if mode:
+            return mode_forward_bytes(mode, m, mt.n, mt.k)
         if sw and mt.name == "gate_up":
             return swiglu_bytes(m, mt.n // 2, mt.k)
         return forward_bytes(m, mt.n, mt.k)
@@ -482,7 +579,7 @@ def main():
     # elapsed / launches.  The quantisation kernel is timed the same way.
     if not fused:  # make sure the codes are current for forward-only replays
         with torch.cuda.stream(stream):
-            launch_kernel_only(blq, mats0, m, stream, "quant")
+            launch_kernel_only(blq, mats0, m, stream, "quant", False, args.variant)
         torch.cuda.synchronize()
     replays = max(2, min(10, args.steps))
     dom = "swiglu" if sw else "fused" if fused else "forward"
@@ -502,6 +599,9 @@ def main():
         fw_bytes = sum(swiglu_bytes(m, mt.n // 2, mt.k) + ((m * mt.k + 4 * mt.k - 4 * m) if fused else 0)
                        for mt in dom_mats)
         fw_ops = sum(2 * m * mt.n * mt.k for mt in dom_mats)
+    elif mode:
+        fw_bytes = sum(mode_forward_bytes(mode, m, mt.n, mt.k, fused) for mt in mats0)
+        fw_ops = step_ops
     else:
         fw_bytes = sum(per_call(m, mt.n, mt.k) + (4 * mt.k if norm and fused else 0) for mt in mats0)
         fw_ops = step_ops
@@ -525,9 +625,19 @@ def main():
                       ("bitlinear_rmsnorm_quant_forward (gemv_lds_kernel, RMSNorm + bf16 prologue)" if norm else
                        "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)") if fused else
                       "bitlinear_forward_lut (gemv_lut_kernel)" if lut else "bitlinear_forward (gemv kernel)")
+    kern = "gemm_dma_kernel" if batched else "gemv_lds_kernel"
+    mode_entry = {"tensor128": "bitlinear_forward_tensor_act", "rowscale": "bitlinear_forward_rowscale",
+                  "binary": "bitlinear_quant_forward_binary" if fused else "bitlinear_forward_binary"}
+    if mode:
+        roof["kernel"] = "%s (%s%s)" % (mode_entry[mode], kern, ", bf16 prologue" if fused else "")
     roof["avg_launch_us"] = round(fw_avg_us, 3)
     roof["launches_timed"] = nlaunch
-    if sw:
+    if mode:
+        roof["per_launch"] = "mean over the workload's matrices of %s" % (
+            "2*M*N*K" if batched else
+            {"tensor128": "ceil(N*K/4)+M*K+8+4*M*N bytes", "rowscale": "ceil(N*K/4)+M*K+4M+2N+4*M*N bytes",
+             "binary": "ceil(N*K/8)+%s+4+4*M*N bytes" % ("2*M*K" if fused else "M*K+4M")}[mode])
+    elif sw:
         roof["per_launch"] = "mean over the gate+up matrices of %s" % (
             "2*M*2F*K" if batched else "2*ceil(F*K/4)+2*M*K+4K+8+4*M*F bytes" if fused else
             "2*ceil(F*K/4)+M*K+4M+8+4*M*F bytes")
@@ -567,7 +677,9 @@ def main():
             "matrices_per_step": len(mats0),
             "shapes_kxn": ["%dx%d" % (mt.k, mt.n) for mt in wl.matrices],
             "variant": args.variant,
-            "entry_points": (("gate+up: bitlinear_rmsnorm_quant_forward_swiglu; down: bitlinear_quant_forward_f32; "
+            "entry_points": ((("bitlinear_quant_act_tensor + " if mode == "tensor128" else "" if fused else
+                               "bitlinear_quant_act + ") + mode_entry[mode]) if mode else
+                             ("gate+up: bitlinear_rmsnorm_quant_forward_swiglu; down: bitlinear_quant_forward_f32; "
                               "others: bitlinear_quant_forward") if sw and fused else
                              "gate+up: bitlinear_rmsnorm_quant_act + bitlinear_forward_swiglu; down: "
                              "bitlinear_quant_act_f32 + " + ("bitlinear_forward_batched" if batched else
@@ -577,8 +689,10 @@ def main():
                              ("bitlinear_rmsnorm_quant_act + " if norm else "bitlinear_quant_act + ") +
                              ("bitlinear_forward_batched" if batched else
                               "bitlinear_forward_lut" if lut else "bitlinear_forward")),
-            "launch": ("hip graph, %d kernels per step" % ((1 if fused else 2) * len(mats0))
-                       if not args.eager else "eager"),
+            "launch": ("hip graph, %d kernels per step" % (sum(
+                (1 if fused else 2) + (1 if mode == "tensor128" and
+                                       blq.bitlinear_quant_act_tensor_workspace_bytes(m, mt.k) > 4 else 0)
+                for mt in mats0)) if not args.eager else "eager"),
             "cold_cache": "weights %.0f MB per step x %d replica(s)" % (total_packed / 1e6, len(reps)),
             "step_bytes": step_bytes,
             "step_ops": step_ops,
@@ -711,6 +825,9 @@ def summarize(args):
         mats = [mt for mt in wl.matrices if mt.name == "gate_up"]
         alg = sum(swiglu_bytes(m, mt.n // 2, mt.k) + ((m * mt.k + 4 * mt.k - 4 * m) if m == 1 else 0)
                   for mt in mats) / len(mats)
+    elif variant in MODES:  # binary runs fused at m = 1; the other modes unfused
+        alg = sum(mode_forward_bytes(variant, m, mt.n, mt.k, variant == "binary" and m == 1)
+                  for mt in wl.matrices) / len(wl.matrices)
     else:
         per = fused_bytes if (m == 1 and variant != "lut") else forward_bytes
         alg = sum(per(m, mt.n, mt.k) + (4 * mt.k if variant == "rmsnorm" and m == 1 else 0)

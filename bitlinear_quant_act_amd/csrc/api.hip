@@ -179,7 +179,7 @@ int bitlinear_forward_rowscale(const void* packed, const uint16_t* scales, int64
 
 size_t bitlinear_packed_bytes_binary(int64_t n, int64_t k) {
   if (check_nk(n, k)) return 0;
-  return static_cast<size_t>(bitlinear::row_blocks(n) * bitlinear::k_tiles(k) * bitlinear::kBinTileBytes);
+  return static_cast<size_t>(bitlinear::row_blocks(n) * bitlinear::bin_tiles(k) * bitlinear::kBinTileBytes);
 }
 
 int bitlinear_pack_binary(const float* w, int64_t n, int64_t k, void* packed, size_t packed_bytes, void* stream) {

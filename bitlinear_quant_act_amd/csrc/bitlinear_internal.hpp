@@ -24,13 +24,20 @@ constexpr uint32_t kZeroWord = 0u;  // sixteen zero weights
 constexpr int kWeightShift = 6;     // expanded weight bytes are 64 * w
 
 // ---- packed binary layout (sign bits, one per weight) ----------------------
-// A binary tile is 16 rows x 256 columns = 512 bytes (the same columns as a
-// ternary tile, half the bytes): 64 slots of 8 bytes.  Slot l: row (l % 16),
-// columns 64*(l/16) + [0, 64); word s (0, 1) of a slot covers 32 of them,
-// column c at bit 8*(c%4) + 7 - c/4, set for -1 and clear for +1.  Then
+// A binary tile is 16 rows x 512 columns = 1024 bytes: 64 slots of 16 bytes,
+// one per lane, so a wave reads a tile with one coalesced 16-byte-per-lane
+// load, as for the ternary tiles.  Slot l: row (l % 16), columns
+// 128*(l/16) + [0, 128); word s (0..3) of a slot covers 32 of them, column c
+// at bit 8*(c%4) + 7 - c/4, set for -1 and clear for +1.  Then
 // ((word << i) & 0x80808080) | 0x40404040 yields columns 4i..4i+3 in order as
-// four int8 bytes equal to 64 * w, the ternary expansion's scale.
-constexpr int kBinTileBytes = 512;
+// four int8 bytes equal to 64 * w, the ternary expansion's scale.  The
+// 256-column halves of a tile are contiguous (slots 0-31, then 32-63), so a
+// matrix-core k-step of 256 columns reads 512 bytes per row block.
+constexpr int kBinTileCols = 512;
+constexpr int kBinTileBytes = 1024;
+constexpr int kBinStepBytes = 512;  // one 256-column half of a binary tile
+
+__host__ __device__ inline int64_t bin_tiles(int64_t k) { return (k + kBinTileCols - 1) / kBinTileCols; }
 
 __host__ __device__ inline int64_t row_blocks(int64_t n) { return (n + kTileRows - 1) / kTileRows; }
 __host__ __device__ inline int64_t k_tiles(int64_t k) { return (k + kTileCols - 1) / kTileCols; }
@@ -93,12 +100,6 @@ __device__ __forceinline__ uint4 load_weights_nt(const uint4* p) {
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
-}
-
-__device__ __forceinline__ uint2 load_weights_nt2(const uint2* p) {
-  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-  const v2u t = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
-  return make_uint2(t.x, t.y);
 }
 
 // One packed word (16 weights) -> the 16-byte int8 operand 64 * w of one

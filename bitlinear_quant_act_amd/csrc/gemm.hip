@@ -64,35 +64,37 @@ __device__ __forceinline__ uint4 load_a16(const int8_t* __restrict__ xq, int64_t
   return r;
 }
 
-// WB: 2 = ternary 1 KiB tiles, 1 = binary 512-byte tiles (same 256 columns)
+// WB: 2 = ternary, 1 = binary.  Bytes of one row block's weights per
+// 256-column k-step: a whole ternary tile, or one half of a binary tile.
 template <int WB>
 constexpr int wtile_bytes() {
-  return WB == 1 ? kBinTileBytes : kTileBytes;
+  return WB == 1 ? kBinStepBytes : kTileBytes;
 }
 
-// The lane's weight slot of 64-column group g and its operand for step
-// `half` (columns 64g + 32 half + 16h + [0, 16)): ternary slots are 16 bytes
-// (word 2 half + h); binary slots 8 bytes (half h of word `half`).
+// The lane's 16-byte weight slot for 64-column group g of a k-step, and its
+// operand for step `half` (columns 64g + 32 half + 16h + [0, 16)).  Ternary:
+// slot g (64 columns), word 2 half + h.  Binary: slot g / 2 of the half tile
+// (128 columns), word 2 (g % 2) + half, half h of that word.
 template <int WB>
-__device__ __forceinline__ uint4 read_slot(const uint8_t* p) {
+__device__ __forceinline__ int group_offset(int g) {
+  return WB == 1 ? (g >> 1) * 256 : g * 256;
+}
+
+template <int WB>
+__device__ __forceinline__ v4i slot_operand(uint4 slot, int g, int half, int h) {
+  // g and half are compile-time constants at every call
   if (WB == 1) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    return make_uint4(v.x, v.y, 0, 0);
+    const uint32_t word = (g & 1) ? (half == 0 ? slot.z : slot.w) : (half == 0 ? slot.x : slot.y);
+    return expand_binary(word, h);
   }
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-template <int WB>
-__device__ __forceinline__ v4i slot_operand(uint4 slot, int half, int h) {
-  const uint32_t lo = half == 0 ? slot.x : slot.z;  // half is a compile-time constant at every call
+  const uint32_t lo = half == 0 ? slot.x : slot.z;
   const uint32_t hi = half == 0 ? slot.y : slot.w;
-  if (WB == 1) return expand_binary(half == 0 ? slot.x : slot.y, h);
   return expand_ternary(h == 0 ? lo : hi);
 }
 
 template <int WB>
-__device__ __forceinline__ int slot_offset(int b_row) {  // + nb * 2 tiles + g * (slot bytes * 16)
-  return WB == 1 ? (b_row >> 4) * kBinTileBytes + (b_row & 15) * 8 : (b_row >> 4) * kTileBytes + (b_row & 15) * 16;
+__device__ __forceinline__ int slot_offset(int b_row) {  // + nb * 2 row blocks + group_offset(g)
+  return (b_row >> 4) * wtile_bytes<WB>() + (b_row & 15) * 16;
 }
 
 // Output scale of token t (LDS-staged): gamma * a / qdiv, or a alone when the
@@ -151,6 +153,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
   const int64_t n0 = static_cast<int64_t>(nt) * BN;
   const int64_t rb0 = n0 / kTileRows;
   const int64_t rb_count = row_blocks(n);
+  const int bt = (kt_count + 1) / 2;  // binary tiles per row block
 
   uint4 areg[A_PER];
   uint4 breg[B_PER];
@@ -164,7 +167,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
     for (int i = 0; i < B_PER; ++i) {
       const int c = tid + kThreads * i;
       const int64_t rbg = rb0 + c / CPT;
-      breg[i] = (c < B_CHUNKS && rbg < rb_count) ? packed[(rbg * kt_count + kt) * CPT + c % CPT]
+      // binary: half kt % 2 of tile kt / 2 (bt tiles per row block)
+      const int64_t src = WB == 1 ? (rbg * bt + kt / 2) * 64 + (kt & 1) * 32 + c % CPT
+                                  : (rbg * kt_count + kt) * CPT + c % CPT;
+      breg[i] = (c < B_CHUNKS && rbg < rb_count) ? packed[src]
                                                  : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
     }
   };
@@ -214,12 +220,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
       // + [0,16)) and 2 + h (columns 64g + 32 + 16h + [0,16))
       uint4 slot[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) slot[nb] = read_slot<WB>(Bs + b_off + nb * 2 * TB + g * (TB / 4));
+      for (int nb = 0; nb < NB; ++nb)
+        slot[nb] = *reinterpret_cast<const uint4*>(Bs + b_off + nb * 2 * TB + group_offset<WB>(g));
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         v4i b[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) b[nb] = slot_operand<WB>(slot[nb], half, h);
+        for (int nb = 0; nb < NB; ++nb) b[nb] = slot_operand<WB>(slot[nb], g, half, h);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const v4i a = *reinterpret_cast<const v4i*>(As + a_off + mb * 32 * kAPitch + g * 64 + half * 32);
@@ -302,10 +309,11 @@ constexpr int kPastDescriptor = 0x7fffff00;  // byte offset beyond any descripto
 // rows 32 * (v / 2) + [0, 32) of the workgroup's features, from gate for even
 // v and from up for odd v (b_rsrc / u_rsrc).
 //
-// Binary weights (WB = 1): one 1 KiB copy carries the 512-byte tiles of two
-// row blocks (lanes 0-31 the first, 32-63 the second); the BN / 32 copies of
-// a stage are dealt to the waves round-robin, so waves may issue different
-// counts (the binary kernel runs two stages and waits for all copies).
+// Binary weights (WB = 1): one 1 KiB copy carries the k-step's 512-byte half
+// tiles of two row blocks (lanes 0-31 the first, 32-63 the second); the
+// BN / 32 copies of a stage are dealt to the waves round-robin, so waves may
+// issue different counts (the binary kernel runs two stages and waits for
+// all copies).
 template <int BM, int BN, bool SWIGLU = false, int WB = 2>
 __device__ __forceinline__ void issue_tile(uint8_t* stage, __amdgpu_buffer_rsrc_t a_rsrc, __amdgpu_buffer_rsrc_t b_rsrc,
                                            __amdgpu_buffer_rsrc_t u_rsrc, int k, int kt_count, int kt, int wave,
@@ -325,9 +333,10 @@ __device__ __forceinline__ void issue_tile(uint8_t* stage, __amdgpu_buffer_rsrc_
     __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, BITLINEAR_LDS(stage + blk * 1024), 16, off, 0, 0, 0);
   }
   if (WB == 1) {
+    const int bt = (kt_count + 1) / 2;
     for (int i = wave; i < BN / 32; i += kThreads / 64) {
       const int rbl = 2 * i + (lane >> 5);
-      const int off = (rbl * kt_count + ktc) * kBinTileBytes + (lane & 31) * 16;
+      const int off = (rbl * bt + (ktc >> 1)) * kBinTileBytes + (ktc & 1) * kBinStepBytes + (lane & 31) * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, BITLINEAR_LDS(stage + DS::kABytes + i * 1024), 16, off, 0, 0, 0);
     }
     return;
@@ -419,7 +428,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   };
   auto read_ops = [&](const uint8_t* st, int g, Ops& o) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o.slot[nb] = read_slot<WB>(st + b_off + nb * 2 * TB + g * (TB / 4));
+    for (int nb = 0; nb < NB; ++nb) o.slot[nb] = *reinterpret_cast<const uint4*>(st + b_off + nb * 2 * TB + group_offset<WB>(g));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int chunk = (4 * g + 2 * half) ^ a_x;  // logical chunk 4g + 2 half + h, swizzled by row % 16
@@ -428,12 +437,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
         o.a[half][mb] = *reinterpret_cast<const v4i*>(st + (a_row0 + mb * 32) * kTileCols + chunk * 16);
     }
   };
-  auto math = [&](const Ops& o) {
+  auto math = [&](const Ops& o, int g) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       v4i b[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[nb] = slot_operand<WB>(o.slot[nb], half, h);
+      for (int nb = 0; nb < NB; ++nb) b[nb] = slot_operand<WB>(o.slot[nb], g, half, h);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -450,17 +459,17 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
     __builtin_amdgcn_sched_barrier(0);
     read_ops(st, 1, o1);
     __builtin_amdgcn_sched_barrier(0);
-    math(o0);
+    math(o0, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_ops(st, 2, o0);
     __builtin_amdgcn_sched_barrier(0);
-    math(o1);
+    math(o1, 1);
     __builtin_amdgcn_sched_barrier(0);
     read_ops(st, 3, o1);
     __builtin_amdgcn_sched_barrier(0);
-    math(o0);
+    math(o0, 2);
     __builtin_amdgcn_sched_barrier(0);
-    math(o1);
+    math(o1, 3);
   };
 
   // per-token output scale gamma * a'[t] / 127, staged once (one per matrix)
@@ -478,8 +487,10 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   const int64_t rbs_here = rb_count - rb0 < FB / kTileRows ? rb_count - rb0 : FB / kTileRows;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(xq + m0 * k), 0, static_cast<int>(rows_here * k), kBufferWord3);
+  const int64_t row_bytes = WB == 1 ? static_cast<int64_t>((kt_count + 1) / 2) * kBinTileBytes
+                                    : static_cast<int64_t>(kt_count) * kTileBytes;  // one row block's weights
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(packed_b + rb0 * kt_count * TB), 0, static_cast<int>(rbs_here * kt_count * TB), kBufferWord3);
+      const_cast<uint8_t*>(packed_b + rb0 * row_bytes), 0, static_cast<int>(rbs_here * row_bytes), kBufferWord3);
   const __amdgpu_buffer_rsrc_t u_rsrc = SWIGLU ? __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(packed_u + rb0 * kt_count * kTileBytes), 0,
       static_cast<int>(rbs_here * kt_count * kTileBytes), kBufferWord3) : b_rsrc;

@@ -587,10 +587,9 @@ __device__ __forceinline__ void prefetch_f32(uint4 (&cache)[kCachedChunks], cons
 // With an up matrix (SwiGLU) an item walks 2 * kt_count tiles: the row
 // block's gate tiles, then its up tiles.
 //
-// Binary weights (WB = 1): an item is a pair of 512-byte tiles (512 columns),
-// loaded as two 8-byte-per-lane reads into one register quad (tile 2i in
-// x, y; tile 2i + 1 in z, w); kt_count is then the tile count rounded up to
-// even and kt_real the stored tile count of a row block.
+// Binary weights (WB = 1): an item is one 1 KiB binary tile (512 columns),
+// one 16-byte-per-lane load; kt_count is then the staged 256-column count
+// (twice the binary tiles) and kt_real the binary tiles of a row block.
 template <int WAVES, int U, bool SWIGLU, int WB = 2>
 __device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict__ packed,
                                           const uint4* __restrict__ packed_u, int64_t rb, int c, int kt_count,
@@ -600,13 +599,8 @@ __device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict
   for (int u = 0; u < U; ++u) {
     const int kv = c * U * WAVES + wave + u * WAVES;
     if (WB == 1) {
-      w[u] = make_uint4(0, 0, 0, 0);
-      if (valid && kv < kt_items) {
-        const uint2* t = reinterpret_cast<const uint2*>(packed) + (rb * kt_real + 2 * kv) * 64 + lane;
-        const uint2 lo = load_weights_nt2(t);
-        const uint2 hi = 2 * kv + 1 < kt_real ? load_weights_nt2(t + 64) : make_uint2(0, 0);
-        w[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
+      w[u] = (valid && kv < kt_items) ? load_weights_nt(packed + (rb * kt_real + kv) * 64 + lane)
+                                      : make_uint4(0, 0, 0, 0);
       continue;
     }
     const bool up = SWIGLU && kv >= kt_count;
@@ -617,12 +611,17 @@ __device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict
 }
 
 // Operand j of an item: its activation column offset (inside the lane's
-// 64-column group) and its expanded weight bytes.  Ternary: word j of the
-// tile's slot, 16 columns each.  Binary: tile j / 4 of the pair, word
-// (j / 2) % 2 of its slot, half j % 2 of the word.
+// column group: 64 columns of a ternary tile, 128 of a binary one) and its
+// expanded weight bytes.  Ternary: word j of the slot, 16 columns each.
+// Binary: word j / 2 of the slot (32 columns), half j % 2 of the word.
 template <int WB>
 __device__ __forceinline__ int item_col(int item, int j) {
-  return WB == 1 ? item * 512 + (j >> 2) * kTileCols + ((j >> 1) & 1) * 32 + (j & 1) * 16 : item * kTileCols + 16 * j;
+  return WB == 1 ? item * kBinTileCols + (j >> 1) * 32 + (j & 1) * 16 : item * kTileCols + 16 * j;
+}
+
+template <int WB>
+constexpr int group_cols() {
+  return WB == 1 ? 128 : 64;
 }
 
 template <int WB>
@@ -705,7 +704,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   const float gamma = dq.row_scale ? 0.0f : *gamma_p;  // no tensor scale with per-row scales
   const float gamma_up = SWIGLU ? *gamma_u : 0.0f;
   const v4i zero4 = {0, 0, 0, 0};
-  const int8_t* xrow = xs + (has_tok ? tok : 0) * pitch + g * 64;
+  const int8_t* xrow = xs + (has_tok ? tok : 0) * pitch + g * group_cols<WB>();
   v4i acc = zero4;
   v4i acc_u = zero4;  // SwiGLU: the up projection's partial sums
   while (rb < rb_count) {
@@ -849,18 +848,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_global_kernel(const uint4* __
     for (int u = 0; u < U; ++u) {
       const int it = i0 + u * WAVES;
       const bool in = it < items;
-      wv[u] = make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
-      if (in && WB == 1) {  // binary: tiles 2 it and 2 it + 1 of 512 bytes
-        const uint2* t = reinterpret_cast<const uint2*>(packed) + (rb * kt_real + 2 * it) * 64 + lane;
-        const uint2 lo = load_weights_nt2(t);
-        const uint2 hi = 2 * it + 1 < kt_real ? load_weights_nt2(t + 64) : make_uint2(0, 0);
-        wv[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      } else if (in) {  // ternary: item it is tile it
-        wv[u] = load_weights_nt(packed + (rb * kt_count + it) * 64 + lane);
-      }
+      wv[u] = in ? load_weights_nt(packed + (rb * kt_real + it) * 64 + lane)  // item it is tile it
+                 : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
 #pragma unroll
       for (int j = 0; j < kOps; ++j)
-        xv[u][j] = load_x16(xrow, static_cast<int64_t>(item_col<WB>(it, j)) + g * 64, k, in && has_tok, VEC);
+        xv[u][j] = load_x16(xrow, static_cast<int64_t>(item_col<WB>(it, j)) + g * group_cols<WB>(), k,
+                            in && has_tok, VEC);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -903,7 +896,7 @@ hipError_t launch_lds(const void* packed, const float* gamma, Dequant dq, int64_
                       const float* gain, float eps, hipStream_t s, bool vec, const void* packed_u = nullptr,
                       const float* gamma_u = nullptr) {
   const int kt = static_cast<int>(staged_tiles(k, WB));
-  const int kt_real = static_cast<int>(k_tiles(k));
+  const int kt_real = static_cast<int>(WB == 1 ? bin_tiles(k) : k_tiles(k));
   const int64_t rbs = row_blocks(n);
   // balanced persistent grid: every workgroup takes the same number of row blocks (+-1)
   const int64_t per = (rbs + kMaxResidentGroups - 1) / kMaxResidentGroups;
@@ -949,7 +942,7 @@ template <int WB>
 hipError_t launch_global(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
                          const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s, bool vec) {
   const int kt = static_cast<int>(staged_tiles(k, WB));
-  const int kt_real = static_cast<int>(k_tiles(k));
+  const int kt_real = static_cast<int>(WB == 1 ? bin_tiles(k) : k_tiles(k));
   const dim3 grid(static_cast<unsigned>(row_blocks(n)));
   const uint4* p = static_cast<const uint4*>(packed);
   if (vec)

@@ -164,14 +164,19 @@ __global__ __launch_bounds__(kThreads) void ternarize_pack_rows(const float* __r
 // ---- binary sign bits ("BitNet's 1-Bit Transformer: Architecture
 // Breakdown", "Binary Weight Matrices with Learnable Scaling": W_bit =
 // s * sign(W)); bit set for W < 0, so zero packs as +1.  One thread per
-// 32-column word; word cw of a row is word cw % 2 of slot (row % 16) +
-// 16 * ((cw % 8) / 2) in tile (row / 16, cw / 8).
+// 32-column word; word cw of a row is word cw % 4 of slot (row % 16) +
+// 16 * ((cw % 16) / 4) in tile (row / 16, cw / 16).
 __device__ __forceinline__ int sign_bit_pos(int c) { return 8 * (c & 3) + 7 - (c >> 2); }
+
+__device__ __forceinline__ int64_t bin_word_index(int64_t row, int64_t cw, int64_t bt) {
+  const int64_t slot = (row & 15) + 16 * ((cw & 15) >> 2);
+  return ((row >> 4) * bt + (cw >> 4)) * 256 + slot * 4 + (cw & 3);
+}
 
 template <bool kVec>
 __global__ __launch_bounds__(kThreads) void pack_binary_kernel(const float* __restrict__ w, int64_t n, int64_t k,
-                                                               int64_t kt_count, uint32_t* __restrict__ packed) {
-  const int64_t words_per_row = kt_count * 8;
+                                                               int64_t bt, uint32_t* __restrict__ packed) {
+  const int64_t words_per_row = bt * 16;
   const int64_t total = row_blocks(n) * kTileRows * words_per_row;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * kThreads) {
@@ -193,22 +198,20 @@ __global__ __launch_bounds__(kThreads) void pack_binary_kernel(const float* __re
       for (int c = 0; c < 32; ++c)
         if (k0 + c < k) word |= static_cast<uint32_t>(w[row * k + k0 + c] < 0.0f) << sign_bit_pos(c);
     }
-    const int64_t slot = (row & 15) + 16 * ((cw & 7) >> 1);
-    packed[((row >> 4) * kt_count + (cw >> 3)) * 128 + slot * 2 + (cw & 1)] = word;
+    packed[bin_word_index(row, cw, bt)] = word;
   }
 }
 
 __global__ __launch_bounds__(kThreads) void unpack_binary_kernel(const uint32_t* __restrict__ packed, int64_t n,
-                                                                 int64_t k, int64_t kt_count,
+                                                                 int64_t k, int64_t bt,
                                                                  int8_t* __restrict__ codes) {
-  const int64_t words_per_row = kt_count * 8;
+  const int64_t words_per_row = bt * 16;
   const int64_t total = n * words_per_row;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * kThreads) {
     const int64_t row = idx / words_per_row;
     const int64_t cw = idx - row * words_per_row;
-    const int64_t slot = (row & 15) + 16 * ((cw & 7) >> 1);
-    const uint32_t word = packed[((row >> 4) * kt_count + (cw >> 3)) * 128 + slot * 2 + (cw & 1)];
+    const uint32_t word = packed[bin_word_index(row, cw, bt)];
     const int64_t k0 = cw * 32;
     for (int c = 0; c < 32; ++c)
       if (k0 + c < k) codes[row * k + k0 + c] = ((word >> sign_bit_pos(c)) & 1u) ? int8_t(-1) : int8_t(1);
@@ -291,20 +294,20 @@ hipError_t launch_pack_rowscale(const float* w, int64_t n, int64_t k, void* pack
 }
 
 hipError_t launch_pack_binary(const float* w, int64_t n, int64_t k, void* packed, hipStream_t s) {
-  const int64_t kt = k_tiles(k);
-  const int64_t words = row_blocks(n) * kTileRows * kt * 8;
+  const int64_t bt = bin_tiles(k);
+  const int64_t words = row_blocks(n) * kTileRows * bt * 16;
   const bool vec = (reinterpret_cast<uintptr_t>(w) % 16 == 0) && (k % 4 == 0);
   if (vec)
-    pack_binary_kernel<true><<<grid_for(words), kThreads, 0, s>>>(w, n, k, kt, static_cast<uint32_t*>(packed));
+    pack_binary_kernel<true><<<grid_for(words), kThreads, 0, s>>>(w, n, k, bt, static_cast<uint32_t*>(packed));
   else
-    pack_binary_kernel<false><<<grid_for(words), kThreads, 0, s>>>(w, n, k, kt, static_cast<uint32_t*>(packed));
+    pack_binary_kernel<false><<<grid_for(words), kThreads, 0, s>>>(w, n, k, bt, static_cast<uint32_t*>(packed));
   return hipGetLastError();
 }
 
 hipError_t launch_unpack_binary(const void* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t s) {
-  const int64_t kt = k_tiles(k);
-  unpack_binary_kernel<<<grid_for(n * kt * 8), kThreads, 0, s>>>(static_cast<const uint32_t*>(packed), n, k, kt,
-                                                                 codes);
+  const int64_t bt = bin_tiles(k);
+  unpack_binary_kernel<<<grid_for(n * bt * 16), kThreads, 0, s>>>(static_cast<const uint32_t*>(packed), n, k, bt,
+                                                                  codes);
   return hipGetLastError();
 }
 

@@ -363,10 +363,10 @@ int bitlinear_forward_rowscale(const void *packed, const uint16_t *scales, int64
  * Weight Matrices with Learnable Scaling"), one bit per weight.  sign(0) is
  * taken as +1 (one bit has no code for 0): the bit is set exactly where
  * W < 0.  s is learned, so it is an input of the forward, not computed here.
- * Layout: tiles of 16 rows x 256 columns, 512 bytes each, tile (rb, kt) at
- * byte (rb * ceil(k/256) + kt) * 512; 8-byte slot l (0..63) holds row
- * 16*rb + (l % 16) and columns 256*kt + 64*(l / 16) + [0, 64); its 32-bit
- * word s (0, 1) covers 32 of those columns, column c of the word in bit
+ * Layout: tiles of 16 rows x 512 columns, 1024 bytes each, tile (rb, kt) at
+ * byte (rb * ceil(k/512) + kt) * 1024; 16-byte slot l (0..63) holds row
+ * 16*rb + (l % 16) and columns 512*kt + 128*(l / 16) + [0, 128); its 32-bit
+ * word s (0..3) covers 32 of those columns, column c of the word in bit
  * 8*(c % 4) + 7 - c/4 (set = -1, clear = +1).  Padding bits are clear.
  */
 size_t bitlinear_packed_bytes_binary(int64_t n, int64_t k);

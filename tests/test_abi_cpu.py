@@ -274,10 +274,11 @@ def test_fused_ffn_entry_validation(blq):
 # ---------------------------------------------------------------------------
 
 def test_variant_sizes(blq):
-    # binary tiles: 16 x 256 columns in 512 bytes (one bit per weight)
+    # binary tiles: 16 x 512 columns in 1024 bytes (one bit per weight)
     assert blq.bitlinear_packed_bytes_binary(2048, 2048) == 2048 * 2048 // 8
-    assert blq.bitlinear_packed_bytes_binary(1, 1) == 512
-    assert blq.bitlinear_packed_bytes_binary(17, 257) == 2 * 2 * 512
+    assert blq.bitlinear_packed_bytes_binary(1, 1) == 1024
+    assert blq.bitlinear_packed_bytes_binary(17, 257) == 2 * 1 * 1024
+    assert blq.bitlinear_packed_bytes_binary(17, 513) == 2 * 2 * 1024
     assert blq.bitlinear_packed_bytes_binary(0, 5) == 0
     # per-tensor quantisation: one launch (no partials) up to 16384 values, at most 1024 partials
     assert blq.bitlinear_quant_act_tensor_workspace_bytes(1, 16384) == 4

@@ -173,16 +173,16 @@ def test_rowscale_forward_parity(blq, n, k, m):
 def decode_binary_layout(raw: np.ndarray, n: int, k: int) -> np.ndarray:
     """Sign codes from the packed bytes, read by the layout the header states
     (independent of the library's own unpack)."""
-    kt = (k + 255) // 256
+    kt = (k + 511) // 512
     words = raw.view(np.uint32)
     out = np.empty((n, k), np.int8)
     for r in range(n):
         for c in range(k):
-            t, cc = divmod(c, 256)
-            g, cw = divmod(cc, 64)
+            t, cc = divmod(c, 512)
+            g, cw = divmod(cc, 128)
             s, col = divmod(cw, 32)
             slot = (r % 16) + 16 * g
-            word = words[((r // 16) * kt + t) * 128 + slot * 2 + s]
+            word = words[((r // 16) * kt + t) * 256 + slot * 4 + s]
             bit = 8 * (col % 4) + 7 - col // 4
             out[r, c] = -1 if (int(word) >> bit) & 1 else 1
     return out
