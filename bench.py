@@ -422,6 +422,8 @@ def main():
     ap.add_argument("--m", type=int, default=None, help="tokens per matrix (default: workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
+    ap.add_argument("--fused", action="store_true",
+                    help="decode with m > 1: the fused quant + forward entry point (default only at m = 1)")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
     ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu", "lut") + MODES,
@@ -483,7 +485,7 @@ def main():
         fused = (m == 1 and not args.unfused and
                  all(blq.bitlinear_quant_forward_binary_supported(m, mt.k) for mt in wl.matrices))
     else:
-        fused = (m == 1 and not args.unfused and not lut and mode is None and
+        fused = ((m == 1 or args.fused) and not args.unfused and not lut and mode is None and
                  all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
     want_cpu = not args.no_cpu_baseline
     oracle_mod = None

@@ -905,7 +905,9 @@ hipError_t launch_lds(const void* packed, const float* gamma, Dequant dq, int64_
   const int kt_real = static_cast<int>(WB == 1 ? bin_tiles(k) : k_tiles(k));
   const int64_t rbs = row_blocks(n);
   // balanced persistent grid: every workgroup takes the same number of row blocks (+-1)
-  const int64_t per = (rbs + kMaxResidentGroups - 1) / kMaxResidentGroups;
+  // the same number of resident waves whatever the workgroup size
+  const int64_t cap = kMaxResidentGroups * kWaves / WAVES;
+  const int64_t per = (rbs + cap - 1) / cap;
   const dim3 grid(static_cast<unsigned>((rbs + per - 1) / per));
   const size_t lds = lds_bytes(m, kt);
   const uint4* p = static_cast<const uint4*>(packed);
@@ -938,16 +940,18 @@ hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int6
                         const float* gain, float eps, hipStream_t s, bool vec, const void* packed_u = nullptr,
                         const float* gamma_u = nullptr) {
   const int64_t items = WB == 1 ? staged_tiles(k, 1) / 2 : (SWIGLU ? 2 : 1) * k_tiles(k);
-  if (items <= kWaves)
-    return launch_lds<SRC, kWaves, 1, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
+  // the RMSNorm prologue alone measured faster with two 8-wave workgroups per CU
+  constexpr int W = (SRC == kFromBf16Norm && !SWIGLU) ? 8 : kWaves;
+  if (items <= W)
+    return launch_lds<SRC, W, 1, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
                                                   gain, eps, s, vec, packed_u, gamma_u);
-  if (items <= 2 * kWaves)
-    return launch_lds<SRC, kWaves, 2, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
+  if (items <= 2 * W)
+    return launch_lds<SRC, W, 2, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
                                                   gain, eps, s, vec, packed_u, gamma_u);
-  if (items <= 4 * kWaves)
-    return launch_lds<SRC, kWaves, 4, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
+  if (items <= 4 * W)
+    return launch_lds<SRC, W, 4, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
                                                   gain, eps, s, vec, packed_u, gamma_u);
-  return launch_lds<SRC, kWaves, 8, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
+  return launch_lds<SRC, W, 8, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
                                                 gain, eps, s, vec, packed_u, gamma_u);
 }
 
