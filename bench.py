@@ -448,7 +448,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the path is single-device; "
+        print("bench.py: measures one GPU only (the path is single-device; "
               "--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -174,7 +174,7 @@ def test_ternary_zero_and_clip_fraction(oracle_mod):
     assert abs((q == 0).mean() - p_zero) < 1.2e-3
     t = np.abs(w.astype(np.float64)) / d
     assert abs((t >= 1.5).mean() - p_clip) < 1.2e-3
-    # the values the survey of the recipe expects (~31% zeros, ~23% clipped)
+    # the analytic values for N(0, 0.02) latents (~31% zeros, ~23% clipped)
     assert abs(p_zero - 0.3102) < 2e-3 and abs(p_clip - 0.2311) < 2e-3
 
 
