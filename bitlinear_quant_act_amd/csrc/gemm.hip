@@ -80,6 +80,16 @@ __device__ __forceinline__ int group_offset(int g) {
   return WB == 1 ? (g >> 1) * 256 : g * 256;
 }
 
+// A lane's part of a slot: binary lanes keep the whole slot; ternary lanes of
+// half h need only words h and 2 + h, fetched at a lane-dependent offset by
+// one two-dword LDS read (no per-lane select, half the bytes).
+template <int WB>
+__device__ __forceinline__ uint4 read_slot(const uint8_t* p, int h) {
+  if (WB == 1) return *reinterpret_cast<const uint4*>(p);
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p) + h;
+  return make_uint4(w[0], w[2], 0, 0);
+}
+
 template <int WB>
 __device__ __forceinline__ v4i slot_operand(uint4 slot, int g, int half, int h) {
   // g and half are compile-time constants at every call
@@ -87,9 +97,7 @@ __device__ __forceinline__ v4i slot_operand(uint4 slot, int g, int half, int h) 
     const uint32_t word = (g & 1) ? (half == 0 ? slot.z : slot.w) : (half == 0 ? slot.x : slot.y);
     return expand_binary(word, h);
   }
-  const uint32_t lo = half == 0 ? slot.x : slot.z;
-  const uint32_t hi = half == 0 ? slot.y : slot.w;
-  return expand_ternary(h == 0 ? lo : hi);
+  return expand_ternary(half == 0 ? slot.x : slot.y);  // words h and 2 + h (read_slot)
 }
 
 template <int WB>
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps stage addresses scalar
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31;  // operand row (token for A, weight row for B)
   const int h = lane >> 5;    // which 16 of the step's 32 columns
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
       uint4 slot[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        slot[nb] = *reinterpret_cast<const uint4*>(Bs + b_off + nb * 2 * TB + group_offset<WB>(g));
+        slot[nb] = read_slot<WB>(Bs + b_off + nb * 2 * TB + group_offset<WB>(g), h);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         v4i b[NB];
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps stage addresses scalar
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31;
   const int h = lane >> 5;
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   };
   auto read_ops = [&](const uint8_t* st, int g, Ops& o) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o.slot[nb] = *reinterpret_cast<const uint4*>(st + b_off + nb * 2 * TB + group_offset<WB>(g));
+    for (int nb = 0; nb < NB; ++nb) o.slot[nb] = read_slot<WB>(st + b_off + nb * 2 * TB + group_offset<WB>(g), h);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int chunk = (4 * g + 2 * half) ^ a_x;  // logical chunk 4g + 2 half + h, swizzled by row % 16
