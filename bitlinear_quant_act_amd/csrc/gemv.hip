@@ -930,10 +930,28 @@ hipError_t launch_lds(const void* packed, const float* gamma, Dequant dq, int64_
   return hipGetLastError();
 }
 
-// U = items per wave per chunk: one chunk covers a row block of up to
-// 8 * WAVES items; longer rows are walked in chunks of that many items.
-// SWIGLU items hold 2 * kt tiles (gate then up) and binary items two tiles,
-// so U follows the item count.
+// U = items per wave per chunk. A chunk is U * waves items of one row block;
+// each wave requests the next chunk's items before it consumes the current
+// one's. The smallest U that covers the row block in one chunk is the start.
+// U is then halved while a workgroup walks fewer than 8 chunks in all, as long
+// as the last chunk of a row block stays at least half full. Shorter chunks
+// put the first contraction and the last row block's tail closer to the bytes'
+// arrival; a mostly empty last chunk costs a loop trip with idle waves. On the
+// 70B-shaped down projection (112 items, 2 row blocks per workgroup) U = 2
+// against 8 took the layer from 4.22 to 4.59 TB/s.
+int items_per_wave(int64_t items, int64_t row_blocks_per_group, int waves) {
+  int u = items <= waves ? 1 : items <= 2 * waves ? 2 : items <= 4 * waves ? 4 : 8;
+  while (u > 1) {
+    const int64_t half = u / 2 * waves;  // items per chunk after halving
+    const int64_t last = items % half == 0 ? half : items % half;
+    const int64_t walk = row_blocks_per_group * ((items + u * waves - 1) / (u * waves));
+    if (walk >= 8 || 2 * last < half) break;
+    u /= 2;
+  }
+  return u;
+}
+
+// SWIGLU items hold 2 * kt tiles (gate then up) and binary items two tiles.
 template <int SRC, bool SWIGLU = false, int WB = 2>
 hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const void* xsrc,
                         const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
@@ -942,13 +960,16 @@ hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int6
   const int64_t items = WB == 1 ? staged_tiles(k, 1) / 2 : (SWIGLU ? 2 : 1) * k_tiles(k);
   // the RMSNorm prologue alone measured faster with two 8-wave workgroups per CU
   constexpr int W = (SRC == kFromBf16Norm && !SWIGLU) ? 8 : kWaves;
-  if (items <= W)
+  const int64_t cap = kMaxResidentGroups * kWaves / W;  // the grid cap of launch_lds
+  const int64_t per = (row_blocks(n) + cap - 1) / cap;
+  const int u = items_per_wave(items, per, W);
+  if (u == 1)
     return launch_lds<SRC, W, 1, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
                                                   gain, eps, s, vec, packed_u, gamma_u);
-  if (items <= 2 * W)
+  if (u == 2)
     return launch_lds<SRC, W, 2, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
                                                   gain, eps, s, vec, packed_u, gamma_u);
-  if (items <= 4 * W)
+  if (u == 4)
     return launch_lds<SRC, W, 4, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
                                                   gain, eps, s, vec, packed_u, gamma_u);
   return launch_lds<SRC, W, 8, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
