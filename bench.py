@@ -75,6 +75,18 @@ def quant_bytes(m: int, k: int) -> int:
 #   binary    -- 1-bit sign weights with a per-layer scale (bitlinear_forward_binary; fused at m = 1)
 MODES = ("tensor128", "rowscale", "binary")
 
+# Decode token counts up to which the fused entry point (the quantisation, or
+# RMSNorm + quantisation, in the GEMV prologue) is the default.  Every
+# workgroup re-quantises all m tokens, so the fusion saves a launch but adds
+# m * k of redundant prologue work; measured on the 2B and 8B stacks it wins
+# up to m = 4 (plain) and m = 2 (RMSNorm), and only at m = 1 for the SwiGLU
+# block and the variant modes.
+FUSED_MAX_M = {"plain": 4, "rmsnorm": 2}
+
+
+def fused_default(variant: str, m: int) -> bool:
+    return m <= FUSED_MAX_M.get(variant, 1)
+
 
 def mode_forward_bytes(variant: str, m: int, n: int, k: int, fused: bool = False) -> int:
     """Algorithmic bytes of one forward call of a variant mode."""
@@ -423,7 +435,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
     ap.add_argument("--fused", action="store_true",
-                    help="decode with m > 1: the fused quant + forward entry point (default only at m = 1)")
+                    help="decode: the fused quant + forward entry point at any m (default up to FUSED_MAX_M)")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
     ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu", "lut") + MODES,
@@ -473,7 +485,7 @@ def main():
     m = args.m if args.m is not None else wl.ms[0]
     batched = m > blq.BITLINEAR_FORWARD_MAX_M
     # the fused entry point re-quantises the tokens in every workgroup, which
-    # pays off for a single token; several tokens go through quant + forward
+    # pays off for a few tokens (FUSED_MAX_M); more go through quant + forward
     lut = args.variant == "lut"
     if lut and (m > blq.BITLINEAR_FORWARD_MAX_M or
                 not all(blq.bitlinear_forward_lut_supported(mt.k) for mt in wl.matrices)):
@@ -485,7 +497,7 @@ def main():
         fused = (m == 1 and not args.unfused and
                  all(blq.bitlinear_quant_forward_binary_supported(m, mt.k) for mt in wl.matrices))
     else:
-        fused = ((m == 1 or args.fused) and not args.unfused and not lut and mode is None and
+        fused = ((fused_default(args.variant, m) or args.fused) and not args.unfused and not lut and mode is None and
                  all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
     want_cpu = not args.no_cpu_baseline
     oracle_mod = None
@@ -805,8 +817,8 @@ def summarize(args):
 
     --summarize KEY[:VARIANT] M STATS_CSV FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB KERNEL_PAT CMD...
     The algorithmic bytes are those of the dominant kernel bench.py times for
-    that workload and variant (fused quant + forward at m = 1 unless the
-    variant is lut)."""
+    that workload and variant (fused quant + forward up to FUSED_MAX_M unless
+    the variant is lut)."""
     key, m, stats, fetch, write, cfetch, cwrite, copy_mib, pat = args[:9]
     key, _, variant = key.partition(":")
     variant = variant or "plain"
@@ -831,8 +843,8 @@ def summarize(args):
         alg = sum(mode_forward_bytes(variant, m, mt.n, mt.k, variant == "binary" and m == 1)
                   for mt in wl.matrices) / len(wl.matrices)
     else:
-        per = fused_bytes if (m == 1 and variant != "lut") else forward_bytes
-        alg = sum(per(m, mt.n, mt.k) + (4 * mt.k if variant == "rmsnorm" and m == 1 else 0)
+        per = fused_bytes if (fused_default(variant, m) and variant != "lut") else forward_bytes
+        alg = sum(per(m, mt.n, mt.k) + (4 * mt.k if variant == "rmsnorm" and fused_default(variant, m) else 0)
                   for mt in wl.matrices) / len(wl.matrices)
     suffix = "" if variant == "plain" else "_" + variant
     sources = LUT_SOURCES if variant == "lut" else DECODE_SOURCES if m <= 16 else BATCHED_SOURCES

@@ -149,6 +149,18 @@ __device__ __forceinline__ void prefetch_codes(uint4 (&cache)[kCachedChunks], co
   }
 }
 
+// Waves per token when m tokens share a workgroup's waves: the largest power
+// of two G with m * G <= WAVES (m <= WAVES).  Token t belongs to waves
+// [t G, t G + G); inside them, thread tt = threadIdx.x - 64 t G takes the
+// token's 16-byte chunks tt, tt + 64 G, ...  With m = 1 that is every thread
+// over the whole row.
+template <int WAVES>
+__device__ __forceinline__ int token_group(int m) {
+  int g = WAVES;
+  while (g > 1 && g * m > WAVES) g >>= 1;
+  return g;
+}
+
 __device__ __forceinline__ void prefetch_bf16(uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int m,
                                               int64_t k) {
   const int total = m * static_cast<int>(k / 8);
@@ -156,6 +168,22 @@ __device__ __forceinline__ void prefetch_bf16(uint4 (&cache)[kCachedChunks], con
   for (int j = 0; j < kCachedChunks; ++j) {
     const int c = threadIdx.x + j * static_cast<int>(blockDim.x);
     cache[j] = c < total ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// m > 1 tokens (m <= WAVES): chunk order of stage_bf16_group
+template <int WAVES>
+__device__ __forceinline__ void prefetch_bf16_group(uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int m,
+                                                    int64_t k) {
+  const int G = token_group<WAVES>(m);
+  const int t = (threadIdx.x >> 6) / G;
+  const int tt = static_cast<int>(threadIdx.x) - 64 * G * t;
+  const int cpr = static_cast<int>(k / 8);
+  const uint4* row = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t < m ? t : 0) * k);
+#pragma unroll
+  for (int j = 0; j < kCachedChunks; ++j) {
+    const int c = tt + j * 64 * G;
+    cache[j] = (t < m && c < cpr) ? row[c] : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -219,7 +247,58 @@ __device__ void stage_bf16_single(int8_t* xs, float* amax_s, unsigned* wmax_s, c
   for (int c = total + threadIdx.x; c < kpad / 8; c += nthreads) *reinterpret_cast<uint2*>(xs + c * 8) = make_uint2(0, 0);
 }
 
+// Vector path, 1 < m <= WAVES tokens: the waves of a token group
+// (token_group) reduce max|x| over their chunks with DPP wave operations; with
+// more than one wave per token the wave maxima meet through one LDS slot per
+// wave and one barrier.  No atomics.  The chunk order is prefetch_bf16_group's.
+template <int WAVES>
+__device__ void stage_bf16_group(int8_t* xs, int pitch, float* amax_s, unsigned* wmax_s,
+                                 const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int m, int64_t k,
+                                 int kpad, int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
+  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
+  const int G = token_group<WAVES>(m);
+  const int wave = threadIdx.x >> 6;
+  const int t = wave / G;
+  const int tt = static_cast<int>(threadIdx.x) - 64 * G * t;
+  const int step = 64 * G;
+  const bool active = t < m;
+  const int cpr = static_cast<int>(k / 8);
+  const uint4* row = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(active ? t : 0) * k);
+  unsigned mx = 0;
+  int j = 0;
+  if (active)
+    for (int c = tt; c < cpr; c += step, ++j) mx = max(mx, chunk_absmax(j < kCachedChunks ? cached(cache, j) : row[c]));
+  mx = wave_max(mx);
+  if (G > 1) {  // uniform: m is the same for the whole workgroup
+    if ((threadIdx.x & 63) == 0) wmax_s[wave] = mx;
+    lds_barrier();
+    const int w0 = t * G;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+      if (w >= w0 && w < w0 + G) mx = max(mx, wmax_s[w]);
+  }
+  if (!active) return;
+  const float a = fmaxf(bf16_to_f32(mx), 1e-8f);
+  const float s = 127.0f / a;
+  if (tt == 0) {
+    amax_s[t] = a;
+    if (write_out) amax_out[t] = a;
+  }
+  int8_t* xrow = xs + t * pitch;
+  j = 0;
+  for (int c = tt; c < cpr; c += step, ++j) {
+    const uint2 q = quant_chunk(j < kCachedChunks ? cached(cache, j) : row[c], s);
+    *reinterpret_cast<uint2*>(xrow + c * 8) = q;
+    if (write_out) *reinterpret_cast<uint2*>(xq_out + static_cast<int64_t>(t) * k + c * 8) = q;
+  }
+  for (int c = cpr + tt; c < kpad / 8; c += step) *reinterpret_cast<uint2*>(xrow + c * 8) = make_uint2(0, 0);
+}
+
 // Any token count: per-token max through LDS atomics (one per token change).
+// Used where stage_bf16_group does not apply (unaligned rows, more tokens than
+// waves, or a kernel built without it).  CACHED: cache holds prefetch_bf16's
+// thread-major chunks; otherwise the activations are read here.
+template <bool CACHED>
 __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s, const uint4 (&cache)[kCachedChunks],
                            const uint16_t* __restrict__ x, int m, int64_t k, int kpad, bool vec,
                            int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
@@ -240,7 +319,7 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
         cur_t = t;
         cur = 0;
       }
-      cur = max(cur, chunk_absmax(j < kCachedChunks ? cached(cache, j)
+      cur = max(cur, chunk_absmax(CACHED && j < kCachedChunks ? cached(cache, j)
                                                     : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8)));
     }
     if (cur_t >= 0) atomicMax(&max_s[cur_t], cur);
@@ -250,7 +329,7 @@ __device__ void stage_bf16(int8_t* xs, int pitch, float* amax_s, unsigned* max_s
     j = 0;
     for (int c = threadIdx.x; c < total; c += nthreads, ++j) {
       const int t = c / cpr, cc = c - t * cpr;
-      const uint2 q = quant_chunk(j < kCachedChunks ? cached(cache, j)
+      const uint2 q = quant_chunk(CACHED && j < kCachedChunks ? cached(cache, j)
                                                     : *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(c) * 8),
                                   127.0f / amax_s[t]);
       *reinterpret_cast<uint2*>(xs + t * pitch + cc * 8) = q;
@@ -329,6 +408,26 @@ __device__ __forceinline__ void prefetch_gain(float4 (&gc)[kCachedChunks][2], co
   for (int j = 0; j < kCachedChunks; ++j) {
     const int c = threadIdx.x + j * static_cast<int>(blockDim.x);
     if (gain && c < total) {
+      gc[j][0] = *reinterpret_cast<const float4*>(gain + c * 8);
+      gc[j][1] = *reinterpret_cast<const float4*>(gain + c * 8 + 4);
+    } else {
+      gc[j][0] = gc[j][1] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    }
+  }
+}
+
+// gains of the chunks whose activations prefetch_bf16_group requests
+template <int WAVES>
+__device__ __forceinline__ void prefetch_gain_group(float4 (&gc)[kCachedChunks][2], const float* __restrict__ gain, int m,
+                                                    int64_t k) {
+  const int G = token_group<WAVES>(m);
+  const int t = (threadIdx.x >> 6) / G;
+  const int tt = static_cast<int>(threadIdx.x) - 64 * G * t;
+  const int cpr = static_cast<int>(k / 8);
+#pragma unroll
+  for (int j = 0; j < kCachedChunks; ++j) {
+    const int c = tt + j * 64 * G;
+    if (gain && t < m && c < cpr) {
       gc[j][0] = *reinterpret_cast<const float4*>(gain + c * 8);
       gc[j][1] = *reinterpret_cast<const float4*>(gain + c * 8 + 4);
     } else {
@@ -431,6 +530,92 @@ __device__ void stage_bf16_norm_single(int8_t* xs, float* amax_s, float* quant_s
     if (write_out) *reinterpret_cast<uint2*>(xq_out + c * 8) = q;
   }
   for (int c = total + threadIdx.x; c < kpad / 8; c += nthreads) *reinterpret_cast<uint2*>(xs + c * 8) = make_uint2(0, 0);
+}
+
+// Vector path, 1 < m <= WAVES tokens: the waves of a token group
+// (token_group) reduce max|v| and the fp64 sum of x^2 over their chunks
+// (per lane in chunk order, then across the wave with DPP), and the group's
+// wave partials meet through one LDS slot per wave in wave order: a fixed
+// summation order, no atomics.  The chunk order is prefetch_bf16_group's.
+template <int WAVES>
+__device__ void stage_bf16_norm_group(int8_t* xs, int pitch, float* amax_s, float* quant_s, unsigned* wmax_s,
+                                      double* wss_s, const uint4 (&cache)[kCachedChunks],
+                                      const float4 (&gcache)[kCachedChunks][2], const uint16_t* __restrict__ x,
+                                      const float* __restrict__ gain, float eps, int m, int64_t k, int kpad,
+                                      int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
+  const bool write_out = xq_out != nullptr && blockIdx.x == 0;
+  const int G = token_group<WAVES>(m);
+  const int wave = threadIdx.x >> 6;
+  const int t = wave / G;
+  const int tt = static_cast<int>(threadIdx.x) - 64 * G * t;
+  const int step = 64 * G;
+  const bool active = t < m;
+  const int cpr = static_cast<int>(k / 8);
+  const uint16_t* xr = x + static_cast<int64_t>(active ? t : 0) * k;
+  const bool has_gain = gain != nullptr;
+  auto values = [&](int c, int jj, float (&v)[8], float (&xv)[8]) {
+    if (jj < kCachedChunks)
+      norm_values_reg(cached(cache, jj), cached_gain(gcache, jj, 0), cached_gain(gcache, jj, 1), has_gain, v, xv);
+    else
+      norm_values(*reinterpret_cast<const uint4*>(xr + c * 8), gain ? gain + c * 8 : nullptr, v, xv);
+  };
+  unsigned mx = 0;
+  double ss = 0.0;
+  int j = 0;
+  if (active)
+    for (int c = tt; c < cpr; c += step, ++j) {
+      float v[8], xv[8];
+      values(c, j, v, xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ss += static_cast<double>(xv[i]) * static_cast<double>(xv[i]);
+        mx = max(mx, __float_as_uint(fabsf(v[i])));
+      }
+    }
+  mx = wave_max(mx);
+  ss = wave_sum_d(ss);
+  if (G > 1) {  // uniform: m is the same for the whole workgroup
+    if ((threadIdx.x & 63) == 0) {
+      wmax_s[wave] = mx;
+      wss_s[wave] = ss;
+    }
+    lds_barrier();
+    const int w0 = t * G;  // < WAVES for every wave, active or not
+    unsigned mall = 0;
+    double sall = 0.0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+      if (w >= w0 && w < w0 + G) {
+        mall = max(mall, wmax_s[w]);
+        sall += wss_s[w];
+      }
+    mx = mall;
+    ss = sall;
+  }
+  if (!active) return;
+  float ap, qs;
+  norm_scales(mx, ss, k, eps, &ap, &qs);
+  if (tt == 0) {
+    amax_s[t] = ap;
+    quant_s[t] = qs;
+    if (write_out) amax_out[t] = ap;
+  }
+  int8_t* xrow = xs + t * pitch;
+  j = 0;
+  for (int c = tt; c < cpr; c += step, ++j) {
+    float v[8], xv[8];
+    values(c, j, v, xv);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= norm_code(v[i], qs) << (8 * i);
+      hi |= norm_code(v[4 + i], qs) << (8 * i);
+    }
+    const uint2 q = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(xrow + c * 8) = q;
+    if (write_out) *reinterpret_cast<uint2*>(xq_out + static_cast<int64_t>(t) * k + c * 8) = q;
+  }
+  for (int c = cpr + tt; c < kpad / 8; c += step) *reinterpret_cast<uint2*>(xrow + c * 8) = make_uint2(0, 0);
 }
 
 // Any token count: token t belongs to wave t % WAVES, whose lanes reduce it
@@ -638,7 +823,11 @@ __device__ __forceinline__ v4i item_weights(const uint32_t (&words)[4], int j) {
 // SWIGLU: packed / gamma_p are the gate projection, packed_u / gamma_u the up
 // projection; y receives h = silu(y_gate) * y_up [m][n] and acc_out (if set)
 // the gate then the up accumulators, [m][2n].
-template <int WAVES, int U, int SRC, bool VEC, bool SWIGLU = false, int WB = 2>
+// MULTI: the multi-token bf16 prologues (stage_bf16_group,
+// stage_bf16_norm_group) are compiled in.  The host launches MULTI = false for
+// a single bf16 token: that kernel carries only the single-token prologue
+// (measured 1-2% faster per launch than one that carries both).
+template <int WAVES, int U, int SRC, bool VEC, bool SWIGLU = false, int WB = 2, bool MULTI = true>
 __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __restrict__ packed,
                                                               const float* __restrict__ gamma_p, Dequant dq, int64_t n,
                                                               int64_t k, int kt_count, int kt_real, int64_t rb_count,
@@ -675,14 +864,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   int c = 0;
   uint4 cache[kCachedChunks];
   float4 gcache[kCachedChunks][2];
-  if (SRC == kFromBf16Norm && VEC && m == 1) prefetch_gain(gcache, gain, k);
+  if (SRC == kFromBf16Norm && VEC && m == 1)
+    prefetch_gain(gcache, gain, k);
+  else if (SRC == kFromBf16Norm && VEC && MULTI && m <= WAVES)
+    prefetch_gain_group<WAVES>(gcache, gain, m, k);
   if (VEC) {
     if (SRC == kFromCodes)
       prefetch_codes(cache, static_cast<const int8_t*>(xsrc), m, k, kpad);
     else if (SRC == kFromF32)
       prefetch_f32(cache, static_cast<const float*>(xsrc), m, k);
-    else if (SRC == kFromBf16 || m == 1)
+    else if ((SRC == kFromBf16 && !MULTI) || m == 1)  // thread-major; unconditional without MULTI
       prefetch_bf16(cache, static_cast<const uint16_t*>(xsrc), m, k);
+    else if (MULTI && m <= WAVES)  // bf16, with or without RMSNorm
+      prefetch_bf16_group<WAVES>(cache, static_cast<const uint16_t*>(xsrc), m, k);
   }
   uint4 wcur[U];
   load_item<WAVES, U, SWIGLU, WB>(wcur, packed, packed_u, rb, c, kt_count, kt_real, wave, lane, rb < rb_count);
@@ -693,6 +887,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   } else if (SRC == kFromBf16Norm && VEC && m == 1) {
     stage_bf16_norm_single<WAVES>(xs, amax_s, quant_s, wmax_s, wss_s, cache, gcache, static_cast<const uint16_t*>(xsrc),
                                   gain, eps, k, kpad, xq_out, amax_out);
+  } else if (SRC == kFromBf16Norm && VEC && MULTI && m <= WAVES) {
+    stage_bf16_norm_group<WAVES>(xs, pitch, amax_s, quant_s, wmax_s, wss_s, cache, gcache,
+                                 static_cast<const uint16_t*>(xsrc), gain, eps, m, k, kpad, xq_out, amax_out);
   } else if (SRC == kFromBf16Norm) {
     stage_bf16_norm<WAVES>(xs, pitch, amax_s, quant_s, static_cast<const uint16_t*>(xsrc), gain, eps, m, k, kpad, VEC,
                            xq_out, amax_out);
@@ -701,8 +898,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   } else if (VEC && m == 1) {
     stage_bf16_single<WAVES>(xs, amax_s, wmax_s, cache, static_cast<const uint16_t*>(xsrc), k, kpad, xq_out,
                              amax_out);
+  } else if (VEC && MULTI && m <= WAVES) {
+    stage_bf16_group<WAVES>(xs, pitch, amax_s, wmax_s, cache, static_cast<const uint16_t*>(xsrc), m, k, kpad, xq_out,
+                            amax_out);
   } else {
-    stage_bf16(xs, pitch, amax_s, max_s, cache, static_cast<const uint16_t*>(xsrc), m, k, kpad, VEC, xq_out,
+    stage_bf16<!MULTI>(xs, pitch, amax_s, max_s, cache, static_cast<const uint16_t*>(xsrc), m, k, kpad, VEC, xq_out,
                amax_out);
   }
   lds_barrier();
@@ -912,14 +1112,23 @@ hipError_t launch_lds(const void* packed, const float* gamma, Dequant dq, int64_
   const size_t lds = lds_bytes(m, kt);
   const uint4* p = static_cast<const uint4*>(packed);
   const uint4* pu = static_cast<const uint4*>(packed_u);
+  constexpr bool kBf16 = SRC == kFromBf16 || SRC == kFromBf16Norm;
+  const bool one = kBf16 && m == 1;  // single bf16 token: the kernel without the multi-token prologues
   static const bool attr_vec = hipFuncSetAttribute(
       reinterpret_cast<const void*>(gemv_lds_kernel<WAVES, U, SRC, true, SWIGLU, WB>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
+  static const bool attr_one = !kBf16 || hipFuncSetAttribute(
+      reinterpret_cast<const void*>(gemv_lds_kernel<WAVES, U, SRC, true, SWIGLU, WB, !kBf16>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
   static const bool attr_any = hipFuncSetAttribute(
       reinterpret_cast<const void*>(gemv_lds_kernel<WAVES, U, SRC, false, SWIGLU, WB>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes) == hipSuccess;
-  if (!(vec ? attr_vec : attr_any)) return hipErrorInvalidConfiguration;
-  if (vec)
+  if (!(vec ? (one ? attr_one : attr_vec) : attr_any)) return hipErrorInvalidConfiguration;
+  if (vec && one)
+    gemv_lds_kernel<WAVES, U, SRC, true, SWIGLU, WB, !kBf16><<<grid, WAVES * 64, lds, s>>>(
+        p, gamma, dq, n, k, kt, kt_real, rbs, xsrc, amax_in, static_cast<int>(m), y, acc, xq_out, amax_out, gain, eps,
+        pu, gamma_u);
+  else if (vec)
     gemv_lds_kernel<WAVES, U, SRC, true, SWIGLU, WB><<<grid, WAVES * 64, lds, s>>>(
         p, gamma, dq, n, k, kt, kt_real, rbs, xsrc, amax_in, static_cast<int>(m), y, acc, xq_out, amax_out, gain, eps,
         pu, gamma_u);

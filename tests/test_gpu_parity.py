@@ -265,7 +265,7 @@ def test_forward_on_a_side_stream(blq):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n,k", SHAPES + [(2560, 6912), (64, 14336)])
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 16])
 def test_quant_forward_parity(blq, n, k, m):
     if not blq.bitlinear_quant_forward_supported(m, k):
         pytest.skip("m*k beyond the fused path's on-chip budget")
