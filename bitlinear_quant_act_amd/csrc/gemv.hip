@@ -73,10 +73,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #endif
 constexpr int64_t kMaxResidentGroups = BITLINEAR_GEMV_MAX_GROUPS;  // persistent grid cap
 constexpr int kWaves = BITLINEAR_GEMV_WAVES;                        // waves per workgroup
-// dynamic LDS budget for the staged codes: 64 KiB less 512 bytes.  With the
-// static reduction buffer on top a workgroup can exceed 64 KiB, so the launch
-// raises the kernel's dynamic-LDS limit; one workgroup per CU leaves room.
-constexpr int kMaxLdsBytes = 65536 - 512;
+// dynamic LDS budget for the staged codes: 140 KiB, which leaves the static
+// reduction buffer (16 KiB at 16 waves) and the small arrays room inside the
+// CU's 160 KiB.  The launch raises the kernel's dynamic-LDS limit to it.  The
+// persistent grid holds one 16-wave workgroup per CU; the 8-wave kernels
+// (two per CU) keep two resident while their codes take at most ~70 KiB.
+constexpr int kMaxLdsBytes = 140 * 1024;
 constexpr int kCachedChunks = 4;  // activation chunks per thread held in registers by the prologue
 
 enum Source { kFromCodes = 0, kFromBf16 = 1, kFromBf16Norm = 2, kFromF32 = 3 };

@@ -166,14 +166,16 @@ def test_quant_forward_validation(blq):
     assert lib.bitlinear_quant_forward_supported(1, 2560) == 1
     assert lib.bitlinear_quant_forward_supported(1, 28672) == 1
     assert lib.bitlinear_quant_forward_supported(2, 14336) == 1
-    assert lib.bitlinear_quant_forward_supported(8, 14336) == 0
+    assert lib.bitlinear_quant_forward_supported(8, 14336) == 1
+    assert lib.bitlinear_quant_forward_supported(16, 14336) == 0
     assert lib.bitlinear_quant_forward_supported(17, 256) == 0
     assert lib.bitlinear_quant_forward_supported(0, 256) == 0
-    # supported sizes keep the staged codes (padded rows) inside 64 KiB of LDS
+    # supported sizes are exactly those whose staged codes (padded rows, 16
+    # bytes apart) fit 140 KiB of LDS, beside the 16-wave reduction buffer
     for m in range(1, 17):
-        for k in (1, 255, 256, 4096, 6912, 14336, 28672, 40000):
-            if lib.bitlinear_quant_forward_supported(m, k):
-                assert m * (((k + 255) // 256) * 256 + 16) <= 65536
+        for k in (1, 255, 256, 4096, 6912, 8960, 14336, 28672, 40000, 57344):
+            staged = m * (((k + 255) // 256) * 256 + 16)
+            assert lib.bitlinear_quant_forward_supported(m, k) == (1 if staged <= 140 * 1024 else 0), (m, k)
 
 
 def test_norm_and_f32_quant_validation(blq):
