@@ -376,7 +376,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // up projection (same [n][k] shape, n = features); the workgroup covers
 // BN / 2 features and writes h = silu(y_gate) * y_up to y [m][n] (acc_out, if
 // set, is [m][2n]: gate accumulators, then up accumulators).
-template <int BM, int BN, int WM, int WN, int S, int OCC, bool SWIGLU = false, int WB = 2>
+//
+// SPLIT: the grid holds ceil(kt_count / kt_per) k-slices of every output tile
+// (slice-major); a workgroup walks k-steps [slice * kt_per, ...) and adds its
+// partial sums, exact in int32, to split_acc with atomics (zeroed before,
+// converted by split_finish_kernel after).
+template <int BM, int BN, int WM, int WN, int S, int OCC, bool SWIGLU = false, int WB = 2, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* __restrict__ packed_b,
                                                                const float* __restrict__ gamma_p, Dequant dq, int64_t n,
                                                                int64_t k, int kt_count, const int8_t* __restrict__ xq,
@@ -384,10 +389,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
                                                                int mt_count, int nt_count, float* __restrict__ y,
                                                                int32_t* __restrict__ acc_out,
                                                                const uint8_t* __restrict__ packed_u,
-                                                               const float* __restrict__ gamma_u) {
+                                                               const float* __restrict__ gamma_u, int kt_per = 0,
+                                                               int32_t* __restrict__ split_acc = nullptr) {
   static_assert(WM * WN == kThreads / 64, "4 waves");
   static_assert(S >= 2 && S <= 4, "2..4 stages");
   static_assert(WB == 2 || (S == 2 && !SWIGLU), "binary weights: two stages, plain epilogue");
+  static_assert(!(SPLIT && SWIGLU), "k-slices: plain epilogue only");
   using DS = DmaShape<BM, BN, WB>;
   constexpr int TB = wtile_bytes<WB>();
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -410,6 +417,14 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
 
   const int total = mt_count * nt_count;
   int id = blockIdx.x;
+  int kt_begin = 0, kt_end = kt_count;
+  if (SPLIT) {
+    const int slice = id / total;
+    id -= slice * total;
+    kt_begin = slice * kt_per;
+    kt_end = kt_begin + kt_per < kt_count ? kt_begin + kt_per : kt_count;
+  }
+  // (with SPLIT and total % 8 == 0 the hardware XCD of a workgroup is still id % 8)
   if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
   const int nt = id / mt_count, mt = id - nt * mt_count;
   const int64_t m0 = static_cast<int64_t>(mt) * BM;
@@ -504,25 +519,45 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
       static_cast<int>(rbs_here * kt_count * kTileBytes), kBufferWord3) : b_rsrc;
   const int k32 = static_cast<int>(k);
 
-  // prologue: tiles 0 .. S-2 in flight
-  issue_tile<BM, BN, SWIGLU, WB>(st0, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 0, wave, lane);
-  if (S > 2) issue_tile<BM, BN, SWIGLU, WB>(st1, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 1, wave, lane);
-  if (S > 3) issue_tile<BM, BN, SWIGLU, WB>(st2, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, 2, wave, lane);
+  // prologue: tiles 0 .. S-2 in flight (k-slice: relative to kt_begin; a tile
+  // past the slice re-reads its first tile into a stage nothing reads)
+  auto tile_at = [&](int kt) { return SPLIT ? (kt < kt_end ? kt : kt_begin) : kt; };
+  issue_tile<BM, BN, SWIGLU, WB>(st0, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, tile_at(kt_begin), wave, lane);
+  if (S > 2) issue_tile<BM, BN, SWIGLU, WB>(st1, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, tile_at(kt_begin + 1), wave, lane);
+  if (S > 3) issue_tile<BM, BN, SWIGLU, WB>(st2, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, tile_at(kt_begin + 2), wave, lane);
 
   // one pipeline step: tile kt sits in stage `cur`; tile kt + S - 1 goes to `nxt`
   auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
     wait_vmcnt<(S - 2) * DS::kDma>();
     __builtin_amdgcn_s_barrier();
-    issue_tile<BM, BN, SWIGLU, WB>(nxt, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, kt + S - 1, wave, lane);
+    issue_tile<BM, BN, SWIGLU, WB>(nxt, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, tile_at(kt + S - 1), wave, lane);
     compute(cur);
   };
-  for (int kt = 0; kt < kt_count; kt += S) {
+  for (int kt = kt_begin; kt < kt_end; kt += S) {
     step(kt, st0, S == 2 ? st1 : S == 3 ? st2 : st3);
-    if (kt + 1 < kt_count) step(kt + 1, st1, S == 2 ? st0 : S == 3 ? st0 : st0);
-    if (S > 2 && kt + 2 < kt_count) step(kt + 2, st2, S == 3 ? st1 : st1);
-    if (S > 3 && kt + 3 < kt_count) step(kt + 3, st3, st2);
+    if (kt + 1 < kt_end) step(kt + 1, st1, S == 2 ? st0 : S == 3 ? st0 : st0);
+    if (S > 2 && kt + 2 < kt_end) step(kt + 2, st2, S == 3 ? st1 : st1);
+    if (S > 3 && kt + 3 < kt_end) step(kt + 3, st3, st2);
   }
   wait_vmcnt<0>();
+
+  if (SPLIT) {
+    // partial sums of this k-slice (multiples of 64, shifted exactly)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = m0 + wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (t >= m) continue;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int64_t j = n0 + wn * TN + nb * 32 + l32;
+          if (j < n) atomicAdd(&split_acc[t * n + j], acc[mb][nb][r] >> kWeightShift);
+        }
+      }
+    }
+    return;
+  }
 
   if (SWIGLU) {
     // blocks nb (gate) and nb + 1 (up) hold the same 32 features; the lane's
@@ -617,6 +652,48 @@ Cand choose(int64_t m, int64_t /*n*/) {
 
 // ---- direct-to-LDS pipeline configurations ---------------------------------
 
+// k-slices: zero the int32 target, and afterwards turn the summed
+// accumulators into y with the per-token (and per-row) scale of the one-pass
+// epilogue, the same functions in the same order, so y is bit-identical.
+__global__ void split_zero_kernel(int32_t* __restrict__ p, int64_t count) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) p[i] = 0;
+}
+
+__global__ void split_finish_kernel(const int32_t* acc, float* y, const float* __restrict__ gamma_p, Dequant dq,
+                                    const float* __restrict__ amax, int64_t m, int64_t n) {
+  // acc may alias y (the sums are held in y's own memory): each element is
+  // read and then written by the same thread
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < m * n; i += stride) {
+    const int64_t t = i / n, j = i - t * n;
+    const int v = acc[i];
+    y[i] = static_cast<float>(v) * out_scale(dq, token_scale(gamma_p, dq, amax, t), j);
+  }
+}
+
+// k-steps per slice for a grid of `tiles` output tiles with `occ` resident
+// workgroups per CU (0: no split).  Only a grid that fills at most a quarter
+// of the resident slots is split, into up to 4 slices of at least
+// kMinSliceSteps k-steps.  The sums cost one device-scope atomic per output
+// and slice plus the zeroing and finishing passes (about 2.5 us per million
+// atomics), so filling a half-empty chip does not pay: the 6144-wide QKV
+// matrix at m = 512 (256 tiles in 512 slots) went from 22 to 38 us split in
+// two.  At m = 64, 8192 x 28672 (128 tiles in 768 slots) took 51.2 us
+// unsplit and 38.9 / 37.6 / 33.9 / 37.0 / 38.3 us in 2 / 3 / 4 / 6 / 8
+// slices.
+constexpr int kCus = 256;
+constexpr int kMinSliceSteps = 8;
+constexpr int kMaxSlices = 4;
+int slice_steps(int64_t tiles, int occ, int kt) {
+  const int64_t slots = static_cast<int64_t>(kCus) * occ;
+  if (4 * tiles > slots) return 0;
+  int ks = kMaxSlices;
+  if (ks > kt / kMinSliceSteps) ks = kt / kMinSliceSteps;
+  if (ks < 2) return 0;
+  return (kt + ks - 1) / ks;
+}
+
 template <int BM, int BN, int WM, int WN, int S, int OCC, int WB = 2>
 hipError_t launch_dma(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
                       const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
@@ -628,9 +705,23 @@ hipError_t launch_dma(const void* packed, const float* gamma, Dequant dq, int64_
   const int64_t mt = (m + BM - 1) / BM;
   const int64_t ntl = (n + BN - 1) / BN;
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
-  gemm_dma_kernel<BM, BN, WM, WN, S, OCC, false, WB><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
-      static_cast<const uint8_t*>(packed), gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl),
-      y, acc, nullptr, nullptr);
+  const int kt_per = slice_steps(mt * ntl, OCC, kt);
+  if (kt_per == 0) {
+    gemm_dma_kernel<BM, BN, WM, WN, S, OCC, false, WB><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+        static_cast<const uint8_t*>(packed), gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt),
+        static_cast<int>(ntl), y, acc, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  // the int32 sums go to acc when the caller wants them, else into y's memory
+  int32_t* sums = acc ? acc : reinterpret_cast<int32_t*>(y);
+  const int64_t slices = (kt + kt_per - 1) / kt_per;
+  const int64_t count = m * n;
+  const unsigned fill_grid = static_cast<unsigned>(count / 256 + 1 < 2048 ? count / 256 + 1 : 2048);
+  split_zero_kernel<<<fill_grid, 256, 0, s>>>(sums, count);
+  gemm_dma_kernel<BM, BN, WM, WN, S, OCC, false, WB, true><<<dim3(static_cast<unsigned>(mt * ntl * slices)), kThreads, 0, s>>>(
+      static_cast<const uint8_t*>(packed), gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt),
+      static_cast<int>(ntl), y, acc, nullptr, nullptr, kt_per, sums);
+  split_finish_kernel<<<fill_grid, 256, 0, s>>>(sums, y, gamma, dq, amax, m, n);
   return hipGetLastError();
 }
 

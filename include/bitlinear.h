@@ -167,6 +167,12 @@ int bitlinear_quant_forward_supported(int64_t m, int64_t k);
  * bitlinear_forward, computed as a tiled int8 matrix-core contraction with
  * the ternary tiles expanded on chip.  Larger m returns
  * BITLINEAR_E_UNSUPPORTED (split the tokens into several calls).
+ * When the output tiles are too few to fill the device, the k extent is
+ * split across workgroups: the exact int32 partial sums are added with
+ * atomics in acc_or_null, or else in y's own memory (y is scratch until the
+ * call's last kernel writes it), and a last pass scales them into y.  The
+ * results are bit-identical either way; the call then enqueues three
+ * kernels on the stream instead of one.
  */
 int bitlinear_forward_batched(const void *packed, const float *gamma, int64_t n, int64_t k,
                               const int8_t *xq, const float *x_absmax, int64_t m,

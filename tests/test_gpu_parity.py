@@ -208,6 +208,36 @@ def test_forward_degenerate(blq):
     assert acc[0, 0] == 127 * k
 
 
+def test_batched_k_slices_stay_in_bounds(blq):
+    """Sizes the matrix-core path splits over k (zeroed int32 sums in y's or
+    acc's memory, atomics, an in-place finish): bitwise equal with and
+    without acc, deterministic, and guard bands around y and acc intact."""
+    torch = torch_mod()
+    for n, k, m in ((100, 5000, 70), (33, 28672, 20)):
+        w = synth.latent_weights(n + k, n, k)
+        packed, gamma = gpu_pack(blq, w)
+        x = synth.activations_bf16(m + k, m, k, 0.01)
+        xq, amax = blq.bitlinear_quant_act(to_dev_bits(x))
+        guard = 64
+        yb = torch.full((m * n + 2 * guard,), float("nan"), device="cuda")
+        ab = torch.full((m * n + 2 * guard,), -7, dtype=torch.int32, device="cuda")
+        y1 = yb[guard:guard + m * n].view(m, n)
+        a1 = ab[guard:guard + m * n].view(m, n)
+        blq.bitlinear_forward_batched(packed, gamma, n, k, xq, amax, y=y1, acc=a1)
+        y2 = blq.bitlinear_forward_batched(packed, gamma, n, k, xq, amax)
+        y3 = blq.bitlinear_forward_batched(packed, gamma, n, k, xq, amax)
+        assert torch.equal(y1, y2) and torch.equal(y2, y3), (n, k, m)
+        assert torch.isnan(yb[:guard]).all() and torch.isnan(yb[-guard:]).all()
+        assert (ab[:guard] == -7).all() and (ab[-guard:] == -7).all()
+        ref = oracle.forward(x, w)
+        g_same = check_gamma(host(gamma)[0], ref["gamma"], "k-slices")
+        bad = compare_codes(host(blq.bitlinear_unpack_weights(packed, n, k)), ref["q"], w, ref["gamma"], g_same,
+                            "k-slices")
+        keep = np.setdiff1d(np.arange(n), bad)
+        assert np.array_equal(host(a1)[:, keep], ref["acc"][:, keep])
+        compare_y(host(y1)[:, keep], ref["y"][:, keep], "k-slices")
+
+
 def test_decode_and_batched_agree_bitwise(blq):
     torch = torch_mod()
     n, k = 300, 4096
