@@ -90,3 +90,15 @@ def test_counter_scaling(tmp_path):
     kw, nw = bench._counter_avg_kib(str(pw), "gemv_lds_kernel")
     assert (kf, nf, kw, nw) == (300.0, 2, 10.0, 2)
     assert (kf * f_fetch + kw * f_write) * 1024 == 610 * 1024
+
+
+def test_fused_default_follows_the_measured_limits():
+    # the fused quant + forward entry is the step's default only where it was
+    # measured faster than quant + forward
+    assert [bench.fused_default("plain", m) for m in (1, 2, 4, 5, 8)] == [True, True, True, False, False]
+    assert [bench.fused_default("rmsnorm", m) for m in (1, 2, 3)] == [True, True, False]
+    for variant in ("swiglu", "lut", "binary", "tensor128", "rowscale"):
+        assert bench.fused_default(variant, 1) and not bench.fused_default(variant, 2)
+    # the fused call's algorithmic bytes: bf16 activations instead of codes and a'
+    n, k, m = 4096, 14336, 4
+    assert bench.fused_bytes(m, n, k) - bench.forward_bytes(m, n, k) == 2 * m * k - (m * k + 4 * m)
