@@ -238,6 +238,36 @@ def test_batched_k_slices_stay_in_bounds(blq):
         compare_y(host(y1)[:, keep], ref["y"][:, keep], "k-slices")
 
 
+def test_batched_k_slices_in_a_graph(blq):
+    """The split path's three launches (zero fill, k-slices, finish) captured
+    in a HIP graph: every replay, with eager work between replays, matches
+    the eager result bit for bit."""
+    torch = torch_mod()
+    n, k, m = 96, 8192, 40
+    w = synth.latent_weights(77, n, k)
+    packed, gamma = gpu_pack(blq, w)
+    xq, amax = blq.bitlinear_quant_act(to_dev_bits(synth.activations_bf16(78, m, k, 0.01)))
+    y_ref = blq.bitlinear_forward_batched(packed, gamma, n, k, xq, amax)
+    a_ref = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    blq.bitlinear_forward_batched(packed, gamma, n, k, xq, amax, acc=a_ref)
+    y = torch.empty((m, n), device="cuda")
+    a = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        blq.bitlinear_forward_batched(packed, gamma, n, k, xq, amax, y=y, acc=a)
+    for _ in range(3):
+        y.fill_(float("nan"))
+        a.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(a, a_ref)
+        blq.bitlinear_forward_batched(packed, gamma, n, k, xq, amax)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_decode_and_batched_agree_bitwise(blq):
     torch = torch_mod()
     n, k = 300, 4096
