@@ -333,6 +333,20 @@ def fused_bytes(m: int, n: int, k: int) -> int:
     return (n * k + 3) // 4 + 2 * m * k + 4 + 4 * m * n
 
 
+def nonzero_fraction(blq, torch, mats, mode):
+    """Fraction of non-zero ternary codes over the given matrices, weighted by
+    their sizes, decoded from the packed weights on the device."""
+    if mode == "binary":
+        return 1.0
+    nz = total = 0
+    for mt in mats:
+        codes = blq.bitlinear_unpack_weights(mt.packed, mt.n, mt.k)
+        nz += int(torch.count_nonzero(codes))
+        total += mt.n * mt.k
+        del codes
+    return nz / total
+
+
 def time_graph(torch, stream, fn, replays):
     """Capture fn(stream) once, replay it `replays` times between two HIP
     events on that stream; returns ms per replay."""
@@ -718,6 +732,17 @@ def main():
         "pack": {"seconds": round(pack["seconds"], 4),
                  "gbs": round(pack["bytes"] / pack["seconds"] / 1e9, 1) if pack["seconds"] > 0 else None},
     }
+
+    if batched:
+        # Beside the dense 2*M*N*K: the method's own work is one add or
+        # subtract per non-zero weight and token.  The non-zero fraction is
+        # read from the packed codes of the first layer's matrices (binary
+        # weights have none that are zero).
+        nz = nonzero_fraction(blq, torch, mats0[:len(wl.matrices)], mode)
+        out["nonzero_weight_adds"] = {"fraction_nonzero": round(nz, 4), "tops": round(value * nz / 2, 2),
+                                      "definition": "nonzero(q) * M * N * K adds per step / time"}
+        # the other roof: algorithmic bytes of the step against the HBM peak
+        out["hbm_frac_of_step"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
 
     if want_cpu:
         log("cpu baseline (oracle) ...")
