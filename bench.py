@@ -111,6 +111,7 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
     batch = 8
     t_pack = 0.0
     pack_bytes = 0
+    oracle_pack = {"seconds": 0.0, "bytes": 0, "matrices": 0}  # the oracle's weight preparation
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for b0 in range(0, len(jobs), batch):
         chunk = jobs[b0:b0 + batch]
@@ -160,6 +161,7 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             # SwiGLU variant: the gate+up BitLinear writes h [m][n/2] instead of y
             mat.h = (torch.empty((m, mt.n // 2), dtype=torch.float32, device=dev)
                      if variant == "swiglu" and mt.name == "gate_up" else None)
+            t_or = time.perf_counter()
             if keep_oracle_codes and variant == "binary":
                 mat.g_or = s_bin
                 mat.q_or = oracle_mod.binarize(w)
@@ -170,8 +172,13 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             elif keep_oracle_codes:
                 mat.g_or = oracle_mod.gamma(w)
                 mat.q_or = oracle_mod.ternarize(w, mat.g_or)
+                oracle_mod.pack_canonical(mat.q_or)  # the oracle's own 2-bit layout, timed with the rest
             else:
                 mat.g_or = mat.q_or = None
+            if keep_oracle_codes:
+                oracle_pack["seconds"] += time.perf_counter() - t_or
+                oracle_pack["bytes"] += 4 * mt.n * mt.k
+                oracle_pack["matrices"] += 1
             mats.append(mat)
             del wd
         del ws
@@ -190,7 +197,7 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             c.q_or = None
             cp.append(c)
         reps.append(cp)
-    return reps, {"seconds": t_pack, "bytes": pack_bytes}
+    return reps, {"seconds": t_pack, "bytes": pack_bytes, "oracle": oracle_pack}
 
 
 def _quant(blq, mat, stream):
@@ -381,6 +388,7 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
     nmat = 0
     h_prev = None
     rows_used = m
+    phase = {"quant": 0.0, "contract": 0.0, "dequant": 0.0}
     for mat in mats:
         t0 = time.perf_counter()
         rows = m if m * mat.n * mat.k <= 2e10 else max(1, int(2e10 // (mat.n * mat.k)))
@@ -396,8 +404,10 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
             xq = xq[:rows]
         else:
             xq, amax = oracle_mod.quant_act(mat.x_np[:rows])
+        t1 = time.perf_counter()
         acc = (oracle_mod.contract_q128(xq, mat.q_or) if variant == "tensor128"
                else oracle_mod.contract(xq, mat.q_or))
+        t2 = time.perf_counter()
         if variant == "tensor128":
             y = oracle_mod.dequant_tensor(acc, mat.g_or, gx)
         elif variant == "rowscale":
@@ -409,7 +419,11 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
             h_prev = y
         else:
             y = oracle_mod.dequant(acc, mat.g_or, amax)
-        t_total += time.perf_counter() - t0
+        t3 = time.perf_counter()
+        phase["quant"] += t1 - t0
+        phase["contract"] += t2 - t1
+        phase["dequant"] += t3 - t2
+        t_total += t3 - t0
         rows_used = rows
         done_bytes += (swiglu_bytes(rows, mat.n // 2, mat.k) if variant == "swiglu" and mat.name == "gate_up"
                        else mode_forward_bytes(variant, rows, mat.n, mat.k) if variant in MODES
@@ -436,7 +450,7 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
         if t_total > budget_s and not (variant == "swiglu" and mat.name == "gate_up"):
             break
     return {"seconds": t_total, "bytes": done_bytes, "ops": done_ops, "matrices": nmat, "rows": rows_used,
-            "max_rel_err": worst, "chain_ok": chain_ok}
+            "max_rel_err": worst, "chain_ok": chain_ok, "phases": phase}
 
 
 def main():
@@ -599,6 +613,17 @@ def main():
     steps_timed = runs_t * per_run
     ms_per_step = ev0.elapsed_time(ev1) / steps_timed
     log("timed %d steps: %.4f ms/step" % (steps_timed, ms_per_step))
+    # the same K steps timed four more times, reported beside `value`
+    # (which is the first timing): the spread between repeats
+    repeat_ms = [ms_per_step]
+    for _ in range(4):
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(runs_t):
+            run()
+        ev1.record()
+        torch.cuda.synchronize()
+        repeat_ms.append(ev0.elapsed_time(ev1) / steps_timed)
 
     # Dominant kernel (the forward, or the fused quant + forward): HIP events
     # on its stream around graph replays that hold only that kernel's
@@ -726,6 +751,9 @@ def main():
             "step_ops": step_ops,
         },
         "pct_of_peak": round(100 * value / (MFMA_I8_PEAK_TOPS if batched else HBM_PEAK_GBS), 2),
+        "repeats": {"count": len(repeat_ms), "ms_per_step_min": round(min(repeat_ms), 4),
+                    "ms_per_step_median": round(float(np.median(repeat_ms)), 4),
+                    "ms_per_step_max": round(max(repeat_ms), 4)},
         "roofline": roof,
         "quant_kernel": {"avg_launch_us": round(q_avg_us, 3),
                          "gbs": round(step_quant_bytes / (q_ms * 1e-3) / 1e9, 1)},
@@ -759,6 +787,13 @@ def main():
             "sample": "%d of %d matrices in layer order, %d token(s) each: quant + contraction + dequant "
                       "(%.2f s)" % (cb["matrices"], len(mats0), cb["rows"], cb["seconds"]),
             "cpu": _cpu_model(),
+            # the sample's time by oracle step, and the oracle's weight
+            # preparation (gamma, ternarisation, canonical 2-bit pack) over the
+            # matrices it kept codes for
+            "phases_seconds": {kk: round(vv, 4) for kk, vv in cb["phases"].items()},
+            "pack": {"seconds": round(pack["oracle"]["seconds"], 4), "matrices": pack["oracle"]["matrices"],
+                     "gbs_fp32_read": (round(pack["oracle"]["bytes"] / pack["oracle"]["seconds"] / 1e9, 3)
+                                       if pack["oracle"]["seconds"] > 0 else None)},
         }
         out["parity_vs_oracle"] = {"matrices": cb["matrices"], "max_rel_err_y": cb["max_rel_err"],
                                    "ok": bool(cb["max_rel_err"] <= 1e-5 and cb["chain_ok"])}
