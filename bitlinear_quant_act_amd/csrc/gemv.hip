@@ -1163,14 +1163,12 @@ int items_per_wave(int64_t items, int64_t row_blocks_per_group, int waves) {
 }
 
 // SWIGLU items hold 2 * kt tiles (gate then up) and binary items two tiles.
-template <int SRC, bool SWIGLU = false, int WB = 2>
-hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const void* xsrc,
-                        const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
-                        const float* gain, float eps, hipStream_t s, bool vec, const void* packed_u = nullptr,
-                        const float* gamma_u = nullptr) {
+template <int SRC, int W, bool SWIGLU, int WB>
+hipError_t dispatch_lds_waves(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k,
+                              const void* xsrc, const float* amax_in, int64_t m, float* y, int32_t* acc,
+                              int8_t* xq_out, float* amax_out, const float* gain, float eps, hipStream_t s, bool vec,
+                              const void* packed_u, const float* gamma_u) {
   const int64_t items = WB == 1 ? staged_tiles(k, 1) / 2 : (SWIGLU ? 2 : 1) * k_tiles(k);
-  // the RMSNorm prologue alone measured faster with two 8-wave workgroups per CU
-  constexpr int W = (SRC == kFromBf16Norm && !SWIGLU) ? 8 : kWaves;
   const int64_t cap = kMaxResidentGroups * kWaves / W;  // the grid cap of launch_lds
   const int64_t per = (row_blocks(n) + cap - 1) / cap;
   const int u = items_per_wave(items, per, W);
@@ -1185,6 +1183,26 @@ hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int6
                                                   gain, eps, s, vec, packed_u, gamma_u);
   return launch_lds<SRC, W, 8, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out, amax_out,
                                                 gain, eps, s, vec, packed_u, gamma_u);
+}
+
+// Workgroup size.  16 waves (one workgroup per CU) everywhere except the
+// RMSNorm prologue on rows of at most 8192 values, which measured faster as
+// two 8-wave workgroups per CU (3840 x 2560: 4.39 against 4.70 us per
+// launch).  On longer rows every workgroup's fp64 RMSNorm pass over the row
+// dominates, and two workgroups per CU do it twice: 4096 x 14336 took 9.55 us
+// with 8 waves and 8.40 with 16, 8192 x 28672 24.5 and 16.8.
+template <int SRC, bool SWIGLU = false, int WB = 2>
+hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const void* xsrc,
+                        const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
+                        const float* gain, float eps, hipStream_t s, bool vec, const void* packed_u = nullptr,
+                        const float* gamma_u = nullptr) {
+  if constexpr (SRC == kFromBf16Norm && !SWIGLU) {
+    if (k <= 8192)
+      return dispatch_lds_waves<SRC, 8, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out,
+                                                    amax_out, gain, eps, s, vec, packed_u, gamma_u);
+  }
+  return dispatch_lds_waves<SRC, kWaves, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out,
+                                                     amax_out, gain, eps, s, vec, packed_u, gamma_u);
 }
 
 template <int WB>
