@@ -78,10 +78,12 @@ MODES = ("tensor128", "rowscale", "binary")
 # Decode token counts up to which the fused entry point (the quantisation, or
 # RMSNorm + quantisation, in the GEMV prologue) is the default.  Every
 # workgroup re-quantises all m tokens, so the fusion saves a launch but adds
-# m * k of redundant prologue work; measured on the 2B and 8B stacks it wins
-# up to m = 4 (plain) and m = 2 (RMSNorm), and only at m = 1 for the SwiGLU
-# block and the variant modes.
-FUSED_MAX_M = {"plain": 4, "rmsnorm": 2}
+# m * k of redundant prologue work.  Measured on the 2B and 8B stacks against
+# quant + forward: plain, fused wins at m = 2 (+9% / +14%); at m = 4 it wins
+# on the 2B stack (+4%) and loses on the 8B stack (-2%).  RMSNorm at m = 2:
+# +7% on the 2B stack, -4% on the 8B stack.  The SwiGLU block and the variant
+# modes: only m = 1.
+FUSED_MAX_M = {"plain": 2, "rmsnorm": 2}
 
 
 def fused_default(variant: str, m: int) -> bool:

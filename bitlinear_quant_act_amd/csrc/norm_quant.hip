@@ -18,7 +18,7 @@
 // One workgroup per token; rows are read with 16-byte loads, the max is
 // reduced as fp32 bit patterns (non-negative floats order like their bits)
 // and the mean square as fp64, across the wave with shuffles and across the
-// four waves in LDS (the in-wave steps on DPP row operations).
+// workgroup's waves in LDS (the in-wave steps on DPP row operations).
 #include "bitlinear_internal.hpp"
 
 namespace bitlinear {
@@ -65,31 +65,35 @@ __device__ __forceinline__ void chunk_values(const uint4& xc, const float* __res
   }
 }
 
-// Vector path: k % 8 == 0, x and gain 16-byte aligned, xq 8-byte aligned;
-// the row fits in CPT chunks per thread (kept in registers between passes).
+// Vector path: k % 8 == 0, x and gain 16-byte aligned, xq 8-byte aligned.
+// 1024 threads per token; the row fits in CPT chunks per thread, and the
+// products v = x * gain stay in registers between the two passes, so x and
+// the gains are read once.
+constexpr int kNormThreads = 1024;
+constexpr int kNormWaves = kNormThreads / 64;
+
 template <int CPT>
-__global__ __launch_bounds__(kThreads) void rmsnorm_quant_vec(const uint16_t* __restrict__ x,
-                                                              const float* __restrict__ gain, float eps, int k,
-                                                              int8_t* __restrict__ xq, float* __restrict__ amax) {
-  __shared__ uint32_t red_max[kWaves];
-  __shared__ double red_ss[kWaves];
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_vec(const uint16_t* __restrict__ x,
+                                                                  const float* __restrict__ gain, float eps, int k,
+                                                                  int8_t* __restrict__ xq, float* __restrict__ amax) {
+  __shared__ uint32_t red_max[kNormWaves];
+  __shared__ double red_ss[kNormWaves];
   const int64_t row = blockIdx.x;
   const uint4* xr = reinterpret_cast<const uint4*>(x + row * k);
   const int chunks = k >> 3;
-  uint4 c[CPT];
+  float vk[CPT][8];
   uint32_t mx = 0;
   double ss = 0.0;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
+    const int idx = threadIdx.x + i * kNormThreads;
     if (idx < chunks) {
-      c[i] = xr[idx];
-      float v[8], xv[8];
-      chunk_values(c[i], gain ? gain + idx * 8 : nullptr, v, xv);
+      float xv[8];
+      chunk_values(xr[idx], gain ? gain + idx * 8 : nullptr, vk[i], xv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         ss += static_cast<double>(xv[j]) * static_cast<double>(xv[j]);
-        mx = max(mx, __float_as_uint(fabsf(v[j])));
+        mx = max(mx, __float_as_uint(fabsf(vk[i][j])));
       }
     }
   }
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_vec(const uint16_t* __
   uint32_t mall = red_max[0];
   double sall = red_ss[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
+  for (int w = 1; w < kNormWaves; ++w) {
     mall = max(mall, red_max[w]);
     sall += red_ss[w];
   }
@@ -113,15 +117,13 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_vec(const uint16_t* __
   uint2* out = reinterpret_cast<uint2*>(xq + row * k);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
+    const int idx = threadIdx.x + i * kNormThreads;
     if (idx < chunks) {
-      float v[8], xv[8];
-      chunk_values(c[i], gain ? gain + idx * 8 : nullptr, v, xv);
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        lo |= code_of(v[j], s) << (8 * j);
-        hi |= code_of(v[4 + j], s) << (8 * j);
+        lo |= code_of(vk[i][j], s) << (8 * j);
+        hi |= code_of(vk[i][4 + j], s) << (8 * j);
       }
       out[idx] = make_uint2(lo, hi);
     }
@@ -249,19 +251,17 @@ hipError_t launch_rmsnorm_quant_act(const uint16_t* x, const float* gain, float 
   const bool vec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (gain == nullptr || reinterpret_cast<uintptr_t>(gain) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(xq) % 8 == 0);
-  const int64_t per_thread = (k / 8 + kThreads - 1) / kThreads;
+  const int64_t per_thread = (k / 8 + kNormThreads - 1) / kNormThreads;
   const dim3 grid(static_cast<unsigned>(m));
   const int ki = static_cast<int>(k);
   if (vec && per_thread <= 1)
-    rmsnorm_quant_vec<1><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+    rmsnorm_quant_vec<1><<<grid, kNormThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
   else if (vec && per_thread <= 2)
-    rmsnorm_quant_vec<2><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+    rmsnorm_quant_vec<2><<<grid, kNormThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
   else if (vec && per_thread <= 4)
-    rmsnorm_quant_vec<4><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+    rmsnorm_quant_vec<4><<<grid, kNormThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
   else if (vec && per_thread <= 8)
-    rmsnorm_quant_vec<8><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
-  else if (vec && per_thread <= 16)
-    rmsnorm_quant_vec<16><<<grid, kThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
+    rmsnorm_quant_vec<8><<<grid, kNormThreads, 0, s>>>(x, gain, eps, ki, xq, amax);
   else
     rmsnorm_quant_any<<<grid, kThreads, 0, s>>>(x, gain, eps, k, xq, amax);
   return hipGetLastError();

@@ -34,7 +34,8 @@ __device__ __forceinline__ uint32_t abs_max2(uint32_t word) {
   return max(word & 0x7fffu, (word >> 16) & 0x7fffu);
 }
 
-// max over the workgroup; every thread receives the result
+// max over a workgroup of T threads; every thread receives the result
+template <int T = kThreads>
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   v = wave_max_u32(v);
   const int wave = threadIdx.x >> 6;
@@ -42,17 +43,21 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   __syncthreads();
   uint32_t r = red[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = max(r, red[i]);
+  for (int i = 1; i < T / 64; ++i) r = max(r, red[i]);
   return r;
 }
 
+// rows longer than kThreads chunks: a workgroup of kLongThreads per token,
+// so each thread converts at most a few chunks
+constexpr int kLongThreads = 1024;
+
 // Vector path: k % 8 == 0, x 16-byte aligned, xq 8-byte aligned; the row
-// (k / 8 chunks of 8 values) fits in CPT chunks per thread.
-template <int CPT>
-__global__ __launch_bounds__(kThreads) void quant_act_vec(const uint16_t* __restrict__ x, int k,
-                                                          int8_t* __restrict__ xq,
-                                                          float* __restrict__ amax) {
-  __shared__ uint32_t red[kWaves];
+// (k / 8 chunks of 8 values) fits in CPT chunks per thread of T.
+template <int CPT, int T = kThreads>
+__global__ __launch_bounds__(T) void quant_act_vec(const uint16_t* __restrict__ x, int k,
+                                                   int8_t* __restrict__ xq,
+                                                   float* __restrict__ amax) {
+  __shared__ uint32_t red[T / 64];
   const int64_t row = blockIdx.x;
   const uint4* xr = reinterpret_cast<const uint4*>(x + row * k);
   const int chunks = k >> 3;
@@ -60,19 +65,19 @@ __global__ __launch_bounds__(kThreads) void quant_act_vec(const uint16_t* __rest
   uint32_t mx = 0;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
+    const int idx = threadIdx.x + i * T;
     if (idx < chunks) {
       c[i] = xr[idx];
       mx = max(mx, max(max(abs_max2(c[i].x), abs_max2(c[i].y)), max(abs_max2(c[i].z), abs_max2(c[i].w))));
     }
   }
-  mx = block_max(mx, red);
+  mx = block_max<T>(mx, red);
   const float a = fmaxf(bf16_to_f32(mx), 1e-8f);
   const float s = 127.0f / a;
   uint2* out = reinterpret_cast<uint2*>(xq + row * k);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
+    const int idx = threadIdx.x + i * T;
     if (idx < chunks) {
       const uint32_t w[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
       uint32_t lo = 0, hi = 0;
@@ -238,7 +243,17 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq,
   const int64_t per_thread = (chunks + kThreads - 1) / kThreads;
   const dim3 grid(static_cast<unsigned>(m));
   const int ki = static_cast<int>(k);
-  if (vec && per_thread <= 1)
+  const int64_t per_long = (chunks + kLongThreads - 1) / kLongThreads;
+  if (vec && per_thread > 1 && per_long <= 8) {  // long rows: 1024 threads per token
+    if (per_long <= 1)
+      quant_act_vec<1, kLongThreads><<<grid, kLongThreads, 0, s>>>(x, ki, xq, amax);
+    else if (per_long <= 2)
+      quant_act_vec<2, kLongThreads><<<grid, kLongThreads, 0, s>>>(x, ki, xq, amax);
+    else if (per_long <= 4)
+      quant_act_vec<4, kLongThreads><<<grid, kLongThreads, 0, s>>>(x, ki, xq, amax);
+    else
+      quant_act_vec<8, kLongThreads><<<grid, kLongThreads, 0, s>>>(x, ki, xq, amax);
+  } else if (vec && per_thread <= 1)
     quant_act_vec<1><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
   else if (vec && per_thread <= 2)
     quant_act_vec<2><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
