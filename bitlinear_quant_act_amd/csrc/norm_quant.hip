@@ -186,10 +186,10 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_any(const uint16_t* __
 // ---------------------------------------------------------------------------
 
 // Vector path: k % 4 == 0, x 16-byte aligned, xq 4-byte aligned.
-template <int CPT>
-__global__ __launch_bounds__(kThreads) void quant_f32_vec(const float* __restrict__ x, int k, int8_t* __restrict__ xq,
-                                                          float* __restrict__ amax) {
-  __shared__ uint32_t red_max[kWaves];
+template <int CPT, int T = kThreads>
+__global__ __launch_bounds__(T) void quant_f32_vec(const float* __restrict__ x, int k, int8_t* __restrict__ xq,
+                                                   float* __restrict__ amax) {
+  __shared__ uint32_t red_max[T / 64];
   const int64_t row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + row * k);
   const int chunks = k >> 2;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void quant_f32_vec(const float* __restric
   uint32_t mx = 0;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
+    const int idx = threadIdx.x + i * T;
     if (idx < chunks) {
       c[i] = xr[idx];
       mx = max(max(mx, max(__float_as_uint(fabsf(c[i].x)), __float_as_uint(fabsf(c[i].y)))),
@@ -210,13 +210,13 @@ __global__ __launch_bounds__(kThreads) void quant_f32_vec(const float* __restric
   __syncthreads();
   uint32_t mall = red_max[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) mall = max(mall, red_max[w]);
+  for (int w = 1; w < T / 64; ++w) mall = max(mall, red_max[w]);
   const float a = fmaxf(__uint_as_float(mall), 1e-8f);
   const float s = 127.0f / a;
   uint32_t* out = reinterpret_cast<uint32_t*>(xq + row * k);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
+    const int idx = threadIdx.x + i * T;
     if (idx < chunks)
       out[idx] = code_of(c[i].x, s) | (code_of(c[i].y, s) << 8) | (code_of(c[i].z, s) << 16) | (code_of(c[i].w, s) << 24);
   }
@@ -271,9 +271,19 @@ hipError_t launch_quant_act_f32(const float* x, int64_t m, int64_t k, int8_t* xq
   const bool vec = (k % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(xq) % 4 == 0);
   const int64_t per_thread = (k / 4 + kThreads - 1) / kThreads;
+  const int64_t per_long = (k / 4 + kNormThreads - 1) / kNormThreads;
   const dim3 grid(static_cast<unsigned>(m));
   const int ki = static_cast<int>(k);
-  if (vec && per_thread <= 1)
+  if (vec && per_thread > 1 && per_long <= 8) {  // rows of more than 1024 values: 1024 threads per token
+    if (per_long <= 1)
+      quant_f32_vec<1, kNormThreads><<<grid, kNormThreads, 0, s>>>(x, ki, xq, amax);
+    else if (per_long <= 2)
+      quant_f32_vec<2, kNormThreads><<<grid, kNormThreads, 0, s>>>(x, ki, xq, amax);
+    else if (per_long <= 4)
+      quant_f32_vec<4, kNormThreads><<<grid, kNormThreads, 0, s>>>(x, ki, xq, amax);
+    else
+      quant_f32_vec<8, kNormThreads><<<grid, kNormThreads, 0, s>>>(x, ki, xq, amax);
+  } else if (vec && per_thread <= 1)
     quant_f32_vec<1><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
   else if (vec && per_thread <= 2)
     quant_f32_vec<2><<<grid, kThreads, 0, s>>>(x, ki, xq, amax);
