@@ -81,6 +81,22 @@ constexpr int kWaves = BITLINEAR_GEMV_WAVES;                        // waves per
 constexpr int kMaxLdsBytes = 140 * 1024;
 constexpr int kCachedChunks = 4;  // activation chunks per thread held in registers by the prologue
 
+// Weight tiles are read as a raw buffer: a buffer resource names a base
+// address and a byte extent, and a load past the extent returns zero without
+// touching memory.  Every lane issues every tile load, with no branch around
+// it, so on every path the loads complete in issue order and the prologue's
+// waits for the activations (requested first) leave the weight tiles
+// requested after them in flight.
+constexpr int kRawBuffer = 0x00020000;  // descriptor word 3: untyped, 32-bit data format
+constexpr int kLoadNonTemporal = 2;     // cache policy: read once
+
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_tile_nt(__amdgpu_buffer_rsrc_t r, int offset) {
+  const v4u_t t = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kLoadNonTemporal);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 enum Source { kFromCodes = 0, kFromBf16 = 1, kFromBf16Norm = 2, kFromF32 = 3 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -787,19 +803,20 @@ template <int WAVES, int U, bool SWIGLU, int WB = 2>
 __device__ __forceinline__ void load_item(uint4 (&w)[U], const uint4* __restrict__ packed,
                                           const uint4* __restrict__ packed_u, int64_t rb, int c, int kt_count,
                                           int kt_real, int wave, int lane, bool valid) {
-  const int kt_items = WB == 1 ? kt_count / 2 : SWIGLU ? 2 * kt_count : kt_count;
+  // this row block's tiles as a buffer (empty past the last row block); an
+  // item past the row block reads as zero and is never contracted
+  const int row_tiles = WB == 1 ? kt_real : kt_count;
+  const int64_t row_bytes = valid ? static_cast<int64_t>(row_tiles) * kTileBytes : 0;
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(packed + rb * row_tiles * 64), 0, static_cast<int>(row_bytes), kRawBuffer);
+  const __amdgpu_buffer_rsrc_t ru = SWIGLU ? __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(packed_u + rb * row_tiles * 64), 0, static_cast<int>(row_bytes), kRawBuffer) : rg;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // uniform: the resource choice stays scalar
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int kv = c * U * WAVES + wave + u * WAVES;
-    if (WB == 1) {
-      w[u] = (valid && kv < kt_items) ? load_weights_nt(packed + (rb * kt_real + kv) * 64 + lane)
-                                      : make_uint4(0, 0, 0, 0);
-      continue;
-    }
+    const int kv = c * U * WAVES + wv + u * WAVES;
     const bool up = SWIGLU && kv >= kt_count;
-    const int kt = up ? kv - kt_count : kv;
-    w[u] = (valid && kv < kt_items) ? load_weights_nt((up ? packed_u : packed) + (rb * kt_count + kt) * 64 + lane)
-                                    : make_uint4(kZeroWord, kZeroWord, kZeroWord, kZeroWord);
+    w[u] = load_tile_nt(up ? ru : rg, ((up ? kv - kt_count : kv) * 64 + lane) * 16);
   }
 }
 
