@@ -110,7 +110,8 @@ def test_rmsnorm_quant_rejects_bad_eps(blq):
 # fused RMSNorm + quantisation + decode forward
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n,k", [(2560, 2560), (700, 1000), (3840, 2560), (2560, 6912), (64, 14336), (33, 1003)])
+@pytest.mark.parametrize("n,k", [(2560, 2560), (700, 1000), (3840, 2560), (2560, 6912), (64, 14336), (33, 1003),
+                                 (601 * 16 - 7, 300)])  # last: 601 row blocks, several per workgroup
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("gain_kind", ["none", "synthetic"])
 def test_rmsnorm_quant_forward_parity(blq, n, k, m, gain_kind):

@@ -174,9 +174,13 @@ def test_pack_is_deterministic(blq):
 # ---------------------------------------------------------------------------
 
 SHAPES = [(16, 256), (17, 257), (48, 1000), (200, 2048), (257, 4112), (64, 6912), (5, 1), (40, 16)]
+# 601 row blocks (the last one ragged) on the decode kernels' persistent grid:
+# three row blocks per workgroup for all but the last, which takes two; two
+# tiles per row block, so most waves of a workgroup have none
+MANY_ROW_BLOCKS = (601 * 16 - 7, 300)
 
 
-@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("n,k", SHAPES + [MANY_ROW_BLOCKS])
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 9, 16])
 def test_forward_decode_parity(blq, n, k, m):
     run_case(blq, n, k, m, seed=n + 7 * k + m, batched=False)
@@ -324,7 +328,7 @@ def test_forward_on_a_side_stream(blq):
 # fused activation quantisation + decode forward
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n,k", SHAPES + [(2560, 6912), (64, 14336)])
+@pytest.mark.parametrize("n,k", SHAPES + [(2560, 6912), (64, 14336), MANY_ROW_BLOCKS])
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 16])
 def test_quant_forward_parity(blq, n, k, m):
     if not blq.bitlinear_quant_forward_supported(m, k):

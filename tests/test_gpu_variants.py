@@ -237,7 +237,7 @@ def test_binary_forward_parity(blq, n, k, m):
     binary_case(blq, n, k, m, seed=7 * n + k + m)
 
 
-@pytest.mark.parametrize("n,k", SHAPES + [(2560, 6912)])
+@pytest.mark.parametrize("n,k", SHAPES + [(2560, 6912), (601 * 16 - 7, 300)])  # last: 601 row blocks
 @pytest.mark.parametrize("m", [1, 3, 16])
 def test_binary_fused_forward_parity(blq, n, k, m):
     binary_case(blq, n, k, m, seed=11 * n + k + m, fused=True)
