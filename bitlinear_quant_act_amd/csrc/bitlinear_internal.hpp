@@ -121,6 +121,30 @@ __device__ __forceinline__ expand_v4i expand_binary(uint32_t word, int o) {
                     static_cast<int>(((word << (i0 + 3)) & 0x80808080u) | 0x40404040u)};
 }
 
+// Scales of one token for RMSNorm folded into the absmax quantisation.
+// RMSNorm scales the token by r = 1 / sqrt(mean x^2 + eps) and channel c by
+// the gain w_c; the absmax rule is then applied to the normalised token,
+// whose maximum is about av * r with av = max_c |x_c * w_c|.  Absmax
+// quantisation is invariant under the positive factor r, so the codes are
+// taken from v = x * w directly:
+//   - max|x_norm| = fl32(av * r) at or above the 1e-8 floor: scale 127 / av
+//     on v, and a' = fl32(av * r) for the de-quantisation;
+//   - below the floor (a tiny token or gain): the floor is the token's
+//     scale, so v is scaled by r * 127 / 1e-8 (binary64, rounded once, kept
+//     finite) and a' = 1e-8.  An all-zero v gets codes 0.
+// The codes equal those of the normalised token except where the value lies
+// within a few roundings of a tie.
+__device__ __forceinline__ void rmsnorm_scales(float av, double r, float* amax_dst, float* quant_dst) {
+  const float ap = static_cast<float>(static_cast<double>(av) * r);
+  if (ap >= 1e-8f) {  // false for NaN (av = 0 with r = inf)
+    *amax_dst = ap;
+    *quant_dst = 127.0f / av;
+  } else {
+    *amax_dst = 1e-8f;
+    *quant_dst = fminf(static_cast<float>(r * (127.0 / static_cast<double>(1e-8f))), 3.40282347e+38f);
+  }
+}
+
 // binary16 bit pattern -> binary32 (exact)
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));

@@ -27,8 +27,8 @@
 //   * kFromBf16Norm: RMSNorm fused as well ("bit_linear.py" listing: the
 //     BitLinear input passes nn.RMSNorm first): codes of v = x * gain, and
 //     a' = max|v| / sqrt(mean x^2 + eps) (the per-token factor cancels in
-//     the codes), equal to bitlinear_rmsnorm_quant_act's (a' within one ulp:
-//     the mean square is an fp64 sum in another order);
+//     the codes; rmsnorm_scales), equal to bitlinear_rmsnorm_quant_act's
+//     (a' within one ulp: the mean square is an fp64 sum in another order);
 //   * kFromF32: computed from fp32 activations, bit-identical to
 //     bitlinear_quant_act_f32.
 // The activations are requested before the first weight tiles: vector-memory
@@ -473,11 +473,8 @@ __device__ __forceinline__ double wave_sum_d(double v) { return wave_sum_f64(v);
 // a' and the quantisation scale of one token from max|v| and the sum of x^2
 __device__ __forceinline__ void norm_scales(unsigned mx, double ss, int64_t k, float eps, float* amax_dst,
                                             float* quant_dst) {
-  const float av = __uint_as_float(mx);
   const double r = 1.0 / sqrt(ss / static_cast<double>(k) + static_cast<double>(eps));
-  const float ap = static_cast<float>(static_cast<double>(av) * r);
-  *amax_dst = av > 0.0f ? fmaxf(ap, 1e-8f) : 1e-8f;
-  *quant_dst = av > 0.0f ? 127.0f / av : 0.0f;  // all-zero v: every code is 0
+  rmsnorm_scales(__uint_as_float(mx), r, amax_dst, quant_dst);
 }
 
 // Single token, vector path: wave shuffles and one LDS slot per wave for both

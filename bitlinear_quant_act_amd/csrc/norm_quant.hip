@@ -6,10 +6,12 @@
 // passes nn.RMSNorm before activation_quant).  RMSNorm multiplies token t by
 // r_t = 1 / sqrt(mean_k x^2 + eps) and channel c by a gain w_c.  Per-token
 // absmax quantisation is invariant under the positive factor r_t, so the
-// codes are those of v = x * w (one fp32 multiply per value) and r_t is
+// codes are taken from v = x * w (one fp32 multiply per value) and r_t is
 // folded into the de-quantisation scale: a'_t = max_c |v| * r_t, with the
-// mean square accumulated in fp64 and the product rounded once to fp32.  A
-// token whose v is all zero gets codes 0 and a' = 1e-8.
+// mean square accumulated in fp64 and the product rounded once to fp32
+// (rmsnorm_scales, which also applies the 1e-8 floor of the normalised
+// token).  The codes are those of the normalised token except where its
+// scaled value lies within a few roundings of a tie.
 //
 // Quantisation from fp32: the same per-token rule as the bf16 kernel
 // (section "The Mathematical Mechanism", item 2), for activations produced in
@@ -112,8 +114,8 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_vec(const uint16_t
     mall = max(mall, red_max[w]);
     sall += red_ss[w];
   }
-  const float av = __uint_as_float(mall);
-  const float s = av > 0.0f ? 127.0f / av : 0.0f;  // all-zero v: every code is 0
+  float ap, s;
+  rmsnorm_scales(__uint_as_float(mall), 1.0 / sqrt(sall / static_cast<double>(k) + static_cast<double>(eps)), &ap, &s);
   uint2* out = reinterpret_cast<uint2*>(xq + row * k);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -128,11 +130,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_vec(const uint16_t
       out[idx] = make_uint2(lo, hi);
     }
   }
-  if (threadIdx.x == 0) {
-    const double r = 1.0 / sqrt(sall / static_cast<double>(k) + static_cast<double>(eps));
-    const float ap = static_cast<float>(static_cast<double>(av) * r);
-    amax[row] = av > 0.0f ? fmaxf(ap, 1e-8f) : 1e-8f;
-  }
+  if (threadIdx.x == 0) amax[row] = ap;
 }
 
 // General path: any k and alignment; two passes over the row with scalar loads.
@@ -166,19 +164,15 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_any(const uint16_t* __
     mall = max(mall, red_max[w]);
     sall += red_ss[w];
   }
-  const float av = __uint_as_float(mall);
-  const float s = av > 0.0f ? 127.0f / av : 0.0f;
+  float ap, s;
+  rmsnorm_scales(__uint_as_float(mall), 1.0 / sqrt(sall / static_cast<double>(k) + static_cast<double>(eps)), &ap, &s);
   int8_t* out = xq + row * k;
   for (int64_t i = threadIdx.x; i < k; i += kThreads) {
     const float xv = __uint_as_float(static_cast<uint32_t>(xr[i]) << 16);
     const float v = gain ? xv * gain[i] : xv;
     out[i] = static_cast<int8_t>(code_of(v, s));
   }
-  if (threadIdx.x == 0) {
-    const double r = 1.0 / sqrt(sall / static_cast<double>(k) + static_cast<double>(eps));
-    const float ap = static_cast<float>(static_cast<double>(av) * r);
-    amax[row] = av > 0.0f ? fmaxf(ap, 1e-8f) : 1e-8f;
-  }
+  if (threadIdx.x == 0) amax[row] = ap;
 }
 
 // ---------------------------------------------------------------------------

@@ -181,19 +181,28 @@ int bitlinear_forward_batched(const void *packed, const float *gamma, int64_t n,
 /*
  * RMSNorm ahead of the activation quantisation ("BitNet b1.58 in
  * Production", listing "bit_linear.py": the BitLinear input passes
- * nn.RMSNorm before activation_quant).  Per token r = 1 / sqrt(mean_k x^2 +
- * eps), and the normalised input is x * r * gain.  Absmax quantisation is
- * invariant under the positive per-token factor r, so the codes are computed
- * from v = x * gain (one fp32 multiply per value; gain = 1 when NULL) by the
- * rule of bitlinear_quant_act, and r is carried by the scale:
+ * nn.RMSNorm, and activation_quant is applied to the normalised input).  Per
+ * token r = 1 / sqrt(mean_k x^2 + eps) and x_norm = x * r * gain; then the
+ * rule of bitlinear_quant_act on x_norm: a' = max(max_k |x_norm|, 1e-8),
+ * x_q = Clip(Round(x_norm * 127 / a'), -127, 127).
+ * Absmax quantisation is invariant under the positive per-token factor r, so
+ * the codes are computed from v = x * gain (one fp32 multiply per value;
+ * gain = 1 when NULL) and r is carried by the scale:
  *   s = 127 / max_k |v| (IEEE fp32 divide); x_q = Clip(Round(v * s), -127, 127);
- *   a' = max(max_k |v| * r, 1e-8), mean square in fp64, product rounded once;
- * y = acc * gamma * a' / 127 then de-quantises the normalised input.  A
- * token whose v is all zero gets codes 0 and a' = 1e-8.
+ *   a' = max_k |v| * r (mean square in fp64, product rounded once);
+ * when that a' is below 1e-8 the floor is the token's scale instead
+ * (s = r * 127 / 1e-8 on v, a' = 1e-8), as the listing's clamp makes it.
+ * The codes therefore equal Round(x_norm * 127 / a') except where that
+ * value lies within a few fp32 roundings of a tie (2^-19 relative), where
+ * they may be the other neighbour; a' agrees with max|x_norm| to within a
+ * few ulps.  A token whose v is all zero gets codes 0 and a' = 1e-8.
+ * y = acc * gamma * a' / 127 then de-quantises the normalised input.
  *   x             in   bf16 bit patterns [m][k], 2-byte aligned
  *   gain_or_null  in   fp32 [k] per-channel gain, 4-byte aligned, or NULL
  *   eps           in   finite and >= 0 (nn.RMSNorm's default for fp32 input
- *                      is FLT_EPSILON), else BITLINEAR_E_VALUE
+ *                      is FLT_EPSILON), else BITLINEAR_E_VALUE; with eps = 0
+ *                      an all-zero token has no defined x_norm (0 / 0) and
+ *                      is outside the contract
  *   xq, x_absmax  out  int8 [m][k] and fp32 [m] (a')
  */
 int bitlinear_rmsnorm_quant_act(const uint16_t *x, const float *gain_or_null, float eps,

@@ -13,9 +13,13 @@ section in the C file):
                          Kernel Works (codes 00 = 0, 01 = +1, 10 = -1);
   quant_act           -- "BitNet b1.58 in Production", item 2 (per-token
                          absmax, Q_b = 127);
-  contract            -- item 3 (add / skip / subtract) and the LUT section's
-                         scalar loop;
-  dequant             -- item 4 (gamma * max|x| / Q_b).
+  contract            -- item 3 (integer dot product with weights in
+                         {-1, 0, 1});
+  dequant             -- item 4 (gamma * max|x| / Q_b);
+  rmsnorm_quant_act   -- the same page's "bit_linear.py" listing: nn.RMSNorm,
+                         then activation_quant of the normalised input;
+  swiglu              -- "BitNet 1-bit LLM Inference Framework", "A Deep Look
+                         at the BitNet Architecture" (the block's ffn).
 Variant modes:
   quant_act_tensor, dequant_tensor, contract_q128
                       -- "BitNet 1-bit LLM Inference Framework", the BitLinear
@@ -73,7 +77,7 @@ def _load():
     lib.oracle_dequant.restype = None
     lib.oracle_quant_act_f32.argtypes = [_p, _i64, _i64, _p, _p]
     lib.oracle_quant_act_f32.restype = None
-    lib.oracle_rmsnorm_quant_act.argtypes = [_p, _p, _ct.c_float, _i64, _i64, _p, _p, _p]
+    lib.oracle_rmsnorm_quant_act.argtypes = [_p, _p, _ct.c_float, _i64, _i64, _p, _p, _p, _p]
     lib.oracle_rmsnorm_quant_act.restype = None
     lib.oracle_swiglu.argtypes = [_p, _p, _i64, _p]
     lib.oracle_swiglu.restype = None
@@ -187,9 +191,11 @@ def quant_act_f32(x: np.ndarray):
 RMS_EPS = float(np.finfo(np.float32).eps)
 
 
-def rmsnorm_quant_act(x_bits: np.ndarray, w=None, eps: float = RMS_EPS):
-    """RMSNorm (optional gain w [k]) then per-token quantization.
-    Returns (xq int8 [m][k], a' fp32 [m], r fp32 [m])."""
+def rmsnorm_quant_act(x_bits: np.ndarray, w=None, eps: float = RMS_EPS, with_xnorm: bool = False):
+    """RMSNorm (optional gain w [k]) then per-token quantization of the
+    normalised input, in the listing's order.
+    Returns (xq int8 [m][k], a' fp32 [m], r fp32 [m]), and x_norm fp32 [m][k]
+    as a fourth element when with_xnorm."""
     x = _c(x_bits, np.uint16)
     m, k = x.shape
     wp = None
@@ -201,8 +207,10 @@ def rmsnorm_quant_act(x_bits: np.ndarray, w=None, eps: float = RMS_EPS):
     xq = np.empty((m, k), dtype=np.int8)
     amax = np.empty(m, dtype=np.float32)
     rr = np.empty(m, dtype=np.float32)
-    _load().oracle_rmsnorm_quant_act(_ptr(x), wp, float(np.float32(eps)), m, k, _ptr(xq), _ptr(amax), _ptr(rr))
-    return xq, amax, rr
+    xn = np.empty((m, k), dtype=np.float32) if with_xnorm else None
+    _load().oracle_rmsnorm_quant_act(_ptr(x), wp, float(np.float32(eps)), m, k, _ptr(xq), _ptr(amax), _ptr(rr),
+                                     _ptr(xn) if with_xnorm else None)
+    return (xq, amax, rr, xn) if with_xnorm else (xq, amax, rr)
 
 
 def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:

@@ -14,8 +14,7 @@
  *        BitLinear.forward), used only where the items leave a step open.
  *   [P5] "BitNet 1-bit LLM Inference Framework: Running Large Language Models
  *        on CPU", section "How the LUT Kernel Works" (2-bit code assignment
- *        00 = 0, 01 = +1, 10 = -1; conditional add / skip / subtract loop),
- *        and section "The Difference in How Computation Works" (mask form).
+ *        00 = 0, 01 = +1, 10 = -1, four weights per byte).
  *
  * Readings where the pages leave a choice open (all documented with the tests):
  *   - gamma is one scalar per weight matrix: the mean of |W| accumulated in
@@ -36,12 +35,11 @@
  *        BitNet Architecture", the ffn of the transformer block:
  *        down_proj(silu(gate_proj(x)) * up_proj(x)).
  * Readings taken there:
- *   - RMSNorm: r = 1 / sqrt(mean_k x^2 + eps) per token (binary64), times an
- *     optional per-channel gain w.  Absmax quantization is invariant under a
- *     positive per-token factor, so the codes are those of v = x * w (one
- *     binary32 multiply) and r is carried by the scale instead:
- *     a' = max(max_k |v| * r, 1e-8) (binary64 product, rounded once).  An
- *     all-zero v gives codes 0 and a' = 1e-8;
+ *   - RMSNorm, in the listing's order: r = 1 / sqrt(mean_k x^2 + eps) per
+ *     token (binary64, rounded once to binary32), x_norm = (x * r) * w with
+ *     an optional per-channel gain w (binary32), and then the per-token
+ *     absmax rule of O5 on x_norm.  An all-zero x_norm gives codes 0 and
+ *     a' = 1e-8;
  *   - SwiGLU: h = silu(g) * u = g * u / (1 + exp(-g)) in binary64, rounded
  *     once to binary32, from the two de-quantized BitLinear outputs;
  *   - h is requantized for the next BitLinear from binary32 with the same
@@ -275,56 +273,78 @@ void oracle_quant_act_f32(const float *x, int64_t m, int64_t k, int8_t *xq, floa
 /*   [P4, "bit_linear.py": x_norm = rms_norm(x); activation_quant(x_norm)]*/
 /* ------------------------------------------------------------------ */
 
-/* x: bf16 bits [m][k]; w: per-channel gain [k] (NULL: all ones); eps added to
- * the mean square.  Codes quantize v = x * w; the factor r = 1/sqrt(mean x^2 +
- * eps), which cancels in the codes, is folded into a'.  rms_out (may be NULL)
- * receives r rounded to binary32. */
+/* The listing's order, value by value: first the normalised input
+ *   r = 1 / sqrt(mean_k x^2 + eps)   (mean square in binary64, r rounded once
+ *                                     to binary32),
+ *   x_norm = (x * r) * w              (two binary32 multiplies; w = 1 when
+ *                                     the gain is NULL),
+ * then O5's per-token absmax rule applied to x_norm:
+ *   a' = max(max_k |x_norm|, 1e-8), s = 127 / a' (binary32 divide),
+ *   code = Clip(Round(x_norm * s), -127, 127).
+ * x: bf16 bits [m][k]; xq: int8 [m][k]; amax: [m] receives a'.  rms_out (may
+ * be NULL) receives r; xnorm_out (may be NULL) receives x_norm, fp32 [m][k]. */
 void oracle_rmsnorm_quant_act(const uint16_t *x, const float *w, float eps, int64_t m, int64_t k,
-                              int8_t *xq, float *amax, float *rms_out)
+                              int8_t *xq, float *amax, float *rms_out, float *xnorm_out)
 {
     int64_t r;
 #pragma omp parallel for schedule(static)
     for (r = 0; r < m; ++r) {
+        /* nn.RMSNorm: the mean of the squares, then its reciprocal root */
         double ss = 0.0;
+        for (int64_t c = 0; c < k; ++c) {
+            const double xv = (double)bf16_to_f32(x[r * k + c]);
+            ss += xv * xv;
+        }
+        const float rr = (float)(1.0 / sqrt(ss / (double)k + (double)eps));
+        if (rms_out)
+            rms_out[r] = rr;
+        /* the normalised token, then activation_quant of it */
         float a = 0.0f;
         for (int64_t c = 0; c < k; ++c) {
-            const float xv = bf16_to_f32(x[r * k + c]);
-            ss += (double)xv * (double)xv;
-            const float v = fabsf(w ? xv * w[c] : xv);
-            if (v > a)
-                a = v;
+            float xn = bf16_to_f32(x[r * k + c]) * rr;
+            if (w)
+                xn = xn * w[c];
+            if (xnorm_out)
+                xnorm_out[r * k + c] = xn;
+            if (fabsf(xn) > a)
+                a = fabsf(xn);
         }
-        const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);
-        if (rms_out)
-            rms_out[r] = (float)rr;
-        if (a == 0.0f) {
-            for (int64_t c = 0; c < k; ++c)
-                xq[r * k + c] = 0;
-            amax[r] = 1e-8f;
-            continue;
-        }
+        if (a < 1e-8f)
+            a = 1e-8f;
         const float s = 127.0f / a;
         for (int64_t c = 0; c < k; ++c) {
-            const float xv = bf16_to_f32(x[r * k + c]);
-            const float v = w ? xv * w[c] : xv;
-            xq[r * k + c] = (int8_t)clip(round_half_even(v * s), -127.0, 127.0);
+            float xn = bf16_to_f32(x[r * k + c]) * rr;
+            if (w)
+                xn = xn * w[c];
+            xq[r * k + c] = (int8_t)clip(round_half_even(xn * s), -127.0, 127.0);
         }
-        float ap = (float)((double)a * rr);
-        amax[r] = ap < 1e-8f ? 1e-8f : ap;
+        amax[r] = a;
     }
 }
 
 /* ------------------------------------------------------------------ */
-/* O6: ternary x int8 contraction by add / skip / subtract              */
-/*     [P4, Mathematical Mechanism, item 3; P5, How the LUT Kernel Works]*/
+/* O6: ternary x int8 contraction  [P4, Mathematical Mechanism, item 3] */
 /* ------------------------------------------------------------------ */
 
-/* acc[i][j] = sum_k xq[i][k] * q[j][k], computed as: +x where the weight is
- * +1, nothing where it is 0, -x where it is -1.  The sum is kept in int64 and
- * checked against the bound |acc| <= 127 * k (128 * k for the V1 codes, which
- * reach -128) before it is stored as int32.
+/* acc[i][j] = sum_k xq[i][k] * q[j][k]: the plain integer dot product of a
+ * token's codes with a weight row whose entries are -1, 0 or +1, so every
+ * term is the code itself, zero, or its negation and no real multiplication
+ * is needed.  The terms are summed in int64, in column order, and the sum is
+ * checked against |acc| <= qmax * k (127 * k; 128 * k for the V1 codes,
+ * which reach -128) before it is stored as int32.
  * Returns 0, or -1 if the bound (or int32 range) is violated, or -2 if a
  * weight is not in {-1, 0, 1}. */
+static int64_t ternary_dot(const int8_t *a, const int8_t *w, int64_t k, int *bad)
+{
+    int64_t s = 0;
+    for (int64_t c = 0; c < k; ++c) {
+        if (w[c] < -1 || w[c] > 1)
+            *bad |= 2;
+        s += (int64_t)a[c] * (int64_t)w[c];
+    }
+    return s;
+}
+
 static int contract_bounded(const int8_t *xq, const int8_t *q, int64_t m, int64_t n, int64_t k,
                             int64_t qmax, int32_t *acc)
 {
@@ -334,17 +354,7 @@ static int contract_bounded(const int8_t *xq, const int8_t *q, int64_t m, int64_
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (i = 0; i < m * n; ++i) {
         const int64_t row = i / n, col = i % n;
-        const int8_t *a = xq + row * k;
-        const int8_t *w = q + col * k;
-        int64_t s = 0;
-        for (int64_t c = 0; c < k; ++c) {
-            if (w[c] == 1)
-                s += a[c];
-            else if (w[c] == -1)
-                s -= a[c];
-            else if (w[c] != 0)
-                bad |= 2;
-        }
+        const int64_t s = ternary_dot(xq + row * k, q + col * k, k, &bad);
         if (s > bound || s < -bound || s > INT32_MAX || s < INT32_MIN)
             bad |= 1;
         acc[i] = (int32_t)s;
@@ -371,17 +381,7 @@ int oracle_contract_pairs(const int8_t *xq, const int8_t *q_rows, int64_t k,
     int64_t p;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (p = 0; p < npairs; ++p) {
-        const int8_t *a = xq + row_of_pair[p] * k;
-        const int8_t *w = q_rows + qrow_of_pair[p] * k;
-        int64_t s = 0;
-        for (int64_t c = 0; c < k; ++c) {
-            if (w[c] == 1)
-                s += a[c];
-            else if (w[c] == -1)
-                s -= a[c];
-            else if (w[c] != 0)
-                bad |= 2;
-        }
+        const int64_t s = ternary_dot(xq + row_of_pair[p] * k, q_rows + qrow_of_pair[p] * k, k, &bad);
         if (s > bound || s < -bound)
             bad |= 1;
         acc[p] = (int32_t)s;

@@ -7,6 +7,13 @@ the int32 accumulators bit-exact / fp32 outputs within 1e-5 relative -- on
 every output where the oracle can afford the whole contraction, otherwise on
 all outputs of the first and last token plus 4096 random (token, row) pairs,
 each computed by the oracle one by one.
+
+The fused entry points the decode benchmark times (the quantisation, or
+RMSNorm and the quantisation, in the decode prologue; the fp32 quantisation
+for the down projection) run at every matrix shape of the decode workloads
+with one and two tokens; their codes, a', accumulators and outputs are
+compared on every output (RMSNorm: with the per-position tie allowance of
+tests/gpu_util.py).
 """
 from __future__ import annotations
 
@@ -15,7 +22,8 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import check_gamma, compare_codes, compare_y, host, log, to_dev, to_dev_bits, torch_mod
+from tests.gpu_util import (check_gamma, check_norm_codes, compare_acc_flips, compare_codes, compare_y,
+                            compare_y_flips, host, log, to_dev, to_dev_bits, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,3 +84,44 @@ def test_workload_matrix_full_size(blq, wkey, j):
             sel = rows == t
             y_or[sel] = oracle.dequant(acc_or[sel][None, :], g_or, amax_or[t:t + 1])[0]
         compare_y(y[rows, cols], y_or, tag)
+    if min(wl.ms) <= 2:  # a decode workload: the fused entry points it times, at one and two tokens
+        fused_checks(blq, wl, j, packed, gamma, q_or, g_or, bad_rows, tag)
+
+
+def fused_checks(blq, wl, j, packed, gamma, q_or, g_or, bad_rows, tag):
+    torch = torch_mod()
+    n, k = wl.matrices[j].n, wl.matrices[j].k
+    keep = np.setdiff1d(np.arange(n), bad_rows)
+    gain = synth.norm_gain(synth.seed_for(wl, 0, j, synth.ROLE_GAIN), k)
+    for m in (1, 2):
+        if not blq.bitlinear_quant_forward_supported(m, k):
+            continue
+        x = synth.activations_bf16(synth.seed_for(wl, 0, j, synth.ROLE_ACT, extra=100 + m), m, k, wl.outlier_frac)
+        xd = to_dev_bits(x)
+        for kind in ("plain", "rmsnorm", "f32"):
+            if kind == "f32" and m != 1:
+                continue
+            t = "%s fused %s m=%d" % (tag, kind, m)
+            log("  " + t)
+            acc_d = torch.empty((m, n), dtype=torch.int32, device="cuda")
+            xq_d = torch.empty((m, k), dtype=torch.int8, device="cuda")
+            a_d = torch.empty(m, dtype=torch.float32, device="cuda")
+            flips = np.zeros(m, np.int64)
+            if kind == "plain":
+                y_d = blq.bitlinear_quant_forward(packed, gamma, n, k, xd, acc=acc_d, xq=xq_d, x_absmax=a_d)
+                xq_o, a_o = oracle.quant_act(x)
+                assert np.array_equal(host(xq_d), xq_o) and np.array_equal(host(a_d), a_o), t
+            elif kind == "rmsnorm":
+                y_d = blq.bitlinear_rmsnorm_quant_forward(packed, gamma, n, k, xd, gain=to_dev(gain), acc=acc_d,
+                                                          xq=xq_d, x_absmax=a_d)
+                xq_o, a_o, _, xn_o = oracle.rmsnorm_quant_act(x, gain, with_xnorm=True)
+                flips = check_norm_codes(host(xq_d), host(a_d), xq_o, a_o, xn_o, t)
+            else:
+                xf = synth.activations_f32(synth.seed_for(wl, 0, j, synth.ROLE_ACT, extra=200 + m), m, k, 0.5)
+                y_d = blq.bitlinear_quant_forward_f32(packed, gamma, n, k, to_dev(xf), acc=acc_d, xq=xq_d,
+                                                      x_absmax=a_d)
+                xq_o, a_o = oracle.quant_act_f32(xf)
+                assert np.array_equal(host(xq_d), xq_o) and np.array_equal(host(a_d), a_o), t
+            acc_o = oracle.contract(xq_o, q_or)
+            compare_acc_flips(host(acc_d)[:, keep], acc_o[:, keep], flips, t)
+            compare_y_flips(host(y_d)[:, keep], oracle.dequant(acc_o, g_or, a_o)[:, keep], flips, g_or, a_o, t)

@@ -358,6 +358,29 @@ def test_quant_forward_parity(blq, n, k, m):
     assert torch.equal(y, y2), tag
 
 
+def test_quant_forward_long_row_one_token(blq):
+    """One token of more than 32768 values: the fused prologue reads the row
+    again for the quantisation instead of keeping it in registers."""
+    torch = torch_mod()
+    n, k, m = 300, 40000, 1
+    assert blq.bitlinear_quant_forward_supported(m, k)
+    w = synth.latent_weights(23, n, k)
+    x = synth.activations_bf16(24, m, k, 0.01)
+    packed, gamma = gpu_pack(blq, w)
+    acc = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    amax = torch.empty(m, dtype=torch.float32, device="cuda")
+    y = blq.bitlinear_quant_forward(packed, gamma, n, k, to_dev_bits(x), acc=acc, xq=xq, x_absmax=amax)
+    ref = oracle.forward(x, w)
+    same = check_gamma(host(gamma)[0], ref["gamma"], "fused k=40000")
+    bad = compare_codes(host(blq.bitlinear_unpack_weights(packed, n, k)), ref["q"], w, ref["gamma"], same,
+                        "fused k=40000")
+    keep = np.setdiff1d(np.arange(n), bad)
+    assert np.array_equal(host(xq), ref["xq"]) and np.array_equal(host(amax), ref["amax"])
+    assert np.array_equal(host(acc)[:, keep], ref["acc"][:, keep])
+    compare_y(host(y)[:, keep], ref["y"][:, keep], "fused k=40000")
+
+
 def test_quant_forward_without_optional_outputs(blq):
     torch = torch_mod()
     n, k, m = 300, 2560, 1

@@ -35,22 +35,31 @@ MUTATIONS = {
     "pack field order reversed": ("byte |= code << (2 * i);", "byte |= code << (6 - 2 * i);"),
     "codes +1/-1 swapped": ("code = (v == 1) ? 1u : (v == -1) ? 2u : 0u;",
                             "code = (v == 1) ? 2u : (v == -1) ? 1u : 0u;"),
-    "subtract becomes add": ("            else if (w[c] == -1)\n                s -= a[c];\n            else if (w[c] != 0)\n                bad |= 2;\n        }\n        if (s > bound || s < -bound || s > INT32_MAX",
-                             "            else if (w[c] == -1)\n                s += a[c];\n            else if (w[c] != 0)\n                bad |= 2;\n        }\n        if (s > bound || s < -bound || s > INT32_MAX"),
-    "weight row indexed by token": ("const int8_t *w = q + col * k;", "const int8_t *w = q + (row % n) * k;"),
+    "weight sign dropped": ("s += (int64_t)a[c] * (int64_t)w[c];", "s += (int64_t)a[c] * (int64_t)(w[c] != 0);"),
+    "contraction skips the last column": ("for (int64_t c = 0; c < k; ++c) {\n        if (w[c] < -1 || w[c] > 1)",
+                                          "for (int64_t c = 0; c + 1 < k; ++c) {\n        if (w[c] < -1 || w[c] > 1)"),
+    "weight row indexed by token": ("ternary_dot(xq + row * k, q + col * k, k, &bad)", "ternary_dot(xq + row * k, q + (row % n) * k, k, &bad)"),
     "dequant without 1/127": ("(double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0",
                               "(double)acc[i * n + j] * (double)gamma * (double)amax[i]"),
     "dequant uses token 0 scale": ("(double)acc[i * n + j] * (double)gamma * (double)amax[i] / 127.0",
                                    "(double)acc[i * n + j] * (double)gamma * (double)amax[0] / 127.0"),
-    "rmsnorm eps dropped": ("const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);",
-                            "const double rr = 1.0 / sqrt(ss / (double)k);"),
-    "rmsnorm sum, not mean": ("const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);",
-                              "const double rr = 1.0 / sqrt(ss + (double)eps);"),
-    "rmsnorm sqrt dropped": ("const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);",
-                             "const double rr = 1.0 / (ss / (double)k + (double)eps);"),
-    "rmsnorm gain ignored in max": ("const float v = fabsf(w ? xv * w[c] : xv);", "const float v = fabsf(xv);"),
-    "rmsnorm gain ignored in codes": ("const float v = w ? xv * w[c] : xv;", "const float v = xv;"),
-    "rmsnorm r not folded into a'": ("float ap = (float)((double)a * rr);", "float ap = a;"),
+    "rmsnorm eps dropped": ("(float)(1.0 / sqrt(ss / (double)k + (double)eps));",
+                            "(float)(1.0 / sqrt(ss / (double)k));"),
+    "rmsnorm sum, not mean": ("(float)(1.0 / sqrt(ss / (double)k + (double)eps));",
+                              "(float)(1.0 / sqrt(ss + (double)eps));"),
+    "rmsnorm sqrt dropped": ("(float)(1.0 / sqrt(ss / (double)k + (double)eps));",
+                             "(float)(1.0 / (ss / (double)k + (double)eps));"),
+    "rmsnorm r kept in binary64": ("float xn = bf16_to_f32(x[r * k + c]) * rr;\n            if (w)\n                xn = xn * w[c];\n            if (xnorm_out)",
+                                   "float xn = (float)((double)bf16_to_f32(x[r * k + c]) * (1.0 / sqrt(ss / (double)k + (double)eps)));\n            if (w)\n                xn = xn * w[c];\n            if (xnorm_out)"),
+    "rmsnorm gain ignored in max": ("            if (w)\n                xn = xn * w[c];\n            if (xnorm_out)",
+                                    "            if (xnorm_out)"),
+    "rmsnorm gain ignored in codes": ("            if (w)\n                xn = xn * w[c];\n            xq[r * k + c]",
+                                      "            xq[r * k + c]"),
+    "rmsnorm r not applied": ("float xn = bf16_to_f32(x[r * k + c]) * rr;\n            if (w)\n                xn = xn * w[c];\n            if (xnorm_out)",
+                              "float xn = bf16_to_f32(x[r * k + c]);\n            if (w)\n                xn = xn * w[c];\n            if (xnorm_out)"),
+    "rmsnorm floor only on a'": ("        if (a < 1e-8f)\n            a = 1e-8f;\n        const float s = 127.0f / a;\n        for (int64_t c = 0; c < k; ++c) {\n            float xn",
+                                 "        const float s = a > 0.0f ? 127.0f / a : 0.0f;\n        if (a < 1e-8f)\n            a = 1e-8f;\n        for (int64_t c = 0; c < k; ++c) {\n            float xn"),
+    "rmsnorm max of x_norm, not |x_norm|": ("            if (fabsf(xn) > a)\n                a = fabsf(xn);", "            if (xn > a)\n                a = xn;"),
     "f32 quant max of x, not |x|": ("float v = fabsf(x[r * k + c]);", "float v = (x[r * k + c]);"),
     "silu with exp(+g)": ("h[i] = (float)(gd * (double)u[i] / (1.0 + exp(-gd)));",
                           "h[i] = (float)(gd * (double)u[i] / (1.0 + exp(gd)));"),

@@ -461,10 +461,18 @@ def test_golden_end_to_end(oracle_mod):
 
 # ---------------------------------------------------------------------------
 # RMSNorm ahead of the quantization ("BitNet b1.58 in Production", listing
-# "bit_linear.py": x_norm = nn.RMSNorm(in_features)(x), then activation_quant)
+# "bit_linear.py": x_norm = nn.RMSNorm(in_features)(x), then
+# activation_quant(x_norm)).  The oracle forms x_norm value by value:
+# r = 1 / sqrt(mean x^2 + eps) (binary64, rounded once to binary32),
+# x_norm = (x * r) * w in binary32, then the per-token absmax rule.
 # ---------------------------------------------------------------------------
 
 RMS_EPS = float(np.finfo(np.float32).eps)
+# |x_norm * s| of two evaluations that differ by a few roundings (a binary32
+# mean square summed in another order, or binary64 throughout) differ by at
+# most 2^-19 |x_norm * s|; a code may differ only where the value lies that
+# close to a rounding tie
+TIE_BAND = 2.0 ** -19
 
 
 def _r_exact(x_bits_row, eps):
@@ -474,41 +482,92 @@ def _r_exact(x_bits_row, eps):
     return 1.0 / math.sqrt(float(ms))
 
 
-def test_rmsnorm_unit_gain_keeps_codes(oracle_mod):
+def _near_tie(t):
+    t = np.abs(np.asarray(t, dtype=np.float64))
+    return np.abs(t - np.floor(t) - 0.5) <= TIE_BAND * t + 1e-30
+
+
+def _listing_activation_quant(torch, xn):
+    """activation_quant of the listing, evaluated by torch in xn's dtype."""
+    qmax = 2 ** (8 - 1) - 1
+    scale = torch.max(torch.abs(xn), dim=-1, keepdim=True)[0].clamp(min=1e-8)
+    x_scaled = xn * (qmax / scale)
+    return torch.clamp(torch.round(x_scaled), -qmax, qmax), scale[:, 0], x_scaled
+
+
+def test_rmsnorm_r_is_the_rounded_reciprocal_rms(oracle_mod):
+    """r is the reciprocal rms of the exact rational mean square, rounded to
+    binary32 (within one ulp: a binary64 evaluation rounded twice), and
+    x_norm is x times that binary32 r, times the gain, each product rounded
+    to binary32."""
     x = synth.activations_bf16(11, 5, 384, 0.01)
-    xq0, a0 = oracle_mod.quant_act(x)
-    for w in (None, np.ones(384, dtype=np.float32)):
-        xq, a, r = oracle_mod.rmsnorm_quant_act(x, w)
-        assert np.array_equal(xq, xq0)           # a positive per-token factor cancels
-        for t in range(5):
-            ref = np.float32(float(a0[t]) * _r_exact(x[t], RMS_EPS))
-            assert abs(int(ulp_diff(a[t], ref))) <= 1
+    w = synth.norm_gain(23, 384)
+    _, _, r, xn = oracle_mod.rmsnorm_quant_act(x, w, with_xnorm=True)
+    xf = synth.bf16_bits_to_fp32(x)
+    for t in range(5):
+        assert abs(int(ulp_diff(r[t], f32_nearest(Fraction(_r_exact(x[t], RMS_EPS)))))) <= 1
+        assert np.array_equal(xn[t], (xf[t] * np.float32(r[t])) * w)
 
 
-def test_rmsnorm_vs_torch_rms_norm(oracle_mod):
+def test_rmsnorm_power_of_two_rms_gives_the_gain(oracle_mod):
+    """|x| == 2^j everywhere and eps = 0: r = 2^-j exactly, so x_norm = +-w
+    exactly and the codes, a' and x_norm are those of the plain quantiser
+    applied to the token +-w (w bf16-exact)."""
+    k = 300
+    rng = np.random.default_rng(19)
+    w = synth.bf16_bits_to_fp32(bits(synth.norm_gain(20, k)))
+    for j in (-3, 0, 5):
+        signs = np.where(rng.random(k) < 0.5, -1.0, 1.0).astype(np.float32)
+        x = bits((signs * np.float32(2.0 ** j))[None, :])
+        xq, a, r, xn = oracle_mod.rmsnorm_quant_act(x, w, eps=0.0, with_xnorm=True)
+        assert r[0] == np.float32(2.0 ** -j)
+        assert np.array_equal(xn[0], signs * w)
+        xq0, a0 = oracle_mod.quant_act(bits((signs * w)[None, :]))
+        assert np.array_equal(xq, xq0) and a[0] == a0[0] == np.abs(w).max()
+
+
+def test_rmsnorm_vs_torch_fp32_listing(oracle_mod):
+    """torch's own rms_norm in binary32 followed by the listing's
+    activation_quant: codes equal except at values within the tie band,
+    a' within 1e-6 relative (torch sums the squares in binary32)."""
     torch = pytest.importorskip("torch")
-    x = synth.activations_bf16(12, 6, 512, 0.01)
-    w = synth.norm_gain(13, 512)
-    xq, a, r = oracle_mod.rmsnorm_quant_act(x, w)
+    for seed, (m, k) in ((12, (6, 512)), (21, (3, 4096)), (22, (2, 1001))):
+        x = synth.activations_bf16(seed, m, k, 0.01)
+        w = synth.norm_gain(seed + 1, k)
+        xq, a, _ = oracle_mod.rmsnorm_quant_act(x, w)
+        xf = torch.from_numpy(synth.bf16_bits_to_fp32(x))
+        xn = torch.nn.functional.rms_norm(xf, (k,), torch.from_numpy(w), RMS_EPS)
+        codes, scale, t = _listing_activation_quant(torch, xn)
+        codes, scale, t = codes.numpy(), scale.numpy(), t.numpy()
+        assert np.allclose(a, scale, rtol=1e-6, atol=0)
+        diff = codes.astype(np.int64) - xq.astype(np.int64)
+        assert np.all(np.abs(diff) <= 1)
+        assert np.all(_near_tie(t)[diff != 0])
+
+
+def test_rmsnorm_vs_torch_fp64_listing(oracle_mod):
+    """The same listing evaluated by torch in binary64 throughout."""
+    torch = pytest.importorskip("torch")
+    m, k = 6, 512
+    x = synth.activations_bf16(12, m, k, 0.01)
+    w = synth.norm_gain(13, k)
+    xq, a, _ = oracle_mod.rmsnorm_quant_act(x, w)
     xf = torch.from_numpy(synth.bf16_bits_to_fp32(x).astype(np.float64))
-    xn = torch.nn.functional.rms_norm(xf, (512,), torch.from_numpy(w.astype(np.float64)), RMS_EPS).numpy()
-    amax_ref = np.abs(xn).max(axis=1)
-    assert np.allclose(a, amax_ref, rtol=2e-7, atol=0)
-    # literal quantization of the normalized activations in binary64: equal
-    # codes except where the value sits within rounding distance of a tie
-    lit = xn * (127.0 / amax_ref[:, None])
-    codes = np.clip(np.round(lit), -127, 127)
-    diff = codes - xq.astype(np.float64)
-    near_tie = np.abs(np.abs(lit - np.floor(lit)) - 0.5) < 1e-4
+    xn = torch.nn.functional.rms_norm(xf, (k,), torch.from_numpy(w.astype(np.float64)), RMS_EPS)
+    codes, scale, t = _listing_activation_quant(torch, xn)
+    codes, scale, t = codes.numpy(), scale.numpy(), t.numpy()
+    assert np.allclose(a, scale, rtol=4e-7, atol=0)
+    diff = codes.astype(np.int64) - xq.astype(np.int64)
     assert np.all(np.abs(diff) <= 1)
-    assert np.all(near_tie[diff != 0])
+    assert np.all(_near_tie(t)[diff != 0])
 
 
 def test_rmsnorm_invariances(oracle_mod):
     x = synth.activations_bf16(14, 4, 256)
     w = synth.norm_gain(15, 256)
     xq, a, _ = oracle_mod.rmsnorm_quant_act(x, w, eps=0.0)
-    # power-of-two scaling of x (exact in bf16): same codes and, with eps = 0, same a'
+    # power-of-two scaling of x (exact in bf16), eps = 0: r scales inversely
+    # and exactly, so x_norm, the codes and a' are unchanged
     xs = bits(synth.bf16_bits_to_fp32(x) * np.float32(8.0))
     xq2, a2, _ = oracle_mod.rmsnorm_quant_act(xs, w, eps=0.0)
     assert np.array_equal(xq, xq2) and np.array_equal(a, a2)
@@ -520,7 +579,8 @@ def test_rmsnorm_invariances(oracle_mod):
 
 def test_rmsnorm_closed_forms(oracle_mod):
     k = 64
-    # constant token c: every code is sign(c) * 127, a' = |c| / sqrt(c^2 + eps)
+    # constant token c: x_norm = c * r everywhere, every code is sign(c) * 127,
+    # a' = |c| / sqrt(c^2 + eps)
     for c in (0.75, -3.0, 40.0):
         x = bits(np.full((1, k), c, dtype=np.float32))
         xq, a, r = oracle_mod.rmsnorm_quant_act(x)
@@ -540,6 +600,23 @@ def test_rmsnorm_closed_forms(oracle_mod):
     x = synth.activations_bf16(16, 1, k)
     xq, a, _ = oracle_mod.rmsnorm_quant_act(x, np.zeros(k, dtype=np.float32))
     assert np.all(xq == 0) and a[0] == np.float32(1e-8)
+
+
+def test_rmsnorm_floor_binds_on_the_normalised_token(oracle_mod):
+    """The 1e-8 floor of the listing's activation_quant applies to
+    max|x_norm|: a constant token (x_norm = c * r * w everywhere) with a gain
+    small enough that x_norm stays below 1e-8 is quantised with the scale
+    127 / 1e-8, not stretched to +-127."""
+    k = 32
+    c = 1.5
+    for w_val, code in ((2.0 ** -30, 12), (-(2.0 ** -31), -6), (2.0 ** -40, 0)):
+        x = bits(np.full((1, k), c, dtype=np.float32))
+        w = np.full(k, w_val, dtype=np.float32)
+        xq, a, _ = oracle_mod.rmsnorm_quant_act(x, w, eps=0.0)
+        t = abs(w_val) * 127.0 / 1e-8      # c * r = 1 exactly with eps = 0
+        assert abs(abs(t) - math.floor(abs(t)) - 0.5) > 1e-3        # away from a tie
+        assert np.all(xq == code) and round(t) == abs(code)
+        assert a[0] == np.float32(1e-8)
 
 
 # ---------------------------------------------------------------------------
