@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.bitlinear_pack_workspace_bytes.restype = _ct.c_size_t
     lib.bitlinear_pack_weights.argtypes = [_p, _i64, _i64, _p, _ct.c_size_t, _p, _p, _ct.c_size_t, _p]
     lib.bitlinear_pack_weights.restype = _ct.c_int
+    lib.bitlinear_pack_weights_noalloc.argtypes = [_p, _i64, _i64, _p, _ct.c_size_t, _p, _p]
+    lib.bitlinear_pack_weights_noalloc.restype = _ct.c_int
     lib.bitlinear_unpack_weights.argtypes = [_p, _i64, _i64, _p, _p]
     lib.bitlinear_unpack_weights.restype = _ct.c_int
     lib.bitlinear_quant_act.argtypes = [_p, _i64, _i64, _p, _p, _p]
@@ -199,6 +201,26 @@ def bitlinear_pack_weights(w, packed=None, gamma=None, workspace=None, stream=No
         _dev(workspace, "workspace", (_torch.uint8, _torch.float64, _torch.int64)),
         workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(rc, "bitlinear_pack_weights")
+    return packed, gamma
+
+
+BITLINEAR_PACK_NOALLOC_SCRATCH_BYTES = 8192
+
+
+def bitlinear_pack_weights_noalloc(w, packed, gamma, stream=None):
+    """bitlinear_pack_weights with the library's static device scratch in
+    place of a workspace: the caller passes the outputs (packed uint8 with at
+    least bitlinear_packed_bytes(n, k) bytes, gamma fp32 [1]); nothing is
+    allocated."""
+    lib = load_library()
+    if w.dim() != 2:
+        raise ValueError("w must be [n][k]")
+    n, k = w.shape
+    rc = lib.bitlinear_pack_weights_noalloc(
+        _dev(w, "w", (_torch.float32,)), n, k,
+        _dev(packed, "packed", (_torch.uint8,)), packed.numel() * packed.element_size(),
+        _dev(gamma, "gamma", (_torch.float32,), 1), _stream_handle(stream))
+    _check(rc, "bitlinear_pack_weights_noalloc")
     return packed, gamma
 
 

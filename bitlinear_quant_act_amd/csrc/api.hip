@@ -87,6 +87,16 @@ int bitlinear_pack_weights(const float* w, int64_t n, int64_t k, void* packed, s
                                           static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_pack_weights_noalloc(const float* w, int64_t n, int64_t k, void* packed, size_t packed_bytes,
+                                   float* gamma, void* stream) {
+  if (!w || !packed || !gamma) return BITLINEAR_E_NULL;
+  if (int rc = check_nk(n, k)) return rc;
+  if (!aligned(w, 4) || !aligned(packed, 16) || !aligned(gamma, 4)) return BITLINEAR_E_ALIGN;
+  if (packed_bytes < bitlinear_packed_bytes(n, k)) return BITLINEAR_E_SIZE;
+  if (bitlinear_pack_workspace_bytes(n, k) > BITLINEAR_PACK_NOALLOC_SCRATCH_BYTES) return BITLINEAR_E_SIZE;
+  return status_of(bitlinear::launch_pack_noalloc(w, n, k, packed, gamma, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_unpack_weights(const void* packed, int64_t n, int64_t k, int8_t* codes, void* stream) {
   if (!packed || !codes) return BITLINEAR_E_NULL;
   if (int rc = check_nk(n, k)) return rc;

@@ -193,6 +193,7 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq,
 int pack_partial_count(int64_t n, int64_t k);
 hipError_t launch_pack(const float* w, int64_t n, int64_t k, void* packed, float* gamma,
                        double* partials, hipStream_t s);
+hipError_t launch_pack_noalloc(const float* w, int64_t n, int64_t k, void* packed, float* gamma, hipStream_t s);
 hipError_t launch_unpack(const void* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t s);
 
 hipError_t launch_gemv(const void* packed, const float* gamma, int64_t n, int64_t k,

@@ -13,9 +13,20 @@
 // the packed tiles.  gamma = fp32(fp64 sum / (n k)), one rounding to fp32.
 // Both kernels read W with 16-byte loads, consecutive lanes on consecutive
 // addresses; the 16x smaller packed output is scattered into 1 KiB tiles.
+#include <mutex>
+
 #include "bitlinear_internal.hpp"
 
 namespace bitlinear {
+
+// Scratch of the allocation-free pack (bitlinear_pack_weights_noalloc): the
+// fp64 partial sums of |W| that the caller's workspace holds otherwise, at
+// most kPackPartials of them (8 KiB).  Every GPU the library runs on holds
+// its own copy until the process ends; each call overwrites every slot it
+// reads, so nothing needs clearing, and calls that overlap on one GPU race
+// on it.
+static __device__ __align__(256) double scratch[kPackPartials];
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -277,6 +288,36 @@ hipError_t launch_pack(const float* w, int64_t n, int64_t k, void* packed, float
     ternarize_pack<false><<<grid_for(words), kThreads, 0, s>>>(w, n, k, kt, partials, parts, gamma,
                                                                 static_cast<uint32_t*>(packed));
   return hipGetLastError();
+}
+
+// Device address of `scratch` on each GPU, looked up once per device with
+// that device current (the host-side name is not a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t pack_scratch(double** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<double*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_pack_noalloc(const float* w, int64_t n, int64_t k, void* packed, float* gamma, hipStream_t s) {
+  if (pack_partial_count(n, k) > kPackPartials) return hipErrorInvalidValue;  // never for accepted shapes
+  double* partials = nullptr;
+  const hipError_t e = pack_scratch(&partials);
+  if (e != hipSuccess) return e;
+  return launch_pack(w, n, k, packed, gamma, partials, s);
 }
 
 hipError_t launch_pack_rowscale(const float* w, int64_t n, int64_t k, void* packed, uint16_t* scales, hipStream_t s) {

@@ -104,6 +104,24 @@ int bitlinear_pack_weights(const float *w, int64_t n, int64_t k,
                            void *stream);
 
 /*
+ * bitlinear_pack_weights for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same result, bit for bit, from the same two kernels; the fp64
+ * partial sums that the workspace argument holds otherwise live in a static
+ * device array of BITLINEAR_PACK_NOALLOC_SCRATCH_BYTES inside the library
+ * (one per GPU, held until the process ends, its address looked up on the
+ * first call on each device).  Every accepted (n, k) needs at most that
+ * much; a larger need returns BITLINEAR_E_SIZE.  The call allocates nothing.
+ * Calls that overlap on one GPU (on different streams, or from different
+ * threads) share the array and race: serialise them.
+ *   w, packed, packed_bytes, gamma, stream   as bitlinear_pack_weights
+ */
+#define BITLINEAR_PACK_NOALLOC_SCRATCH_BYTES 8192
+int bitlinear_pack_weights_noalloc(const float *w, int64_t n, int64_t k,
+                                   void *packed, size_t packed_bytes,
+                                   float *gamma, void *stream);
+
+/*
  * Decode the packed layout back to ternary codes (for tests and inspection).
  *   packed  in   bitlinear_packed_bytes(n, k) bytes, 16-byte aligned
  *   codes   out  int8 [n][k] in {-1, 0, 1}
