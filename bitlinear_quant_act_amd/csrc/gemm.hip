@@ -270,98 +270,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint4* __restri
 }
 
 // ---------------------------------------------------------------------------
-// S-stage pipeline with buffer-to-LDS loads (k % 16 == 0, codes 16-byte aligned)
+// Matrix-core kernel: activations through LDS, weights straight to registers
 // ---------------------------------------------------------------------------
 //
-// buffer_load_dwordx4 ... lds moves 16 bytes per lane straight into LDS (64
-// lanes -> 1 KiB contiguous), so no registers stage the tiles and S - 1 tiles
-// can be in flight while one is consumed.  Each stage is its own LDS array so
-// the compiler tracks the outstanding copies per stage; a wave waits for its
-// own copies of the tile it is about to read (s_waitcnt vmcnt), then a plain
-// s_barrier (no memory fence, which would drain every copy) publishes them.
-// The buffer (MUBUF) form rather than the global (FLAT) one keeps the
-// compiler's LDS-read waits exact: a pending FLAT operation forces every
-// lgkmcnt wait to zero.
+// A workgroup of WM x WN = 4 waves owns a BM x BN output tile, BM = WM * MB *
+// 32 tokens and BN = WN * NB * 32 weight rows; each wave holds MB x NB
+// accumulator blocks of 32 x 32.  It walks k in 256-column steps:
+//   * the BM x 256 activation codes of a step are copied into LDS by
+//     buffer-to-LDS loads (two stages, one step in flight), read by every
+//     wave of the same token rows;
+//   * each wave reads the packed weights of its own rows straight into
+//     registers (no other wave uses them), one step ahead, still 2 bits per
+//     weight, and expands each 16-column word once for its MB token blocks.
 //
-// Each workgroup addresses its operands through two buffer descriptors: its
-// BM token rows of codes and its BN / 16 weight row blocks.  Reads past a
-// descriptor's byte count return zeros, which covers token rows past m and
-// row blocks past n; columns past k (inside the last token row) meet zero
-// weight padding.
+// k order inside a step: MFMA step q (0..7) of the lanes of half h takes the
+// 16 columns of chunk 8h + q.  A ternary lane (weight row r, half h) holds
+// slots (r % 16) + 32h and (r % 16) + 32h + 16 of its row block's tile:
+// columns 128h + [0, 128), words 0-3 of the first slot for q < 4 and of the
+// second for q >= 4.  A binary lane holds slot (r % 16) + 16h of the step's
+// half tile, word q / 2, half q % 2.  Either way a lane's weight bytes are
+// whole 16-byte slots, and a wave's loads cover contiguous 256-byte runs.
 //
-// The activation tile has no padding; instead the 16 chunks of 16 bytes in
-// a 256-byte row are stored XOR-swizzled by (row % 16), which keeps the 32
-// token rows of one MFMA operand read on distinct banks.
+// The activation tile is stored with chunk c of row t at position
+// c ^ (t % 16), so the 16 lanes of a half that read one chunk of 16
+// consecutive rows meet 16 different 16-byte bank groups.  The LDS address of
+// a lane's chunk for each q is computed once; the token blocks and the two
+// stages add constants.
+//
+// Reads past a buffer descriptor's byte count return zeros: token rows past
+// m, weight row blocks past n; columns past k meet zero ternary weights (the
+// packed padding), and for binary weights (whose padding is +1) their
+// activation chunks are sent past the descriptor.
+
+constexpr int kRawBufferWord3 = 0x00020000;     // raw (untyped) buffer, 32-bit data format
+constexpr int kOffPastDescriptor = 0x7fffff00;  // byte offset beyond any descriptor's range (reads return 0)
 
 #define BITLINEAR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int BM, int BN, int WB = 2>
-struct DmaShape {
-  static constexpr int kABytes = BM * kTileCols;
-  static constexpr int kBBytes = (BN / kTileRows) * wtile_bytes<WB>();
-  static constexpr int kStage = kABytes + kBBytes;
-  static constexpr int kADma = BM / 16;   // 1 KiB copies per wave for the activation tile
-  static constexpr int kBDma = BN / 64;   // 1 KiB copies per wave for the (ternary) weight tiles
-  static constexpr int kDma = kADma + kBDma;
-};
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-constexpr int DmaStageBytes(int bm, int bn, int wb = 2) {
-  return bm * kTileCols + (bn / kTileRows) * (wb == 1 ? kBinTileBytes : kTileBytes);
-}
-
-constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
-constexpr int kPastDescriptor = 0x7fffff00;  // byte offset beyond any descriptor's range (reads return 0)
-
-// With SWIGLU the BN weight rows of a stage come from two matrices, gate and
-// up, in alternating 32-row blocks over BN / 2 features: 32-row block v holds
-// rows 32 * (v / 2) + [0, 32) of the workgroup's features, from gate for even
-// v and from up for odd v (b_rsrc / u_rsrc).
-//
-// Binary weights (WB = 1): one 1 KiB copy carries the k-step's 512-byte half
-// tiles of two row blocks (lanes 0-31 the first, 32-63 the second); the
-// BN / 32 copies of a stage are dealt to the waves round-robin, so waves may
-// issue different counts (the binary kernel runs two stages and waits for
-// all copies).
-template <int BM, int BN, bool SWIGLU = false, int WB = 2>
-__device__ __forceinline__ void issue_tile(uint8_t* stage, __amdgpu_buffer_rsrc_t a_rsrc, __amdgpu_buffer_rsrc_t b_rsrc,
-                                           __amdgpu_buffer_rsrc_t u_rsrc, int k, int kt_count, int kt, int wave,
-                                           int lane) {
-  using DS = DmaShape<BM, BN, WB>;
-  const int ktc = kt < kt_count ? kt : 0;  // tiles past the end re-read tile 0 into an unused stage
-#pragma unroll
-  for (int i = 0; i < DS::kADma; ++i) {
-    const int blk = wave * DS::kADma + i;  // 1 KiB = 4 rows
-    const int row = 4 * blk + (lane >> 4);
-    const int chunk = (lane & 15) ^ (row & 15);
-    int off = row * k + ktc * kTileCols + chunk * 16;
-    // binary padding weights are +1, not 0: columns past k must read as zero
-    // codes, so their chunk is sent past the descriptor (which returns zeros)
-    // instead of into the next token's row
-    if (WB == 1 && ktc * kTileCols + chunk * 16 >= k) off = kPastDescriptor;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, BITLINEAR_LDS(stage + blk * 1024), 16, off, 0, 0, 0);
-  }
-  if (WB == 1) {
-    const int bt = (kt_count + 1) / 2;
-    for (int i = wave; i < BN / 32; i += kThreads / 64) {
-      const int rbl = 2 * i + (lane >> 5);
-      const int off = (rbl * bt + (ktc >> 1)) * kBinTileBytes + (ktc & 1) * kBinStepBytes + (lane & 31) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, BITLINEAR_LDS(stage + DS::kABytes + i * 1024), 16, off, 0, 0, 0);
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < DS::kBDma; ++i) {
-    const int rbl = wave * DS::kBDma + i;
-    if (SWIGLU) {
-      const int src = ((rbl >> 2) << 1) | (rbl & 1);  // row block of the features
-      const int off = (src * kt_count + ktc) * kTileBytes + lane * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((rbl & 2) ? u_rsrc : b_rsrc,
-                                               BITLINEAR_LDS(stage + DS::kABytes + rbl * 1024), 16, off, 0, 0, 0);
-    } else {
-      const int off = (rbl * kt_count + ktc) * kTileBytes + lane * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, BITLINEAR_LDS(stage + DS::kABytes + rbl * 1024), 16, off, 0, 0, 0);
-    }
-  }
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(t.x, t.y, t.z, t.w);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -372,41 +322,51 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// weight operand of MFMA step q from a lane's slots (BREGS 16-byte slots per 32-row block)
+template <int WB>
+__device__ __forceinline__ v4i weight_operand(const uint4* s, int q) {
+  if (WB == 1) {
+    const uint4 v = s[0];
+    const uint32_t w = (q >> 1) == 0 ? v.x : (q >> 1) == 1 ? v.y : (q >> 1) == 2 ? v.z : v.w;
+    return expand_binary(w, q & 1);
+  }
+  const uint4 v = s[q >> 2];
+  const uint32_t w = (q & 3) == 0 ? v.x : (q & 3) == 1 ? v.y : (q & 3) == 2 ? v.z : v.w;
+  return expand_ternary(w);
+}
+
 // SWIGLU: packed_b / gamma_p are the gate projection, packed_u / gamma_u the
-// up projection (same [n][k] shape, n = features); the workgroup covers
-// BN / 2 features and writes h = silu(y_gate) * y_up to y [m][n] (acc_out, if
-// set, is [m][2n]: gate accumulators, then up accumulators).
+// up projection (both [n][k], n = features); a wave's first NB / 2 blocks are
+// gate rows and its last NB / 2 the up rows of the same features, so the
+// workgroup covers BN / 2 features and writes h = silu(y_gate) * y_up to
+// y [m][n] (acc_out, if set, is [m][2n]: gate accumulators, then up).
 //
 // SPLIT: the grid holds ceil(kt_count / kt_per) k-slices of every output tile
 // (slice-major); a workgroup walks k-steps [slice * kt_per, ...) and adds its
 // partial sums, exact in int32, to split_acc with atomics (zeroed before,
 // converted by split_finish_kernel after).
-template <int BM, int BN, int WM, int WN, int S, int OCC, bool SWIGLU = false, int WB = 2, bool SPLIT = false>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* __restrict__ packed_b,
-                                                               const float* __restrict__ gamma_p, Dequant dq, int64_t n,
-                                                               int64_t k, int kt_count, const int8_t* __restrict__ xq,
-                                                               const float* __restrict__ amax, int64_t m,
-                                                               int mt_count, int nt_count, float* __restrict__ y,
-                                                               int32_t* __restrict__ acc_out,
-                                                               const uint8_t* __restrict__ packed_u,
-                                                               const float* __restrict__ gamma_u, int kt_per = 0,
-                                                               int32_t* __restrict__ split_acc = nullptr) {
+template <int MB, int NB, int WM, int WN, int OCC, int WB = 2, bool SWIGLU = false, bool SPLIT = false>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
+    const uint8_t* __restrict__ packed_b, const float* __restrict__ gamma_p, Dequant dq, int64_t n, int64_t k,
+    int kt_count, const int8_t* __restrict__ xq, const float* __restrict__ amax, int64_t m, int mt_count,
+    int nt_count, float* __restrict__ y, int32_t* __restrict__ acc_out, const uint8_t* __restrict__ packed_u,
+    const float* __restrict__ gamma_u, int kt_per, int32_t* __restrict__ split_acc) {
   static_assert(WM * WN == kThreads / 64, "4 waves");
-  static_assert(S >= 2 && S <= 4, "2..4 stages");
-  static_assert(WB == 2 || (S == 2 && !SWIGLU), "binary weights: two stages, plain epilogue");
+  static_assert(WB == 2 || !SWIGLU, "binary weights: plain epilogue");
   static_assert(!(SPLIT && SWIGLU), "k-slices: plain epilogue only");
-  using DS = DmaShape<BM, BN, WB>;
-  constexpr int TB = wtile_bytes<WB>();
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int MB = TM / 32, NB = TN / 32;
-  static_assert(MB >= 1 && NB >= 1 && TM % 32 == 0 && TN % 32 == 0 && BN % 64 == 0, "tile shape");
   static_assert(!SWIGLU || NB % 2 == 0, "gate and up blocks pair up inside a wave");
-  constexpr int FB = SWIGLU ? BN / 2 : BN;  // output columns (features) per workgroup
+  constexpr int BM = WM * MB * 32;
+  constexpr int BN = WN * NB * 32;
+  constexpr int FB = SWIGLU ? BN / 2 : BN;          // output columns (features) per workgroup
+  constexpr int kStage = BM * kTileCols;            // activation bytes per stage
+  constexpr int kDma = BM / 16;                     // 1 KiB copies per wave per stage
+  constexpr int BREGS = WB == 1 ? 1 : 2;            // 16-byte slots per 32-row block per step
+  constexpr int NBH = SWIGLU ? NB / 2 : NB;         // 32-row blocks per wave and matrix
 
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[DS::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[DS::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? DS::kStage : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? DS::kStage : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
+  __shared__ __attribute__((aligned(16))) float scale_s[BM];
+  __shared__ __attribute__((aligned(16))) float scale_u[SWIGLU ? BM : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -424,13 +384,82 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
     kt_begin = slice * kt_per;
     kt_end = kt_begin + kt_per < kt_count ? kt_begin + kt_per : kt_count;
   }
+  // XCD-aware order: the token tiles of one weight tile run on one XCD and share its L2
   // (with SPLIT and total % 8 == 0 the hardware XCD of a workgroup is still id % 8)
   if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
   const int nt = id / mt_count, mt = id - nt * mt_count;
   const int64_t m0 = static_cast<int64_t>(mt) * BM;
-  const int64_t n0 = static_cast<int64_t>(nt) * FB;
-  const int64_t rb0 = n0 / kTileRows;
+  const int64_t f0 = static_cast<int64_t>(nt) * FB;
+  const int64_t rb0 = f0 / kTileRows;
   const int64_t rb_count = row_blocks(n);
+
+  // per-token output scale gamma * a'[t] / 127 (one per matrix), staged once
+  if (tid < BM) {
+    const int64_t t = m0 + tid;
+    scale_s[tid] = t < m ? token_scale(gamma_p, dq, amax, t) : 0.0f;
+    if (SWIGLU) scale_u[tid] = t < m ? *gamma_u * amax[t] / 127.0f : 0.0f;
+  }
+
+  // operand descriptors: this workgroup's token rows and weight row blocks
+  const int64_t rows_here = m - m0 < BM ? m - m0 : BM;
+  const int64_t rbs_here = rb_count - rb0 < FB / kTileRows ? rb_count - rb0 : FB / kTileRows;
+  const int row_tiles = WB == 1 ? (kt_count + 1) / 2 : kt_count;  // 1 KiB tiles per row block
+  const int64_t row_bytes = static_cast<int64_t>(row_tiles) * kTileBytes;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(xq + m0 * k), 0, static_cast<int>(rows_here * k), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed_b + rb0 * row_bytes), 0, static_cast<int>(rbs_here * row_bytes), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t u_rsrc = SWIGLU ? __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed_u + rb0 * row_bytes), 0, static_cast<int>(rbs_here * row_bytes), kRawBufferWord3)
+                                               : b_rsrc;
+  const int k32 = static_cast<int>(k);
+
+  // activation copies: copy i of this wave moves rows 4 * (wave * kDma + i) + lane / 16,
+  // stored chunk lane % 16 = logical chunk (lane % 16) ^ (row % 16)
+  int a_src[kDma];
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    const int row = 4 * (wave * kDma + i) + (lane >> 4);
+    a_src[i] = row * k32 + (((lane & 15) ^ (row & 15)) << 4);
+  }
+  // (the whole offset goes in the range-checked part: a chunk past the end
+  // of the last token row reads zero instead of the memory beyond it)
+  auto issue_a = [&](uint8_t* stage, int kt) {
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) {
+      int off = a_src[i] + kt * kTileCols;
+      if (WB == 1) {  // binary padding weights are +1: columns past k must read as zero codes
+        const int col = kt * kTileCols + (((lane & 15) ^ ((4 * (wave * kDma + i) + (lane >> 4)) & 15)) << 4);
+        if (col >= k32) off = kOffPastDescriptor;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, BITLINEAR_LDS(stage + (wave * kDma + i) * 1024), 16, off, 0, 0,
+                                               0);
+    }
+  };
+
+  // weight loads: 32-row block nb of the wave, lane row l32, half h
+  int b_src[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int blk = wn * NBH + (SWIGLU ? nb % NBH : nb);  // 32-row block inside the workgroup (per matrix)
+    const int rbl = 2 * blk + (l32 >> 4);                 // row block inside the descriptor
+    b_src[nb] = rbl * row_tiles * kTileBytes + (l32 & 15) * 16 + (WB == 1 ? 256 * h : 512 * h);
+  }
+  const int b_step = WB == 1 ? kBinStepBytes : kTileBytes;  // bytes of a row block per k-step
+  auto issue_b = [&](uint4 (&br)[NB][BREGS], int kt) {
+    const int soff = __builtin_amdgcn_readfirstlane(kt * b_step);  // uniform: the k-step's offset in a row block
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const __amdgpu_buffer_rsrc_t r = (SWIGLU && nb >= NBH) ? u_rsrc : b_rsrc;
+#pragma unroll
+      for (int j = 0; j < BREGS; ++j) br[nb][j] = load_b128(r, b_src[nb] + 256 * j, soff);
+    }
+  };
+
+  // LDS offsets of the lane's activation chunk for each MFMA step (token block 0, stage 0)
+  int a_off[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) a_off[q] = (wm * MB * 32 + l32) * kTileCols + (((8 * h + q) ^ (l32 & 15)) << 4);
 
   v16i acc[MB][NB];
 #pragma unroll
@@ -438,120 +467,80 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v16i{};
 
-  // per-lane LDS offsets
-  const int a_row0 = wm * TM + l32;                                   // + mb * 32; row % 16 == l32 % 16
-  const int a_x = (l32 & 15) ^ h;                                     // swizzle key with the lane's half folded in
-  const int b_row = wn * TN + l32;                                    // + nb * 32
-  const int b_off = DS::kABytes + slot_offset<WB>(b_row);              // + nb * 2 tiles + g * 16 slots
-
-  // operands of one 64-column group: NB weight slots and 2 x MB activation chunks
-  struct Ops {
-    uint4 slot[NB];
-    v4i a[2][MB];
+  // The activation operands of step q + 1 are read while step q multiplies;
+  // scheduling barriers keep that order, so at most two steps' operands are
+  // live next to the accumulators and the weight slots.
+  auto read_a = [&](const uint8_t* st, int q, v4i (&a)[MB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i*>(st + a_off[q] + mb * 32 * kTileCols);
   };
-  auto read_ops = [&](const uint8_t* st, int g, Ops& o) {
+  auto mul = [&](const v4i (&a)[MB], const uint4 (&br)[NB][BREGS], int q) {
+    v4i b[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o.slot[nb] = read_slot<WB>(st + b_off + nb * 2 * TB + group_offset<WB>(g), h);
+    for (int nb = 0; nb < NB; ++nb) b[nb] = weight_operand<WB>(br[nb], q);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int chunk = (4 * g + 2 * half) ^ a_x;  // logical chunk 4g + 2 half + h, swizzled by row % 16
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        o.a[half][mb] = *reinterpret_cast<const v4i*>(st + (a_row0 + mb * 32) * kTileCols + chunk * 16);
+        acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+  };
+  auto compute = [&](const uint8_t* st, const uint4 (&br)[NB][BREGS]) {
+    v4i a0[MB], a1[MB];
+    read_a(st, 0, a0);
+#pragma unroll
+    for (int q = 0; q < 8; q += 2) {
+      read_a(st, q + 1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(a0, br, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q + 2 < 8) read_a(st, q + 2, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(a1, br, q + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto math = [&](const Ops& o, int g) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      v4i b[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[nb] = slot_operand<WB>(o.slot[nb], g, half, h);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[half][mb], b[nb], acc[mb][nb], 0, 0, 0);
-    }
-  };
-  // software-pipelined over the tile's four 64-column groups: the operands
-  // of group g + 1 are read from LDS while group g is on the matrix cores
-  // (scheduling barriers keep that order)
-  auto compute = [&](const uint8_t* st) {
-    Ops o0, o1;
-    read_ops(st, 0, o0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_ops(st, 1, o1);
-    __builtin_amdgcn_sched_barrier(0);
-    math(o0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_ops(st, 2, o0);
-    __builtin_amdgcn_sched_barrier(0);
-    math(o1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_ops(st, 3, o1);
-    __builtin_amdgcn_sched_barrier(0);
-    math(o0, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    math(o1, 3);
-  };
 
-  // per-token output scale gamma * a'[t] / 127, staged once (one per matrix)
-  __shared__ float scale_s[BM];
-  __shared__ float scale_u[SWIGLU ? BM : 1];
-  if (tid < BM) {
-    const int64_t t = m0 + tid;
-    scale_s[tid] = t < m ? token_scale(gamma_p, dq, amax, t) : 0.0f;
-    if (SWIGLU) scale_u[tid] = t < m ? *gamma_u * amax[t] / 127.0f : 0.0f;
-  }
-  lds_barrier();
-
-  // operand descriptors: this workgroup's token rows and weight row blocks
-  const int64_t rows_here = m - m0 < BM ? m - m0 : BM;
-  const int64_t rbs_here = rb_count - rb0 < FB / kTileRows ? rb_count - rb0 : FB / kTileRows;
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(xq + m0 * k), 0, static_cast<int>(rows_here * k), kBufferWord3);
-  const int64_t row_bytes = WB == 1 ? static_cast<int64_t>((kt_count + 1) / 2) * kBinTileBytes
-                                    : static_cast<int64_t>(kt_count) * kTileBytes;  // one row block's weights
-  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(packed_b + rb0 * row_bytes), 0, static_cast<int>(rbs_here * row_bytes), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t u_rsrc = SWIGLU ? __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(packed_u + rb0 * kt_count * kTileBytes), 0,
-      static_cast<int>(rbs_here * kt_count * kTileBytes), kBufferWord3) : b_rsrc;
-  const int k32 = static_cast<int>(k);
-
-  // prologue: tiles 0 .. S-2 in flight (k-slice: relative to kt_begin; a tile
-  // past the slice re-reads its first tile into a stage nothing reads)
-  auto tile_at = [&](int kt) { return SPLIT ? (kt < kt_end ? kt : kt_begin) : kt; };
-  issue_tile<BM, BN, SWIGLU, WB>(st0, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, tile_at(kt_begin), wave, lane);
-  if (S > 2) issue_tile<BM, BN, SWIGLU, WB>(st1, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, tile_at(kt_begin + 1), wave, lane);
-  if (S > 3) issue_tile<BM, BN, SWIGLU, WB>(st2, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, tile_at(kt_begin + 2), wave, lane);
-
-  // one pipeline step: tile kt sits in stage `cur`; tile kt + S - 1 goes to `nxt`
-  auto step = [&](int kt, uint8_t* cur, uint8_t* nxt) {
-    wait_vmcnt<(S - 2) * DS::kDma>();
+  // one step ahead: copies of step kt + 1 go out while step kt is multiplied;
+  // the wait at the top of a step covers the wave's own copies, the barrier
+  // everyone's (and that every wave is done with the stage about to be refilled)
+  // (steps go in pairs, stage 0 then stage 1, with the same code on every
+  // trip; an odd last step runs after the loop)
+  uint4 b0[NB][BREGS], b1[NB][BREGS];
+  issue_a(st0, kt_begin);
+  issue_b(b0, kt_begin);
+  int kt = kt_begin;
+  for (; kt + 1 < kt_end; kt += 2) {
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    issue_tile<BM, BN, SWIGLU, WB>(nxt, a_rsrc, b_rsrc, u_rsrc, k32, kt_count, tile_at(kt + S - 1), wave, lane);
-    compute(cur);
-  };
-  for (int kt = kt_begin; kt < kt_end; kt += S) {
-    step(kt, st0, S == 2 ? st1 : S == 3 ? st2 : st3);
-    if (kt + 1 < kt_end) step(kt + 1, st1, S == 2 ? st0 : S == 3 ? st0 : st0);
-    if (S > 2 && kt + 2 < kt_end) step(kt + 2, st2, S == 3 ? st1 : st1);
-    if (S > 3 && kt + 3 < kt_end) step(kt + 3, st3, st2);
+    issue_a(st1, kt + 1);
+    issue_b(b1, kt + 1);
+    compute(st0, b0);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < kt_end) {  // uniform
+      issue_a(st0, kt + 2);
+      issue_b(b0, kt + 2);
+    }
+    compute(st1, b1);
   }
-  wait_vmcnt<0>();
+  if (kt < kt_end) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    compute(st0, b0);
+  }
 
+  // 32 x 32 block layout: element r of lane l is token 8 * (r / 4) + 4 * (l / 32) + r % 4, row l % 32
+  const int tw = wm * MB * 32;  // the wave's first token inside the tile
   if (SPLIT) {
-    // partial sums of this k-slice (multiples of 64, shifted exactly)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t t = m0 + wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t t = m0 + tw + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (t >= m) continue;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const int64_t j = n0 + wn * TN + nb * 32 + l32;
+          const int64_t j = f0 + (wn * NB + nb) * 32 + l32;
           if (j < n) atomicAdd(&split_acc[t * n + j], acc[mb][nb][r] >> kWeightShift);
         }
       }
@@ -560,22 +549,21 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
   }
 
   if (SWIGLU) {
-    // blocks nb (gate) and nb + 1 (up) hold the same 32 features; the lane's
-    // elements line up, so h = silu(g) * u is formed in registers
+    // blocks nb (gate) and nb + NBH (up) hold the same 32 features: h = silu(g) * u in registers
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int tl = wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int tl = tw + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         const int64_t t = m0 + tl;
         if (t >= m) continue;
         const float sg = scale_s[tl], su = scale_u[tl];
 #pragma unroll
-        for (int nb = 0; nb < NB; nb += 2) {
-          const int64_t j = n0 + 16 * (wn * NB + nb) + l32;
+        for (int nb = 0; nb < NBH; ++nb) {
+          const int64_t j = f0 + (wn * NBH + nb) * 32 + l32;
           if (j < n) {
             const int vg = acc[mb][nb][r] >> kWeightShift;
-            const int vu = acc[mb][nb + 1][r] >> kWeightShift;
+            const int vu = acc[mb][nb + NBH][r] >> kWeightShift;
             const float g = static_cast<float>(vg) * sg;
             const float u = static_cast<float>(vu) * su;
             y[t * n + j] = g * u / (1.0f + expf(-g));
@@ -589,21 +577,27 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(const uint8_t* 
     }
     return;
   }
+
+  // plain epilogue: y = (acc >> 6) * (gamma * a'[t] / 127), or with the
+  // row's own scale; rows and tokens of a full tile need no bounds checks
+  const bool full = m0 + BM <= m && f0 + FB <= n;
+  float* yl = y + (m0 + tw + 4 * h) * n + f0 + wn * NB * 32 + l32;
+  int32_t* al = acc_out ? acc_out + (m0 + tw + 4 * h) * n + f0 + wn * NB * 32 + l32 : nullptr;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int tl = wm * TM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      const int64_t t = m0 + tl;
-      if (t >= m) continue;
+      const int tr = mb * 32 + 8 * (r >> 2) + (r & 3);  // token of the lane's element, less 4h
+      const int tl = tw + tr + 4 * h;
+      if (!full && m0 + tl >= m) continue;
+      const float sc = scale_s[tl];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int64_t j = n0 + wn * TN + nb * 32 + l32;
-        if (j < n) {
-          const int v = acc[mb][nb][r] >> kWeightShift;
-          y[t * n + j] = static_cast<float>(v) * out_scale(dq, scale_s[tl], j);
-          if (acc_out) acc_out[t * n + j] = v;
-        }
+        if (!full && f0 + (wn * NB + nb) * 32 + l32 >= n) continue;
+        const int v = acc[mb][nb][r] >> kWeightShift;
+        const int64_t o = static_cast<int64_t>(tr) * n + nb * 32;
+        yl[o] = static_cast<float>(v) * out_scale(dq, sc, f0 + (wn * NB + nb) * 32 + l32);
+        if (al) al[o] = v;
       }
     }
   }
@@ -694,22 +688,27 @@ int slice_steps(int64_t tiles, int occ, int kt) {
   return (kt + ks - 1) / ks;
 }
 
-template <int BM, int BN, int WM, int WN, int S, int OCC, int WB = 2>
-hipError_t launch_dma(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
-                      const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
-  static_assert(S * DmaStageBytes(BM, BN, WB) <= 163840, "LDS per workgroup");  // OCC: register-budget hint
+// Launch of the matrix-core kernel for one configuration; the k extent is
+// split when the output tiles fill at most a quarter of the resident slots.
+template <int MB, int NB, int WM, int WN, int OCC, int WB = 2>
+hipError_t launch_mfma(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
+                       const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
+  constexpr int BM = WM * MB * 32, BN = WN * NB * 32;
+  static_assert(2 * BM * kTileCols + 2 * BM * 4 <= 163840 / OCC, "LDS per workgroup");
   // 32-bit buffer offsets: BM rows of at most 2^18 codes, BN / 16 row blocks of at most 1024 tiles
-  static_assert(static_cast<int64_t>(BM) << 18 <= 0x7fffffff && static_cast<int64_t>(BN / kTileRows) * 1024 * kTileBytes <= 0x7fffffff,
+  static_assert(static_cast<int64_t>(BM) << 18 <= 0x7fffffff &&
+                    static_cast<int64_t>(BN / kTileRows) * 1024 * kTileBytes <= 0x7fffffff,
                 "buffer offsets fit 31 bits");
   const int kt = static_cast<int>(k_tiles(k));
   const int64_t mt = (m + BM - 1) / BM;
   const int64_t ntl = (n + BN - 1) / BN;
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int kt_per = slice_steps(mt * ntl, OCC, kt);
+  const uint8_t* p = static_cast<const uint8_t*>(packed);
   if (kt_per == 0) {
-    gemm_dma_kernel<BM, BN, WM, WN, S, OCC, false, WB><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
-        static_cast<const uint8_t*>(packed), gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt),
-        static_cast<int>(ntl), y, acc, nullptr, nullptr);
+    gemm_mfma_kernel<MB, NB, WM, WN, OCC, WB><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+        p, gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl), y, acc, nullptr, nullptr,
+        0, nullptr);
     return hipGetLastError();
   }
   // the int32 sums go to acc when the caller wants them, else into y's memory
@@ -718,50 +717,69 @@ hipError_t launch_dma(const void* packed, const float* gamma, Dequant dq, int64_
   const int64_t count = m * n;
   const unsigned fill_grid = static_cast<unsigned>(count / 256 + 1 < 2048 ? count / 256 + 1 : 2048);
   split_zero_kernel<<<fill_grid, 256, 0, s>>>(sums, count);
-  gemm_dma_kernel<BM, BN, WM, WN, S, OCC, false, WB, true><<<dim3(static_cast<unsigned>(mt * ntl * slices)), kThreads, 0, s>>>(
-      static_cast<const uint8_t*>(packed), gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt),
-      static_cast<int>(ntl), y, acc, nullptr, nullptr, kt_per, sums);
+  gemm_mfma_kernel<MB, NB, WM, WN, OCC, WB, false, true><<<dim3(static_cast<unsigned>(mt * ntl * slices)), kThreads, 0,
+                                                            s>>>(
+      p, gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl), y, acc, nullptr, nullptr,
+      kt_per, sums);
   split_finish_kernel<<<fill_grid, 256, 0, s>>>(sums, y, gamma, dq, amax, m, n);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int S, int OCC>
-hipError_t launch_dma_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
-                             int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
-                             int32_t* acc, hipStream_t s) {
-  static_assert(S * DmaStageBytes(BM, BN) <= 163840, "LDS per workgroup");
-  static_assert(static_cast<int64_t>(BM) << 18 <= 0x7fffffff && static_cast<int64_t>(BN / kTileRows) * 1024 * kTileBytes <= 0x7fffffff,
-                "buffer offsets fit 31 bits");
+template <int MB, int NB, int WM, int WN, int OCC>
+hipError_t launch_mfma_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
+                              int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
+                              int32_t* acc, hipStream_t s) {
+  constexpr int BM = WM * MB * 32, FB = WN * NB * 16;
   const int kt = static_cast<int>(k_tiles(k));
   const int64_t mt = (m + BM - 1) / BM;
-  const int64_t ntl = (f + BN / 2 - 1) / (BN / 2);
+  const int64_t ntl = (f + FB - 1) / FB;
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
-  gemm_dma_kernel<BM, BN, WM, WN, S, OCC, true><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+  gemm_mfma_kernel<MB, NB, WM, WN, OCC, 2, true><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
       static_cast<const uint8_t*>(packed_g), gamma_g, kTokenDequant, f, k, kt, xq, amax, m, static_cast<int>(mt),
-      static_cast<int>(ntl), h, acc, static_cast<const uint8_t*>(packed_u), gamma_u);
+      static_cast<int>(ntl), h, acc, static_cast<const uint8_t*>(packed_u), gamma_u, 0, nullptr);
   return hipGetLastError();
 }
 
-// Tile choice, from measurements on MI355X of every (tile, stages,
-// workgroups per CU) candidate on the 8B- and 70B-shaped layers: wide weight
-// tiles with two resident workgroups per CU for wide matrices, their four
-// waves side by side along n (each wave 64 tokens x 64 rows, so every
-// expanded weight operand feeds two matrix-core steps; about 5% faster than
-// 2 x 2 waves); 64 x 192 for
-// mid widths; small 64 x 64 tiles with three workgroups per CU otherwise
-// (enough workgroups to fill 256 CUs, and one workgroup's barrier and copy
-// latency hidden behind the others' matrix-core work).
-enum DmaConfig { kWide = 0, kMid = 1, kSmall = 2 };
+// Configurations of the matrix-core kernel: (token blocks, row blocks) per
+// wave and the waves' layout.  Tile choice: see choose_mfma.
+enum MfmaConfig {
+  kT128x256 = 0,  // MB 4, NB 2, 1 x 4 waves
+  kT64x256 = 1,   // MB 2, NB 2, 1 x 4
+  kT64x128 = 2,   // MB 2, NB 1, 1 x 4
+  kT128x128 = 3,  // MB 2, NB 2, 2 x 2
+  kT128x128b = 4, // MB 4, NB 1, 1 x 4
+  kT64x128b = 5,  // MB 1, NB 2, 2 x 2
+  kT128x64 = 6,   // MB 2, NB 1, 2 x 2
+};
 
 #ifndef BITLINEAR_GEMM_FORCE
 #define BITLINEAR_GEMM_FORCE -1
 #endif
 
-DmaConfig choose_dma(int64_t m, int64_t n) {
-  if (BITLINEAR_GEMM_FORCE >= 0) return static_cast<DmaConfig>(BITLINEAR_GEMM_FORCE);
-  if (n >= 16384) return kWide;
-  if (m > 64 && n >= 6144) return kMid;
-  return kSmall;
+// Measured on MI355X over the 8B- and 70B-shaped matrices (every config at
+// every shape): 128 x 256 for more than 64 tokens on wide matrices (512 x
+// 28672 x 4096: 57.0 us against 59.3 for 64 x 128 and 60.4 for 64 x 256);
+// 64 x 128 everywhere else (512 x 4096 x 14336: 35.4 us, the next best 38.1;
+// 64 x 57344 x 8192: 39.0 us against 40.3 for 64 x 256).
+MfmaConfig choose_mfma(int64_t m, int64_t n) {
+  if (BITLINEAR_GEMM_FORCE >= 0) return static_cast<MfmaConfig>(BITLINEAR_GEMM_FORCE);
+  if (m > 64 && n >= 16384) return kT128x256;
+  return kT64x128;
+}
+
+template <int WB>
+hipError_t launch_mfma_any(MfmaConfig c, const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k,
+                           const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
+  switch (c) {
+    case kT128x256: return launch_mfma<4, 2, 1, 4, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+    case kT64x256: return launch_mfma<2, 2, 1, 4, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+    case kT64x128: return launch_mfma<2, 1, 1, 4, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+    case kT128x128: return launch_mfma<2, 2, 2, 2, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+    case kT128x128b: return launch_mfma<4, 1, 1, 4, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+    case kT64x128b: return launch_mfma<1, 2, 2, 2, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+    case kT128x64: return launch_mfma<2, 1, 2, 2, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -774,27 +792,18 @@ hipError_t launch_gemm_swiglu(const void* packed_g, const float* gamma_g, const 
                               int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
                               int32_t* acc, hipStream_t s) {
   if (!gemm_swiglu_supported(k, xq)) return hipErrorInvalidValue;
-  if (f >= 8192)
-    return launch_dma_swiglu<64, 256, 2, 2, 2, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
-  return launch_dma_swiglu<64, 128, 2, 2, 2, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
+  if (m > 64)
+    return launch_mfma_swiglu<4, 2, 1, 4, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
+  return launch_mfma_swiglu<2, 2, 1, 4, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
 }
 
 hipError_t launch_gemm_ex(const void* packed, bool binary, const float* gamma, Dequant dq, int64_t n, int64_t k,
                           const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   const bool vec = (k % 16 == 0) && (reinterpret_cast<uintptr_t>(xq) % 16 == 0);
-  if (vec && binary) {  // two stages: the binary tiles' copies are not the same count on every wave
-    switch (choose_dma(m, n)) {
-      case kWide: return launch_dma<64, 256, 1, 4, 2, 2, 1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-      case kMid: return launch_dma<64, 192, 2, 2, 2, 2, 1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-      case kSmall: return launch_dma<64, 64, 2, 2, 2, 3, 1>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-    }
-  }
   if (vec) {
-    switch (choose_dma(m, n)) {
-      case kWide: return launch_dma<64, 256, 1, 4, 2, 2>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-      case kMid: return launch_dma<64, 192, 2, 2, 2, 2>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-      case kSmall: return launch_dma<64, 64, 2, 2, 3, 3>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-    }
+    const MfmaConfig c = choose_mfma(m, n);
+    return binary ? launch_mfma_any<1>(c, packed, gamma, dq, n, k, xq, amax, m, y, acc, s)
+                  : launch_mfma_any<2>(c, packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
   }
   const Cand c = choose(m, n);
 #define BITLINEAR_GEMM_CASE(BM_, BN_, WM_, WN_)                                                            \

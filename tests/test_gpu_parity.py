@@ -76,7 +76,7 @@ def test_native_library_is_loaded(blq):
 
 @pytest.mark.parametrize("m,k", [(1, 1), (1, 7), (3, 255), (2, 256), (5, 257), (1, 2048), (4, 2560),
                                  (9, 4096), (16, 6912), (1, 28672), (64, 8192), (512, 4096),
-                                 (3, 40000)])
+                                 (3, 40000), (65, 1000), (77, 2056), (100, 14336), (66, 28672)])
 def test_quant_act_parity(blq, m, k):
     log("quant m=%d k=%d" % (m, k))
     x = synth.activations_bf16(m * 7 + k, m, k, 0.01)
