@@ -322,6 +322,42 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Deeper rings (S > 2 stages) copy both operands with buffer-to-LDS loads
+// written as inline assembly, so the compiler tracks none of them: it would
+// otherwise assume any outstanding copy may write the stage being read and
+// wait for all of them before every LDS read.  The kernel waits for its own
+// copies instead (copies_landed), in the same assembly block as the barrier,
+// with a memory clobber so no LDS read moves above it.  These copies have no
+// output registers.
+typedef unsigned v4u_d __attribute__((ext_vector_type(4)));
+
+// raw buffer descriptor (32-bit untyped records, no stride) of `bytes` bytes at `base`
+__device__ __forceinline__ v4u_d raw_descriptor(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4u_d r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bytes));
+  r.w = kRawBufferWord3;
+  return r;
+}
+
+// 16 bytes per lane from byte `voff` of the buffer into LDS at lds_addr + 16 * lane
+__device__ __forceinline__ void lds_copy16(v4u_d rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+
+// wait until at most N of the wave's copies are outstanding, then the workgroup barrier
+template <int N>
+__device__ __forceinline__ void copies_landed() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(BITLINEAR_LDS(p)));
+}
+
 // weight operand of MFMA step q from a lane's slots (BREGS 16-byte slots per 32-row block)
 template <int WB>
 __device__ __forceinline__ v4i weight_operand(const uint4* s, int q) {
@@ -345,7 +381,7 @@ __device__ __forceinline__ v4i weight_operand(const uint4* s, int q) {
 // (slice-major); a workgroup walks k-steps [slice * kt_per, ...) and adds its
 // partial sums, exact in int32, to split_acc with atomics (zeroed before,
 // converted by split_finish_kernel after).
-template <int MB, int NB, int WM, int WN, int OCC, int WB = 2, bool SWIGLU = false, bool SPLIT = false>
+template <int MB, int NB, int WM, int WN, int S, int OCC, int WB = 2, bool SWIGLU = false, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
     const uint8_t* __restrict__ packed_b, const float* __restrict__ gamma_p, Dequant dq, int64_t n, int64_t k,
     int kt_count, const int8_t* __restrict__ xq, const float* __restrict__ amax, int64_t m, int mt_count,
@@ -363,8 +399,19 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
   constexpr int BREGS = WB == 1 ? 1 : 2;            // 16-byte slots per 32-row block per step
   constexpr int NBH = SWIGLU ? NB / 2 : NB;         // 32-row blocks per wave and matrix
 
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
+  static_assert(S >= 2 && S <= 6, "2..6 stages");
+  // S = 2: activations in two stage arrays (one per stage: the compiler tells
+  // their outstanding copies apart), weights in registers.  S > 2: a ring of
+  // S stages, each the activation tile followed by the weight tiles of the
+  // workgroup's row blocks, filled by untracked copies.
+  constexpr bool kRing = S > 2;
+  constexpr int TBS = WB == 1 ? kBinStepBytes : kTileBytes;           // one row block's bytes per k-step
+  constexpr int kStageBytes = kStage + (kRing ? (BN / kTileRows) * TBS : 0);
+  constexpr int kBDma = kRing ? (BN / kTileRows) * TBS / 1024 / 4 : 0;  // weight copies per wave per stage
+  static_assert(!kRing || (BN / kTileRows) * TBS % 4096 == 0, "weight copies split over the four waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kRing ? 16 : kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kRing ? 16 : kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing ? S * kStageBytes : 16];
   __shared__ __attribute__((aligned(16))) float scale_s[BM];
   __shared__ __attribute__((aligned(16))) float scale_u[SWIGLU ? BM : 4];
 
@@ -500,33 +547,116 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
     }
   };
 
-  // one step ahead: copies of step kt + 1 go out while step kt is multiplied;
-  // the wait at the top of a step covers the wave's own copies, the barrier
-  // everyone's (and that every wave is done with the stage about to be refilled)
-  // (steps go in pairs, stage 0 then stage 1, with the same code on every
-  // trip; an odd last step runs after the loop)
-  uint4 b0[NB][BREGS], b1[NB][BREGS];
-  issue_a(st0, kt_begin);
-  issue_b(b0, kt_begin);
-  int kt = kt_begin;
-  for (; kt + 1 < kt_end; kt += 2) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    issue_a(st1, kt + 1);
-    issue_b(b1, kt + 1);
-    compute(st0, b0);
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + 2 < kt_end) {  // uniform
-      issue_a(st0, kt + 2);
-      issue_b(b0, kt + 2);
+  // S - 1 steps in flight: the copies of step kt + S - 1 go out while step kt
+  // is multiplied.  At the top of a step each wave waits for its own copies
+  // of that step (the younger ones stay in flight), then the barrier covers
+  // everyone's and makes sure no wave still reads the stage about to be
+  // refilled.  The body is unrolled S times so the stages are compile-time
+  // offsets.
+  if constexpr (kRing) {
+    // untracked copies: descriptors as plain registers
+    const v4u_d a_desc = raw_descriptor(xq + m0 * k, rows_here * k);
+    const v4u_d b_desc = raw_descriptor(packed_b + rb0 * row_bytes, rbs_here * row_bytes);
+    const v4u_d u_desc = SWIGLU ? raw_descriptor(packed_u + rb0 * row_bytes, rbs_here * row_bytes) : b_desc;
+    const uint32_t ring0 = lds_address(ring);
+    // weight copy i of this wave: LDS row block d = wave * kBDma + i of the stage's weight region
+    // (ternary: one 1 KiB tile; binary: the 512-byte step halves of row blocks 2d and 2d + 1)
+    auto issue = [&](int u, int kt) {
+      const uint32_t base = ring0 + u * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) {
+        int off = a_src[i] + kt * kTileCols;
+        if (WB == 1) {
+          const int col = kt * kTileCols + (((lane & 15) ^ ((4 * (wave * kDma + i) + (lane >> 4)) & 15)) << 4);
+          if (col >= k32) off = kOffPastDescriptor;
+        }
+        lds_copy16(a_desc, off, base + (wave * kDma + i) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < kBDma; ++i) {
+        const int d = wave * kBDma + i;
+        if (WB == 1) {
+          const int rb = 2 * d + (lane >> 5);
+          lds_copy16(b_desc, rb * row_tiles * kTileBytes + kt * kBinStepBytes + (lane & 31) * 16,
+                     base + kStage + d * 1024);
+        } else if (SWIGLU) {
+          const bool up = d >= FB / kTileRows;  // uniform
+          const int rb = up ? d - FB / kTileRows : d;
+          lds_copy16(up ? u_desc : b_desc, (rb * row_tiles + kt) * kTileBytes + lane * 16, base + kStage + d * 1024);
+        } else {
+          lds_copy16(b_desc, (d * row_tiles + kt) * kTileBytes + lane * 16, base + kStage + d * 1024);
+        }
+      }
+    };
+    // LDS offset (inside a stage's weight region) of the lane's slot j for 32-row block nb
+    int b_lds[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int lblk = SWIGLU ? (nb < NBH ? wn * NBH + nb : FB / 32 + wn * NBH + nb - NBH) : wn * NB + nb;
+      b_lds[nb] = kStage + (2 * lblk + (l32 >> 4)) * TBS + ((l32 & 15) + (WB == 1 ? 16 : 32) * h) * 16;
     }
-    compute(st1, b1);
-  }
-  if (kt < kt_end) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    compute(st0, b0);
+    auto compute_ring = [&](int u) {
+      const uint8_t* st = ring + u * kStageBytes;
+      uint4 bc[NB][BREGS];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < BREGS; ++j) bc[nb][j] = *reinterpret_cast<const uint4*>(st + b_lds[nb] + 256 * j);
+      compute(st, bc);
+    };
+    constexpr int kPer = kDma + kBDma;  // copies per step and wave
+    static_assert((S - 2) * kPer < 64, "vmcnt range");
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u)
+      if (kt_begin + u < kt_end) issue(u, kt_begin + u);  // uniform
+    for (int kt0 = kt_begin; kt0 < kt_end; kt0 += S) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        const int kt = kt0 + u;
+        if (kt < kt_end) {  // uniform
+          // steps issued after this one: min(S - 2, kt_end - 1 - kt)
+          const int younger = kt_end - 1 - kt;
+          if (S > 5 && younger >= 4)
+            copies_landed<(S > 5 ? 4 : 0) * kPer>();
+          else if (S > 4 && younger >= 3)
+            copies_landed<(S > 4 ? 3 : 0) * kPer>();
+          else if (S > 3 && younger >= 2)
+            copies_landed<(S > 3 ? 2 : 0) * kPer>();
+          else if (younger >= 1)
+            copies_landed<kPer>();
+          else
+            copies_landed<0>();
+          if (kt + S - 1 < kt_end) issue((u + S - 1) % S, kt + S - 1);
+          compute_ring(u);
+        }
+      }
+    }
+  } else {
+    // two stages, weights in registers; steps go in pairs with the same code
+    // on every trip, an odd last step after the loop
+    uint4 b0[NB][BREGS], b1[NB][BREGS];
+    issue_a(st0, kt_begin);
+    issue_b(b0, kt_begin);
+    int kt = kt_begin;
+    for (; kt + 1 < kt_end; kt += 2) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      issue_a(st1, kt + 1);
+      issue_b(b1, kt + 1);
+      compute(st0, b0);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + 2 < kt_end) {  // uniform
+        issue_a(st0, kt + 2);
+        issue_b(b0, kt + 2);
+      }
+      compute(st1, b1);
+    }
+    if (kt < kt_end) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      compute(st0, b0);
+    }
   }
 
   // 32 x 32 block layout: element r of lane l is token 8 * (r / 4) + 4 * (l / 32) + r % 4, row l % 32
@@ -690,11 +820,12 @@ int slice_steps(int64_t tiles, int occ, int kt) {
 
 // Launch of the matrix-core kernel for one configuration; the k extent is
 // split when the output tiles fill at most a quarter of the resident slots.
-template <int MB, int NB, int WM, int WN, int OCC, int WB = 2>
+template <int MB, int NB, int WM, int WN, int S, int OCC, int WB = 2>
 hipError_t launch_mfma(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   constexpr int BM = WM * MB * 32, BN = WN * NB * 32;
-  static_assert(2 * BM * kTileCols + 2 * BM * 4 <= 163840 / OCC, "LDS per workgroup");
+  static_assert(S * (BM * kTileCols + (S > 2 ? BN * kTileBytes / kTileRows : 0)) + 2 * BM * 4 <= 163840 / OCC,
+                "LDS per workgroup");
   // 32-bit buffer offsets: BM rows of at most 2^18 codes, BN / 16 row blocks of at most 1024 tiles
   static_assert(static_cast<int64_t>(BM) << 18 <= 0x7fffffff &&
                     static_cast<int64_t>(BN / kTileRows) * 1024 * kTileBytes <= 0x7fffffff,
@@ -706,7 +837,7 @@ hipError_t launch_mfma(const void* packed, const float* gamma, Dequant dq, int64
   const int kt_per = slice_steps(mt * ntl, OCC, kt);
   const uint8_t* p = static_cast<const uint8_t*>(packed);
   if (kt_per == 0) {
-    gemm_mfma_kernel<MB, NB, WM, WN, OCC, WB><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+    gemm_mfma_kernel<MB, NB, WM, WN, S, OCC, WB><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
         p, gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl), y, acc, nullptr, nullptr,
         0, nullptr);
     return hipGetLastError();
@@ -717,15 +848,15 @@ hipError_t launch_mfma(const void* packed, const float* gamma, Dequant dq, int64
   const int64_t count = m * n;
   const unsigned fill_grid = static_cast<unsigned>(count / 256 + 1 < 2048 ? count / 256 + 1 : 2048);
   split_zero_kernel<<<fill_grid, 256, 0, s>>>(sums, count);
-  gemm_mfma_kernel<MB, NB, WM, WN, OCC, WB, false, true><<<dim3(static_cast<unsigned>(mt * ntl * slices)), kThreads, 0,
-                                                            s>>>(
+  gemm_mfma_kernel<MB, NB, WM, WN, S, OCC, WB, false, true><<<dim3(static_cast<unsigned>(mt * ntl * slices)), kThreads,
+                                                               0, s>>>(
       p, gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl), y, acc, nullptr, nullptr,
       kt_per, sums);
   split_finish_kernel<<<fill_grid, 256, 0, s>>>(sums, y, gamma, dq, amax, m, n);
   return hipGetLastError();
 }
 
-template <int MB, int NB, int WM, int WN, int OCC>
+template <int MB, int NB, int WM, int WN, int S, int OCC>
 hipError_t launch_mfma_swiglu(const void* packed_g, const float* gamma_g, const void* packed_u, const float* gamma_u,
                               int64_t f, int64_t k, const int8_t* xq, const float* amax, int64_t m, float* h,
                               int32_t* acc, hipStream_t s) {
@@ -734,33 +865,33 @@ hipError_t launch_mfma_swiglu(const void* packed_g, const float* gamma_g, const 
   const int64_t mt = (m + BM - 1) / BM;
   const int64_t ntl = (f + FB - 1) / FB;
   if (mt * ntl > 0x7fffffff) return hipErrorInvalidConfiguration;
-  gemm_mfma_kernel<MB, NB, WM, WN, OCC, 2, true><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+  gemm_mfma_kernel<MB, NB, WM, WN, S, OCC, 2, true><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
       static_cast<const uint8_t*>(packed_g), gamma_g, kTokenDequant, f, k, kt, xq, amax, m, static_cast<int>(mt),
       static_cast<int>(ntl), h, acc, static_cast<const uint8_t*>(packed_u), gamma_u, 0, nullptr);
   return hipGetLastError();
 }
 
-// Configurations of the matrix-core kernel: (token blocks, row blocks) per
-// wave and the waves' layout.  Tile choice: see choose_mfma.
+// Configurations of the matrix-core kernel.  Measured on MI355X over the 8B-
+// and 70B-shaped matrices, every candidate at every shape (us per launch):
+//   * 128 x 256, two stages, weights in registers (MB 4, NB 2, 1 x 4 waves)
+//     for more than 64 tokens on wide matrices: 512 x 28672 x 4096 57.0,
+//     against 59.3 for 64 x 128 and 60.4 for 64 x 256;
+//   * 64 x 128 with a ring of three stages (MB 2, NB 1, 1 x 4) otherwise:
+//     512 x 6144 x 4096 19.7, 512 x 4096 x 14336 35.8, 64 x 57344 x 8192
+//     40.5, 64 x 8192 x 28672 29.1 (k-sliced; 34.2 with two stages).
+//     Rings of four or six stages (one workgroup per CU) were no faster, nor
+//     were 64 x 256, 128 x 128 or 2 x 2-wave tiles: the small tiles are
+//     bound by the activation operand reads from LDS (1 KiB per MFMA, LDS
+//     active about 64% of the time), not by memory latency.
 enum MfmaConfig {
-  kT128x256 = 0,  // MB 4, NB 2, 1 x 4 waves
-  kT64x256 = 1,   // MB 2, NB 2, 1 x 4
-  kT64x128 = 2,   // MB 2, NB 1, 1 x 4
-  kT128x128 = 3,  // MB 2, NB 2, 2 x 2
-  kT128x128b = 4, // MB 4, NB 1, 1 x 4
-  kT64x128b = 5,  // MB 1, NB 2, 2 x 2
-  kT128x64 = 6,   // MB 2, NB 1, 2 x 2
+  kT128x256 = 0,  // MB 4, NB 2, 1 x 4 waves, 2 stages (weights in registers)
+  kT64x128 = 1,   // MB 2, NB 1, 1 x 4 waves, ring of 3 stages
 };
 
 #ifndef BITLINEAR_GEMM_FORCE
 #define BITLINEAR_GEMM_FORCE -1
 #endif
 
-// Measured on MI355X over the 8B- and 70B-shaped matrices (every config at
-// every shape): 128 x 256 for more than 64 tokens on wide matrices (512 x
-// 28672 x 4096: 57.0 us against 59.3 for 64 x 128 and 60.4 for 64 x 256);
-// 64 x 128 everywhere else (512 x 4096 x 14336: 35.4 us, the next best 38.1;
-// 64 x 57344 x 8192: 39.0 us against 40.3 for 64 x 256).
 MfmaConfig choose_mfma(int64_t m, int64_t n) {
   if (BITLINEAR_GEMM_FORCE >= 0) return static_cast<MfmaConfig>(BITLINEAR_GEMM_FORCE);
   if (m > 64 && n >= 16384) return kT128x256;
@@ -770,16 +901,8 @@ MfmaConfig choose_mfma(int64_t m, int64_t n) {
 template <int WB>
 hipError_t launch_mfma_any(MfmaConfig c, const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k,
                            const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
-  switch (c) {
-    case kT128x256: return launch_mfma<4, 2, 1, 4, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-    case kT64x256: return launch_mfma<2, 2, 1, 4, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-    case kT64x128: return launch_mfma<2, 1, 1, 4, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-    case kT128x128: return launch_mfma<2, 2, 2, 2, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-    case kT128x128b: return launch_mfma<4, 1, 1, 4, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-    case kT64x128b: return launch_mfma<1, 2, 2, 2, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-    case kT128x64: return launch_mfma<2, 1, 2, 2, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
-  }
-  return hipErrorInvalidValue;
+  if (c == kT128x256) return launch_mfma<4, 2, 1, 4, 2, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+  return launch_mfma<2, 1, 1, 4, 3, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
 }
 
 }  // namespace
@@ -793,8 +916,8 @@ hipError_t launch_gemm_swiglu(const void* packed_g, const float* gamma_g, const 
                               int32_t* acc, hipStream_t s) {
   if (!gemm_swiglu_supported(k, xq)) return hipErrorInvalidValue;
   if (m > 64)
-    return launch_mfma_swiglu<4, 2, 1, 4, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
-  return launch_mfma_swiglu<2, 2, 1, 4, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
+    return launch_mfma_swiglu<4, 2, 1, 4, 2, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
+  return launch_mfma_swiglu<2, 2, 1, 4, 2, 2>(packed_g, gamma_g, packed_u, gamma_u, f, k, xq, amax, m, h, acc, s);
 }
 
 hipError_t launch_gemm_ex(const void* packed, bool binary, const float* gamma, Dequant dq, int64_t n, int64_t k,
