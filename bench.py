@@ -3,23 +3,29 @@
 
 One step = one pass of the per-token path over every BitLinear of the
 workload, in layer order: bitlinear_quant_act (bf16 -> int8 codes + a') then
-bitlinear_forward (m <= 16) or bitlinear_forward_batched (m > 16) per matrix.
-The weights are packed once before timing (the one-time preparation step);
+bitlinear_forward (m <= 16) or bitlinear_forward_batched (m > 16) per matrix
+(decode at one or two tokens: the fused bitlinear_quant_forward).  The
+weights are packed once before timing (the one-time preparation step);
 packing is timed separately and reported under "pack".  The step is captured
 once into a HIP graph and replayed; inputs are resident in HBM and the
 weights of consecutive steps are not cache-resident (the stack is larger than
 the 256 MB last-level cache, or is replicated until it is).
+
+Default run: the largest configuration, the LLaMA-3-8B-shaped stack at 512
+tokens per matrix (7.1 T int8 operations per step), as the headline; then the
+same stack's decode at 1, 4 and 8 tokens on the same packed weights, each
+with its own rate and roofline under "extra_configs".
 
 Prints ONE JSON line:
   value        algorithmic bytes per step / step time (GB/s) for decode
                workloads, or 2*M*N*K per step / step time (TOPS) for the
                batched workload;
   roofline     the dominant kernel (forward) against HBM or int8 MFMA peak,
-               from HIP events around each of its launches;
+               from HIP events around graph replays of its launches;
   cpu_baseline the CPU oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload KEY] [--m M]
-Workloads: single2048, b2b_decode (default), l8b_decode, l8b_prefill, l70b_layer.
+Workloads: single2048, b2b_decode, l8b_decode, l8b_prefill (default), l70b_layer.
 """
 from __future__ import annotations
 
@@ -105,8 +111,10 @@ class Mat:
                  "gain", "gain_np", "name", "h", "ws", "s16_or")
 
 
-def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"):
-    """Generate, upload and pack every matrix; returns replicas x [Mat]."""
+def pack_weights(wl, torch, blq, oracle_quota, oracle_mod, variant="plain"):
+    """Generate, upload and pack every matrix of the workload once (the
+    one-time preparation step, timed on the device); the oracle re-derives the
+    codes of the first oracle_quota matrices.  Returns ([Mat], pack info)."""
     dev = torch.device("cuda")
     mats = []
     jobs = list(synth.iter_layer_matrices(wl))
@@ -146,23 +154,8 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             mat.layer, mat.j, mat.n, mat.k = layer, j, mt.n, mt.k
             mat.name = mt.name
             mat.packed, mat.gamma = packed, gamma
-            x = synth.activations_bf16(synth.seed_for(wl, layer, j, synth.ROLE_ACT, extra=m), m, mt.k,
-                                       wl.outlier_frac)
-            keep_oracle_codes = len(mats) < oracle_quota
-            mat.x_np = x if keep_oracle_codes else None
-            mat.x = torch.from_numpy(x.view(np.int16)).to(dev)
-            mat.xq = torch.empty((m, mt.k), dtype=torch.int8, device=dev)
-            mat.amax = torch.empty(1 if variant == "tensor128" else m, dtype=torch.float32, device=dev)
-            mat.ws = (torch.empty(max(4, blq.bitlinear_quant_act_tensor_workspace_bytes(m, mt.k)), dtype=torch.uint8,
-                                  device=dev) if variant == "tensor128" else None)
             mat.s16_or = None
-            mat.y = torch.empty((m, mt.n), dtype=torch.float32, device=dev)
-            mat.gain_np = (synth.norm_gain(synth.seed_for(wl, layer, j, synth.ROLE_GAIN), mt.k)
-                           if variant == "rmsnorm" or (variant == "swiglu" and mt.name == "gate_up") else None)
-            mat.gain = None if mat.gain_np is None else torch.from_numpy(mat.gain_np).to(dev)
-            # SwiGLU variant: the gate+up BitLinear writes h [m][n/2] instead of y
-            mat.h = (torch.empty((m, mt.n // 2), dtype=torch.float32, device=dev)
-                     if variant == "swiglu" and mt.name == "gate_up" else None)
+            keep_oracle_codes = len(mats) < oracle_quota
             t_or = time.perf_counter()
             if keep_oracle_codes and variant == "binary":
                 mat.g_or = s_bin
@@ -185,21 +178,51 @@ def setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, variant="plain"
             del wd
         del ws
         log("  packed %d/%d matrices" % (min(b0 + batch, len(jobs)), len(jobs)))
+    return mats, {"seconds": t_pack, "bytes": pack_bytes, "oracle": oracle_pack}
+
+
+def attach_activations(mats, wl, m, torch, blq, variant="plain"):
+    """Seeded activations of m tokens for every matrix (the activations of
+    workload wl at that token count) and the device buffers of one step; the
+    host copy is kept where the oracle holds the matrix's codes."""
+    dev = torch.device("cuda")
+    for mat in mats:
+        x = synth.activations_bf16(synth.seed_for(wl, mat.layer, mat.j, synth.ROLE_ACT, extra=m), m, mat.k,
+                                   wl.outlier_frac)
+        mat.x_np = x if mat.q_or is not None else None
+        mat.x = torch.from_numpy(x.view(np.int16)).to(dev)
+        mat.xq = torch.empty((m, mat.k), dtype=torch.int8, device=dev)
+        mat.amax = torch.empty(1 if variant == "tensor128" else m, dtype=torch.float32, device=dev)
+        mat.ws = (torch.empty(max(4, blq.bitlinear_quant_act_tensor_workspace_bytes(m, mat.k)), dtype=torch.uint8,
+                              device=dev) if variant == "tensor128" else None)
+        mat.y = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
+        mat.gain_np = (synth.norm_gain(synth.seed_for(wl, mat.layer, mat.j, synth.ROLE_GAIN), mat.k)
+                       if variant == "rmsnorm" or (variant == "swiglu" and mat.name == "gate_up") else None)
+        mat.gain = None if mat.gain_np is None else torch.from_numpy(mat.gain_np).to(dev)
+        # SwiGLU variant: the gate+up BitLinear writes h [m][n/2] instead of y
+        mat.h = (torch.empty((m, mat.n // 2), dtype=torch.float32, device=dev)
+                 if variant == "swiglu" and mat.name == "gate_up" else None)
+
+
+def replicate(mats, replicas):
+    """replicas x [Mat]: copies of the packed weights and of every buffer (the
+    oracle's codes stay with the first)."""
     reps = [mats]
-    for r in range(1, replicas):
+    for _ in range(1, replicas):
         cp = []
         for mat in mats:
             c = Mat()
             for s in Mat.__slots__:
                 setattr(c, s, getattr(mat, s))
             c.packed = mat.packed.clone()
-            c.x, c.xq, c.amax, c.y = mat.x.clone(), torch.empty_like(mat.xq), torch.empty_like(mat.amax), torch.empty_like(mat.y)
-            c.ws = None if mat.ws is None else torch.empty_like(mat.ws)
-            c.h = None if mat.h is None else torch.empty_like(mat.h)
+            c.x, c.xq, c.amax, c.y = mat.x.clone(), mat.xq.new_empty(mat.xq.shape), mat.amax.new_empty(mat.amax.shape), \
+                mat.y.new_empty(mat.y.shape)
+            c.ws = None if mat.ws is None else mat.ws.new_empty(mat.ws.shape)
+            c.h = None if mat.h is None else mat.h.new_empty(mat.h.shape)
             c.q_or = None
             cp.append(c)
         reps.append(cp)
-    return reps, {"seconds": t_pack, "bytes": pack_bytes, "oracle": oracle_pack}
+    return reps
 
 
 def _quant(blq, mat, stream):
@@ -475,14 +498,281 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
             "max_rel_err": worst, "chain_ok": chain_ok, "phases": phase}
 
 
+def choose_fused(blq, wl, m, variant, force_fused=False, force_unfused=False):
+    """Whether the step takes the fused quant + forward entry point: it
+    re-quantises the tokens in every workgroup, which pays off for a few
+    tokens (FUSED_MAX_M); more go through quant + forward."""
+    mode = variant if variant in MODES else None
+    if mode == "binary":
+        return (m == 1 and not force_unfused and
+                all(blq.bitlinear_quant_forward_binary_supported(m, mt.k) for mt in wl.matrices))
+    return ((fused_default(variant, m) or force_fused) and not force_unfused and variant != "lut" and mode is None
+            and all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
+
+
+def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_frac=None):
+    """Time K steps (after W warmup steps) of the per-token path over the
+    packed workload, and the dominant kernel on its own.  Returns the record
+    without the CPU baseline."""
+    batched = m > blq.BITLINEAR_FORWARD_MAX_M
+    mode = variant if variant in MODES else None
+    lut = variant == "lut"
+    norm = variant == "rmsnorm"
+    sw = variant == "swiglu"
+    mats0 = reps[0]
+
+    def call_bytes(mt):
+        if mode:
+            return mode_forward_bytes(mode, m, mt.n, mt.k)
+        if sw and mt.name == "gate_up":
+            return swiglu_bytes(m, mt.n // 2, mt.k)
+        return forward_bytes(m, mt.n, mt.k)
+
+    step_bytes = sum(call_bytes(mt) for mt in mats0)
+    step_quant_bytes = sum(quant_bytes(m, mt.k) for mt in mats0)
+    step_ops = sum(2 * m * mt.n * mt.k for mt in mats0)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    # One graph holds one step over every replica in turn (one replay = len(reps)
+    # steps), so a small workload is not timed as graph-launch overhead.
+    graph = None
+    if not eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for mats in reps:
+                launch_step(blq, mats, m, torch.cuda.current_stream(), fused, variant)
+        torch.cuda.synchronize()
+    per_run = len(reps)
+
+    def run():
+        if eager:
+            with torch.cuda.stream(stream):
+                for mats in reps:
+                    launch_step(blq, mats, m, stream, fused, variant)
+        else:
+            graph.replay()
+
+    runs_w = max(1, -(-warmup // per_run))
+    runs_t = max(1, -(-steps // per_run))
+    for _ in range(runs_w):
+        run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    repeat_ms = []
+    for _ in range(5):  # the K steps timed five times; `value` is the first timing
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(runs_t):
+            run()
+        ev1.record()
+        torch.cuda.synchronize()
+        repeat_ms.append(ev0.elapsed_time(ev1) / (runs_t * per_run))
+    steps_timed = runs_t * per_run
+    ms_per_step = repeat_ms[0]
+    log("%s m=%d: timed %d steps: %.4f ms/step" % (wl.key, m, steps_timed, ms_per_step))
+
+    # Dominant kernel (the forward, or the fused quant + forward): HIP events
+    # on its stream around graph replays that hold only that kernel's
+    # launches over every matrix of the workload (no event per launch: an
+    # event pair costs more than a small kernel).  Average launch duration =
+    # elapsed / launches.  The quantisation kernel is timed the same way.
+    if not fused:  # make sure the codes are current for forward-only replays
+        with torch.cuda.stream(stream):
+            launch_kernel_only(blq, mats0, m, stream, "quant", False, variant)
+        torch.cuda.synchronize()
+    replays = max(2, min(10, steps))
+    dom = "swiglu" if sw else "fused" if fused else "forward"
+    dom_mats = [mt for mt in mats0 if mt.name == "gate_up"] if sw else mats0
+
+    def all_reps(which):
+        return lambda st: [launch_kernel_only(blq, mats, m, st, which, fused, variant) for mats in reps]
+
+    dom_ms = time_graph(torch, stream, all_reps(dom), replays) / len(reps)
+    fw_avg_us = dom_ms / len(dom_mats) * 1e3
+    q_ms = None
+    if not fused:
+        q_ms = time_graph(torch, stream, all_reps("quant"), replays) / len(reps)
+    per_call = fused_bytes if fused else forward_bytes
+    if sw:
+        # fused: bf16 input and gains instead of codes and a'
+        fw_bytes = sum(swiglu_bytes(m, mt.n // 2, mt.k) + ((m * mt.k + 4 * mt.k - 4 * m) if fused else 0)
+                       for mt in dom_mats)
+        fw_ops = sum(2 * m * mt.n * mt.k for mt in dom_mats)
+    elif mode:
+        fw_bytes = sum(mode_forward_bytes(mode, m, mt.n, mt.k, fused) for mt in mats0)
+        fw_ops = step_ops
+    else:
+        fw_bytes = sum(per_call(m, mt.n, mt.k) + (4 * mt.k if norm and fused else 0) for mt in mats0)
+        fw_ops = step_ops
+    # The isolated replay includes each launch's dispatch gap, so its time per
+    # step can exceed the kernel's share of the real step; the kernel's time
+    # per step is then bounded by the step itself, and that bound is used.
+    kern_ms_step = dom_ms
+    capped = kern_ms_step > ms_per_step
+    if capped:
+        kern_ms_step = ms_per_step
+    if batched:
+        value = step_ops / (ms_per_step * 1e-3) / 1e12
+        unit = "TOPS"
+        achieved = fw_ops / (kern_ms_step * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_I8_PEAK_TOPS, "unit": "TOPS",
+                "frac": round(achieved / MFMA_I8_PEAK_TOPS, 4)}
+    else:
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = fw_bytes / (kern_ms_step * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    kern = "gemm_mfma_kernel" if batched else "gemv_lds_kernel"
+    roof["kernel"] = (("bitlinear_rmsnorm_quant_forward_swiglu (gemv_lds_kernel, RMSNorm prologue, SwiGLU epilogue)"
+                       if fused else "bitlinear_forward_swiglu (%s, SwiGLU epilogue)" % kern)
+                      if sw else "bitlinear_forward_batched (gemm_mfma_kernel)" if batched else
+                      ("bitlinear_rmsnorm_quant_forward (gemv_lds_kernel, RMSNorm + bf16 prologue)" if norm else
+                       "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)") if fused else
+                      "bitlinear_forward_lut (gemv_lut_kernel)" if lut else "bitlinear_forward (gemv_lds_kernel)")
+    mode_entry = {"tensor128": "bitlinear_forward_tensor_act", "rowscale": "bitlinear_forward_rowscale",
+                  "binary": "bitlinear_quant_forward_binary" if fused else "bitlinear_forward_binary"}
+    if mode:
+        roof["kernel"] = "%s (%s%s)" % (mode_entry[mode], kern, ", bf16 prologue" if fused else "")
+    roof["avg_launch_us"] = round(fw_avg_us, 3)
+    roof["launches_per_step"] = len(dom_mats)
+    roof["kernel_ms_per_step"] = round(dom_ms, 4)
+    if mode:
+        roof["per_launch"] = "mean over the workload's matrices of %s" % (
+            "2*M*N*K" if batched else
+            {"tensor128": "ceil(N*K/4)+M*K+8+4*M*N bytes", "rowscale": "ceil(N*K/4)+M*K+4M+2N+4*M*N bytes",
+             "binary": "ceil(N*K/8)+%s+4+4*M*N bytes" % ("2*M*K" if fused else "M*K+4M")}[mode])
+    elif sw:
+        roof["per_launch"] = "mean over the gate+up matrices of %s" % (
+            "2*M*2F*K" if batched else "2*ceil(F*K/4)+2*M*K+4K+8+4*M*F bytes" if fused else
+            "2*ceil(F*K/4)+M*K+4M+8+4*M*F bytes")
+    else:
+        roof["per_launch"] = "mean over the workload's matrices of %s" % (
+            "2*M*N*K" if batched else ("ceil(N*K/4)+2*M*K+4K+4+4*M*N bytes" if norm else "ceil(N*K/4)+2*M*K+4+4*M*N bytes")
+            if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
+    roof["timing"] = ("HIP events around %d graph replays of the kernel's %d launches per step%s" % (
+        replays, len(dom_mats),
+        "; their time per step (%.4f ms, dispatch gaps included) exceeds the step's, so the kernel's time per "
+        "step is taken as the step's" % dom_ms if capped else ""))
+    roof["traffic"] = None
+    prof = os.path.join(ROOT, "profiles", "counters_%s_m%d%s.json" % (
+        wl.key, m, "" if variant == "plain" else "_" + variant))
+    if os.path.exists(prof):
+        with open(prof) as f:
+            c = json.load(f)
+        if c.get("kernel_source_hash") == kernel_source_hash(
+                BATCHED_SOURCES if batched else LUT_SOURCES if lut else DECODE_SOURCES):
+            roof["traffic"] = c.get("hbm_bytes_per_launch")
+    if batched and nz_frac is not None:
+        # the method's own work: one add or subtract per non-zero weight and token
+        roof["frac_nonzero_adds"] = round(achieved * nz_frac / 2 / MFMA_I8_PEAK_TOPS, 4)
+
+    entry = (((("bitlinear_quant_act_tensor + " if mode == "tensor128" else "" if fused else
+                "bitlinear_quant_act + ") + mode_entry[mode]) if mode else
+             ("gate+up: bitlinear_rmsnorm_quant_forward_swiglu; down: bitlinear_quant_forward_f32; "
+              "others: bitlinear_quant_forward") if sw and fused else
+             "gate+up: bitlinear_rmsnorm_quant_act + bitlinear_forward_swiglu; down: "
+             "bitlinear_quant_act_f32 + " + ("bitlinear_forward_batched" if batched else
+                                             "bitlinear_forward") + "; others as plain"
+             if sw else
+             ("bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward") if fused else
+             ("bitlinear_rmsnorm_quant_act + " if norm else "bitlinear_quant_act + ") +
+             ("bitlinear_forward_batched" if batched else
+              "bitlinear_forward_lut" if lut else "bitlinear_forward")))
+    out = {
+        "value": round(value, 2 if batched else 1),
+        "unit": unit,
+        "steps": steps_timed,
+        "warmup": runs_w * per_run,
+        "ms_per_step": round(ms_per_step, 4),
+        "config": {
+            "workload": wl.title,
+            "key": wl.key,
+            "m": m,
+            "layers": wl.layers,
+            "matrices_per_step": len(mats0),
+            "shapes_kxn": ["%dx%d" % (mt.k, mt.n) for mt in wl.matrices],
+            "variant": variant,
+            "entry_points": entry,
+            "launch": ("hip graph, %d kernels per step" % (sum(
+                (1 if fused else 2) + (1 if mode == "tensor128" and
+                                       blq.bitlinear_quant_act_tensor_workspace_bytes(m, mt.k) > 4 else 0)
+                for mt in mats0)) if not eager else "eager"),
+            "cold_cache": "weights %.0f MB per step x %d replica(s)" % (
+                sum(mt.packed.numel() for mt in mats0) / 1e6, len(reps)),
+            "step_bytes": step_bytes,
+            "step_ops": step_ops,
+        },
+        "pct_of_peak": round(100 * value / (MFMA_I8_PEAK_TOPS if batched else HBM_PEAK_GBS), 2),
+        "repeats": {"count": len(repeat_ms), "ms_per_step_min": round(min(repeat_ms), 4),
+                    "ms_per_step_median": round(float(np.median(repeat_ms)), 4),
+                    "ms_per_step_max": round(max(repeat_ms), 4)},
+        "roofline": roof,
+    }
+    if q_ms is not None:
+        out["quant_kernel"] = {"avg_launch_us": round(q_ms / len(mats0) * 1e3, 3),
+                               "gbs": round(step_quant_bytes / (q_ms * 1e-3) / 1e9, 1)}
+    if batched:
+        if nz_frac is not None:
+            out["nonzero_weight_adds"] = {"fraction_nonzero": round(nz_frac, 4), "tops": round(value * nz_frac / 2, 2),
+                                          "definition": "nonzero(q) * M * N * K adds per step / time"}
+        # the other roof: algorithmic bytes of the step against the HBM peak
+        out["hbm_frac_of_step"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    return out
+
+
+def cpu_record(oracle_mod, mats0, m, wl, budget, variant, pack):
+    cb = cpu_baseline(oracle_mod, mats0, m, wl, budget, variant)
+    cores = oracle_mod.num_threads()
+    batched = m > 16
+    if batched:
+        v, u = cb["ops"] / cb["seconds"] / 1e12, "TOPS"
+    else:
+        v, u = cb["bytes"] / cb["seconds"] / 1e9, "GB/s"
+    rec = {
+        "value": round(v, 4), "unit": u, "cores": cores, "kind": "oracle",
+        "sample": "%d of %d matrices in layer order, %d token(s) each: quant + contraction + dequant "
+                  "(%.2f s)" % (cb["matrices"], len(mats0), cb["rows"], cb["seconds"]),
+        "cpu": _cpu_model(),
+        # the sample's time by oracle step, and the oracle's weight
+        # preparation (gamma, ternarisation, canonical 2-bit pack) over the
+        # matrices it kept codes for
+        "phases_seconds": {kk: round(vv, 4) for kk, vv in cb["phases"].items()},
+        "pack": {"seconds": round(pack["oracle"]["seconds"], 4), "matrices": pack["oracle"]["matrices"],
+                 "gbs_fp32_read": (round(pack["oracle"]["bytes"] / pack["oracle"]["seconds"] / 1e9, 3)
+                                   if pack["oracle"]["seconds"] > 0 else None)},
+    }
+    parity = {"matrices": cb["matrices"], "max_rel_err_y": cb["max_rel_err"],
+              "ok": bool(cb["max_rel_err"] <= 1e-5 and cb["chain_ok"])}
+    if variant == "swiglu":
+        parity["down_chain_ok"] = cb["chain_ok"]
+    return rec, parity
+
+
+# Rough rate of the oracle's contraction on 16 host cores (int8 x ternary
+# products summed in int64), used only to size its bounded sample.
+ORACLE_MACS_PER_S = 2.0e10
+
+# Workload of the default run: the largest configuration (the LLaMA-3-8B-shaped
+# stack at 512 tokens per matrix, 7.1 T int8 operations per step), with the
+# same stack's decode at 1, 4 and 8 tokens measured on the same packed weights.
+DEFAULT_WORKLOAD = "l8b_prefill"
+DEFAULT_EXTRA = "l8b_decode"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="b2b_decode", choices=sorted(synth.BY_KEY))
+    ap.add_argument("--workload", default=None, choices=sorted(synth.BY_KEY),
+                    help="default: %s, plus %s at each of its token counts on the same weights" % (
+                        DEFAULT_WORKLOAD, DEFAULT_EXTRA))
     ap.add_argument("--m", type=int, default=None, help="tokens per matrix (default: workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="default workload without the decode measurements")
     ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
     ap.add_argument("--fused", action="store_true",
                     help="decode: the fused quant + forward entry point at any m (default up to FUSED_MAX_M)")
@@ -531,28 +821,25 @@ def main():
         print(json.dumps({"copy_bytes": nbytes, "launches": 3}))
         return
 
-    wl = synth.BY_KEY[args.workload]
+    default_run = args.workload is None
+    wl = synth.BY_KEY[args.workload or DEFAULT_WORKLOAD]
     m = args.m if args.m is not None else wl.ms[0]
-    batched = m > blq.BITLINEAR_FORWARD_MAX_M
-    # the fused entry point re-quantises the tokens in every workgroup, which
-    # pays off for a few tokens (FUSED_MAX_M); more go through quant + forward
-    lut = args.variant == "lut"
+    variant = args.variant
+    lut = variant == "lut"
+    mode = variant if variant in MODES else None
     if lut and (m > blq.BITLINEAR_FORWARD_MAX_M or
                 not all(blq.bitlinear_forward_lut_supported(mt.k) for mt in wl.matrices)):
         print("bench.py: --variant lut needs m <= %d and every k within the on-chip table "
               "(k <= 9984)" % blq.BITLINEAR_FORWARD_MAX_M, file=sys.stderr)
         sys.exit(2)
-    mode = args.variant if args.variant in MODES else None
-    if mode == "binary":
-        fused = (m == 1 and not args.unfused and
-                 all(blq.bitlinear_quant_forward_binary_supported(m, mt.k) for mt in wl.matrices))
-    else:
-        fused = ((fused_default(args.variant, m) or args.fused) and not args.unfused and not lut and mode is None and
-                 all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
+    if variant == "swiglu" and not any(mt.name == "gate_up" for mt in wl.matrices):
+        print("bench.py: --variant swiglu needs a workload with a gate+up matrix", file=sys.stderr)
+        sys.exit(2)
+    fused = choose_fused(blq, wl, m, variant, args.fused, args.unfused)
     want_cpu = not args.no_cpu_baseline
     oracle_mod = None
-    if want_cpu:
-        import oracle as oracle_mod  # CPU baseline leg only
+    if want_cpu or default_run:
+        import oracle as oracle_mod  # CPU baseline leg only (and its parity check)
         oracle_mod._load()
 
     total_packed = synth.packed_weight_bytes_2bit(wl)
@@ -568,261 +855,66 @@ def main():
     # the oracle re-derives ternary codes only for the matrices its bounded
     # sample can cover (about cpu_budget seconds of contraction work)
     oracle_quota = 0
-    if want_cpu:
+    if want_cpu or default_run:
         macs = 0.0
         for _, _, mt in synth.iter_layer_matrices(wl):
             rows = m if m * mt.n * mt.k <= 2e10 else max(1, int(2e10 // (mt.n * mt.k)))
             macs += rows * mt.n * mt.k
             oracle_quota += 1
-            if macs > args.cpu_budget * 3e9:
+            if macs > args.cpu_budget * ORACLE_MACS_PER_S:
                 break
-    reps, pack = setup(wl, m, torch, blq, replicas, oracle_quota, oracle_mod, args.variant)
-    norm = args.variant == "rmsnorm"
-    sw = args.variant == "swiglu"
+    mats, pack = pack_weights(wl, torch, blq, oracle_quota, oracle_mod, variant)
+    attach_activations(mats, wl, m, torch, blq, variant)
+    reps = replicate(mats, replicas)
     log("setup %.1f s" % (time.time() - t0))
 
-    mats0 = reps[0]
-    if sw and not any(mt.name == "gate_up" for mt in mats0):
-        print("bench.py: --variant swiglu needs a workload with a gate+up matrix", file=sys.stderr)
-        sys.exit(2)
-
-    def call_bytes(mt):
-        if mode:
-            return mode_forward_bytes(mode, m, mt.n, mt.k)
-        if sw and mt.name == "gate_up":
-            return swiglu_bytes(m, mt.n // 2, mt.k)
-        return forward_bytes(m, mt.n, mt.k)
-
-    step_bytes = sum(call_bytes(mt) for mt in mats0)
-    step_quant_bytes = sum(quant_bytes(m, mt.k) for mt in mats0)
-    step_ops = sum(2 * m * mt.n * mt.k for mt in mats0)
-
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    # One graph holds one step over every replica in turn (one replay = len(reps)
-    # steps), so a small workload is not timed as graph-launch overhead.
-    graph = None
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for mats in reps:
-                launch_step(blq, mats, m, torch.cuda.current_stream(), fused, args.variant)
-        torch.cuda.synchronize()
-    per_run = len(reps)
-
-    def run():
-        if args.eager:
-            with torch.cuda.stream(stream):
-                for mats in reps:
-                    launch_step(blq, mats, m, stream, fused, args.variant)
-        else:
-            graph.replay()
-
-    runs_w = max(1, -(-args.warmup // per_run))
-    runs_t = max(1, -(-args.steps // per_run))
-    for _ in range(runs_w):
-        run()
-    torch.cuda.synchronize()
-    log("warmup done")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(runs_t):
-        run()
-    ev1.record()
-    torch.cuda.synchronize()
-    steps_timed = runs_t * per_run
-    ms_per_step = ev0.elapsed_time(ev1) / steps_timed
-    log("timed %d steps: %.4f ms/step" % (steps_timed, ms_per_step))
-    # the same K steps timed four more times, reported beside `value`
-    # (which is the first timing): the spread between repeats
-    repeat_ms = [ms_per_step]
-    for _ in range(4):
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(runs_t):
-            run()
-        ev1.record()
-        torch.cuda.synchronize()
-        repeat_ms.append(ev0.elapsed_time(ev1) / steps_timed)
-
-    # Dominant kernel (the forward, or the fused quant + forward): HIP events
-    # on its stream around graph replays that hold only that kernel's
-    # launches over every matrix of the workload (no event per launch: an
-    # event pair costs more than a small kernel).  Average launch duration =
-    # elapsed / launches.  The quantisation kernel is timed the same way.
-    if not fused:  # make sure the codes are current for forward-only replays
-        with torch.cuda.stream(stream):
-            launch_kernel_only(blq, mats0, m, stream, "quant", False, args.variant)
-        torch.cuda.synchronize()
-    replays = max(2, min(10, args.steps))
-    dom = "swiglu" if sw else "fused" if fused else "forward"
-    dom_mats = [mt for mt in mats0 if mt.name == "gate_up"] if sw else mats0
-
-    def all_reps(which):
-        return lambda st: [launch_kernel_only(blq, mats, m, st, which, fused, args.variant) for mats in reps]
-
-    dom_ms = time_graph(torch, stream, all_reps(dom), replays) / len(reps)
-    nlaunch = len(dom_mats) * replays * len(reps)
-    fw_avg_us = dom_ms / len(dom_mats) * 1e3
-    q_ms = time_graph(torch, stream, all_reps("quant"), replays) / len(reps)
-    q_avg_us = q_ms / len(mats0) * 1e3
-    per_call = fused_bytes if fused else forward_bytes
-    if sw:
-        # fused: bf16 input and gains instead of codes and a'
-        fw_bytes = sum(swiglu_bytes(m, mt.n // 2, mt.k) + ((m * mt.k + 4 * mt.k - 4 * m) if fused else 0)
-                       for mt in dom_mats)
-        fw_ops = sum(2 * m * mt.n * mt.k for mt in dom_mats)
-    elif mode:
-        fw_bytes = sum(mode_forward_bytes(mode, m, mt.n, mt.k, fused) for mt in mats0)
-        fw_ops = step_ops
-    else:
-        fw_bytes = sum(per_call(m, mt.n, mt.k) + (4 * mt.k if norm and fused else 0) for mt in mats0)
-        fw_ops = step_ops
-    fw_ms = dom_ms
-    if batched:
-        value = step_ops / (ms_per_step * 1e-3) / 1e12
-        unit = "TOPS"
-        achieved = fw_ops / (fw_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_I8_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_I8_PEAK_TOPS, 4)}
-    else:
-        value = step_bytes / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        achieved = fw_bytes / (fw_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = (("bitlinear_rmsnorm_quant_forward_swiglu (gemv_lds_kernel, RMSNorm prologue, SwiGLU epilogue)"
-                       if fused else "bitlinear_forward_swiglu (%s, SwiGLU epilogue)" % (
-                           "gemm_dma_kernel" if batched else "gemv_lds_kernel"))
-                      if sw else "bitlinear_forward_batched (gemm_kernel)" if batched else
-                      ("bitlinear_rmsnorm_quant_forward (gemv_lds_kernel, RMSNorm + bf16 prologue)" if norm else
-                       "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)") if fused else
-                      "bitlinear_forward_lut (gemv_lut_kernel)" if lut else "bitlinear_forward (gemv kernel)")
-    kern = "gemm_dma_kernel" if batched else "gemv_lds_kernel"
-    mode_entry = {"tensor128": "bitlinear_forward_tensor_act", "rowscale": "bitlinear_forward_rowscale",
-                  "binary": "bitlinear_quant_forward_binary" if fused else "bitlinear_forward_binary"}
-    if mode:
-        roof["kernel"] = "%s (%s%s)" % (mode_entry[mode], kern, ", bf16 prologue" if fused else "")
-    roof["avg_launch_us"] = round(fw_avg_us, 3)
-    roof["launches_timed"] = nlaunch
-    if mode:
-        roof["per_launch"] = "mean over the workload's matrices of %s" % (
-            "2*M*N*K" if batched else
-            {"tensor128": "ceil(N*K/4)+M*K+8+4*M*N bytes", "rowscale": "ceil(N*K/4)+M*K+4M+2N+4*M*N bytes",
-             "binary": "ceil(N*K/8)+%s+4+4*M*N bytes" % ("2*M*K" if fused else "M*K+4M")}[mode])
-    elif sw:
-        roof["per_launch"] = "mean over the gate+up matrices of %s" % (
-            "2*M*2F*K" if batched else "2*ceil(F*K/4)+2*M*K+4K+8+4*M*F bytes" if fused else
-            "2*ceil(F*K/4)+M*K+4M+8+4*M*F bytes")
-    else:
-        roof["per_launch"] = "mean over the workload's matrices of %s" % (
-            "2*M*N*K" if batched else ("ceil(N*K/4)+2*M*K+4K+4+4*M*N bytes" if norm else "ceil(N*K/4)+2*M*K+4+4*M*N bytes")
-            if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
-    roof["timing"] = "HIP events around %d graph replays of the kernel's %d launches" % (replays, len(dom_mats) * len(reps))
-    roof["traffic"] = None
-    prof = os.path.join(ROOT, "profiles", "counters_%s_m%d%s.json" % (
-        wl.key, m, "" if args.variant == "plain" else "_" + args.variant))
-    if os.path.exists(prof):
-        with open(prof) as f:
-            c = json.load(f)
-        if c.get("kernel_source_hash") == kernel_source_hash(
-                BATCHED_SOURCES if batched else LUT_SOURCES if lut else DECODE_SOURCES):
-            roof["traffic"] = c.get("hbm_bytes_per_launch")
-
+    nz = None
+    if m > blq.BITLINEAR_FORWARD_MAX_M:
+        # the non-zero fraction, read from the packed codes of the first layer's matrices
+        nz = nonzero_fraction(blq, torch, mats[:len(wl.matrices)], mode)
+    rec = measure(torch, blq, wl, m, reps, variant, fused, args.steps, args.warmup, args.eager, nz)
     out = {
         "metric": "BitLinear GEMV effective HBM GB/s (% of peak); batched int8 TOPS (% MFMA peak)",
-        "value": round(value, 2 if batched else 1),
-        "unit": unit,
+        "value": rec.pop("value"),
+        "unit": rec.pop("unit"),
         "n_gpus": 1,
-        "steps": steps_timed,
-        "warmup": runs_w * per_run,
-        "ms_per_step": round(ms_per_step, 4),
+        "steps": rec.pop("steps"),
+        "warmup": rec.pop("warmup"),
+        "ms_per_step": rec.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded N(0,0.02) latent weights, N(0,1) bf16 activations)",
-        "config": {
-            "workload": wl.title,
-            "key": wl.key,
-            "m": m,
-            "layers": wl.layers,
-            "matrices_per_step": len(mats0),
-            "shapes_kxn": ["%dx%d" % (mt.k, mt.n) for mt in wl.matrices],
-            "variant": args.variant,
-            "entry_points": ((("bitlinear_quant_act_tensor + " if mode == "tensor128" else "" if fused else
-                               "bitlinear_quant_act + ") + mode_entry[mode]) if mode else
-                             ("gate+up: bitlinear_rmsnorm_quant_forward_swiglu; down: bitlinear_quant_forward_f32; "
-                              "others: bitlinear_quant_forward") if sw and fused else
-                             "gate+up: bitlinear_rmsnorm_quant_act + bitlinear_forward_swiglu; down: "
-                             "bitlinear_quant_act_f32 + " + ("bitlinear_forward_batched" if batched else
-                                                             "bitlinear_forward") + "; others as plain"
-                             if sw else
-                             ("bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward") if fused else
-                             ("bitlinear_rmsnorm_quant_act + " if norm else "bitlinear_quant_act + ") +
-                             ("bitlinear_forward_batched" if batched else
-                              "bitlinear_forward_lut" if lut else "bitlinear_forward")),
-            "launch": ("hip graph, %d kernels per step" % (sum(
-                (1 if fused else 2) + (1 if mode == "tensor128" and
-                                       blq.bitlinear_quant_act_tensor_workspace_bytes(m, mt.k) > 4 else 0)
-                for mt in mats0)) if not args.eager else "eager"),
-            "cold_cache": "weights %.0f MB per step x %d replica(s)" % (total_packed / 1e6, len(reps)),
-            "step_bytes": step_bytes,
-            "step_ops": step_ops,
-        },
-        "pct_of_peak": round(100 * value / (MFMA_I8_PEAK_TOPS if batched else HBM_PEAK_GBS), 2),
-        "repeats": {"count": len(repeat_ms), "ms_per_step_min": round(min(repeat_ms), 4),
-                    "ms_per_step_median": round(float(np.median(repeat_ms)), 4),
-                    "ms_per_step_max": round(max(repeat_ms), 4)},
-        "roofline": roof,
-        "quant_kernel": {"avg_launch_us": round(q_avg_us, 3),
-                         "gbs": round(step_quant_bytes / (q_ms * 1e-3) / 1e9, 1)},
-        "pack": {"seconds": round(pack["seconds"], 4),
-                 "gbs": round(pack["bytes"] / pack["seconds"] / 1e9, 1) if pack["seconds"] > 0 else None},
     }
-
-    if batched:
-        # Beside the dense 2*M*N*K: the method's own work is one add or
-        # subtract per non-zero weight and token.  The non-zero fraction is
-        # read from the packed codes of the first layer's matrices (binary
-        # weights have none that are zero).
-        nz = nonzero_fraction(blq, torch, mats0[:len(wl.matrices)], mode)
-        out["nonzero_weight_adds"] = {"fraction_nonzero": round(nz, 4), "tops": round(value * nz / 2, 2),
-                                      "definition": "nonzero(q) * M * N * K adds per step / time"}
-        # the other roof: algorithmic bytes of the step against the HBM peak
-        out["hbm_frac_of_step"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-
+    out.update(rec)
+    out["pack"] = {"seconds": round(pack["seconds"], 4),
+                   "gbs": round(pack["bytes"] / pack["seconds"] / 1e9, 1) if pack["seconds"] > 0 else None}
     if want_cpu:
         log("cpu baseline (oracle) ...")
-        cb = cpu_baseline(oracle_mod, mats0, m, wl, args.cpu_budget, args.variant)
-        cores = oracle_mod.num_threads()
-        if batched:
-            v = cb["ops"] / cb["seconds"] / 1e12
-            u = "TOPS"
-        else:
-            v = cb["bytes"] / cb["seconds"] / 1e9
-            u = "GB/s"
-        out["cpu_baseline"] = {
-            "value": round(v, 4), "unit": u, "cores": cores, "kind": "oracle",
-            "sample": "%d of %d matrices in layer order, %d token(s) each: quant + contraction + dequant "
-                      "(%.2f s)" % (cb["matrices"], len(mats0), cb["rows"], cb["seconds"]),
-            "cpu": _cpu_model(),
-            # the sample's time by oracle step, and the oracle's weight
-            # preparation (gamma, ternarisation, canonical 2-bit pack) over the
-            # matrices it kept codes for
-            "phases_seconds": {kk: round(vv, 4) for kk, vv in cb["phases"].items()},
-            "pack": {"seconds": round(pack["oracle"]["seconds"], 4), "matrices": pack["oracle"]["matrices"],
-                     "gbs_fp32_read": (round(pack["oracle"]["bytes"] / pack["oracle"]["seconds"] / 1e9, 3)
-                                       if pack["oracle"]["seconds"] > 0 else None)},
-        }
-        out["parity_vs_oracle"] = {"matrices": cb["matrices"], "max_rel_err_y": cb["max_rel_err"],
-                                   "ok": bool(cb["max_rel_err"] <= 1e-5 and cb["chain_ok"])}
-        if sw:
-            out["parity_vs_oracle"]["down_chain_ok"] = cb["chain_ok"]
+        out["cpu_baseline"], out["parity_vs_oracle"] = cpu_record(oracle_mod, reps[0], m, wl, args.cpu_budget,
+                                                                  variant, pack)
     else:
         out["cpu_baseline"] = None
+
+    if default_run and not args.no_extra:
+        # the same stack's decode (the LLaMA-3-8B-shaped decode workload's
+        # activations at 1, 4 and 8 tokens) on the same packed weights
+        ewl = synth.BY_KEY[DEFAULT_EXTRA]
+        out["extra_configs"] = {}
+        for me in ewl.ms:
+            for r in reps:
+                for mat in r:
+                    mat.x = mat.xq = mat.amax = mat.y = mat.h = mat.ws = mat.gain = None
+            torch.cuda.empty_cache()
+            attach_activations(mats, ewl, me, torch, blq, variant)
+            ereps = replicate(mats, replicas)
+            efused = choose_fused(blq, ewl, me, variant, args.fused, args.unfused)
+            sub = measure(torch, blq, ewl, me, ereps, variant, efused, args.steps, args.warmup, args.eager)
+            # parity of the same step's outputs against the oracle, on the matrices whose codes it holds
+            sub["parity_vs_oracle"] = cpu_record(oracle_mod, ereps[0], me, ewl, 1.0, variant, pack)[1]
+            sub["weights"] = "the packed weights of the headline workload (the same seeded stack)"
+            out["extra_configs"]["%s_m%d" % (ewl.key, me)] = sub
     print(json.dumps(out), flush=True)
 
 

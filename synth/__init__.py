@@ -47,6 +47,7 @@ class Workload:
     weight_seed: int = -1         # >= 0: single-matrix workload with a fixed seed
     act_seed: int = -1
     index: int = 0                # position in the workload list (seed namespace)
+    weight_index: int = -1        # >= 0: draw the weights of that workload instead (same layers)
 
 
 _L2B = (Matrix("qkv", 2560, 3840), Matrix("o", 2560, 2560),
@@ -61,8 +62,9 @@ WORKLOADS: Tuple[Workload, ...] = (
              _L2B, (1,), 0.0, index=1),
     Workload("l8b_decode", "LLaMA-3-8B-shaped stack, 32 layers, decode M=1/4/8", 32,
              _L8B, (1, 4, 8), 0.005, index=2),
+    # prefill: the decode stack's weights (same seeds), 512 tokens per matrix
     Workload("l8b_prefill", "LLaMA-3-8B-shaped stack, 32 layers, prefill M=512", 32,
-             _L8B, (512,), 0.005, index=3),
+             _L8B, (512,), 0.005, index=3, weight_index=2),
     Workload("l70b_layer", "70B-shaped layer, d_model 8192, M=1/64", 1,
              (Matrix("gate_up", 8192, 57344), Matrix("down", 28672, 8192)), (1, 64), 0.0,
              index=4),
@@ -79,12 +81,14 @@ def seed_for(wl: Workload, layer: int, mat: int, role: int, extra: int = 0):
 
     The single-layer 2048 workload uses the fixed seeds 0 (weights) and 1
     (activations); every other tensor uses SeedSequence([workload, layer,
-    matrix, role, extra])."""
+    matrix, role, extra]), where a workload that shares another's weights
+    (weight_index) names that workload for its weight tensors."""
     if role == ROLE_WEIGHT and wl.weight_seed >= 0:
         return wl.weight_seed
     if role == ROLE_ACT and wl.act_seed >= 0 and extra == 0:
         return wl.act_seed
-    return np.random.SeedSequence([wl.index, layer, mat, role, extra])
+    index = wl.weight_index if role == ROLE_WEIGHT and wl.weight_index >= 0 else wl.index
+    return np.random.SeedSequence([index, layer, mat, role, extra])
 
 
 def _rng(seed) -> np.random.Generator:

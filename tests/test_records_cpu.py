@@ -16,7 +16,7 @@ import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 RECORDS = sorted(glob.glob(os.path.join(ROOT, "profiles", "bench_*.json")))
-PEAKS = {"GB/s": 8000.0, "TFLOP/s": 5000.0}  # MI355X HBM; dense int8 matrix cores (5.0 POP/s)
+PEAKS = {"GB/s": 8000.0, "TOPS": 5000.0, "TFLOP/s": 5000.0}  # MI355X HBM; dense int8 matrix cores (5.0 POP/s)
 
 
 def _load(path):
