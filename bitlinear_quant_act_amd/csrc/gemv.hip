@@ -61,10 +61,9 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// One 16-wave workgroup per compute unit: measured 6-7% faster on the 2B- and
-// 8B-shaped decode stacks than two 8-wave workgroups per CU (each workgroup
-// stages the activations once, so the prologue is paid once per CU), and
-// equal on the 70B-shaped layer.
+// Persistent grid: at most 256 workgroups of 16 waves (one per compute unit,
+// which stages the activations once), or 512 of 8 waves; dispatch_lds picks
+// the size per row length.
 #ifndef BITLINEAR_GEMV_MAX_GROUPS
 #define BITLINEAR_GEMV_MAX_GROUPS 256
 #endif
@@ -1199,12 +1198,19 @@ hipError_t dispatch_lds_waves(const void* packed, const float* gamma, Dequant dq
                                                 gain, eps, s, vec, packed_u, gamma_u);
 }
 
-// Workgroup size.  16 waves (one workgroup per CU) everywhere except the
-// RMSNorm prologue on rows of at most 8192 values, which measured faster as
-// two 8-wave workgroups per CU (3840 x 2560: 4.39 against 4.70 us per
-// launch).  On longer rows every workgroup's fp64 RMSNorm pass over the row
-// dominates, and two workgroups per CU do it twice: 4096 x 14336 took 9.55 us
-// with 8 waves and 8.40 with 16, 8192 x 28672 24.5 and 16.8.
+// Workgroup size: one 16-wave workgroup per CU, or two 8-wave workgroups
+// (the same resident waves), each of which stages the activations itself.
+//   * Fused quantisation + decode: two 8-wave workgroups for rows of at most 3072
+//     values, where staging is cheap and the second workgroup overlaps the
+//     first one's prologue and tail (fused, one token, us per launch, 16 vs
+//     2 x 8 waves: 13824 x 2560 5.27 / 4.54, 3840 x 2560 3.13 / 2.92,
+//     2048 x 2048 2.91 / 2.71); 16 waves on longer rows (28672 x 4096 8.38 /
+//     9.03, 4096 x 14336 5.80 / 7.31, 8192 x 28672 13.56 / 17.79).
+//   * RMSNorm prologue: two 8-wave workgroups on rows of at most 8192 values
+//     (3840 x 2560: 4.39 against 4.70 us per launch).  On longer rows every
+//     workgroup's fp64 RMSNorm pass over the row dominates, and two
+//     workgroups per CU do it twice: 4096 x 14336 took 9.55 us with 8 waves
+//     and 8.40 with 16, 8192 x 28672 24.5 and 16.8.
 template <int SRC, bool SWIGLU = false, int WB = 2>
 hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const void* xsrc,
                         const float* amax_in, int64_t m, float* y, int32_t* acc, int8_t* xq_out, float* amax_out,
@@ -1212,6 +1218,11 @@ hipError_t dispatch_lds(const void* packed, const float* gamma, Dequant dq, int6
                         const float* gamma_u = nullptr) {
   if constexpr (SRC == kFromBf16Norm && !SWIGLU) {
     if (k <= 8192)
+      return dispatch_lds_waves<SRC, 8, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out,
+                                                    amax_out, gain, eps, s, vec, packed_u, gamma_u);
+  }
+  if constexpr (SRC == kFromBf16 && !SWIGLU && WB == 2) {
+    if (k <= 3072)
       return dispatch_lds_waves<SRC, 8, SWIGLU, WB>(packed, gamma, dq, n, k, xsrc, amax_in, m, y, acc, xq_out,
                                                     amax_out, gain, eps, s, vec, packed_u, gamma_u);
   }
