@@ -122,7 +122,11 @@ int bitlinear_pack_weights_noalloc(const float *w, int64_t n, int64_t k,
                                    float *gamma, void *stream);
 
 /*
- * Decode the packed layout back to ternary codes (for tests and inspection).
+ * Decode the packed layout back to ternary codes (for tests and inspection):
+ * the W_q of "The Mathematical Mechanism", item 1, one int8 per weight, from
+ * the 2-bit fields described at bitlinear_packed_bytes ("BitNet 1-bit LLM
+ * Inference Framework", "How the LUT Kernel Works": four ternary values per
+ * byte, here in this library's tiled order).
  *   packed  in   bitlinear_packed_bytes(n, k) bytes, 16-byte aligned
  *   codes   out  int8 [n][k] in {-1, 0, 1}
  */
@@ -181,9 +185,11 @@ int bitlinear_quant_forward(const void *packed, const float *gamma, int64_t n, i
 int bitlinear_quant_forward_supported(int64_t m, int64_t k);
 
 /*
- * Batched (prefill) forward for 1 <= m <= 2^21: the same result as
- * bitlinear_forward, computed as a tiled int8 matrix-core contraction with
- * the ternary tiles expanded on chip.  Larger m returns
+ * Batched (prefill) forward for 1 <= m <= 2^21 ("The Mathematical
+ * Mechanism", items 3 and 4, for many tokens at once; "BitNet 1-bit LLM
+ * Inference Framework", "Scalability with Thread Count": prompt processing is
+ * compute-intensive): the same result as bitlinear_forward, computed as a
+ * tiled int8 matrix-core contraction with the ternary tiles expanded on chip.  Larger m returns
  * BITLINEAR_E_UNSUPPORTED (split the tokens into several calls).
  * When the output tiles are too few to fill the device, the k extent is
  * split across workgroups: the exact int32 partial sums are added with

@@ -18,7 +18,9 @@ HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 @pytest.fixture(scope="module")
 def blq():
     import bitlinear_quant_act_amd as m
-    m.load_library()
+    # a host-sanitized build of the same sources may be named here (see
+    # test_sanitizers.py); by default the in-tree library
+    m.load_library(os.environ.get("BITLINEAR_TEST_LIB", m.LIB_PATH))
     return m
 
 
