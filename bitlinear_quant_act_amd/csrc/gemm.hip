@@ -381,13 +381,23 @@ __device__ __forceinline__ v4i weight_operand(const uint4* s, int q) {
 // (slice-major); a workgroup walks k-steps [slice * kt_per, ...) and adds its
 // partial sums, exact in int32, to split_acc with atomics (zeroed before,
 // converted by split_finish_kernel after).
-template <int MB, int NB, int WM, int WN, int S, int OCC, int WB = 2, bool SWIGLU = false, bool SPLIT = false>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
+//
+// KG > 1 (ring configurations only): KG groups of WM x WN waves share the
+// workgroup's tile; group g takes MFMA steps q in [8g / KG, 8(g + 1) / KG)
+// of every k-step, so each wave holds a full MB x NB block of the tile with
+// 1 / KG of its MFMAs, and the CU keeps KG times the waves of one tile.  The
+// groups' partial sums (exact int32) meet in LDS after the last step and the
+// first group writes the outputs.
+template <int MB, int NB, int WM, int WN, int S, int OCC, int WB = 2, bool SWIGLU = false, bool SPLIT = false,
+          int KG = 1>
+__global__ __launch_bounds__(64 * WM * WN * KG, OCC) void gemm_mfma_kernel(
     const uint8_t* __restrict__ packed_b, const float* __restrict__ gamma_p, Dequant dq, int64_t n, int64_t k,
     int kt_count, const int8_t* __restrict__ xq, const float* __restrict__ amax, int64_t m, int mt_count,
     int nt_count, float* __restrict__ y, int32_t* __restrict__ acc_out, const uint8_t* __restrict__ packed_u,
     const float* __restrict__ gamma_u, int kt_per, int32_t* __restrict__ split_acc) {
-  static_assert(WM * WN == kThreads / 64, "4 waves");
+  static_assert(WM * WN * KG == 4 || WM * WN * KG == 8, "4 or 8 waves");
+  static_assert(KG == 1 || KG == 2, "k-groups");
+  static_assert(KG == 1 || (S > 2 && !SWIGLU && WB == 2), "k-groups: ternary ring configurations, plain epilogue");
   static_assert(WB == 2 || !SWIGLU, "binary weights: plain epilogue");
   static_assert(!(SPLIT && SWIGLU), "k-slices: plain epilogue only");
   static_assert(!SWIGLU || NB % 2 == 0, "gate and up blocks pair up inside a wave");
@@ -395,7 +405,10 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
   constexpr int BN = WN * NB * 32;
   constexpr int FB = SWIGLU ? BN / 2 : BN;          // output columns (features) per workgroup
   constexpr int kStage = BM * kTileCols;            // activation bytes per stage
-  constexpr int kDma = BM / 16;                     // 1 KiB copies per wave per stage
+  constexpr int kWavesWG = WM * WN * KG;
+  constexpr int kDma = BM / (4 * kWavesWG);         // 1 KiB activation copies per wave per stage
+  static_assert(kDma >= 1 && kDma * 4 * kWavesWG == BM, "activation copies split over the waves");
+  constexpr int QN = 8 / KG;                        // MFMA steps per k-step and wave
   constexpr int BREGS = WB == 1 ? 1 : 2;            // 16-byte slots per 32-row block per step
   constexpr int NBH = SWIGLU ? NB / 2 : NB;         // 32-row blocks per wave and matrix
 
@@ -407,20 +420,26 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
   constexpr bool kRing = S > 2;
   constexpr int TBS = WB == 1 ? kBinStepBytes : kTileBytes;           // one row block's bytes per k-step
   constexpr int kStageBytes = kStage + (kRing ? (BN / kTileRows) * TBS : 0);
-  constexpr int kBDma = kRing ? (BN / kTileRows) * TBS / 1024 / 4 : 0;  // weight copies per wave per stage
-  static_assert(!kRing || (BN / kTileRows) * TBS % 4096 == 0, "weight copies split over the four waves");
+  constexpr int kBDma = kRing ? (BN / kTileRows) * TBS / 1024 / kWavesWG : 0;  // weight copies per wave per stage
+  static_assert(!kRing || (BN / kTileRows) * TBS % (1024 * kWavesWG) == 0, "weight copies split over the waves");
+  // the k-groups' partial sums after the last step (groups 1 .. KG - 1), in the ring's memory
+  constexpr int kRedBytes = (KG - 1) * WM * WN * MB * NB * 16 * 64 * 4;
+  constexpr int kRingBytes = S * kStageBytes > kRedBytes ? S * kStageBytes : kRedBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kRing ? 16 : kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[kRing ? 16 : kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing ? S * kStageBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing ? kRingBytes : 16];
   __shared__ __attribute__((aligned(16))) float scale_s[BM];
   __shared__ __attribute__((aligned(16))) float scale_u[SWIGLU ? BM : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps stage addresses scalar
-  const int wm = wave / WN, wn = wave % WN;
+  const int kg = wave / (WM * WN);                              // k-group
+  const int wl = wave - kg * (WM * WN);                         // wave inside the group
+  const int wm = wl / WN, wn = wl % WN;
   const int l32 = lane & 31;
   const int h = lane >> 5;
+  const int q0 = KG == 1 ? 0 : kg * QN;                         // first MFMA step of the group
 
   const int total = mt_count * nt_count;
   int id = blockIdx.x;
@@ -503,10 +522,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
     }
   };
 
-  // LDS offsets of the lane's activation chunk for each MFMA step (token block 0, stage 0)
-  int a_off[8];
+  // LDS offsets of the lane's activation chunk for the group's MFMA steps q0 + qq (token block 0, stage 0)
+  int a_off[QN];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) a_off[q] = (wm * MB * 32 + l32) * kTileCols + (((8 * h + q) ^ (l32 & 15)) << 4);
+  for (int qq = 0; qq < QN; ++qq)
+    a_off[qq] = (wm * MB * 32 + l32) * kTileCols + (((8 * h + q0 + qq) ^ (l32 & 15)) << 4);
 
   v16i acc[MB][NB];
 #pragma unroll
@@ -519,32 +539,34 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
   // order, so at most two steps' operands are live next to the accumulators
   // and the weight slots; the ring configuration leaves the order to the
   // compiler (measured 1-3% faster there, 4% slower on the wide tile).
-  auto read_a = [&](const uint8_t* st, int q, v4i (&a)[MB]) {
+  // (every array index below is a compile-time step qq of the group; the
+  // weight operand of step qq comes from wop(nb, qq))
+  auto read_a = [&](const uint8_t* st, int qq, v4i (&a)[MB]) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i*>(st + a_off[q] + mb * 32 * kTileCols);
+    for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i*>(st + a_off[qq] + mb * 32 * kTileCols);
   };
-  auto mul = [&](const v4i (&a)[MB], const uint4 (&br)[NB][BREGS], int q) {
+  auto mul = [&](const v4i (&a)[MB], auto&& wop, int qq) {
     v4i b[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) b[nb] = weight_operand<WB>(br[nb], q);
+    for (int nb = 0; nb < NB; ++nb) b[nb] = wop(nb, qq);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
   };
-  auto compute = [&](const uint8_t* st, const uint4 (&br)[NB][BREGS]) {
+  auto compute = [&](const uint8_t* st, auto&& wop) {
     v4i a0[MB], a1[MB];
     read_a(st, 0, a0);
 #pragma unroll
-    for (int q = 0; q < 8; q += 2) {
-      read_a(st, q + 1, a1);
+    for (int qq = 0; qq < QN; qq += 2) {
+      read_a(st, qq + 1, a1);
       if (!kRing) __builtin_amdgcn_sched_barrier(0);
-      mul(a0, br, q);
+      mul(a0, wop, qq);
       if (!kRing) __builtin_amdgcn_sched_barrier(0);
-      if (q + 2 < 8) read_a(st, q + 2, a0);
+      if (qq + 2 < QN) read_a(st, qq + 2, a0);
       if (!kRing) __builtin_amdgcn_sched_barrier(0);
-      mul(a1, br, q + 1);
+      mul(a1, wop, qq + 1);
       if (!kRing) __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -599,12 +621,26 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
     }
     auto compute_ring = [&](int u) {
       const uint8_t* st = ring + u * kStageBytes;
-      uint4 bc[NB][BREGS];
+      if constexpr (KG == 1) {
+        uint4 bc[NB][BREGS];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int j = 0; j < BREGS; ++j) bc[nb][j] = *reinterpret_cast<const uint4*>(st + b_lds[nb] + 256 * j);
-      compute(st, bc);
+          for (int j = 0; j < BREGS; ++j) bc[nb][j] = *reinterpret_cast<const uint4*>(st + b_lds[nb] + 256 * j);
+        compute(st, [&](int nb, int qq) { return weight_operand<WB>(bc[nb], qq); });
+      } else {
+        // ternary: the four words of steps q0 .. q0 + 3 are the lane's slot q0 / 4
+        uint32_t bw[NB][QN];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint4 v = *reinterpret_cast<const uint4*>(st + b_lds[nb] + 256 * (q0 >> 2));
+          bw[nb][0] = v.x;
+          bw[nb][1] = v.y;
+          bw[nb][2] = v.z;
+          bw[nb][3] = v.w;
+        }
+        compute(st, [&](int nb, int qq) { return expand_ternary(bw[nb][qq]); });
+      }
     };
     constexpr int kPer = kDma + kBDma;  // copies per step and wave
     static_assert((S - 2) * kPer < 64, "vmcnt range");
@@ -645,20 +681,48 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_mfma_kernel(
       __builtin_amdgcn_s_barrier();
       issue_a(st1, kt + 1);
       issue_b(b1, kt + 1);
-      compute(st0, b0);
+      compute(st0, [&](int nb, int qq) { return weight_operand<WB>(b0[nb], qq); });
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       if (kt + 2 < kt_end) {  // uniform
         issue_a(st0, kt + 2);
         issue_b(b0, kt + 2);
       }
-      compute(st1, b1);
+      compute(st1, [&](int nb, int qq) { return weight_operand<WB>(b1[nb], qq); });
     }
     if (kt < kt_end) {
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      compute(st0, b0);
+      compute(st0, [&](int nb, int qq) { return weight_operand<WB>(b0[nb], qq); });
     }
+  }
+
+  if constexpr (KG > 1) {
+    // the k-groups' partial sums meet in LDS; every wave is past its last
+    // stage read (the barrier), and the last step waited for every copy
+    __syncthreads();
+    int32_t* red = reinterpret_cast<int32_t*>(ring);
+    constexpr int kPerWave = MB * NB * 16 * 64;  // int32 per wave
+    if (kg > 0) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            red[((kg - 1) * WM * WN + wl) * kPerWave + ((mb * NB + nb) * 16 + r) * 64 + lane] = acc[mb][nb][r];
+    }
+    __syncthreads();
+    if (kg > 0) return;  // no barrier follows
+#pragma unroll 1
+    for (int g = 1; g < KG; ++g)  // (one group's partials in flight at a time)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[mb][nb][r] += red[((g - 1) * WM * WN + wl) * kPerWave + ((mb * NB + nb) * 16 + r) * 64 + lane];
   }
 
   // 32 x 32 block layout: element r of lane l is token 8 * (r / 4) + 4 * (l / 32) + r % 4, row l % 32
@@ -823,11 +887,13 @@ int slice_steps(int64_t tiles, int occ, int kt) {
 
 // Launch of the matrix-core kernel for one configuration; the k extent is
 // split when the output tiles fill at most a quarter of the resident slots.
-template <int MB, int NB, int WM, int WN, int S, int OCC, int WB = 2>
+template <int MB, int NB, int WM, int WN, int S, int OCC, int WB = 2, int KG = 1>
 hipError_t launch_mfma(const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k, const int8_t* xq,
                        const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   constexpr int BM = WM * MB * 32, BN = WN * NB * 32;
-  static_assert(S * (BM * kTileCols + (S > 2 ? BN * kTileBytes / kTileRows : 0)) + 2 * BM * 4 <= 163840 / OCC,
+  constexpr int kThreadsWG = 64 * WM * WN * KG;
+  static_assert(S * (BM * kTileCols + (S > 2 ? BN * kTileBytes / kTileRows : 0)) + 2 * BM * 4 <= 163840 / OCC &&
+                    (KG - 1) * WM * WN * MB * NB * 16 * 64 * 4 + 2 * BM * 4 <= 163840 / OCC,
                 "LDS per workgroup");
   // 32-bit buffer offsets: BM rows of at most 2^18 codes, BN / 16 row blocks of at most 1024 tiles
   static_assert(static_cast<int64_t>(BM) << 18 <= 0x7fffffff &&
@@ -840,7 +906,8 @@ hipError_t launch_mfma(const void* packed, const float* gamma, Dequant dq, int64
   const int kt_per = slice_steps(mt * ntl, OCC, kt);
   const uint8_t* p = static_cast<const uint8_t*>(packed);
   if (kt_per == 0) {
-    gemm_mfma_kernel<MB, NB, WM, WN, S, OCC, WB><<<dim3(static_cast<unsigned>(mt * ntl)), kThreads, 0, s>>>(
+    gemm_mfma_kernel<MB, NB, WM, WN, S, OCC, WB, false, false, KG><<<dim3(static_cast<unsigned>(mt * ntl)),
+                                                                    kThreadsWG, 0, s>>>(
         p, gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl), y, acc, nullptr, nullptr,
         0, nullptr);
     return hipGetLastError();
@@ -851,8 +918,8 @@ hipError_t launch_mfma(const void* packed, const float* gamma, Dequant dq, int64
   const int64_t count = m * n;
   const unsigned fill_grid = static_cast<unsigned>(count / 256 + 1 < 2048 ? count / 256 + 1 : 2048);
   split_zero_kernel<<<fill_grid, 256, 0, s>>>(sums, count);
-  gemm_mfma_kernel<MB, NB, WM, WN, S, OCC, WB, false, true><<<dim3(static_cast<unsigned>(mt * ntl * slices)), kThreads,
-                                                               0, s>>>(
+  gemm_mfma_kernel<MB, NB, WM, WN, S, OCC, WB, false, true, KG><<<dim3(static_cast<unsigned>(mt * ntl * slices)),
+                                                                   kThreadsWG, 0, s>>>(
       p, gamma, dq, n, k, kt, xq, amax, m, static_cast<int>(mt), static_cast<int>(ntl), y, acc, nullptr, nullptr,
       kt_per, sums);
   split_finish_kernel<<<fill_grid, 256, 0, s>>>(sums, y, gamma, dq, amax, m, n);
@@ -875,20 +942,27 @@ hipError_t launch_mfma_swiglu(const void* packed_g, const float* gamma_g, const 
 }
 
 // Configurations of the matrix-core kernel.  Measured on MI355X over the 8B-
-// and 70B-shaped matrices, every candidate at every shape (us per launch):
+// and 70B-shaped matrices (us per launch, cold weights):
 //   * 128 x 256, two stages, weights in registers (MB 4, NB 2, 1 x 4 waves)
-//     for more than 64 tokens on wide matrices: 512 x 28672 x 4096 57.0,
-//     against 59.3 for 64 x 128 and 60.4 for 64 x 256;
+//     for more than 64 tokens on wide matrices: 512 x 28672 x 4096 53-54;
+//   * 64 x 128 with two k-groups (MB 2, NB 1, 1 x 4 waves x 2, ring of three)
+//     when the 64 x 128 grid has 129..256 tiles, one workgroup per CU:
+//     512 x 4096 x 4096 12.5 and 512 x 4096 x 14336 31.1-32.0, against
+//     12.8-12.9 and 32.8-33.8 with four waves;
 //   * 64 x 128 with a ring of three stages (MB 2, NB 1, 1 x 4) otherwise:
-//     512 x 6144 x 4096 19.7, 512 x 4096 x 14336 35.8, 64 x 57344 x 8192
-//     40.5, 64 x 8192 x 28672 29.1 (k-sliced; 34.2 with two stages).
-//     Rings of four or six stages (one workgroup per CU) were no faster, nor
-//     were 64 x 256, 128 x 128 or 2 x 2-wave tiles: the small tiles are
-//     bound by the activation operand reads from LDS (1 KiB per MFMA, LDS
-//     active about 64% of the time), not by memory latency.
+//     512 x 6144 x 4096 17.4-18.2, 64 x 57344 x 8192 37.6-38.5,
+//     64 x 8192 x 28672 27.8-28.5 (k-sliced).
+//   Not faster at those shapes: rings of four to six stages, 2 x 2 waves of
+//   32 x 64, waves of 64 x 64 with two or four k-groups, reading operands two
+//   to eight steps ahead.  With four waves per CU each SIMD runs one wave,
+//   whose matrix-core stream stalls at every copy issue, LDS read and weight
+//   expansion (the same instruction mix in isolation: 39% of peak with four
+//   waves, 50% with eight); about 5 us of each launch is fixed (the first
+//   copies from HBM, the fp32 outputs written after the last step).
 enum MfmaConfig {
-  kT128x256 = 0,  // MB 4, NB 2, 1 x 4 waves, 2 stages (weights in registers)
-  kT64x128 = 1,   // MB 2, NB 1, 1 x 4 waves, ring of 3 stages
+  kT128x256 = 0,   // MB 4, NB 2, 1 x 4 waves, 2 stages (weights in registers)
+  kT64x128 = 1,    // MB 2, NB 1, 1 x 4 waves, ring of 3 stages
+  kT64x128k2 = 2,  // MB 2, NB 1, 1 x 4 waves x 2 k-groups, ring of 3 stages
 };
 
 #ifndef BITLINEAR_GEMM_FORCE
@@ -898,6 +972,9 @@ enum MfmaConfig {
 MfmaConfig choose_mfma(int64_t m, int64_t n) {
   if (BITLINEAR_GEMM_FORCE >= 0) return static_cast<MfmaConfig>(BITLINEAR_GEMM_FORCE);
   if (m > 64 && n >= 16384) return kT128x256;
+  // (more than 128 tiles: no k-slices at either occupancy)
+  const int64_t tiles = ((m + 63) / 64) * ((n + 127) / 128);
+  if (tiles > 128 && tiles <= kCus) return kT64x128k2;
   return kT64x128;
 }
 
@@ -905,6 +982,9 @@ template <int WB>
 hipError_t launch_mfma_any(MfmaConfig c, const void* packed, const float* gamma, Dequant dq, int64_t n, int64_t k,
                            const int8_t* xq, const float* amax, int64_t m, float* y, int32_t* acc, hipStream_t s) {
   if (c == kT128x256) return launch_mfma<4, 2, 1, 4, 2, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+  if constexpr (WB == 2) {  // (k-groups: ternary weights)
+    if (c == kT64x128k2) return launch_mfma<2, 1, 1, 4, 3, 1, WB, 2>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
+  }
   return launch_mfma<2, 1, 1, 4, 3, 2, WB>(packed, gamma, dq, n, k, xq, amax, m, y, acc, s);
 }
 

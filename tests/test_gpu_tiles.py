@@ -11,7 +11,9 @@ configurations at a size with ragged token and row tails:
   * mid-width matrices (n around 6144, the QKV projections), with more and
     with fewer than 64 tokens;
   * narrow matrices with long rows (n = 4096 / 8192, the O and down
-    projections), including the k-sliced grid that 64 tokens give;
+    projections), including the k-sliced grid that 64 tokens give and the
+    two-k-group workgroups that 129..256 output tiles take (200 x 4112,
+    130 x 6160);
   * the SwiGLU epilogue on wide gate / up matrices;
 for ternary and for binary weights.  Bar: codes, accumulators bit-exact on
 every output; y within 1e-5 relative and exactly 0 where the oracle's is 0.
