@@ -67,6 +67,17 @@ __device__ __forceinline__ void chunk_values(const uint4& xc, const float* __res
   }
 }
 
+// True when a' = fl32(av * r), r = 1 / sqrt(ms), is certainly at least
+// 1e-8, judged in fp32: ms inside the normal fp32 range, where the fp32
+// estimate of av * r is within a few roundings of the exact one, and that
+// estimate at least twice the floor.  Then the codes' scale is 127 / av
+// (rmsnorm_scales) and no fp64 root is needed for them.
+__device__ __forceinline__ bool floor_cannot_bind(float av, double ms) {
+  if (!(ms >= 1.1754944e-38 && ms <= 3.4028235e+38)) return false;
+  const float est = av * rsqrtf(static_cast<float>(ms));
+  return est >= 2e-8f && est <= 3.0e+38f;
+}
+
 // Vector path: k % 8 == 0, x and gain 16-byte aligned, xq 8-byte aligned.
 // 1024 threads per token; the row fits in CPT chunks per thread, and the
 // products v = x * gain stay in registers between the two passes, so x and
@@ -114,23 +125,40 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_vec(const uint16_t
     mall = max(mall, red_max[w]);
     sall += red_ss[w];
   }
-  float ap, s;
-  rmsnorm_scales(__uint_as_float(mall), 1.0 / sqrt(sall / static_cast<double>(k) + static_cast<double>(eps)), &ap, &s);
   uint2* out = reinterpret_cast<uint2*>(xq + row * k);
+  auto write_codes = [&](float s) {
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int idx = threadIdx.x + i * kNormThreads;
-    if (idx < chunks) {
-      uint32_t lo = 0, hi = 0;
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = threadIdx.x + i * kNormThreads;
+      if (idx < chunks) {
+        uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lo |= code_of(vk[i][j], s) << (8 * j);
-        hi |= code_of(vk[i][4 + j], s) << (8 * j);
+        for (int j = 0; j < 4; ++j) {
+          lo |= code_of(vk[i][j], s) << (8 * j);
+          hi |= code_of(vk[i][4 + j], s) << (8 * j);
+        }
+        out[idx] = make_uint2(lo, hi);
       }
-      out[idx] = make_uint2(lo, hi);
     }
+  };
+  // The codes' scale 127 / max|v| needs no r unless the 1e-8 floor binds on
+  // the normalised token (floor_cannot_bind).  Otherwise every thread takes
+  // the exact fp64 path; only thread 0 forms the exact a' for the output.
+  const float av = __uint_as_float(mall);
+  const double ms = sall / static_cast<double>(k) + static_cast<double>(eps);
+  if (floor_cannot_bind(av, ms)) {
+    write_codes(127.0f / av);
+    if (threadIdx.x == 0) {
+      float ap, s;
+      rmsnorm_scales(av, 1.0 / sqrt(ms), &ap, &s);
+      amax[row] = ap;
+    }
+  } else {
+    float ap, s;
+    rmsnorm_scales(av, 1.0 / sqrt(ms), &ap, &s);
+    write_codes(av > 0.0f ? s : 0.0f);  // all-zero v: every code is 0
+    if (threadIdx.x == 0) amax[row] = ap;
   }
-  if (threadIdx.x == 0) amax[row] = ap;
 }
 
 // General path: any k and alignment; two passes over the row with scalar loads.
@@ -164,15 +192,29 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_any(const uint16_t* __
     mall = max(mall, red_max[w]);
     sall += red_ss[w];
   }
-  float ap, s;
-  rmsnorm_scales(__uint_as_float(mall), 1.0 / sqrt(sall / static_cast<double>(k) + static_cast<double>(eps)), &ap, &s);
   int8_t* out = xq + row * k;
-  for (int64_t i = threadIdx.x; i < k; i += kThreads) {
-    const float xv = __uint_as_float(static_cast<uint32_t>(xr[i]) << 16);
-    const float v = gain ? xv * gain[i] : xv;
-    out[i] = static_cast<int8_t>(code_of(v, s));
+  auto write_codes = [&](float s) {
+    for (int64_t i = threadIdx.x; i < k; i += kThreads) {
+      const float xv = __uint_as_float(static_cast<uint32_t>(xr[i]) << 16);
+      const float v = gain ? xv * gain[i] : xv;
+      out[i] = static_cast<int8_t>(code_of(v, s));
+    }
+  };
+  // (as in rmsnorm_quant_vec)
+  const float av = __uint_as_float(mall);
+  const double ms = sall / static_cast<double>(k) + static_cast<double>(eps);
+  float ap, s;
+  if (floor_cannot_bind(av, ms)) {
+    write_codes(127.0f / av);
+    if (threadIdx.x == 0) {
+      rmsnorm_scales(av, 1.0 / sqrt(ms), &ap, &s);
+      amax[row] = ap;
+    }
+  } else {
+    rmsnorm_scales(av, 1.0 / sqrt(ms), &ap, &s);
+    write_codes(av > 0.0f ? s : 0.0f);
+    if (threadIdx.x == 0) amax[row] = ap;
   }
-  if (threadIdx.x == 0) amax[row] = ap;
 }
 
 // ---------------------------------------------------------------------------
