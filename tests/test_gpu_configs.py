@@ -13,7 +13,8 @@ RMSNorm and the quantisation, in the decode prologue; the fp32 quantisation
 for the down projection) run at every matrix shape of the decode workloads
 with one and two tokens; their codes, a', accumulators and outputs are
 compared on every output (RMSNorm: with the per-position tie allowance of
-tests/gpu_util.py).
+tests/gpu_util.py).  The fused binary decode (1-bit sign weights) runs at
+every such shape with one token, compared the same way.
 """
 from __future__ import annotations
 
@@ -54,7 +55,6 @@ def test_workload_matrix_full_size(blq, wkey, j):
     same = check_gamma(host(gamma)[0], g_or, tag)
     q_or = oracle.ternarize(w, g_or)
     bad_rows = compare_codes(host(blq.bitlinear_unpack_weights(packed, n, k)), q_or, w, g_or, same, tag)
-    del w
     rng = np.random.default_rng(j)
     for m in wl.ms:
         log("  m=%d" % m)
@@ -86,6 +86,7 @@ def test_workload_matrix_full_size(blq, wkey, j):
         compare_y(y[rows, cols], y_or, tag)
     if min(wl.ms) <= 2:  # a decode workload: the fused entry points it times, at one and two tokens
         fused_checks(blq, wl, j, packed, gamma, q_or, g_or, bad_rows, tag)
+        binary_fused_check(blq, wl, j, w, tag)
 
 
 def fused_checks(blq, wl, j, packed, gamma, q_or, g_or, bad_rows, tag):
@@ -125,3 +126,27 @@ def fused_checks(blq, wl, j, packed, gamma, q_or, g_or, bad_rows, tag):
             acc_o = oracle.contract(xq_o, q_or)
             compare_acc_flips(host(acc_d)[:, keep], acc_o[:, keep], flips, t)
             compare_y_flips(host(y_d)[:, keep], oracle.dequant(acc_o, g_or, a_o)[:, keep], flips, g_or, a_o, t)
+
+
+def binary_fused_check(blq, wl, j, w, tag):
+    """The fused binary decode (1-bit sign weights, the layer scale an input)
+    the binary decode records time, at one token: codes, a' and accumulators
+    bit-exact on every output, y within 1e-5."""
+    torch = torch_mod()
+    n, k = wl.matrices[j].n, wl.matrices[j].k
+    if not blq.bitlinear_quant_forward_binary_supported(1, k):
+        return
+    t = "%s fused binary m=1" % tag
+    log("  " + t)
+    s = np.float32(np.abs(w).astype(np.float64).mean())  # a stand-in for the learned layer scale
+    packed = blq.bitlinear_pack_binary(to_dev(w))
+    x = synth.activations_bf16(synth.seed_for(wl, 0, j, synth.ROLE_ACT, extra=300), 1, k, wl.outlier_frac)
+    acc_d = torch.empty((1, n), dtype=torch.int32, device="cuda")
+    xq_d = torch.empty((1, k), dtype=torch.int8, device="cuda")
+    a_d = torch.empty(1, dtype=torch.float32, device="cuda")
+    y_d = blq.bitlinear_quant_forward_binary(packed, to_dev(np.array([s], np.float32)), n, k, to_dev_bits(x),
+                                             acc=acc_d, xq=xq_d, x_absmax=a_d)
+    ref = oracle.forward_binary(x, w, s)
+    assert np.array_equal(host(xq_d), ref["xq"]) and np.array_equal(host(a_d), ref["amax"]), t
+    assert np.array_equal(host(acc_d), ref["acc"]), t
+    compare_y(host(y_d), ref["y"], t)

@@ -16,7 +16,7 @@ import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 RECORDS = sorted(glob.glob(os.path.join(ROOT, "profiles", "bench_*.json")))
-PEAKS = {"GB/s": 8000.0, "TOPS": 5000.0, "TFLOP/s": 5000.0}  # MI355X HBM; dense int8 matrix cores (5.0 POP/s)
+PEAKS = {"GB/s": 8000.0, "TOPS": 5000.0}  # MI355X HBM; dense int8 matrix cores (5.0 POP/s)
 
 
 def _load(path):
@@ -53,6 +53,13 @@ def test_record_is_consistent(path):
     assert r["peak"] == PEAKS[r["unit"]]
     assert r["bound"] == ("hbm" if r["unit"] == "GB/s" else "mfma")
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    # no kernel time longer than the step: the isolated replays' time per step
+    # is either within the step's or the record says it was capped to it
+    assert r["kernel_ms_per_step"] <= ms * 1.0005 or "exceeds the step's" in r["timing"], path
+    assert r["achieved"] <= r["peak"]
+    if r["unit"] == "TOPS":
+        # the method's own work: one add or subtract per non-zero weight and token
+        assert 0 < r["frac_nonzero_adds"] <= r["frac"] / 2 + 1e-4
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0 and c["sample"]
 
@@ -74,6 +81,16 @@ def test_traffic_comes_from_current_counters(path):
     assert counters["kernel_source_hash"] == bench.kernel_source_hash(sources)
 
 
-def test_default_record_carries_traffic():
-    d = _load(os.path.join(ROOT, "profiles", "bench_b2b_decode_m1.json"))
-    assert d["roofline"]["traffic"] is not None
+def test_default_record_carries_traffic_and_the_decode_extras():
+    """The default run (no arguments): the 8B prefill, with the same stack's
+    decode at 1, 4 and 8 tokens on the same weights, each checked against the
+    oracle and each carrying HBM traffic from the current counters."""
+    d = _load(os.path.join(ROOT, "profiles", "bench_l8b_prefill_m512.json"))
+    assert d["config"]["key"] == "l8b_prefill" and d["roofline"]["traffic"] is not None
+    extras = d["extra_configs"]
+    assert sorted(extras) == ["l8b_decode_m1", "l8b_decode_m4", "l8b_decode_m8"]
+    for key, e in extras.items():
+        assert e["parity_vs_oracle"]["ok"] is True, key
+        assert e["unit"] == "GB/s" and e["roofline"]["traffic"] is not None, key
+        assert e["roofline"]["kernel_ms_per_step"] <= e["ms_per_step"] * 1.0005 or \
+            "exceeds the step's" in e["roofline"]["timing"], key
