@@ -47,6 +47,9 @@ TILE_CASES = [
     (64, 8192, 8192),     # 128 output tiles: the k extent is split
     (200, 4112, 4096),    # narrow, long rows
     (513, 4096, 1024),    # 512 tokens plus a one-token tail
+    (200, 4112, 1040),    # two k-groups with a ragged last k-step (1040 = 4 * 256 + 16)
+    (130, 16400, 1040),   # the wide tile with the same ragged k-step
+    (64, 8192, 4112),     # k-sliced grid whose last slice ends in a ragged k-step
 ]
 
 
