@@ -7,26 +7,29 @@
 // Framework", section "Scalability with Thread Count": prompt processing is
 // compute-intensive), so it runs on the int8 matrix cores.
 //
-// Tiling: a workgroup of 4 waves (WM x WN) owns a BM x BN output tile
-// (tokens x weight rows) and walks k in 256-column steps, the width of one
-// packed weight tile.  A step's operands are the BM x 256 int8 activation
-// tile and the BN/16 packed weight tiles (1 KiB each, copied verbatim: still
-// 2 bits per weight).
+// Tiling: a workgroup owns a BM x BN output tile (tokens x weight rows) and
+// walks k in 256-column steps, the width of one packed weight tile.  A step's
+// operands are the BM x 256 int8 activation tile and the BN/16 packed weight
+// tiles (1 KiB each, copied verbatim: still 2 bits per weight).  Its waves
+// are WM x WN blocks of the tile, or KG groups of them that share the tile
+// and each multiply part of every step (gemm_mfma_kernel).
 //
 // Matrix-core instruction: v_mfma_i32_32x32x32_i8 (measured ~4.5 POPS on
-// MI355X, against ~2.5-3.2 for the 16x16x64 form).  With the packed layout
-// unchanged, step q (0..7) of a 256-column tile takes columns 32q .. 32q+31:
-// lane (row r, half h) supplies word 2(q%2)+h of slot (r%16)+16(q/2), i.e.
-// 16 columns, expanded to int8 64*w with one shift and one mask per 4
-// weights (expand_ternary) and reused for every 32-token block of the wave;
-// its A operand is the same 16 columns of its token.  The accumulators hold
+// MI355X, against ~2.5-3.2 for the 16x16x64 form).  A 32-bit word of a
+// packed slot holds 16 columns of one weight row; expand_ternary turns it
+// into the int8 operand 64 * w with one shift and one mask per 4 weights,
+// reused for every 32-token block of the wave.  The accumulators hold
 // 64 * acc exactly; the epilogue shifts, scales by gamma * a'[t] / 127 and
-// stores fp32.
+// stores fp32.  The order in which a step's eight MFMAs take the columns is
+// each kernel's own (gemm_mfma_kernel: chunk 8h + q of the step for MFMA q
+// and lane half h, so a 16-byte slot serves four MFMAs; gemm_kernel: words
+// 2(q % 2) + h of slot (r % 16) + 16(q / 2)); the activation operand takes
+// the same columns.
 //
-// Main path (k % 16 == 0, 16-byte aligned codes): an S-stage ring of LDS
-// buffers filled by buffer-to-LDS copies (buffer_load_dwordx4 ... lds), S - 1
-// steps in flight, one barrier per step; see gemm_dma_kernel.  Otherwise a
-// register-staged two-stage variant (gemm_kernel) handles any k.
+// Main path (k % 16 == 0, 16-byte aligned codes): gemm_mfma_kernel, with the
+// operands in LDS stages filled by buffer-to-LDS copies and one barrier per
+// step.  Otherwise gemm_kernel, register-staged over two stages, handles any
+// k and alignment.
 //
 // The per-token output scale gamma * a'[t] / 127 is computed once per
 // workgroup into LDS, so the epilogue is stores only.

@@ -102,3 +102,16 @@ def test_fused_default_follows_the_measured_limits():
     # the fused call's algorithmic bytes: bf16 activations instead of codes and a'
     n, k, m = 4096, 14336, 4
     assert bench.fused_bytes(m, n, k) - bench.forward_bytes(m, n, k) == 2 * m * k - (m * k + 4 * m)
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    """The counters in profiles/ are tied to the kernels' code: a comment or
+    whitespace edit keeps the hash, any code edit changes it, and comment
+    markers inside string or character literals are code."""
+    import bench
+    base = 'int f(int a) { return a + 1; } // tail\n/* block\n comment */ const char* s = "//x";'
+    assert bench._code_only(base) == bench._code_only(base.replace("// tail", "// other words"))
+    assert bench._code_only(base) == bench._code_only(base.replace("a + 1", "a  +\n 1"))
+    assert bench._code_only(base) != bench._code_only(base.replace("a + 1", "a + 2"))
+    assert bench._code_only(base) != bench._code_only(base.replace('"//x"', '"//y"'))
+    assert "//x" in bench._code_only(base) and "block" not in bench._code_only(base)
