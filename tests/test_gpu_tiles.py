@@ -50,6 +50,8 @@ TILE_CASES = [
     (200, 4112, 1040),    # two k-groups with a ragged last k-step (1040 = 4 * 256 + 16)
     (130, 16400, 1040),   # the wide tile with the same ragged k-step
     (64, 8192, 4112),     # k-sliced grid whose last slice ends in a ragged k-step
+    (256, 8192, 256),     # two k-groups, one k-step (fewer steps than the ring's stages)
+    (130, 6160, 16),      # two k-groups, one partial k-step of 16 columns
 ]
 
 
