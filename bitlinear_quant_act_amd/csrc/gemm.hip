@@ -701,38 +701,46 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void gemm_mfma_kernel(
   }
 
   if constexpr (KG > 1) {
-    // the k-groups' partial sums meet in LDS; every wave is past its last
-    // stage read (the barrier), and the last step waited for every copy
+    // the two k-groups' partial sums meet in LDS, each group finishing one
+    // half of the token blocks (group 0 the first MB / 2, group 1 the rest):
+    // each hands the other its half, so the stores are split between them.
+    // Every wave is past its last stage read (the barrier), and the last
+    // step waited for every copy.
+    static_assert(KG == 2 && MB % 2 == 0, "two k-groups, even token blocks");
     __syncthreads();
     int32_t* red = reinterpret_cast<int32_t*>(ring);
-    constexpr int kPerWave = MB * NB * 16 * 64;  // int32 per wave
-    if (kg > 0) {
+    constexpr int kHalf = MB / 2 * NB * 16 * 64;  // int32 per wave and half
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mh = 0; mh < MB / 2; ++mh)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            red[((kg - 1) * WM * WN + wl) * kPerWave + ((mb * NB + nb) * 16 + r) * 64 + lane] = acc[mb][nb][r];
-    }
+        for (int r = 0; r < 16; ++r)
+          red[(kg * WM * WN + wl) * kHalf + ((mh * NB + nb) * 16 + r) * 64 + lane] =
+              kg == 0 ? acc[MB / 2 + mh][nb][r] : acc[mh][nb][r];
     __syncthreads();
-    if (kg > 0) return;  // no barrier follows
-#pragma unroll 1
-    for (int g = 1; g < KG; ++g)  // (one group's partials in flight at a time)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mh = 0; mh < MB / 2; ++mh)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc[mb][nb][r] += red[((g - 1) * WM * WN + wl) * kPerWave + ((mb * NB + nb) * 16 + r) * 64 + lane];
+        for (int r = 0; r < 16; ++r) {
+          const int v = red[((1 - kg) * WM * WN + wl) * kHalf + ((mh * NB + nb) * 16 + r) * 64 + lane];
+          if (kg == 0)
+            acc[mh][nb][r] += v;
+          else
+            acc[MB / 2 + mh][nb][r] += v;
+        }
   }
+  // token blocks this wave stores: all, or its group's half
+  auto mine = [&](int mb) { return KG == 1 || (mb < MB / 2) == (kg == 0); };
 
   // 32 x 32 block layout: element r of lane l is token 8 * (r / 4) + 4 * (l / 32) + r % 4, row l % 32
   const int tw = wm * MB * 32;  // the wave's first token inside the tile
   if (SPLIT) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      if (!mine(mb)) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t t = m0 + tw + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -784,6 +792,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void gemm_mfma_kernel(
   int32_t* al = acc_out ? acc_out + (m0 + tw + 4 * h) * n + f0 + wn * NB * 32 + l32 : nullptr;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
+    if (!mine(mb)) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tr = mb * 32 + 8 * (r >> 2) + (r & 3);  // token of the lane's element, less 4h
