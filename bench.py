@@ -4,7 +4,8 @@
 One step = one pass of the per-token path over every BitLinear of the
 workload, in layer order: bitlinear_quant_act (bf16 -> int8 codes + a') then
 bitlinear_forward (m <= 16) or bitlinear_forward_batched (m > 16) per matrix
-(decode at one or two tokens: the fused bitlinear_quant_forward).  The
+(decode: the fused bitlinear_quant_forward instead, at one token and wherever
+m * k is small; fused_default).  The
 weights are packed once before timing (the one-time preparation step);
 packing is timed separately and reported under "pack".  The step is captured
 once into a HIP graph and replayed; inputs are resident in HBM and the
@@ -104,19 +105,22 @@ def quant_bytes(m: int, k: int) -> int:
 #   binary    -- 1-bit sign weights with a per-layer scale (bitlinear_forward_binary; fused at m = 1)
 MODES = ("tensor128", "rowscale", "binary")
 
-# Decode token counts up to which the fused entry point (the quantisation, or
-# RMSNorm + quantisation, in the GEMV prologue) is the default.  Every
-# workgroup re-quantises all m tokens, so the fusion saves a launch but adds
-# m * k of redundant prologue work.  Measured on the 2B and 8B stacks against
-# quant + forward: plain, fused wins at m = 2 (+9% / +14%); at m = 4 it wins
-# on the 2B stack (+4%) and loses on the 8B stack (-2%).  RMSNorm at m = 2:
-# +7% on the 2B stack, -4% on the 8B stack.  The SwiGLU block and the variant
-# modes: only m = 1.
-FUSED_MAX_M = {"plain": 2, "rmsnorm": 2}
+# The fused entry point (the quantisation, or RMSNorm + quantisation, in the
+# GEMV prologue) is chosen per matrix: always for one token; for more tokens
+# where m * k is at most FUSED_MAX_MK values.  Every workgroup re-quantises
+# all m tokens, so the fusion saves a launch but adds m * k of redundant
+# prologue work.  Measured per shape (us per call, fused / quant + forward,
+# one box): plain 4096 x 4096 at m = 2 / 4 / 8 4.59 / 5.63, 5.36 / 5.65,
+# 6.56 / 6.03; 2560 x 6912 at m = 4 6.61 / 6.47; 4096 x 14336 at m = 2 7.86 /
+# 8.37, at m = 4 10.37 / 8.87.  RMSNorm: 2560 x 6912 at m = 2 6.64 / 6.94;
+# 6144 x 4096 at m = 4 9.41 / 7.16; 4096 x 14336 at m = 2 10.44 / 9.38.  The
+# SwiGLU block and the variant modes: one token only.
+FUSED_MAX_MK = {"plain": 28672, "rmsnorm": 13824}
+FUSED_MAX_M = 16  # the decode entry points' token limit
 
 
-def fused_default(variant: str, m: int) -> bool:
-    return m <= FUSED_MAX_M.get(variant, 1)
+def fused_default(variant: str, m: int, k: int) -> bool:
+    return m == 1 or (m <= FUSED_MAX_M and m * k <= FUSED_MAX_MK.get(variant, 0))
 
 
 def mode_forward_bytes(variant: str, m: int, n: int, k: int, fused: bool = False) -> int:
@@ -329,51 +333,55 @@ def _mode_fused(blq, mat, stream):  # binary weights, quantisation in the decode
     blq.bitlinear_quant_forward_binary(mat.packed, mat.gamma, mat.n, mat.k, mat.x, y=mat.y, stream=stream)
 
 
-def launch_step(blq, mats, m, stream, fused, variant="plain"):
-    """One pass of the per-token path over every matrix, in layer order."""
+def launch_step(blq, mats, m, stream, fz, variant="plain"):
+    """One pass of the per-token path over every matrix, in layer order;
+    fz[j]: matrix j of a layer takes the fused quant + forward call."""
     if variant in MODES:
         for mat in mats:
-            if fused:
+            if fz[mat.j]:
                 _mode_fused(blq, mat, stream)
             else:
                 _mode_quant(blq, mat, stream, variant)
                 _mode_forward(blq, mat, stream, variant)
         return
     if variant == "swiglu":
-        return launch_step_swiglu(blq, mats, m, stream, fused)
-    if fused:
-        for mat in mats:
+        return launch_step_swiglu(blq, mats, m, stream, all(fz))
+    fwd = _forward_fn(blq, m, variant)
+    for mat in mats:
+        if fz[mat.j]:
             _fused(blq, mat, stream)
-        return
-    fwd = _forward_fn(blq, m, variant)
-    for mat in mats:
-        _quant(blq, mat, stream)
-        fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
+        else:
+            _quant(blq, mat, stream)
+            fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
 
 
-def launch_kernel_only(blq, mats, m, stream, which, fused=False, variant="plain"):
-    """Launches of one kernel over every matrix ('quant', 'forward', 'fused',
-    'swiglu': the gate+up launches of the SwiGLU variant)."""
+def launch_kernel_only(blq, mats, m, stream, which, fz, variant="plain"):
+    """Launches of one kernel over every matrix: 'quant' (the quantisation of
+    the matrices that take it separately), 'main' (each matrix's forward
+    call: the fused quant + forward where fz marks it), 'swiglu' (the gate+up
+    launches of the SwiGLU variant)."""
     fwd = _forward_fn(blq, m, variant)
-    if variant in MODES:
-        for mat in mats:
-            if which == "quant":
-                _mode_quant(blq, mat, stream, variant)
-            elif which == "forward":
-                _mode_forward(blq, mat, stream, variant)
-            else:
-                _mode_fused(blq, mat, stream)
-        return
     for mat in mats:
+        f = fz[mat.j]
         if which == "swiglu":
             if mat.name == "gate_up":
-                _swiglu(blq, mat, stream, fused)
+                _swiglu(blq, mat, stream, f)
         elif which == "quant":
-            _quant(blq, mat, stream)
-        elif which == "forward":
-            fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
-        else:
+            if f:
+                continue
+            if variant in MODES:
+                _mode_quant(blq, mat, stream, variant)
+            else:
+                _quant(blq, mat, stream)
+        elif variant in MODES:
+            if f:
+                _mode_fused(blq, mat, stream)
+            else:
+                _mode_forward(blq, mat, stream, variant)
+        elif f:
             _fused(blq, mat, stream)
+        else:
+            fwd(mat.packed, mat.gamma, mat.n, mat.k, mat.xq, mat.amax, y=mat.y, stream=stream)
 
 
 def swiglu_bytes(m: int, f: int, k: int) -> int:
@@ -540,22 +548,45 @@ def cpu_baseline(oracle_mod, reps_mats, m, wl, budget_s, variant="plain"):
             "max_rel_err": worst, "chain_ok": chain_ok, "chain_skipped": chain_skipped, "phases": phase}
 
 
+def default_fused(wl, m, variant):
+    """Per matrix j of a layer: whether the step's default takes the fused
+    quant + forward call for it (fused_default); the SwiGLU block and the
+    binary mode fuse at one token only, the table-lookup kernel and the
+    other modes never."""
+    if variant == "lut" or variant in ("tensor128", "rowscale"):
+        return (False,) * len(wl.matrices)
+    if variant in ("swiglu", "binary"):
+        return (m == 1,) * len(wl.matrices)
+    return tuple(fused_default(variant, m, mt.k) for mt in wl.matrices)
+
+
 def choose_fused(blq, wl, m, variant, force_fused=False, force_unfused=False):
-    """Whether the step takes the fused quant + forward entry point: it
-    re-quantises the tokens in every workgroup, which pays off for a few
-    tokens (FUSED_MAX_M); more go through quant + forward."""
+    """Per matrix j of a layer: whether the step takes the fused quant +
+    forward call for it.  The fused call re-quantises the tokens in every
+    workgroup, which pays off for a few tokens on short rows (fused_default);
+    the others go through quant + forward.  --fused fuses every matrix the
+    call supports, --unfused none; the SwiGLU block and the binary mode are
+    fused as a whole or not at all."""
     mode = variant if variant in MODES else None
+    nmat = len(wl.matrices)
+    if force_unfused or variant == "lut" or mode in ("tensor128", "rowscale"):
+        return (False,) * nmat
     if mode == "binary":
-        return (m == 1 and not force_unfused and
-                all(blq.bitlinear_quant_forward_binary_supported(m, mt.k) for mt in wl.matrices))
-    return ((fused_default(variant, m) or force_fused) and not force_unfused and variant != "lut" and mode is None
-            and all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices))
+        return (m == 1 and all(blq.bitlinear_quant_forward_binary_supported(m, mt.k) for mt in wl.matrices),) * nmat
+    if variant == "swiglu":
+        return ((m == 1 or force_fused) and
+                all(blq.bitlinear_quant_forward_supported(m, mt.k) for mt in wl.matrices),) * nmat
+    return tuple((fz or force_fused) and blq.bitlinear_quant_forward_supported(m, mt.k)
+                 for fz, mt in zip(default_fused(wl, m, variant), wl.matrices))
 
 
-def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_frac=None):
+def measure(torch, blq, wl, m, reps, variant, fz, steps, warmup, eager, nz_frac=None):
     """Time K steps (after W warmup steps) of the per-token path over the
-    packed workload, and the dominant kernel on its own.  Returns the record
-    without the CPU baseline."""
+    packed workload, and the dominant kernel on its own; fz[j]: matrix j of a
+    layer takes the fused quant + forward call.  Returns the record without
+    the CPU baseline."""
+    fused = all(fz)                # every matrix fused (the SwiGLU block and the modes: all or none)
+    mixed = any(fz) and not fused  # decode: fused where m * k is small, quant + forward elsewhere
     batched = m > blq.BITLINEAR_FORWARD_MAX_M
     mode = variant if variant in MODES else None
     lut = variant == "lut"
@@ -571,7 +602,8 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
         return forward_bytes(m, mt.n, mt.k)
 
     step_bytes = sum(call_bytes(mt) for mt in mats0)
-    step_quant_bytes = sum(quant_bytes(m, mt.k) for mt in mats0)
+    quant_mats = [mt for mt in mats0 if not fz[mt.j]]  # the matrices with a separate quantisation launch
+    step_quant_bytes = sum(quant_bytes(m, mt.k) for mt in quant_mats)
     step_ops = sum(2 * m * mt.n * mt.k for mt in mats0)
 
     stream = torch.cuda.Stream()
@@ -584,7 +616,7 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for mats in reps:
-                launch_step(blq, mats, m, torch.cuda.current_stream(), fused, variant)
+                launch_step(blq, mats, m, torch.cuda.current_stream(), fz, variant)
         torch.cuda.synchronize()
     per_run = len(reps)
 
@@ -592,7 +624,7 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
         if eager:
             with torch.cuda.stream(stream):
                 for mats in reps:
-                    launch_step(blq, mats, m, stream, fused, variant)
+                    launch_step(blq, mats, m, stream, fz, variant)
         else:
             graph.replay()
 
@@ -615,28 +647,32 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
     ms_per_step = repeat_ms[0]
     log("%s m=%d: timed %d steps: %.4f ms/step" % (wl.key, m, steps_timed, ms_per_step))
 
-    # Dominant kernel (the forward, or the fused quant + forward): HIP events
-    # on its stream around graph replays that hold only that kernel's
-    # launches over every matrix of the workload (no event per launch: an
-    # event pair costs more than a small kernel).  Average launch duration =
-    # elapsed / launches.  The quantisation kernel is timed the same way.
-    if not fused:  # make sure the codes are current for forward-only replays
+    # Dominant kernel (each matrix's forward call: the forward, or the fused
+    # quant + forward): HIP events on its stream around graph replays that
+    # hold only that kernel's launches over every matrix of the workload (no
+    # event per launch: an event pair costs more than a small kernel).
+    # Average launch duration = elapsed / launches.  The quantisation kernel
+    # is timed the same way.
+    if quant_mats:  # make sure the codes are current for forward-only replays
         with torch.cuda.stream(stream):
-            launch_kernel_only(blq, mats0, m, stream, "quant", False, variant)
+            launch_kernel_only(blq, mats0, m, stream, "quant", fz, variant)
         torch.cuda.synchronize()
     replays = max(2, min(10, steps))
-    dom = "swiglu" if sw else "fused" if fused else "forward"
+    dom = "swiglu" if sw else "main"
     dom_mats = [mt for mt in mats0 if mt.name == "gate_up"] if sw else mats0
 
     def all_reps(which):
-        return lambda st: [launch_kernel_only(blq, mats, m, st, which, fused, variant) for mats in reps]
+        return lambda st: [launch_kernel_only(blq, mats, m, st, which, fz, variant) for mats in reps]
 
     dom_ms = time_graph(torch, stream, all_reps(dom), replays) / len(reps)
     fw_avg_us = dom_ms / len(dom_mats) * 1e3
     q_ms = None
-    if not fused:
+    if quant_mats:
         q_ms = time_graph(torch, stream, all_reps("quant"), replays) / len(reps)
-    per_call = fused_bytes if fused else forward_bytes
+
+    def main_bytes(mt):  # algorithmic bytes of matrix mt's forward call
+        f = fz[mt.j]
+        return (fused_bytes if f else forward_bytes)(m, mt.n, mt.k) + (4 * mt.k if norm and f else 0)
     if sw:
         # fused: bf16 input and gains instead of codes and a'
         fw_bytes = sum(swiglu_bytes(m, mt.n // 2, mt.k) + ((m * mt.k + 4 * mt.k - 4 * m) if fused else 0)
@@ -646,7 +682,7 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
         fw_bytes = sum(mode_forward_bytes(mode, m, mt.n, mt.k, fused) for mt in mats0)
         fw_ops = step_ops
     else:
-        fw_bytes = sum(per_call(m, mt.n, mt.k) + (4 * mt.k if norm and fused else 0) for mt in mats0)
+        fw_bytes = sum(main_bytes(mt) for mt in mats0)
         fw_ops = step_ops
     # The isolated replay includes each launch's dispatch gap, so its time per
     # step can exceed the kernel's share of the real step; the kernel's time
@@ -673,6 +709,9 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
                       if sw else "bitlinear_forward_batched (gemm_mfma_kernel)" if batched else
                       ("bitlinear_rmsnorm_quant_forward (gemv_lds_kernel, RMSNorm + bf16 prologue)" if norm else
                        "bitlinear_quant_forward (gemv_lds_kernel, bf16 prologue)") if fused else
+                      ("%s where m*k <= %d, else bitlinear_forward (gemv_lds_kernel)" % (
+                          "bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward",
+                          FUSED_MAX_MK[variant])) if mixed else
                       "bitlinear_forward_lut (gemv_lut_kernel)" if lut else "bitlinear_forward (gemv_lds_kernel)")
     mode_entry = {"tensor128": "bitlinear_forward_tensor_act", "rowscale": "bitlinear_forward_rowscale",
                   "binary": "bitlinear_quant_forward_binary" if fused else "bitlinear_forward_binary"}
@@ -691,9 +730,11 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
             "2*M*2F*K" if batched else "2*ceil(F*K/4)+2*M*K+4K+8+4*M*F bytes" if fused else
             "2*ceil(F*K/4)+M*K+4M+8+4*M*F bytes")
     else:
+        fused_call = "ceil(N*K/4)+2*M*K+4K+4+4*M*N bytes" if norm else "ceil(N*K/4)+2*M*K+4+4*M*N bytes"
         roof["per_launch"] = "mean over the workload's matrices of %s" % (
-            "2*M*N*K" if batched else ("ceil(N*K/4)+2*M*K+4K+4+4*M*N bytes" if norm else "ceil(N*K/4)+2*M*K+4+4*M*N bytes")
-            if fused else "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
+            "2*M*N*K" if batched else fused_call if fused else
+            "%s (fused calls) or ceil(N*K/4)+M*K+4M+4+4*M*N bytes (the others)" % fused_call if mixed else
+            "ceil(N*K/4)+M*K+4M+4+4*M*N bytes")
     roof["timing"] = ("HIP events around %d graph replays of the kernel's %d launches per step%s" % (
         replays, len(dom_mats),
         "; their time per step (%.4f ms, dispatch gaps included) exceeds the step's, so the kernel's time per "
@@ -720,6 +761,9 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
                                              "bitlinear_forward") + "; others as plain"
              if sw else
              ("bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward") if fused else
+             ("%s where m*k <= %d; elsewhere %s + bitlinear_forward" % (
+                 "bitlinear_rmsnorm_quant_forward" if norm else "bitlinear_quant_forward", FUSED_MAX_MK[variant],
+                 "bitlinear_rmsnorm_quant_act" if norm else "bitlinear_quant_act")) if mixed else
              ("bitlinear_rmsnorm_quant_act + " if norm else "bitlinear_quant_act + ") +
              ("bitlinear_forward_batched" if batched else
               "bitlinear_forward_lut" if lut else "bitlinear_forward")))
@@ -739,7 +783,7 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
             "variant": variant,
             "entry_points": entry,
             "launch": ("hip graph, %d kernels per step" % (sum(
-                (1 if fused else 2) + (1 if mode == "tensor128" and
+                (1 if fz[mt.j] else 2) + (1 if mode == "tensor128" and
                                        blq.bitlinear_quant_act_tensor_workspace_bytes(m, mt.k) > 4 else 0)
                 for mt in mats0)) if not eager else "eager"),
             "cold_cache": "weights %.0f MB per step x %d replica(s)" % (
@@ -754,7 +798,7 @@ def measure(torch, blq, wl, m, reps, variant, fused, steps, warmup, eager, nz_fr
         "roofline": roof,
     }
     if q_ms is not None:
-        out["quant_kernel"] = {"avg_launch_us": round(q_ms / len(mats0) * 1e3, 3),
+        out["quant_kernel"] = {"avg_launch_us": round(q_ms / len(quant_mats) * 1e3, 3),
                                "gbs": round(step_quant_bytes / (q_ms * 1e-3) / 1e9, 1)}
     if batched:
         if nz_frac is not None:
@@ -820,7 +864,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="default workload without the decode measurements")
     ap.add_argument("--eager", action="store_true", help="launch the step without a HIP graph")
     ap.add_argument("--fused", action="store_true",
-                    help="decode: the fused quant + forward entry point at any m (default up to FUSED_MAX_M)")
+                    help="decode: the fused quant + forward entry point for every matrix (default: per matrix, one token or m*k within FUSED_MAX_MK)")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
     ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu", "lut") + MODES,
@@ -1036,8 +1080,8 @@ def summarize(args):
 
     --summarize KEY[:VARIANT] M STATS_CSV FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB KERNEL_PAT CMD...
     The algorithmic bytes are those of the dominant kernel bench.py times for
-    that workload and variant (fused quant + forward up to FUSED_MAX_M unless
-    the variant is lut)."""
+    that workload and variant: each matrix's forward call, fused with the
+    quantisation where the step's default fuses it (default_fused)."""
     key, m, stats, fetch, write, cfetch, cwrite, copy_mib, pat = args[:9]
     key, _, variant = key.partition(":")
     variant = variant or "plain"
@@ -1062,9 +1106,9 @@ def summarize(args):
         alg = sum(mode_forward_bytes(variant, m, mt.n, mt.k, variant == "binary" and m == 1)
                   for mt in wl.matrices) / len(wl.matrices)
     else:
-        per = fused_bytes if (fused_default(variant, m) and variant != "lut") else forward_bytes
-        alg = sum(per(m, mt.n, mt.k) + (4 * mt.k if variant == "rmsnorm" and fused_default(variant, m) else 0)
-                  for mt in wl.matrices) / len(wl.matrices)
+        fz = default_fused(wl, m, variant)
+        alg = sum((fused_bytes if f else forward_bytes)(m, mt.n, mt.k) + (4 * mt.k if variant == "rmsnorm" and f else 0)
+                  for f, mt in zip(fz, wl.matrices)) / len(wl.matrices)
     suffix = "" if variant == "plain" else "_" + variant
     sources = LUT_SOURCES if variant == "lut" else DECODE_SOURCES if m <= 16 else BATCHED_SOURCES
     out = {

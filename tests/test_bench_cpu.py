@@ -93,12 +93,24 @@ def test_counter_scaling(tmp_path):
 
 
 def test_fused_default_follows_the_measured_limits():
-    # the fused quant + forward entry is the step's default only where it was
-    # measured faster than quant + forward
-    assert [bench.fused_default("plain", m) for m in (1, 2, 3, 4, 8)] == [True, True, False, False, False]
-    assert [bench.fused_default("rmsnorm", m) for m in (1, 2, 3)] == [True, True, False]
+    # the fused quant + forward entry is the step's default, per matrix, only
+    # where it was measured faster than quant + forward: one token, or m * k
+    # values within the limit
+    assert bench.fused_default("plain", 1, 28672) and bench.fused_default("rmsnorm", 1, 28672)
+    assert [bench.fused_default("plain", m, 4096) for m in (2, 4, 8)] == [True, True, False]
+    assert [bench.fused_default("plain", m, 14336) for m in (2, 4)] == [True, False]
+    assert [bench.fused_default("plain", 4, k) for k in (2560, 6912, 14336)] == [True, True, False]
+    assert [bench.fused_default("rmsnorm", m, 2560) for m in (2, 4, 8)] == [True, True, False]
+    assert [bench.fused_default("rmsnorm", 2, k) for k in (4096, 6912, 14336)] == [True, True, False]
+    assert not bench.fused_default("plain", 17, 64)  # past the decode entry points' token limit
     for variant in ("swiglu", "lut", "binary", "tensor128", "rowscale"):
-        assert bench.fused_default(variant, 1) and not bench.fused_default(variant, 2)
+        assert bench.fused_default(variant, 1, 4096) and not bench.fused_default(variant, 2, 64)
+    # per matrix of the 8B stack: the k = 4096 matrices fused at 4 tokens, the down projection not
+    wl = synth.BY_KEY["l8b_decode"]
+    assert bench.default_fused(wl, 4, "plain") == tuple(mt.k == 4096 for mt in wl.matrices)
+    assert bench.default_fused(wl, 8, "plain") == (False,) * len(wl.matrices)
+    assert bench.default_fused(wl, 1, "lut") == (False,) * len(wl.matrices)
+    assert bench.default_fused(wl, 1, "swiglu") == (True,) * len(wl.matrices)
     # the fused call's algorithmic bytes: bf16 activations instead of codes and a'
     n, k, m = 4096, 14336, 4
     assert bench.fused_bytes(m, n, k) - bench.forward_bytes(m, n, k) == 2 * m * k - (m * k + 4 * m)
