@@ -178,6 +178,63 @@ __device__ __forceinline__ int token_group(int m) {
   return g;
 }
 
+// The wave's place in its token group, in scalar registers: every wave of a
+// group runs the same prologue code, so its indices cost no vector
+// instructions (each vector instruction of a prologue is paid by all waves
+// of the workgroup, four to a SIMD).
+struct TokenGroup {
+  int G;     // waves per token
+  int t;     // the wave's token
+  int w0;    // the group's first wave, t * G
+  int tt;    // the lane's thread index inside the group (vector)
+};
+
+template <int WAVES>
+__device__ __forceinline__ TokenGroup token_group_of(int m) {
+  TokenGroup g;
+  g.G = token_group<WAVES>(m);
+  const int lg = __builtin_ctz(static_cast<unsigned>(g.G));
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  g.t = wave >> lg;
+  g.w0 = g.t << lg;
+  g.tt = static_cast<int>(threadIdx.x) - 64 * g.w0;
+  return g;
+}
+
+__device__ __forceinline__ unsigned max4(const uint4& v) { return max(max(v.x, v.y), max(v.z, v.w)); }
+
+// max of the wave slots [w0, w0 + G) of one token group (G a power of two up
+// to 16, w0 a multiple of G, both wave-uniform: one branch runs, with
+// 16-byte slot reads)
+__device__ __forceinline__ unsigned group_slot_max(const unsigned* slots, int w0, int G) {
+  const uint4* p = reinterpret_cast<const uint4*>(slots + w0);
+  if (G == 16) return max(max(max4(p[0]), max4(p[1])), max(max4(p[2]), max4(p[3])));
+  if (G == 8) return max(max4(p[0]), max4(p[1]));
+  if (G == 4) return max4(p[0]);
+  if (G == 2) return max(slots[w0], slots[w0 + 1]);
+  return slots[w0];
+}
+
+// sum of the wave slots [w0, w0 + G) in wave order (the same order for every
+// token count), under the same conditions
+__device__ __forceinline__ double group_slot_sum(const double* slots, int w0, int G) {
+  const double* p = slots + w0;
+  double r = p[0];
+  if (G == 16) {
+#pragma unroll
+    for (int i = 1; i < 16; ++i) r += p[i];
+  } else if (G == 8) {
+#pragma unroll
+    for (int i = 1; i < 8; ++i) r += p[i];
+  } else if (G == 4) {
+#pragma unroll
+    for (int i = 1; i < 4; ++i) r += p[i];
+  } else if (G == 2) {
+    r += p[1];
+  }
+  return r;
+}
+
 __device__ __forceinline__ void prefetch_bf16(uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int m,
                                               int64_t k) {
   const int total = m * static_cast<int>(k / 8);
@@ -192,15 +249,13 @@ __device__ __forceinline__ void prefetch_bf16(uint4 (&cache)[kCachedChunks], con
 template <int WAVES>
 __device__ __forceinline__ void prefetch_bf16_group(uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int m,
                                                     int64_t k) {
-  const int G = token_group<WAVES>(m);
-  const int t = (threadIdx.x >> 6) / G;
-  const int tt = static_cast<int>(threadIdx.x) - 64 * G * t;
+  const TokenGroup g = token_group_of<WAVES>(m);
   const int cpr = static_cast<int>(k / 8);
-  const uint4* row = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t < m ? t : 0) * k);
+  const uint4* row = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(g.t < m ? g.t : 0) * k);
 #pragma unroll
   for (int j = 0; j < kCachedChunks; ++j) {
-    const int c = tt + j * 64 * G;
-    cache[j] = (t < m && c < cpr) ? row[c] : make_uint4(0, 0, 0, 0);
+    const int c = g.tt + j * 64 * g.G;
+    cache[j] = (g.t < m && c < cpr) ? row[c] : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -273,10 +328,8 @@ __device__ void stage_bf16_group(int8_t* xs, int pitch, float* amax_s, unsigned*
                                  const uint4 (&cache)[kCachedChunks], const uint16_t* __restrict__ x, int m, int64_t k,
                                  int kpad, int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
   const bool write_out = xq_out != nullptr && blockIdx.x == 0;
-  const int G = token_group<WAVES>(m);
-  const int wave = threadIdx.x >> 6;
-  const int t = wave / G;
-  const int tt = static_cast<int>(threadIdx.x) - 64 * G * t;
+  const TokenGroup g = token_group_of<WAVES>(m);
+  const int G = g.G, t = g.t, tt = g.tt;
   const int step = 64 * G;
   const bool active = t < m;
   const int cpr = static_cast<int>(k / 8);
@@ -287,12 +340,9 @@ __device__ void stage_bf16_group(int8_t* xs, int pitch, float* amax_s, unsigned*
     for (int c = tt; c < cpr; c += step, ++j) mx = max(mx, chunk_absmax(j < kCachedChunks ? cached(cache, j) : row[c]));
   mx = wave_max(mx);
   if (G > 1) {  // uniform: m is the same for the whole workgroup
-    if ((threadIdx.x & 63) == 0) wmax_s[wave] = mx;
+    if ((threadIdx.x & 63) == 0) wmax_s[threadIdx.x >> 6] = mx;
     lds_barrier();
-    const int w0 = t * G;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w)
-      if (w >= w0 && w < w0 + G) mx = max(mx, wmax_s[w]);
+    mx = group_slot_max(wmax_s, g.w0, G);
   }
   if (!active) return;
   const float a = fmaxf(bf16_to_f32(mx), 1e-8f);
@@ -437,14 +487,12 @@ __device__ __forceinline__ void prefetch_gain(float4 (&gc)[kCachedChunks][2], co
 template <int WAVES>
 __device__ __forceinline__ void prefetch_gain_group(float4 (&gc)[kCachedChunks][2], const float* __restrict__ gain, int m,
                                                     int64_t k) {
-  const int G = token_group<WAVES>(m);
-  const int t = (threadIdx.x >> 6) / G;
-  const int tt = static_cast<int>(threadIdx.x) - 64 * G * t;
+  const TokenGroup g = token_group_of<WAVES>(m);
   const int cpr = static_cast<int>(k / 8);
 #pragma unroll
   for (int j = 0; j < kCachedChunks; ++j) {
-    const int c = tt + j * 64 * G;
-    if (gain && t < m && c < cpr) {
+    const int c = g.tt + j * 64 * g.G;
+    if (gain && g.t < m && c < cpr) {
       gc[j][0] = *reinterpret_cast<const float4*>(gain + c * 8);
       gc[j][1] = *reinterpret_cast<const float4*>(gain + c * 8 + 4);
     } else {
@@ -558,10 +606,8 @@ __device__ void stage_bf16_norm_group(int8_t* xs, int pitch, float* amax_s, floa
                                       const float* __restrict__ gain, float eps, int m, int64_t k, int kpad,
                                       int8_t* __restrict__ xq_out, float* __restrict__ amax_out) {
   const bool write_out = xq_out != nullptr && blockIdx.x == 0;
-  const int G = token_group<WAVES>(m);
-  const int wave = threadIdx.x >> 6;
-  const int t = wave / G;
-  const int tt = static_cast<int>(threadIdx.x) - 64 * G * t;
+  const TokenGroup g = token_group_of<WAVES>(m);
+  const int G = g.G, t = g.t, tt = g.tt;
   const int step = 64 * G;
   const bool active = t < m;
   const int cpr = static_cast<int>(k / 8);
@@ -590,21 +636,13 @@ __device__ void stage_bf16_norm_group(int8_t* xs, int pitch, float* amax_s, floa
   ss = wave_sum_d(ss);
   if (G > 1) {  // uniform: m is the same for the whole workgroup
     if ((threadIdx.x & 63) == 0) {
-      wmax_s[wave] = mx;
-      wss_s[wave] = ss;
+      wmax_s[threadIdx.x >> 6] = mx;
+      wss_s[threadIdx.x >> 6] = ss;
     }
     lds_barrier();
-    const int w0 = t * G;  // < WAVES for every wave, active or not
-    unsigned mall = 0;
-    double sall = 0.0;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w)
-      if (w >= w0 && w < w0 + G) {
-        mall = max(mall, wmax_s[w]);
-        sall += wss_s[w];
-      }
-    mx = mall;
-    ss = sall;
+    // (w0 < WAVES for every wave, active or not)
+    mx = group_slot_max(wmax_s, g.w0, G);
+    ss = group_slot_sum(wss_s, g.w0, G);
   }
   if (!active) return;
   float ap, qs;
@@ -860,9 +898,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   __shared__ int red[WAVES * 4 * 64];
   __shared__ float amax_s[16];
   __shared__ float quant_s[SRC == kFromBf16Norm ? 16 : 1];
-  __shared__ double wss_s[SRC == kFromBf16Norm ? WAVES : 1];
+  __shared__ __attribute__((aligned(16))) double wss_s[SRC == kFromBf16Norm ? WAVES : 1];
   __shared__ unsigned max_s[16];
-  __shared__ unsigned wmax_s[WAVES];
+  __shared__ __attribute__((aligned(16))) unsigned wmax_s[WAVES];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
