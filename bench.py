@@ -109,13 +109,15 @@ MODES = ("tensor128", "rowscale", "binary")
 # GEMV prologue) is chosen per matrix: always for one token; for more tokens
 # where m * k is at most FUSED_MAX_MK values.  Every workgroup re-quantises
 # all m tokens, so the fusion saves a launch but adds m * k of redundant
-# prologue work.  Measured per shape (us per call, fused / quant + forward,
-# one box): plain 4096 x 4096 at m = 2 / 4 / 8 4.59 / 5.63, 5.36 / 5.65,
-# 6.56 / 6.03; 2560 x 6912 at m = 4 6.61 / 6.47; 4096 x 14336 at m = 2 7.86 /
-# 8.37, at m = 4 10.37 / 8.87.  RMSNorm: 2560 x 6912 at m = 2 6.64 / 6.94;
-# 6144 x 4096 at m = 4 9.41 / 7.16; 4096 x 14336 at m = 2 10.44 / 9.38.  The
-# SwiGLU block and the variant modes: one token only.
-FUSED_MAX_MK = {"plain": 28672, "rmsnorm": 13824}
+# prologue work.  Plain, stack GB/s on one box: the 8B stack at m = 8 with
+# its 4096-wide matrices fused (m * k = 32768) 1722 against 1645 unfused; at
+# m = 4 with the 14336-wide down projection fused as well (57344) 1849
+# against 1858; the 2B stack at m = 8 with its 6912-wide down projection
+# fused (55296) 748 against 765.  RMSNorm, us per call (fused / quant +
+# forward): 2560 x 6912 at m = 2 6.64 / 6.94; 6144 x 4096 at m = 4 9.41 /
+# 7.16; 4096 x 14336 at m = 2 10.44 / 9.38.  The SwiGLU block and the variant
+# modes: one token only.
+FUSED_MAX_MK = {"plain": 32768, "rmsnorm": 13824}
 FUSED_MAX_M = 16  # the decode entry points' token limit
 
 
@@ -867,6 +869,8 @@ def main():
                     help="decode: the fused quant + forward entry point for every matrix (default: per matrix, one token or m*k within FUSED_MAX_MK)")
     ap.add_argument("--unfused", action="store_true",
                     help="decode: bitlinear_quant_act + bitlinear_forward instead of bitlinear_quant_forward")
+    ap.add_argument("--fused-max-mk", type=int, default=None, metavar="N",
+                    help="decode: fuse the quantisation where m * k <= N (plain and RMSNorm; default FUSED_MAX_MK)")
     ap.add_argument("--variant", default="plain", choices=("plain", "rmsnorm", "swiglu", "lut") + MODES,
                     help="rmsnorm: every BitLinear normalises its input first (per-channel gains); "
                          "swiglu: the feed-forward block as a unit (RMSNorm, gate+up with the SwiGLU fused, "
@@ -881,6 +885,9 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
                     help="CPU only: write profiles/ summaries from rocprofv3 CSVs (see summarize())")
     args = ap.parse_args()
+    if args.fused_max_mk is not None:
+        for v in FUSED_MAX_MK:
+            FUSED_MAX_MK[v] = args.fused_max_mk
     if args.summarize:
         summarize(args.summarize)
         return

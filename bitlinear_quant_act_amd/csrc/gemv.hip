@@ -106,26 +106,47 @@ __device__ __forceinline__ uint32_t quant_code(uint32_t bits16, float s) {
   return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
 }
 
-// 8 bf16 values (one 16-byte chunk) -> 8 codes (two words)
-__device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    lo |= quant_code(w[q] & 0xffffu, s) << (16 * q);
-    lo |= quant_code(w[q] >> 16, s) << (16 * q + 8);
-    hi |= quant_code(w[q + 2] & 0xffffu, s) << (16 * q);
-    hi |= quant_code(w[q + 2] >> 16, s) << (16 * q + 8);
-  }
-  return make_uint2(lo, hi);
+// The code of a value v of a token with scale s = 127 / a', a' >= max|x|,
+// as the bit pattern of fl(fl(v s) + 1.5 * 2^23).  |fl(v s)| rounds to at
+// most 127, so the clamp to [-127, 127] never binds; in [2^23, 2^24) floats
+// are the integers, so the sum is 1.5 * 2^23 + rint(v s) (ties to even, the
+// default rounding), and its low byte is rint(v s) in two's complement.
+// Two operations per value instead of a round, a clamp and a conversion.
+__device__ __forceinline__ uint32_t code_bits(float v, float s) {
+  return __float_as_uint(__fadd_rn(__fmul_rn(v, s), 12582912.0f));
 }
 
-__device__ __forceinline__ unsigned chunk_absmax(const uint4& v) {
+// the low bytes of four words, in order, as one word
+__device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // b0.byte0, b1.byte0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);               // lo.byte0-1, hi.byte0-1
+}
+
+// 8 bf16 values (one 16-byte chunk) -> 8 codes (two words); value 2q of a
+// chunk is the low half of word q, value 2q + 1 its high half
+__device__ __forceinline__ uint2 quant_chunk(const uint4& v, float s) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  unsigned mx = 0;
+  uint32_t b[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) mx = max(mx, max(w[q] & 0x7fffu, (w[q] >> 16) & 0x7fffu));
-  return mx;
+  for (int q = 0; q < 4; ++q) {
+    b[2 * q] = code_bits(__uint_as_float(w[q] << 16), s);
+    b[2 * q + 1] = code_bits(__uint_as_float(w[q] & 0xffff0000u), s);
+  }
+  return make_uint2(low_bytes(b[0], b[1], b[2], b[3]), low_bytes(b[4], b[5], b[6], b[7]));
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// max |x| of a chunk as a bf16 bit pattern (sign cleared: the patterns of
+// non-negative values order like the values), two halves per packed 16-bit max
+__device__ __forceinline__ unsigned chunk_absmax(const uint4& v) {
+  const u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7fff7fffu);
+  const u16x2 b = __builtin_bit_cast(u16x2, v.y & 0x7fff7fffu);
+  const u16x2 c = __builtin_bit_cast(u16x2, v.z & 0x7fff7fffu);
+  const u16x2 d = __builtin_bit_cast(u16x2, v.w & 0x7fff7fffu);
+  const u16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max(static_cast<unsigned>(mx.x), static_cast<unsigned>(mx.y));
 }
 
 __device__ __forceinline__ unsigned wave_max(unsigned v) { return wave_max_u32(v); }
@@ -156,13 +177,13 @@ __device__ __forceinline__ void prefetch_codes(uint4 (&cache)[kCachedChunks], co
   const int cpr = kpad / 16;
 #pragma unroll
   for (int j = 0; j < kCachedChunks; ++j) {
+    // every thread requests every chunk (a chunk past the codes reads chunk 0,
+    // and stage_codes stores zeros for it), so later waits count exactly
     const int c = threadIdx.x + j * static_cast<int>(blockDim.x);
-    cache[j] = make_uint4(0, 0, 0, 0);
-    if (c < m * cpr) {
-      const int t = c / cpr;
-      const int64_t col = static_cast<int64_t>(c - t * cpr) * 16;
-      if (col < k) cache[j] = *reinterpret_cast<const uint4*>(xq + t * k + col);
-    }
+    const int t = c / cpr;
+    const int64_t col = static_cast<int64_t>(c - t * cpr) * 16;
+    const bool ok = c < m * cpr && col < k;
+    cache[j] = *reinterpret_cast<const uint4*>(xq + (ok ? t * k + col : 0));
   }
 }
 
@@ -264,16 +285,35 @@ __device__ void stage_codes(int8_t* xs, int pitch, const uint4 (&cache)[kCachedC
   const int nthreads = blockDim.x;
   if (vec) {  // k % 16 == 0 and xq 16-byte aligned
     const int cpr = kpad / 16;
-    int j = 0;
-    for (int c = threadIdx.x; c < m * cpr; c += nthreads, ++j) {
+    const int total = m * cpr;
+    // chunk c = threadIdx.x + j * nthreads: the first kCachedChunks are in
+    // registers already and are stored on every path (so none of their
+    // requests is moved behind the weight tiles); the rest are requested
+    // kCachedChunks at a time and then stored, one wait per batch instead of
+    // one per chunk
+    auto store = [&](int j, const uint4& v) {
+      const int c = threadIdx.x + j * nthreads;
       const int t = c / cpr, cc = c - t * cpr;
-      const int64_t col = static_cast<int64_t>(cc) * 16;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < kCachedChunks)
-        v = cached(cache, j);
-      else if (col < k)
-        v = *reinterpret_cast<const uint4*>(xq + t * k + col);
-      *reinterpret_cast<uint4*>(xs + t * pitch + cc * 16) = v;
+      const bool ok = c < total && static_cast<int64_t>(cc) * 16 < k;
+      if (c < total) *reinterpret_cast<uint4*>(xs + t * pitch + cc * 16) = ok ? v : make_uint4(0, 0, 0, 0);
+    };
+#pragma unroll
+    for (int q = 0; q < kCachedChunks; ++q) store(q, cache[q]);
+    for (int j0 = kCachedChunks; j0 * nthreads < total; j0 += kCachedChunks) {
+      uint4 v[kCachedChunks];
+#pragma unroll
+      for (int q = 0; q < kCachedChunks; ++q) {
+        const int c = threadIdx.x + (j0 + q) * nthreads;
+        const int t = c / cpr, cc = c - t * cpr;
+        const int64_t col = static_cast<int64_t>(cc) * 16;
+        v[q] = *reinterpret_cast<const uint4*>(xq + (c < total && col < k ? t * k + col : 0));
+      }
+#pragma unroll
+      for (int q = 0; q < kCachedChunks; ++q) store(j0 + q, v[q]);
+      // everything requested so far has landed (the batch came last); said
+      // explicitly, so that the code after the loop need not assume a batch
+      // request may still write its registers
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only (gfx9 encoding)
     }
   } else {
     for (int c = threadIdx.x; c < m * kpad; c += nthreads) {
@@ -892,7 +932,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
                                                               const float* __restrict__ gain, float eps,
                                                               const uint4* __restrict__ packed_u,
                                                               const float* __restrict__ gamma_u) {
-  static_assert(!SWIGLU || WAVES >= 4, "one token group per wave in the SwiGLU epilogue");
+  static_assert(WAVES >= 4, "one token group per wave in the epilogues (waves 0-3)");
   static_assert(WB == 2 || !SWIGLU, "binary weights: plain epilogue only");
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ int red[WAVES * 4 * 64];
@@ -922,8 +962,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   else if (SRC == kFromBf16Norm && VEC && MULTI && m <= WAVES)
     prefetch_gain_group<WAVES>(gcache, gain, m, k);
   if (VEC) {
-    if (SRC == kFromCodes)
+    if (SRC == kFromCodes) {
       prefetch_codes(cache, static_cast<const int8_t*>(xsrc), m, k, kpad);
+      __builtin_amdgcn_sched_barrier(0);  // the codes are requested before the weight tiles
+    }
     else if (SRC == kFromF32)
       prefetch_f32(cache, static_cast<const float*>(xsrc), m, k);
     else if ((SRC == kFromBf16 && !MULTI) || m == 1)  // thread-major; unconditional without MULTI
@@ -933,10 +975,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
   }
   uint4 wcur[U];
   load_item<WAVES, U, SWIGLU, WB>(wcur, packed, packed_u, rb, c, kt_count, kt_real, wave, lane, rb < rb_count);
+  // codes input: a' of the token this lane scales in the epilogue (token
+  // 4g + wave, waves 0-3), into a register.  Only the epilogue waits for it,
+  // by which time the first weight tiles, requested before it, have landed;
+  // staged through LDS it would hold the prologue barrier, and with it the
+  // next item's request, until those tiles arrive.  Every lane requests one
+  // (clamped) a', so the request count is the same on every path and the
+  // prologue's waits stay exact.
+  float a_lane = 0.0f;
+  if (SRC == kFromCodes) {
+    const int ta = 4 * g + (wave & 3);
+    a_lane = amax_in[(ta < m ? ta : m - 1) * dq.astride];
+  }
 
   if (SRC == kFromCodes) {
     stage_codes(xs, pitch, cache, static_cast<const int8_t*>(xsrc), m, k, kpad, VEC);
-    if (threadIdx.x < m) amax_s[threadIdx.x] = amax_in[threadIdx.x * dq.astride];
   } else if (SRC == kFromBf16Norm && VEC && m == 1) {
     stage_bf16_norm_single<WAVES>(xs, amax_s, quant_s, wmax_s, wss_s, cache, gcache, static_cast<const uint16_t*>(xsrc),
                                   gain, eps, k, kpad, xq_out, amax_out);
@@ -1020,8 +1073,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
         if (t < m && row < n) {
           vg >>= kWeightShift;  // exact: the sums are multiples of 64
           vu >>= kWeightShift;
-          const float gv = static_cast<float>(vg) * (gamma * amax_s[t] / 127.0f);
-          const float uv = static_cast<float>(vu) * (gamma_up * amax_s[t] / 127.0f);
+          const float at = SRC == kFromCodes ? a_lane : amax_s[t];
+          const float gv = static_cast<float>(vg) * (gamma * at / 127.0f);
+          const float uv = static_cast<float>(vu) * (gamma_up * at / 127.0f);
           y[t * n + row] = gv * uv / (1.0f + expf(-gv));
           if (acc_out) {
             acc_out[t * 2 * n + row] = vg;
@@ -1046,7 +1100,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_lds_kernel(const uint4* __res
         if (t < m && row < n) {
           v >>= kWeightShift;  // exact: the sum is a multiple of 64
           const float ws = dq.row_scale ? half_bits_to_float(dq.row_scale[row]) : gamma;
-          const float scale = ws * amax_s[t] / dq.qdiv;
+          const float scale = ws * (SRC == kFromCodes ? a_lane : amax_s[t]) / dq.qdiv;
           y[t * n + row] = static_cast<float>(v) * scale;
           if (acc_out) acc_out[t * n + row] = v;
         }

@@ -97,7 +97,7 @@ def test_fused_default_follows_the_measured_limits():
     # where it was measured faster than quant + forward: one token, or m * k
     # values within the limit
     assert bench.fused_default("plain", 1, 28672) and bench.fused_default("rmsnorm", 1, 28672)
-    assert [bench.fused_default("plain", m, 4096) for m in (2, 4, 8)] == [True, True, False]
+    assert [bench.fused_default("plain", m, 4096) for m in (2, 4, 8, 9)] == [True, True, True, False]
     assert [bench.fused_default("plain", m, 14336) for m in (2, 4)] == [True, False]
     assert [bench.fused_default("plain", 4, k) for k in (2560, 6912, 14336)] == [True, True, False]
     assert [bench.fused_default("rmsnorm", m, 2560) for m in (2, 4, 8)] == [True, True, False]
@@ -105,10 +105,11 @@ def test_fused_default_follows_the_measured_limits():
     assert not bench.fused_default("plain", 17, 64)  # past the decode entry points' token limit
     for variant in ("swiglu", "lut", "binary", "tensor128", "rowscale"):
         assert bench.fused_default(variant, 1, 4096) and not bench.fused_default(variant, 2, 64)
-    # per matrix of the 8B stack: the k = 4096 matrices fused at 4 tokens, the down projection not
+    # per matrix of the 8B stack: the k = 4096 matrices fused at 4 and 8 tokens, the down projection not
     wl = synth.BY_KEY["l8b_decode"]
-    assert bench.default_fused(wl, 4, "plain") == tuple(mt.k == 4096 for mt in wl.matrices)
-    assert bench.default_fused(wl, 8, "plain") == (False,) * len(wl.matrices)
+    for m in (4, 8):
+        assert bench.default_fused(wl, m, "plain") == tuple(mt.k == 4096 for mt in wl.matrices)
+    assert bench.default_fused(wl, 16, "plain") == (False,) * len(wl.matrices)
     assert bench.default_fused(wl, 1, "lut") == (False,) * len(wl.matrices)
     assert bench.default_fused(wl, 1, "swiglu") == (True,) * len(wl.matrices)
     # the fused call's algorithmic bytes: bf16 activations instead of codes and a'
